@@ -1,0 +1,117 @@
+"""fp64 CPU oracle for the gated delta rule (Kimi Delta Attention).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The product path
+(``gated_delta_rule_08_amd``) never imports it, and the two share no code: the
+oracle is the plain sequential recurrence in ``kda_oracle.c`` (see the header
+of that file for the passages of the pages each step follows), built with gcc.
+
+Every function here takes numpy arrays, upcasts them to float64 (bf16 -> fp64
+and fp32 -> fp64 are exact) and calls the C recurrence.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "libkda_oracle.so")
+
+MODE_DELTA = 0       # gated delta rule (KDA / GDN / DeltaNet)
+MODE_ADDITIVE = 1    # delta term disabled: gated linear attention
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (plain -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                               _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.kda_oracle_run.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(ctypes.c_int32)] + \
+            [dp] * 8 + [ctypes.c_int]
+        lib.kda_oracle_run.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f64(x):
+    if x is None:
+        return None
+    try:
+        import torch  # tests hand over torch CPU tensors as well
+        if isinstance(x, torch.Tensor):
+            x = x.detach().to("cpu", torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def run(q, k, v, g, beta, cu_seqlens=None, s0=None, mode: int = MODE_DELTA,
+        nthreads: int | None = None):
+    """Sequential recurrence over packed sequences.
+
+    q, k, g: [T, H, dk]; v: [T, H, dv]; beta: [T, H]; cu_seqlens: [N+1] int
+    (default: one sequence of length T); s0: [N, H, dk, dv] or None (zero state).
+    Returns (o [T, H, dv], s_final [N, H, dk, dv]) as float64 arrays.
+    """
+    lib = _load()
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    assert k.shape == (T, H, dk) and g.shape == (T, H, dk)
+    assert v.shape == (T, H, dv) and beta.shape == (T, H)
+    if cu_seqlens is None:
+        cu = np.array([0, T], dtype=np.int32)
+    else:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    N = len(cu) - 1
+    assert cu[0] == 0 and cu[-1] == T and np.all(np.diff(cu) >= 0)
+    s0 = _f64(s0)
+    if s0 is not None:
+        assert s0.shape == (N, H, dk, dv)
+    o = np.zeros((T, H, dv), dtype=np.float64)
+    sf = np.zeros((N, H, dk, dv), dtype=np.float64)
+    if nthreads is None:
+        nthreads = min(16, os.cpu_count() or 1)
+    rc = lib.kda_oracle_run(int(mode), H, dk, dv, N,
+                            cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0),
+                            _ptr(o), _ptr(sf), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_run failed")
+    return o, sf
+
+
+def decode(q, k, v, g, beta, s):
+    """One token per sequence against the given states.
+
+    q, k, g: [B, H, dk]; v: [B, H, dv]; beta: [B, H]; s: [B, H, dk, dv].
+    Returns (o [B, H, dv], s_new [B, H, dk, dv]) in float64.  A decode step is
+    the recurrence run for one token with the state as the incoming state.
+    """
+    q, k, v, g, beta, s = map(_f64, (q, k, v, g, beta, s))
+    B = q.shape[0]
+    cu = np.arange(B + 1, dtype=np.int32)
+    return run(q, k, v, g, beta, cu_seqlens=cu, s0=s)
