@@ -1,0 +1,249 @@
+"""MI355X (gfx950) gated delta-rule / Kimi Delta Attention library: Python binding.
+
+A thin ctypes layer over ``libkda.so`` (the C ABI in ``include/kda.h``): every
+function has the C entry point's name, checks tensor shapes and dtypes, and
+passes device pointers and the current HIP stream.  All computation happens
+in the library's HIP kernels; PyTorch only supplies device memory and streams.
+If the library is missing the calls raise; there is no fallback.
+
+Build the library first:  ``python -m gated_delta_rule_08_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "KdaError", "load_library", "kda_abi_version", "kda_chunk_fwd", "kda_chunk_fwd_supported",
+    "kda_chunk_fwd_workspace_bytes", "kda_decode_step", "kda_state_init", "kda_state_load",
+    "kda_state_store", "KDA_READ_INITIAL_STATE", "KDA_WRITE_FINAL_STATE",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_OK = 0
+KDA_FP32, KDA_BF16 = 0, 1
+KDA_READ_INITIAL_STATE = 1
+KDA_WRITE_FINAL_STATE = 2
+_STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
+           3: "KDA_ERR_WORKSPACE_TOO_SMALL", 4: "KDA_ERR_HIP"}
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str | None = None):
+    """Load libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m gated_delta_rule_08_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, U32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+    SH = ctypes.POINTER(_Shape)
+    lib.kda_abi_version.restype = I32
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_chunk_fwd_supported.argtypes = [I32, I32, I32, I32]
+    lib.kda_chunk_fwd_supported.restype = I32
+    lib.kda_chunk_fwd_workspace_bytes.argtypes = [SH, I32, I32, I32]
+    lib.kda_chunk_fwd_workspace_bytes.restype = SZ
+    lib.kda_chunk_fwd.argtypes = [SH, I32, I32, I32, P, P, P, P, P, P, P, I32, P, U32, P, P, SZ, P]
+    lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_decode_step.argtypes = [SH, I32, P, P, P, P, P, P, I32, P, P, P]
+    lib.kda_decode_step.restype = ctypes.c_int
+    lib.kda_state_init.argtypes = [SH, P, I32, P]
+    lib.kda_state_init.restype = ctypes.c_int
+    lib.kda_state_load.argtypes = [SH, P, I32, P, I32, P, P]
+    lib.kda_state_load.restype = ctypes.c_int
+    lib.kda_state_store.argtypes = [SH, P, I32, P, I32, P, P]
+    lib.kda_state_store.restype = ctypes.c_int
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != KDA_OK:
+        raise KdaError(status, load_library().kda_last_error().decode())
+
+
+def _io_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_FP32
+    raise TypeError(f"q/k/v must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype) -> None:
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def kda_abi_version() -> int:
+    return int(load_library().kda_abi_version())
+
+
+def kda_chunk_fwd_supported(dk: int, dv: int, chunk: int, io_dtype: torch.dtype) -> bool:
+    code = KDA_BF16 if io_dtype == torch.bfloat16 else KDA_FP32
+    return bool(load_library().kda_chunk_fwd_supported(dk, dv, chunk, code))
+
+
+def kda_chunk_fwd_workspace_bytes(num_heads: int, dk: int, dv: int, io_dtype: torch.dtype,
+                                  chunk: int, total_tokens: int, num_seqs: int) -> int:
+    sh = _Shape(num_heads, dk, dv, KDA_BF16 if io_dtype == torch.bfloat16 else KDA_FP32)
+    return int(load_library().kda_chunk_fwd_workspace_bytes(ctypes.byref(sh), chunk,
+                                                            total_tokens, num_seqs))
+
+
+def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens, chunk: int = 64, states=None, state_slots=None,
+                  read_initial: bool = False, write_final: bool = False, o=None, workspace=None,
+                  stream=None):
+    """Chunked prefill over packed sequences (see kda_chunk_fwd in include/kda.h).
+
+    q, k, g: [T, H, dk]; v: [T, H, dv]; beta: [T, H]; cu_seqlens: int32 [N+1] on
+    the device; states: fp32 pool [S, H, dk, dv]; state_slots: int32 [N] or None.
+    Returns o [T, H, dv] in the dtype of q.  ``workspace`` (uint8, device) is
+    allocated here when not given.
+    """
+    lib = load_library()
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    io = _io_dtype(q)
+    _need(q, "q", (T, H, dk), q.dtype)
+    _need(k, "k", (T, H, dk), q.dtype)
+    _need(v, "v", (T, H, dv), q.dtype)
+    _need(g, "g", (T, H, dk), torch.float32)
+    _need(beta, "beta", (T, H), torch.float32)
+    N = cu_seqlens.numel() - 1
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32)
+    flags = (KDA_READ_INITIAL_STATE if read_initial else 0) | (KDA_WRITE_FINAL_STATE if write_final else 0)
+    num_slots = 0
+    if states is not None:
+        _need(states, "states", (states.shape[0], H, dk, dv), torch.float32)
+        num_slots = states.shape[0]
+    if state_slots is not None:
+        _need(state_slots, "state_slots", (N,), torch.int32)
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
+    else:
+        _need(o, "o", (T, H, dv), q.dtype)
+    sh = _Shape(H, dk, dv, io)
+    need = int(lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(sh), chunk, T, N))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.kda_chunk_fwd(ctypes.byref(sh), chunk, T, N, _ptr(cu_seqlens), _ptr(q), _ptr(k),
+                             _ptr(v), _ptr(g), _ptr(beta), _ptr(states), num_slots,
+                             _ptr(state_slots), flags, _ptr(o), _ptr(workspace), ws_bytes,
+                             _stream(stream)))
+    return o
+
+
+def kda_decode_step(q, k, v, g, beta, states, state_slots=None, o=None, stream=None):
+    """One token per sequence against resident states, updated in place.
+
+    q, k, g: [B, H, dk]; v: [B, H, dv]; beta: [B, H]; states: fp32 pool
+    [S, H, dk, dv]; state_slots: int32 [B] or None.  Returns o [B, H, dv].
+    """
+    lib = load_library()
+    B, H, dk = q.shape
+    dv = v.shape[2]
+    io = _io_dtype(q)
+    _need(q, "q", (B, H, dk), q.dtype)
+    _need(k, "k", (B, H, dk), q.dtype)
+    _need(v, "v", (B, H, dv), q.dtype)
+    _need(g, "g", (B, H, dk), torch.float32)
+    _need(beta, "beta", (B, H), torch.float32)
+    _need(states, "states", (states.shape[0], H, dk, dv), torch.float32)
+    if state_slots is not None:
+        _need(state_slots, "state_slots", (B,), torch.int32)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    else:
+        _need(o, "o", (B, H, dv), q.dtype)
+    sh = _Shape(H, dk, dv, io)
+    _check(lib.kda_decode_step(ctypes.byref(sh), B, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                               _ptr(beta), _ptr(states), states.shape[0], _ptr(state_slots),
+                               _ptr(o), _stream(stream)))
+    return o
+
+
+def _pool_shape(states):
+    _need(states, "states", tuple(states.shape), torch.float32)
+    if states.dim() != 4:
+        raise ValueError("states must be [num_slots, H, dk, dv]")
+    S, H, dk, dv = states.shape
+    return S, _Shape(H, dk, dv, KDA_FP32)
+
+
+def kda_state_init(states, stream=None):
+    """Zero a state pool [num_slots, H, dk, dv]."""
+    S, sh = _pool_shape(states)
+    _check(load_library().kda_state_init(ctypes.byref(sh), _ptr(states), S, _stream(stream)))
+    return states
+
+
+def kda_state_load(states, src, slots=None, stream=None):
+    """Copy dense src [n, H, dk, dv] into pool slots (slots[i], or i)."""
+    S, sh = _pool_shape(states)
+    n = src.shape[0]
+    _need(src, "src", (n,) + tuple(states.shape[1:]), torch.float32)
+    if slots is not None:
+        _need(slots, "slots", (n,), torch.int32)
+    _check(load_library().kda_state_load(ctypes.byref(sh), _ptr(states), S, _ptr(slots), n,
+                                         _ptr(src), _stream(stream)))
+    return states
+
+
+def kda_state_store(states, slots=None, n=None, dst=None, stream=None):
+    """Copy pool slots (slots[i], or i for i < n) into a dense [n, H, dk, dv] tensor."""
+    S, sh = _pool_shape(states)
+    if slots is not None:
+        n = slots.numel()
+        _need(slots, "slots", (n,), torch.int32)
+    if n is None:
+        n = S
+    if dst is None:
+        dst = torch.empty((n,) + tuple(states.shape[1:]), dtype=torch.float32, device=states.device)
+    else:
+        _need(dst, "dst", (n,) + tuple(states.shape[1:]), torch.float32)
+    _check(load_library().kda_state_store(ctypes.byref(sh), _ptr(states), S, _ptr(slots), n,
+                                          _ptr(dst), _stream(stream)))
+    return dst

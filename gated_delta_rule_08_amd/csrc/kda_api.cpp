@@ -1,0 +1,231 @@
+// kda_api.cpp -- the C ABI of libkda.so: host-side validation and dispatch.
+//
+// Every entry point validates its arguments before anything is enqueued; on
+// any error it returns a status, records a message for kda_last_error() and
+// writes nothing.  The library allocates no device memory.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kda_common.h"
+
+namespace kda {
+
+// launchers defined next to their kernels
+kda_status_t launch_state_init(float* states, size_t n_floats, hipStream_t stream);
+kda_status_t launch_state_copy(bool to_pool, float* states, int32_t num_slots,
+                               const int32_t* slots, int32_t n, float* dense,
+                               size_t per_state_floats, hipStream_t stream);
+bool decode_supported(int dk, int dv);
+kda_status_t launch_decode(const kda_shape_t* sh, int32_t batch, const void* q, const void* k,
+                           const void* v, const float* g, const float* beta, float* states,
+                           int32_t num_slots, const int32_t* slots, void* o, hipStream_t stream);
+bool chunk_small_supported(int dk, int dv, int chunk);
+kda_status_t launch_chunk_small(const kda_shape_t* sh, int32_t chunk, int32_t T, int32_t N,
+                                const int32_t* cu, const void* q, const void* k, const void* v,
+                                const float* g, const float* beta, float* states,
+                                int32_t num_slots, const int32_t* slots, uint32_t flags, void* o,
+                                hipStream_t stream);
+bool chunk_mfma_supported(int dk, int dv, int chunk, int io_dtype);
+size_t chunk_mfma_workspace_bytes(int H, int32_t T, int32_t N);
+kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, const int32_t* cu,
+                               const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, float* states, int32_t num_slots,
+                               const int32_t* slots, uint32_t flags, void* o, void* workspace,
+                               hipStream_t stream);
+
+namespace {
+thread_local char g_last_error[512] = "";
+}
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+}
+
+kda_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return KDA_OK;
+  set_error("%s: %s", what, hipGetErrorString(e));
+  return KDA_ERR_HIP;
+}
+
+kda_status_t check_launch(const char* what) { return hip_status(hipGetLastError(), what); }
+
+namespace {
+
+kda_status_t invalid(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return KDA_ERR_INVALID_ARGUMENT;
+}
+
+kda_status_t unsupported(const char* what, const kda_shape_t* sh, int chunk) {
+  set_error("%s: unsupported (dk=%d, dv=%d, chunk=%d, io_dtype=%d)", what, sh->dk, sh->dv, chunk,
+            sh->io_dtype);
+  return KDA_ERR_UNSUPPORTED;
+}
+
+kda_status_t check_shape(const kda_shape_t* sh, const char* what) {
+  if (!sh) return invalid("%s: shape is NULL", what);
+  if (sh->num_heads <= 0) return invalid("%s: num_heads must be >= 1 (got %d)", what, sh->num_heads);
+  if (sh->dk <= 0 || sh->dv <= 0) return invalid("%s: dk and dv must be >= 1", what);
+  if (sh->io_dtype != KDA_FP32 && sh->io_dtype != KDA_BF16)
+    return invalid("%s: io_dtype must be KDA_FP32 or KDA_BF16 (got %d)", what, sh->io_dtype);
+  return KDA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool chunk_supported(const kda_shape_t* sh, int chunk) {
+  return chunk_mfma_supported(sh->dk, sh->dv, chunk, sh->io_dtype) ||
+         chunk_small_supported(sh->dk, sh->dv, chunk);
+}
+
+}  // namespace
+}  // namespace kda
+
+using namespace kda;
+
+extern "C" {
+
+int32_t kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_string(kda_status_t s) {
+  switch (s) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_WORKSPACE_TOO_SMALL: return "KDA_ERR_WORKSPACE_TOO_SMALL";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+  }
+  return "KDA_ERR_UNKNOWN";
+}
+
+const char* kda_last_error(void) { return g_last_error; }
+
+int32_t kda_chunk_fwd_supported(int32_t dk, int32_t dv, int32_t chunk, int32_t io_dtype) {
+  if (io_dtype != KDA_FP32 && io_dtype != KDA_BF16) return 0;
+  return (chunk_mfma_supported(dk, dv, chunk, io_dtype) || chunk_small_supported(dk, dv, chunk))
+             ? 1 : 0;
+}
+
+size_t kda_chunk_fwd_workspace_bytes(const kda_shape_t* sh, int32_t chunk, int32_t total_tokens,
+                                     int32_t num_seqs) {
+  if (!sh || sh->num_heads <= 0 || total_tokens < 0 || num_seqs < 0) return 0;
+  if (chunk_mfma_supported(sh->dk, sh->dv, chunk, sh->io_dtype))
+    return chunk_mfma_workspace_bytes(sh->num_heads, total_tokens, num_seqs);
+  return 0;
+}
+
+kda_status_t kda_chunk_fwd(const kda_shape_t* sh, int32_t chunk, int32_t total_tokens,
+                           int32_t num_seqs, const int32_t* cu_seqlens, const void* q,
+                           const void* k, const void* v, const float* g, const float* beta,
+                           float* states, int32_t num_slots, const int32_t* state_slots,
+                           uint32_t flags, void* o, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  const char* W = "kda_chunk_fwd";
+  kda_status_t st = check_shape(sh, W);
+  if (st != KDA_OK) return st;
+  if (total_tokens < 0 || num_seqs < 0)
+    return invalid("%s: total_tokens and num_seqs must be >= 0", W);
+  if (flags & ~(uint32_t)(KDA_READ_INITIAL_STATE | KDA_WRITE_FINAL_STATE))
+    return invalid("%s: unknown flag bits 0x%x", W, flags);
+  if (chunk <= 0) return invalid("%s: chunk must be >= 1 (got %d)", W, chunk);
+  if (!chunk_supported(sh, chunk)) return unsupported(W, sh, chunk);
+  if (total_tokens == 0 || num_seqs == 0) return KDA_OK;
+  if (!cu_seqlens) return invalid("%s: cu_seqlens is NULL", W);
+  if (!q || !k || !v || !g || !beta || !o) return invalid("%s: a tensor pointer is NULL", W);
+  if (flags != 0) {
+    if (!states) return invalid("%s: states is NULL but flags request state I/O", W);
+    if (num_slots <= 0) return invalid("%s: num_slots must be >= 1 with state I/O", W);
+    if (!state_slots && num_slots < num_seqs)
+      return invalid("%s: num_slots (%d) < num_seqs (%d) with implicit slots", W, num_slots,
+                     num_seqs);
+  }
+  const size_t esz = sh->io_dtype == KDA_BF16 ? 2 : 4;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, esz) ||
+      !aligned(g, 16) || !aligned(beta, 4) || (states && !aligned(states, 16)))
+    return invalid("%s: q, k, v, g, states must be 16-byte aligned", W);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (chunk_mfma_supported(sh->dk, sh->dv, chunk, sh->io_dtype)) {
+    const size_t need = chunk_mfma_workspace_bytes(sh->num_heads, total_tokens, num_seqs);
+    if (!workspace || workspace_bytes < need) {
+      set_error("%s: workspace of %zu bytes needed, %zu given", W, need, workspace_bytes);
+      return KDA_ERR_WORKSPACE_TOO_SMALL;
+    }
+    if (!aligned(workspace, 256)) return invalid("%s: workspace must be 256-byte aligned", W);
+    return launch_chunk_mfma(sh, total_tokens, num_seqs, cu_seqlens, q, k, v, g, beta, states,
+                             num_slots, state_slots, flags, o, workspace, s);
+  }
+  return launch_chunk_small(sh, chunk, total_tokens, num_seqs, cu_seqlens, q, k, v, g, beta,
+                            flags ? states : nullptr, num_slots, state_slots, flags, o, s);
+}
+
+kda_status_t kda_decode_step(const kda_shape_t* sh, int32_t batch, const void* q, const void* k,
+                             const void* v, const float* g, const float* beta, float* states,
+                             int32_t num_slots, const int32_t* state_slots, void* o,
+                             void* stream) {
+  const char* W = "kda_decode_step";
+  kda_status_t st = check_shape(sh, W);
+  if (st != KDA_OK) return st;
+  if (batch < 0) return invalid("%s: batch must be >= 0", W);
+  if (!decode_supported(sh->dk, sh->dv)) return unsupported(W, sh, 0);
+  if (batch == 0) return KDA_OK;
+  if (!q || !k || !v || !g || !beta || !o || !states)
+    return invalid("%s: a tensor pointer is NULL", W);
+  if (num_slots <= 0) return invalid("%s: num_slots must be >= 1", W);
+  if (!state_slots && num_slots < batch)
+    return invalid("%s: num_slots (%d) < batch (%d) with implicit slots", W, num_slots, batch);
+  if (!aligned(states, 16)) return invalid("%s: states must be 16-byte aligned", W);
+  return launch_decode(sh, batch, q, k, v, g, beta, states, num_slots, state_slots, o,
+                       static_cast<hipStream_t>(stream));
+}
+
+kda_status_t kda_state_init(const kda_shape_t* sh, float* states, int32_t num_slots,
+                            void* stream) {
+  const char* W = "kda_state_init";
+  kda_status_t st = check_shape(sh, W);
+  if (st != KDA_OK) return st;
+  if (num_slots < 0) return invalid("%s: num_slots must be >= 0", W);
+  if (num_slots == 0) return KDA_OK;
+  if (!states) return invalid("%s: states is NULL", W);
+  const size_t per = (size_t)sh->num_heads * sh->dk * sh->dv;
+  if (per % 4 != 0 || !aligned(states, 16))
+    return invalid("%s: H*dk*dv must be a multiple of 4 and states 16-byte aligned", W);
+  return launch_state_init(states, per * (size_t)num_slots, static_cast<hipStream_t>(stream));
+}
+
+static kda_status_t state_copy(const char* W, bool to_pool, const kda_shape_t* sh, float* states,
+                               int32_t num_slots, const int32_t* slots, int32_t n, float* dense,
+                               void* stream) {
+  kda_status_t st = check_shape(sh, W);
+  if (st != KDA_OK) return st;
+  if (n < 0 || num_slots < 0) return invalid("%s: n and num_slots must be >= 0", W);
+  if (n == 0) return KDA_OK;
+  if (!states || !dense) return invalid("%s: states or dense buffer is NULL", W);
+  if (!slots && num_slots < n)
+    return invalid("%s: num_slots (%d) < n (%d) with implicit slots", W, num_slots, n);
+  const size_t per = (size_t)sh->num_heads * sh->dk * sh->dv;
+  if (per % 4 != 0 || !aligned(states, 16) || !aligned(dense, 16))
+    return invalid("%s: H*dk*dv must be a multiple of 4 and buffers 16-byte aligned", W);
+  return launch_state_copy(to_pool, states, num_slots, slots, n, dense, per,
+                           static_cast<hipStream_t>(stream));
+}
+
+kda_status_t kda_state_load(const kda_shape_t* sh, float* states, int32_t num_slots,
+                            const int32_t* slots, int32_t n, const float* src, void* stream) {
+  return state_copy("kda_state_load", true, sh, states, num_slots, slots, n,
+                    const_cast<float*>(src), stream);
+}
+
+kda_status_t kda_state_store(const kda_shape_t* sh, const float* states, int32_t num_slots,
+                             const int32_t* slots, int32_t n, float* dst, void* stream) {
+  return state_copy("kda_state_store", false, sh, const_cast<float*>(states), num_slots, slots, n,
+                    dst, stream);
+}
+
+}  // extern "C"

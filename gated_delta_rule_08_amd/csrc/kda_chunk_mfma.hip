@@ -1,0 +1,606 @@
+// kda_chunk_mfma.hip -- chunkwise prefill for dk = dv = 128, chunk = 64, bf16 I/O,
+// on gfx950 bf16 MFMA (v_mfma_f32_16x16x32_bf16) with fp32 state and accumulation.
+//
+// The chunk algebra (one head, chunk of C = 64 tokens entering with state S;
+// G = running sum of the per-channel log-gates inside the chunk, Gam = exp(G)):
+//   A_kk[r,j] = beta_r sum_c k_r[c] k_j[c] exp(G_r[c] - G_j[c])   (j < r)
+//   A_qk[r,j] =        sum_c q_r[c] k_j[c] exp(G_r[c] - G_j[c])   (j <= r)
+//   T  = (I + A_kk)^-1
+//   W  = T Diag(beta) (K*Gam),  Ut = T Diag(beta) V
+//   U  = Ut - W S                                   (corrected values)
+//   O  = (Q*Gam) S + A_qk U                         (state read + in-chunk part)
+//   S' = Diag(Gam_C) S + (K*exp(G_C - G))^T U       (fold the chunk into S)
+// This is the triangular-solve ("WY") packaging of the chunked delta rule
+// (engineermaxxing "From GPT-2 to Kimi K3", ch. 04e; heqinghuang "From GPT2 to
+// Kimi3, Explained", section 10) with the running per-channel decay products
+// folded through it (heqinghuang section 11; engineermaxxing ch. 05d keeps
+// them as sums of logs).  It equals the sequential recurrence up to rounding.
+//
+// Work split (three launches on the caller's stream):
+//  1. index: per-sequence chunk counts and offsets (sanitised, one thread).
+//  2. prep:  one workgroup per (chunk, head), fully parallel over chunks.  It
+//     computes everything that does not depend on the incoming state: the
+//     gated Gram blocks, the triangular inverse (fp32), W, Ut, Q*Gam,
+//     (K*exp(G_C-G))^T, A_qk and Gam_C, and stores the MFMA operands in the
+//     exact per-lane order the scan consumes (one 16-byte load per lane).
+//  3. scan:  one wave per (sequence, head, 16 state columns).  The columns of
+//     S evolve independently given k, beta and g, so the state is split over
+//     8 waves per head.  Each wave keeps its 128 x 16 fp32 slice of S as MFMA
+//     accumulators for the whole sequence and walks the chunks in order: the
+//     only loop-carried dependency of the method (heqinghuang section 10: the
+//     only sequential loop is over chunks).
+//
+// Numerics of the gated Gram products: exp(G_r - G_j) is split at the first
+// row s of the 16-row block of r as exp(G_r - G_s) * exp(G_s - G_j).  For j in
+// an earlier block both factors are <= 1.  For the diagonal block the second
+// factor is >= 1 and bounded by exp(spread), spread = max_c (G_s - G_{s+15});
+// when the spread exceeds kMaxSpread that diagonal block is computed element
+// by element in fp32 instead (exact, slow, only for extreme decay).
+#include "kda_common.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int C = 64;     // chunk
+constexpr int D = 128;    // dk = dv
+constexpr int KP = D + 4;  // bf16 LDS row stride (elements); 264 bytes
+constexpr int GP = D + 4;  // fp32 LDS row stride for G
+constexpr int AP = C + 4;  // fp32 LDS row stride for A_kk and T
+constexpr float kMaxSpread = 80.f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Per chunk-head operand blocks in the workspace (bytes).
+constexpr size_t kWnBytes = 4 * 4 * 64 * 16;   // -W      A operand, M=rows,  K=dk
+constexpr size_t kQgBytes = 4 * 4 * 64 * 16;   // Q*Gam   A operand, M=rows,  K=dk
+constexpr size_t kKdBytes = 8 * 2 * 64 * 16;   // Kd^T    A operand, M=dk,    K=rows
+constexpr size_t kAqBytes = 4 * 2 * 64 * 16;   // A_qk    A operand, M=rows,  K=rows
+constexpr size_t kUtBytes = 4 * 8 * 64 * 16;   // Ut      accumulator layout, fp32
+constexpr size_t kGcBytes = D * 4;             // Gam_C   fp32
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// K index held in slot q (0..7) of lane group g of a 32-deep MFMA operand.
+// Slots 0-3 cover 4g..4g+3 and slots 4-7 cover 16+4g..16+4g+3: this is the row
+// order in which two stacked 16x16 accumulator tiles sit in a lane, so an
+// accumulator pair converts to a B operand without moving data across lanes.
+__device__ __forceinline__ int kpos(int g, int q) { return q < 4 ? 4 * g + q : 12 + 4 * g + q; }
+
+__device__ __forceinline__ bf16x8 pack8(const float* f) {
+  u16x8 u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) u[i] = f32_to_bf16(f[i]);
+  return __builtin_bit_cast(bf16x8, u);
+}
+__device__ __forceinline__ bf16x8 pack_acc(f32x4 lo, f32x4 hi) {
+  float f[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return pack8(f);
+}
+
+struct Workspace {
+  int32_t* seq_start;
+  int32_t* seq_end;
+  int32_t* seq_nch;
+  int32_t* chunk_off;  // [N + 1]
+  uint8_t* wn;
+  uint8_t* qg;
+  uint8_t* kd;
+  uint8_t* aq;
+  uint8_t* ut;
+  uint8_t* gc;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t header_bytes(int32_t N) { return align256(sizeof(int32_t) * (size_t)(4 * N + 1)); }
+
+size_t nchunks_max(int32_t T, int32_t N) { return (size_t)T / C + (size_t)N; }
+
+Workspace carve(void* base, int32_t T, int32_t N, int H) {
+  Workspace w;
+  uint8_t* p = static_cast<uint8_t*>(base);
+  int32_t* hdr = reinterpret_cast<int32_t*>(p);
+  w.seq_start = hdr;
+  w.seq_end = hdr + N;
+  w.seq_nch = hdr + 2 * N;
+  w.chunk_off = hdr + 3 * N;
+  p += header_bytes(N);
+  const size_t ci = nchunks_max(T, N) * (size_t)H;
+  w.wn = p; p += align256(ci * kWnBytes);
+  w.qg = p; p += align256(ci * kQgBytes);
+  w.kd = p; p += align256(ci * kKdBytes);
+  w.aq = p; p += align256(ci * kAqBytes);
+  w.ut = p; p += align256(ci * kUtBytes);
+  w.gc = p;
+  return w;
+}
+
+// ------------------------------------------------------------------ 1. index
+// Sanitised bounds: start = clamp(cu[n]), end = clamp(cu[n+1]) >= start; the
+// running chunk total is capped at the workspace capacity, so malformed
+// offsets can never address memory outside the buffers.
+__global__ void index_kernel(const int32_t* __restrict__ cu, int32_t N, int32_t T, int32_t cap,
+                             Workspace w) {
+  if (threadIdx.x != 0) return;
+  int32_t run = 0;
+  for (int32_t n = 0; n < N; ++n) {
+    const int32_t s = clamp_tok(cu[n], T);
+    int32_t e = clamp_tok(cu[n + 1], T);
+    if (e < s) e = s;
+    int32_t nch = (e - s + C - 1) / C;
+    if (nch > cap - run) {
+      nch = cap - run;
+      e = s + nch * C < e ? s + nch * C : e;
+    }
+    w.seq_start[n] = s;
+    w.seq_end[n] = e;
+    w.seq_nch[n] = nch;
+    w.chunk_off[n] = run;
+    run += nch;
+  }
+  w.chunk_off[N] = run;
+}
+
+// ------------------------------------------------------------------ 2. prep
+struct PrepSmem {
+  uint16_t K[C][KP];
+  uint16_t Q[C][KP];
+  uint16_t V[C][KP];
+  float G[C][GP];
+  float A[C][AP];    // beta-scaled strictly lower A_kk
+  float Tm[C][AP];   // (I + A_kk)^-1
+  float X[4][16][17];
+  float half_tot[D];
+  float bs[C];
+};
+
+__device__ __forceinline__ float ld_bf(const uint16_t* row, int c) { return bf16_to_f32(row[c]); }
+
+__global__ __launch_bounds__(256) void prep_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, int32_t N, int H, Workspace w) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  PrepSmem& sm = *reinterpret_cast<PrepSmem*>(smem_raw);
+  const int gc = blockIdx.x;
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x;
+  if (gc >= w.chunk_off[N]) return;  // uniform: capacity slack
+  // the sequence owning this chunk (binary search over chunk offsets)
+  int lo = 0, hi = N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (w.chunk_off[mid] <= gc) lo = mid; else hi = mid - 1;
+  }
+  const int n = lo;
+  const int t0 = w.seq_start[n] + (gc - w.chunk_off[n]) * C;
+  const int c = min(C, w.seq_end[n] - t0);  // valid rows (>= 1)
+  const size_t ci = (size_t)gc * H + h;
+
+  // ---- phase 0: stage the chunk in LDS (padded rows are neutral tokens)
+  for (int u = tid; u < C * 16; u += 256) {
+    const int r = u >> 4, cc = (u & 15) * 8;
+    uint4 kk = make_uint4(0, 0, 0, 0), qq = kk, vv = kk;
+    if (r < c) {
+      const size_t gi = ((size_t)(t0 + r) * H + h) * D + cc;
+      kk = *reinterpret_cast<const uint4*>(k + gi);
+      qq = *reinterpret_cast<const uint4*>(q + gi);
+      vv = *reinterpret_cast<const uint4*>(v + gi);
+    }
+    uint2* pk = reinterpret_cast<uint2*>(&sm.K[r][cc]);
+    uint2* pq = reinterpret_cast<uint2*>(&sm.Q[r][cc]);
+    uint2* pv = reinterpret_cast<uint2*>(&sm.V[r][cc]);
+    pk[0] = make_uint2(kk.x, kk.y); pk[1] = make_uint2(kk.z, kk.w);
+    pq[0] = make_uint2(qq.x, qq.y); pq[1] = make_uint2(qq.z, qq.w);
+    pv[0] = make_uint2(vv.x, vv.y); pv[1] = make_uint2(vv.z, vv.w);
+  }
+  for (int u = tid; u < C * 32; u += 256) {
+    const int r = u >> 5, cc = (u & 31) * 4;
+    float4 gg = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (r < c) gg = *reinterpret_cast<const float4*>(g + ((size_t)(t0 + r) * H + h) * D + cc);
+    *reinterpret_cast<float4*>(&sm.G[r][cc]) = gg;
+  }
+  if (tid < C) sm.bs[tid] = tid < c ? beta[(size_t)(t0 + tid) * H + h] : 0.f;
+  for (int u = tid; u < C * AP; u += 256) (&sm.Tm[0][0])[u] = 0.f;
+  __syncthreads();
+
+  // ---- phase 1: running sum of the log-gates down each channel
+  {
+    const int col = tid & 127, half = tid >> 7;
+    float x[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = sm.G[half * 32 + i][col];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) x[i] += x[i - 1];
+    if (half == 0) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) sm.G[i][col] = x[i];
+      sm.half_tot[col] = x[31];
+    }
+    __syncthreads();
+    if (half == 1) {
+      const float base = sm.half_tot[col];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) sm.G[32 + i][col] = x[i] + base;
+    }
+  }
+  __syncthreads();
+
+  const int wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+
+  // ---- phase 2: gated Gram blocks; wave R owns block row R (rows 16R..16R+15)
+  {
+    const int R = wave, sR = 16 * R;
+    float sp = fmaxf(sm.G[sR][lane] - sm.G[sR + 15][lane],
+                     sm.G[sR][lane + 64] - sm.G[sR + 15][lane + 64]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sp = fmaxf(sp, __shfl_xor(sp, off, 64));
+    const bool fast_diag = sp <= kMaxSpread;
+
+    // B operands: rows r of block R scaled by exp(G_r - G_s)  (<= 1)
+    bf16x8 bk[4], bq[4];
+    {
+      const int r = sR + li;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        float fk[8], fq[8];
+#pragma unroll
+        for (int qq = 0; qq < 8; ++qq) {
+          const int cc = 32 * s + kpos(lg, qq);
+          const float f = fast_exp(sm.G[r][cc] - sm.G[sR][cc]);
+          fk[qq] = ld_bf(sm.K[r], cc) * f;
+          fq[qq] = ld_bf(sm.Q[r], cc) * f;
+        }
+        bk[s] = pack8(fk);
+        bq[s] = pack8(fq);
+      }
+    }
+    uint16_t* aq_out = reinterpret_cast<uint16_t*>(w.aq + ci * kAqBytes);
+    for (int J = 0; J < 4; ++J) {
+      f32x4 acck = {0.f, 0.f, 0.f, 0.f}, accq = acck;
+      if (J < R || (J == R && fast_diag)) {
+        const int j = 16 * J + li;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          float fa[8];
+#pragma unroll
+          for (int qq = 0; qq < 8; ++qq) {
+            const int cc = 32 * s + kpos(lg, qq);
+            fa[qq] = ld_bf(sm.K[j], cc) * fast_exp(sm.G[sR][cc] - sm.G[j][cc]);
+          }
+          const bf16x8 ak = pack8(fa);
+          acck = mfma(ak, bk[s], acck);
+          accq = mfma(ak, bq[s], accq);
+        }
+      } else if (J == R) {
+        // extreme decay inside the block: exact element-wise fp32 sums
+        const int r = sR + li;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j = sR + 4 * lg + jj;
+          float kk = 0.f, qk = 0.f;
+          if (j <= r) {
+            for (int cc = 0; cc < D; ++cc) {
+              const float e = fast_exp(sm.G[r][cc] - sm.G[j][cc]);
+              const float kj = ld_bf(sm.K[j], cc) * e;
+              kk += ld_bf(sm.K[r], cc) * kj;
+              qk += ld_bf(sm.Q[r], cc) * kj;
+            }
+          }
+          acck[jj] = kk;
+          accq[jj] = qk;
+        }
+      }
+      // lane holds raw A[r = sR + li][j = 16J + 4lg + jj]
+      const int r = sR + li;
+      const float br = sm.bs[r];
+      float4 arow;
+      uint16_t qv[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = 16 * J + 4 * lg + jj;
+        const float akk = j < r ? br * acck[jj] : 0.f;
+        const float aqk = j <= r ? accq[jj] : 0.f;
+        (&arow.x)[jj] = akk;
+        qv[jj] = f32_to_bf16(aqk);
+      }
+      *reinterpret_cast<float4*>(&sm.A[r][16 * J + 4 * lg]) = arow;
+      // A_qk as the scan's A operand: [m = R][s' = J / 2][lane][slots (J & 1) * 4 ..]
+      uint16_t* dst = aq_out + ((size_t)(R * 2 + (J >> 1)) * 64 + lane) * 8 + (J & 1) * 4;
+      *reinterpret_cast<uint2*>(dst) =
+          make_uint2((uint32_t)qv[0] | ((uint32_t)qv[1] << 16), (uint32_t)qv[2] | ((uint32_t)qv[3] << 16));
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 3: T = (I + A_kk)^-1, blocked forward substitution in fp32
+  {
+    const int R = wave, sR = 16 * R;
+    if (lane < 16) {  // diagonal block: lane = column
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float acc = 0.f;
+#pragma unroll
+        for (int m = 0; m < i; ++m) acc += sm.A[sR + i][sR + m] * x[m];
+        x[i] = i < lane ? 0.f : (i == lane ? 1.f : -acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sm.Tm[sR + i][sR + lane] = x[i];
+    }
+    __syncthreads();
+    // off-diagonal blocks by distance: T_RJ = -T_RR sum_{J<=K<R} A_RK T_KJ
+    const int rho = lane >> 2, c4 = (lane & 3) * 4;
+    for (int dist = 1; dist < 4; ++dist) {
+      const bool act = R >= dist;
+      const int J = R - dist;
+      if (act) {
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int Kb = J; Kb < R; ++Kb) {
+#pragma unroll
+          for (int m = 0; m < 16; ++m) {
+            const float a = sm.A[sR + rho][16 * Kb + m];
+            const float4 t = *reinterpret_cast<const float4*>(&sm.Tm[16 * Kb + m][16 * J + c4]);
+            acc[0] += a * t.x; acc[1] += a * t.y; acc[2] += a * t.z; acc[3] += a * t.w;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.X[R][rho][c4 + i] = acc[i];
+      }
+      __syncthreads();
+      if (act) {
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+          const float t = sm.Tm[sR + rho][sR + m];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] += t * sm.X[R][m][c4 + i];
+        }
+        *reinterpret_cast<float4*>(&sm.Tm[sR + rho][16 * J + c4]) =
+            make_float4(-acc[0], -acc[1], -acc[2], -acc[3]);
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- phase 4: W, Ut, Q*Gam, Kd^T, Gam_C in the scan's operand order
+  {
+    // T tiles, used as A operand (M = r) and as B operand of W^T (N = r)
+    bf16x8 tt[4][2];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        if (m < 2 && s2 == 1) continue;  // T is lower triangular: zero block
+        const float* trow = &sm.Tm[16 * m + li][32 * s2 + 4 * lg];
+        const float4 a = *reinterpret_cast<const float4*>(trow);
+        const float4 b = *reinterpret_cast<const float4*>(trow + 16);
+        const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        tt[m][s2] = pack8(f);
+      }
+
+    // (a) W^T for channel tiles 2w, 2w+1 and Kd^T for the same channels
+    uint16_t* kd_out = reinterpret_cast<uint16_t*>(w.kd + ci * kKdBytes);
+    f32x4 wt[2][4];
+#pragma unroll
+    for (int tl = 0; tl < 2; ++tl) {
+      const int tile = 2 * wave + tl, ch = 16 * tile + li;
+      const float gl = sm.G[C - 1][ch];
+      bf16x8 abkg[2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        float fb[8], fd[8];
+#pragma unroll
+        for (int qq = 0; qq < 8; ++qq) {
+          const int j = 32 * s2 + kpos(lg, qq);
+          const float kv = ld_bf(sm.K[j], ch), gv = sm.G[j][ch];
+          fb[qq] = sm.bs[j] * kv * fast_exp(gv);
+          fd[qq] = kv * fast_exp(gl - gv);
+        }
+        abkg[s2] = pack8(fd);  // reuse the register for Kd^T first
+        *reinterpret_cast<bf16x8*>(kd_out + ((size_t)(tile * 2 + s2) * 64 + lane) * 8) = abkg[s2];
+        abkg[s2] = pack8(fb);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mfma(abkg[0], tt[nt][0], acc);
+        if (nt >= 2) acc = mfma(abkg[1], tt[nt][1], acc);
+        wt[tl][nt] = acc;
+      }
+    }
+    // -W as the scan's A operand: [m = nt][s = wave][lane][slots tl*4 + jj]
+    uint16_t* wn_out = reinterpret_cast<uint16_t*>(w.wn + ci * kWnBytes);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const float f[8] = {-wt[0][nt][0], -wt[0][nt][1], -wt[0][nt][2], -wt[0][nt][3],
+                          -wt[1][nt][0], -wt[1][nt][1], -wt[1][nt][2], -wt[1][nt][3]};
+      *reinterpret_cast<bf16x8*>(wn_out + ((size_t)(nt * 4 + wave) * 64 + lane) * 8) = pack8(f);
+    }
+
+    // (b) Ut = T Diag(beta) V for value tiles 2w, 2w+1 (accumulator layout, fp32)
+    float* ut_out = reinterpret_cast<float*>(w.ut + ci * kUtBytes);
+#pragma unroll
+    for (int nl = 0; nl < 2; ++nl) {
+      const int nb = 2 * wave + nl, col = 16 * nb + li;
+      bf16x8 bv[2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        float f[8];
+#pragma unroll
+        for (int qq = 0; qq < 8; ++qq) {
+          const int j = 32 * s2 + kpos(lg, qq);
+          f[qq] = sm.bs[j] * ld_bf(sm.V[j], col);
+        }
+        bv[s2] = pack8(f);
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mfma(tt[m][0], bv[0], acc);
+        if (m >= 2) acc = mfma(tt[m][1], bv[1], acc);
+        *reinterpret_cast<f32x4*>(ut_out + ((size_t)(m * 8 + nb) * 64 + lane) * 4) = acc;
+      }
+    }
+
+    // (c) Q*Gam as the scan's A operand: [m = wave][s][lane]
+    uint16_t* qg_out = reinterpret_cast<uint16_t*>(w.qg + ci * kQgBytes);
+    {
+      const int r = 16 * wave + li;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        float f[8];
+#pragma unroll
+        for (int qq = 0; qq < 8; ++qq) {
+          const int cc = 32 * s + kpos(lg, qq);
+          f[qq] = ld_bf(sm.Q[r], cc) * fast_exp(sm.G[r][cc]);
+        }
+        *reinterpret_cast<bf16x8*>(qg_out + ((size_t)(wave * 4 + s) * 64 + lane) * 8) = pack8(f);
+      }
+    }
+    // (d) Gam_C
+    if (tid < D) reinterpret_cast<float*>(w.gc + ci * kGcBytes)[tid] = fast_exp(sm.G[C - 1][tid]);
+  }
+}
+
+// ------------------------------------------------------------------ 3. scan
+// One wave per (sequence n, head h, column block nb of 16 state columns).
+// Block index b -> head_lin = b % NH, nb = b / NH, so the 8 column blocks of a
+// head land on the same XCD (workgroups are dealt to XCDs round-robin) and
+// share its L2 for the per-chunk operands.
+__global__ __launch_bounds__(64) void scan_kernel(
+    int32_t N, int H, Workspace w, float* __restrict__ states, int32_t num_slots,
+    const int32_t* __restrict__ slots, uint32_t flags, uint16_t* __restrict__ o) {
+  const int NH = N * H;
+  const int head_lin = blockIdx.x % NH;
+  const int nb = blockIdx.x / NH;
+  const int n = head_lin / H, h = head_lin - n * H;
+  const int lane = threadIdx.x, li = lane & 15, lg = lane >> 4;
+  const int col = 16 * nb + li;
+
+  const int start = w.seq_start[n], end = w.seq_end[n], nch = w.seq_nch[n];
+  const int cbase = w.chunk_off[n];
+  const int slot = slots ? slots[n] : n;
+  const bool slot_ok = states != nullptr && slot >= 0 && slot < num_slots;
+  float* Sg = slot_ok ? states + ((size_t)slot * H + h) * (size_t)(D * D) : nullptr;
+
+  // state slice: S[t] lane holds rows 16t + 4lg + jj of column col
+  f32x4 S[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      S[t][jj] = (slot_ok && (flags & KDA_READ_INITIAL_STATE))
+                     ? Sg[(size_t)(16 * t + 4 * lg + jj) * D + col] : 0.f;
+
+  for (int lc = 0; lc < nch; ++lc) {
+    const size_t ci = (size_t)(cbase + lc) * H + h;
+    const bf16x8* wn = reinterpret_cast<const bf16x8*>(w.wn + ci * kWnBytes);
+    const bf16x8* qg = reinterpret_cast<const bf16x8*>(w.qg + ci * kQgBytes);
+    const bf16x8* kd = reinterpret_cast<const bf16x8*>(w.kd + ci * kKdBytes);
+    const bf16x8* aq = reinterpret_cast<const bf16x8*>(w.aq + ci * kAqBytes);
+    const f32x4* ut = reinterpret_cast<const f32x4*>(w.ut + ci * kUtBytes);
+    const f32x4* gcv = reinterpret_cast<const f32x4*>(w.gc + ci * kGcBytes);
+
+    bf16x8 sb[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) sb[s] = pack_acc(S[2 * s], S[2 * s + 1]);
+
+    // U = Ut - W S
+    f32x4 U[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      U[m] = ut[(m * 8 + nb) * 64 + lane];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) U[m] = mfma(wn[(m * 4 + s) * 64 + lane], sb[s], U[m]);
+    }
+    bf16x8 ub[2];
+    ub[0] = pack_acc(U[0], U[1]);
+    ub[1] = pack_acc(U[2], U[3]);
+
+    // O = (Q*Gam) S + A_qk U
+    f32x4 O[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      O[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) O[m] = mfma(qg[(m * 4 + s) * 64 + lane], sb[s], O[m]);
+      O[m] = mfma(aq[(m * 2 + 0) * 64 + lane], ub[0], O[m]);
+      if (m >= 2) O[m] = mfma(aq[(m * 2 + 1) * 64 + lane], ub[1], O[m]);
+    }
+
+    // S' = Diag(Gam_C) S + Kd^T U
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const f32x4 gm = gcv[4 * t + lg];
+      S[t] = S[t] * gm;
+      S[t] = mfma(kd[(t * 2 + 0) * 64 + lane], ub[0], S[t]);
+      S[t] = mfma(kd[(t * 2 + 1) * 64 + lane], ub[1], S[t]);
+    }
+
+    // outputs of the valid rows of this chunk
+    const int tbase = start + lc * C;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int tok = tbase + 16 * m + 4 * lg + jj;
+        if (tok < end) o[((size_t)tok * H + h) * D + col] = f32_to_bf16(O[m][jj]);
+      }
+  }
+
+  if (slot_ok && (flags & KDA_WRITE_FINAL_STATE)) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) Sg[(size_t)(16 * t + 4 * lg + jj) * D + col] = S[t][jj];
+  }
+}
+
+}  // namespace
+
+bool chunk_mfma_supported(int dk, int dv, int chunk, int io_dtype) {
+  return dk == D && dv == D && chunk == C && io_dtype == KDA_BF16;
+}
+
+size_t chunk_mfma_workspace_bytes(int H, int32_t T, int32_t N) {
+  const size_t ci = nchunks_max(T, N) * (size_t)H;
+  return header_bytes(N) + align256(ci * kWnBytes) + align256(ci * kQgBytes) +
+         align256(ci * kKdBytes) + align256(ci * kAqBytes) + align256(ci * kUtBytes) +
+         align256(ci * kGcBytes);
+}
+
+kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, const int32_t* cu,
+                               const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, float* states, int32_t num_slots,
+                               const int32_t* slots, uint32_t flags, void* o, void* workspace,
+                               hipStream_t stream) {
+  const int H = sh->num_heads;
+  Workspace w = carve(workspace, T, N, H);
+  const size_t cap = nchunks_max(T, N);
+  hipLaunchKernelGGL(index_kernel, dim3(1), dim3(64), 0, stream, cu, N, T, (int32_t)cap, w);
+  kda_status_t st = check_launch("chunk_fwd index");
+  if (st != KDA_OK) return st;
+  static bool attr_set = false;  // idempotent; set before first launch
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)sizeof(PrepSmem));
+    if (e != hipSuccess) return hip_status(e, "hipFuncSetAttribute(prep)");
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)cap, (unsigned)H), dim3(256), sizeof(PrepSmem),
+                     stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), g, beta, N, H, w);
+  st = check_launch("chunk_fwd prep");
+  if (st != KDA_OK) return st;
+  hipLaunchKernelGGL(scan_kernel, dim3((unsigned)(N * H * (D / 16))), dim3(64), 0, stream, N, H, w,
+                     states, num_slots, slots, flags, static_cast<uint16_t*>(o));
+  return check_launch("chunk_fwd scan");
+}
+
+}  // namespace kda

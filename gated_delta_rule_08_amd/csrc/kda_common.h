@@ -1,0 +1,48 @@
+// kda_common.h -- internal helpers shared by the gfx950 kernels of libkda.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda.h"
+
+namespace kda {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- bf16 <-> fp32
+// bf16 is carried as raw uint16 bits.  bf16 -> fp32 is exact; fp32 -> bf16
+// rounds to nearest even (NaN stays NaN).
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// I/O element types: float for fp32, uint16_t (bf16 bits) for bf16.
+template <typename IO> struct io_traits;
+template <> struct io_traits<float> {
+  __device__ __forceinline__ static float load(const float* p, size_t i) { return p[i]; }
+  __device__ __forceinline__ static void store(float* p, size_t i, float x) { p[i] = x; }
+};
+template <> struct io_traits<uint16_t> {
+  __device__ __forceinline__ static float load(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+  __device__ __forceinline__ static void store(uint16_t* p, size_t i, float x) { p[i] = f32_to_bf16(x); }
+};
+
+__device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
+
+// Sanitised sequence bounds, shared by every prefill kernel: offsets are
+// clamped to [0, T] and made nondecreasing so that no access leaves [0, T).
+__device__ __forceinline__ int clamp_tok(int x, int T) { return x < 0 ? 0 : (x > T ? T : x); }
+
+// ---------------------------------------------------------------- host-side status
+void set_error(const char* fmt, ...);
+kda_status_t hip_status(hipError_t e, const char* what);
+kda_status_t check_launch(const char* what);
+
+}  // namespace kda

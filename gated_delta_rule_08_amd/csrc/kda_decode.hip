@@ -1,0 +1,166 @@
+// kda_decode.hip -- one decode step of the gated delta rule against resident states.
+//
+// Per (sequence b, head h), with S the resident fp32 dk x dv state:
+//   Sbar = Diag(exp(g)) S            fade each key channel (row of S)
+//   w    = Sbar^T k,  y = Sbar^T q    two reads of the faded state
+//   u    = beta (v - w)               the correction
+//   S    = Sbar + k u^T               written back in place
+//   o    = S^T q = y + (k . q) u      read after the write
+// (dev.to "From GPT-2 to Kimi K3", blocks 4-5: fade, read, correct against the
+// faded state, one retention factor per key channel; heqinghuang "From GPT2 to
+// Kimi3, Explained", section 09: output read after the write.)
+//
+// The step is a streaming read-modify-write of the state: each state is read
+// from HBM once and written once, and the token vectors are tiny, so the kernel
+// is bound by HBM bandwidth (engineermaxxing ch. 02b: a decode step reads the
+// d x d state and writes it back).  Mapping: one workgroup per (b, h); thread
+// (row group rg, column quad cq) keeps rows rg, rg + RG, ... of columns
+// 4cq .. 4cq+3 in registers, so every wave load instruction covers whole
+// consecutive rows (coalesced 16-byte accesses).  The reductions over key
+// channels combine the row groups through LDS.
+#include "kda_common.h"
+
+namespace kda {
+
+namespace {
+
+template <int DK, int DV, int BLOCK, typename IO>
+__global__ __launch_bounds__(BLOCK) void decode_kernel(
+    const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ states,
+    int32_t num_slots, const int32_t* __restrict__ slots, IO* __restrict__ o, int H) {
+  constexpr int NCQ = DV / 4;      // column quads
+  constexpr int RG = BLOCK / NCQ;  // row groups
+  constexpr int RPT = DK / RG;     // rows per thread
+  static_assert(DV % 4 == 0 && BLOCK % NCQ == 0 && DK % RG == 0, "bad decode tiling");
+
+  const int bh = blockIdx.x;  // b * H + h
+  const int b = bh / H;
+  const int h = bh - b * H;
+  const int tid = threadIdx.x;
+  const int cq = tid % NCQ;
+  const int rg = tid / NCQ;
+  const int slot = slots ? slots[b] : b;
+  if (slot < 0 || slot >= num_slots) return;  // uniform across the block
+
+  float* S = states + ((size_t)slot * H + h) * (size_t)(DK * DV);
+
+  __shared__ float ks[DK], qs[DK], as[DK], vs[DV], us[DV];
+  __shared__ float4 wred[RG][NCQ];
+  __shared__ float4 yred[RG][NCQ];
+  __shared__ float kq_sh;
+
+  // 1. issue every state load first (the only large traffic)
+  f32x4_t s[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i)
+    s[i] = __builtin_nontemporal_load(
+        reinterpret_cast<const f32x4_t*>(S + (size_t)(rg + RG * i) * DV + 4 * cq));
+
+  // 2. token vectors to LDS
+  const size_t tk = (size_t)bh * DK, tv = (size_t)bh * DV;
+  for (int i = tid; i < DK; i += BLOCK) {
+    ks[i] = io_traits<IO>::load(k, tk + i);
+    qs[i] = io_traits<IO>::load(q, tk + i);
+    as[i] = fast_exp(g[tk + i]);
+  }
+  for (int i = tid; i < DV; i += BLOCK) vs[i] = io_traits<IO>::load(v, tv + i);
+  __syncthreads();
+
+  // k . q, reduced by the first wave
+  if (tid < 64) {
+    float p = 0.f;
+    for (int i = tid; i < DK; i += 64) p += ks[i] * qs[i];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) p += __shfl_xor(p, off, 64);
+    if (tid == 0) kq_sh = p;
+  }
+
+  // 3. fade and partial reads over this thread's rows
+  float4 w = make_float4(0.f, 0.f, 0.f, 0.f), y = w;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = rg + RG * i;
+    const float a = as[r], kr = ks[r], qr = qs[r];
+    s[i] *= a;
+    w.x += kr * s[i][0]; w.y += kr * s[i][1]; w.z += kr * s[i][2]; w.w += kr * s[i][3];
+    y.x += qr * s[i][0]; y.y += qr * s[i][1]; y.z += qr * s[i][2]; y.w += qr * s[i][3];
+  }
+  wred[rg][cq] = w;
+  yred[rg][cq] = y;
+  __syncthreads();
+
+  // 4. finish the reductions, form the correction and the output
+  if (rg == 0) {
+    float4 W = wred[0][cq], Y = yred[0][cq];
+#pragma unroll
+    for (int j = 1; j < RG; ++j) {
+      const float4 a = wred[j][cq], c = yred[j][cq];
+      W.x += a.x; W.y += a.y; W.z += a.z; W.w += a.w;
+      Y.x += c.x; Y.y += c.y; Y.z += c.z; Y.w += c.w;
+    }
+    const float bt = beta[bh], kq = kq_sh;
+    const int c0 = 4 * cq;
+    const float u0 = bt * (vs[c0 + 0] - W.x), u1 = bt * (vs[c0 + 1] - W.y);
+    const float u2 = bt * (vs[c0 + 2] - W.z), u3 = bt * (vs[c0 + 3] - W.w);
+    us[c0 + 0] = u0; us[c0 + 1] = u1; us[c0 + 2] = u2; us[c0 + 3] = u3;
+    io_traits<IO>::store(o, tv + c0 + 0, Y.x + kq * u0);
+    io_traits<IO>::store(o, tv + c0 + 1, Y.y + kq * u1);
+    io_traits<IO>::store(o, tv + c0 + 2, Y.z + kq * u2);
+    io_traits<IO>::store(o, tv + c0 + 3, Y.w + kq * u3);
+  }
+  __syncthreads();
+
+  // 5. write the updated state in place: S = Sbar + k u^T
+  const float4 u4 = *reinterpret_cast<const float4*>(&us[4 * cq]);
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = rg + RG * i;
+    const float kr = ks[r];
+    f32x4_t t = s[i];
+    t[0] += kr * u4.x; t[1] += kr * u4.y; t[2] += kr * u4.z; t[3] += kr * u4.w;
+    __builtin_nontemporal_store(t, reinterpret_cast<f32x4_t*>(S + (size_t)r * DV + 4 * cq));
+  }
+}
+
+template <int D, int BLOCK, typename IO>
+kda_status_t launch_typed(int32_t batch, int H, const void* q, const void* k, const void* v,
+                          const float* g, const float* beta, float* states, int32_t num_slots,
+                          const int32_t* slots, void* o, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_kernel<D, D, BLOCK, IO>), dim3((unsigned)batch * H), dim3(BLOCK), 0,
+                     stream, static_cast<const IO*>(q), static_cast<const IO*>(k),
+                     static_cast<const IO*>(v), g, beta, states, num_slots, slots,
+                     static_cast<IO*>(o), H);
+  return check_launch("decode_step");
+}
+
+template <typename IO>
+kda_status_t launch_io(int d, int32_t batch, int H, const void* q, const void* k, const void* v,
+                       const float* g, const float* beta, float* states, int32_t num_slots,
+                       const int32_t* slots, void* o, hipStream_t stream) {
+  switch (d) {
+    case 16: return launch_typed<16, 64, IO>(batch, H, q, k, v, g, beta, states, num_slots, slots, o, stream);
+    case 32: return launch_typed<32, 64, IO>(batch, H, q, k, v, g, beta, states, num_slots, slots, o, stream);
+    case 64: return launch_typed<64, 128, IO>(batch, H, q, k, v, g, beta, states, num_slots, slots, o, stream);
+    case 128: return launch_typed<128, 256, IO>(batch, H, q, k, v, g, beta, states, num_slots, slots, o, stream);
+    default: return KDA_ERR_UNSUPPORTED;
+  }
+}
+
+}  // namespace
+
+bool decode_supported(int dk, int dv) {
+  return dk == dv && (dk == 16 || dk == 32 || dk == 64 || dk == 128);
+}
+
+kda_status_t launch_decode(const kda_shape_t* sh, int32_t batch, const void* q, const void* k,
+                           const void* v, const float* g, const float* beta, float* states,
+                           int32_t num_slots, const int32_t* slots, void* o, hipStream_t stream) {
+  if (sh->io_dtype == KDA_BF16)
+    return launch_io<uint16_t>(sh->dk, batch, sh->num_heads, q, k, v, g, beta, states, num_slots,
+                               slots, o, stream);
+  return launch_io<float>(sh->dk, batch, sh->num_heads, q, k, v, g, beta, states, num_slots,
+                          slots, o, stream);
+}
+
+}  // namespace kda

@@ -1,0 +1,74 @@
+// kda_state.hip -- state pool init / load / store (pure bandwidth kernels).
+//
+// A state is one fp32 dk x dv matrix per (slot, head); the pool is
+// [num_slots, H, dk, dv].  The memory these states carry is the whole cache
+// of the operator (heqinghuang "From GPT2 to Kimi3, Explained", section 09:
+// the returned state is the cache), so saving and restoring it is a plain copy
+// by slot index.
+#include "kda_common.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// Zero a contiguous range of float4.
+__global__ __launch_bounds__(kThreads) void zero_kernel(float4* __restrict__ p, size_t n4) {
+  const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (size_t i = blockIdx.x * (size_t)kThreads + threadIdx.x; i < n4;
+       i += (size_t)gridDim.x * kThreads)
+    p[i] = z;
+}
+
+// dense[i] <-> pool[slot(i)], one state = per4 float4 (H * dk * dv / 4).
+template <bool kToPool>
+__global__ __launch_bounds__(kThreads) void gather_scatter_kernel(
+    float4* __restrict__ pool, int32_t num_slots, const int32_t* __restrict__ slots, int32_t n,
+    float4* __restrict__ dense, size_t per4) {
+  const size_t total = (size_t)n * per4;
+  for (size_t e = blockIdx.x * (size_t)kThreads + threadIdx.x; e < total;
+       e += (size_t)gridDim.x * kThreads) {
+    const size_t i = e / per4, off = e - i * per4;
+    const int32_t slot = slots ? slots[i] : (int32_t)i;
+    if (slot < 0 || slot >= num_slots) continue;
+    float4* ps = pool + (size_t)slot * per4 + off;
+    float4* pd = dense + i * per4 + off;
+    if (kToPool) *ps = *pd;
+    else *pd = *ps;
+  }
+}
+
+int grid_for(size_t n4) {
+  size_t blocks = (n4 + kThreads - 1) / kThreads;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  return (int)blocks;
+}
+
+}  // namespace
+
+kda_status_t launch_state_init(float* states, size_t n_floats, hipStream_t stream) {
+  const size_t n4 = n_floats / 4;
+  hipLaunchKernelGGL(zero_kernel, dim3(grid_for(n4)), dim3(kThreads), 0, stream,
+                     reinterpret_cast<float4*>(states), n4);
+  return check_launch("state_init");
+}
+
+kda_status_t launch_state_copy(bool to_pool, float* states, int32_t num_slots,
+                               const int32_t* slots, int32_t n, float* dense,
+                               size_t per_state_floats, hipStream_t stream) {
+  const size_t per4 = per_state_floats / 4;
+  const int grid = grid_for((size_t)n * per4);
+  if (to_pool)
+    hipLaunchKernelGGL(gather_scatter_kernel<true>, dim3(grid), dim3(kThreads), 0, stream,
+                       reinterpret_cast<float4*>(states), num_slots, slots, n,
+                       reinterpret_cast<float4*>(dense), per4);
+  else
+    hipLaunchKernelGGL(gather_scatter_kernel<false>, dim3(grid), dim3(kThreads), 0, stream,
+                       reinterpret_cast<float4*>(states), num_slots, slots, n,
+                       reinterpret_cast<float4*>(dense), per4);
+  return check_launch(to_pool ? "state_load" : "state_store");
+}
+
+}  // namespace kda

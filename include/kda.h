@@ -1,0 +1,175 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) gated delta-rule / Kimi Delta
+ * Attention library (libkda.so).
+ *
+ * The operator (one head, state S in R^{dk x dv}, row r = key channel r):
+ *
+ *   S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *   o_t = S_t^T q_t,                      alpha_t = exp(g_t) per key channel.
+ *
+ * Equivalently, per token: fade the state by the per-channel gate, read the
+ * faded state at the key, write beta times the difference to the value, then
+ * read the output with the query after the write.  Sources on the pages:
+ * dev.to "From GPT-2 to Kimi K3: How Language Models Learned to Manage
+ * Memory", blocks 3-5 (read/compare/write; fade first; a retention factor per
+ * key channel = per row of S); engineermaxxing "From GPT-2 to Kimi K3: one
+ * memory, seven eviction policies", ch. 06b (per-channel decay inside the
+ * delta rule) and ch. 05c (scalar gate = Gated DeltaNet; alpha = 1 =
+ * DeltaNet); heqinghuang "From GPT2 to Kimi3, Explained", section 09 (output
+ * read after the write, no normaliser, missing cache = zero state).
+ *
+ * Conventions shared by every entry point
+ *  - All data pointers are DEVICE pointers (HIP device memory) except the
+ *    kda_shape_t argument, which is a host pointer.  The caller owns every
+ *    buffer; the library allocates no device memory and keeps no device state.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Every call only enqueues work on `stream` and returns; there is no
+ *    implicit synchronisation.  Calls are reentrant: host threads may call
+ *    concurrently on different streams.
+ *  - Layouts are row-major and packed over tokens: q, k, g [T, H, dk];
+ *    v, o [T, H, dv]; beta [T, H]; state pools [num_slots, H, dk, dv].
+ *  - q, k, v, o have the I/O dtype (fp32 or bf16); g, beta and states are
+ *    always fp32.  g = log(alpha) must be finite and <= 0 (alpha in (0, 1]);
+ *    the library does not check values: NaN/Inf propagate, g > 0 is
+ *    undefined.  q and k are used as given (callers L2-normalise them).
+ *  - Arguments are validated on the host BEFORE any launch: on any error
+ *    nothing is enqueued and nothing is written.  Values that live in device
+ *    memory (cu_seqlens, slot indices) cannot be checked synchronously; the
+ *    kernels never access memory out of bounds because of them: offsets are
+ *    clamped to [0, total_tokens] and made nondecreasing, and entries whose
+ *    slot lies outside [0, num_slots) are skipped (their outputs are left
+ *    unwritten and no state is touched).
+ *  - Launch failures return KDA_ERR_HIP; kda_last_error() then holds the HIP
+ *    error text.  No C++ exception crosses this interface.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARGUMENT = 1,  /* bad pointer, shape, count or flag        */
+  KDA_ERR_UNSUPPORTED = 2,       /* valid but not built: (dk, dv, chunk, io)  */
+  KDA_ERR_WORKSPACE_TOO_SMALL = 3,
+  KDA_ERR_HIP = 4                /* a HIP runtime call or launch failed       */
+} kda_status_t;
+
+typedef enum { KDA_FP32 = 0, KDA_BF16 = 1 } kda_dtype_t;  /* dtype of q, k, v, o */
+
+typedef struct {
+  int32_t num_heads;  /* H  >= 1 */
+  int32_t dk;         /* key dimension (rows of S)      */
+  int32_t dv;         /* value dimension (columns of S) */
+  int32_t io_dtype;   /* kda_dtype_t                    */
+} kda_shape_t;
+
+/* flags of kda_chunk_fwd */
+enum {
+  KDA_READ_INITIAL_STATE = 1u,  /* start each sequence from states[slot]; else from 0 */
+  KDA_WRITE_FINAL_STATE = 2u    /* store each sequence's final state to states[slot]  */
+};
+
+/* Version of this interface (KDA_ABI_VERSION). */
+int32_t kda_abi_version(void);
+
+/* Static text for a status code. */
+const char* kda_status_string(kda_status_t status);
+
+/* Detail of the last failing call on the calling host thread ("" if none).
+ * The pointer stays valid until the next failing call on this thread. */
+const char* kda_last_error(void);
+
+/* Whether (dk, dv, chunk, io_dtype) has a built prefill kernel (1) or not (0).
+ * Supported: dk = dv in {16, 32, 64} with chunk in {16, 32, 64} for both
+ * dtypes (fp32 arithmetic); dk = dv = 128 with chunk in {16, 32} for both
+ * dtypes (fp32 arithmetic); dk = dv = 128, chunk = 64, bf16 (bf16 MFMA
+ * products, fp32 state and accumulation). */
+int32_t kda_chunk_fwd_supported(int32_t dk, int32_t dv, int32_t chunk, int32_t io_dtype);
+
+/* Device workspace bytes that kda_chunk_fwd needs for up to `total_tokens`
+ * tokens in up to `num_seqs` sequences (0 if none is needed).  Returns 0 for
+ * invalid or unsupported arguments as well; kda_chunk_fwd reports those. */
+size_t kda_chunk_fwd_workspace_bytes(const kda_shape_t* shape, int32_t chunk,
+                                     int32_t total_tokens, int32_t num_seqs);
+
+/* Chunkwise-parallel prefill over packed variable-length sequences.
+ *
+ * The result equals the token-by-token recurrence above (up to rounding):
+ * the chunked form regroups it into in-chunk products and a triangular solve
+ * plus a sequential pass over chunks (engineermaxxing ch. 04b-04f;
+ * heqinghuang section 10, with the decay products of section 11).  `chunk`
+ * changes cost, not semantics.
+ *
+ * cu_seqlens  device int32 [num_seqs + 1]; sequence n is tokens
+ *             [cu_seqlens[n], cu_seqlens[n+1]); expected cu[0] = 0,
+ *             nondecreasing, cu[num_seqs] = total_tokens.  Lengths need not
+ *             be multiples of `chunk`; a zero-length sequence is allowed.
+ * q, k        device [total_tokens, H, dk], io dtype.
+ * v           device [total_tokens, H, dv], io dtype.
+ * g           device fp32 [total_tokens, H, dk], log of the per-channel gate.
+ * beta        device fp32 [total_tokens, H], write strengths.
+ * states      device fp32 pool [num_slots, H, dk, dv] (may be NULL when
+ *             flags == 0).  Read at the start of sequence n when
+ *             KDA_READ_INITIAL_STATE is set, overwritten with its final state
+ *             when KDA_WRITE_FINAL_STATE is set.
+ * state_slots device int32 [num_seqs] (slot of sequence n), or NULL for slot n
+ *             (then num_slots >= num_seqs is required).  Slots must be
+ *             distinct within a call.
+ * o           device [total_tokens, H, dv], io dtype, fully overwritten.
+ * workspace   device scratch of at least kda_chunk_fwd_workspace_bytes()
+ *             bytes, 256-byte aligned; contents on entry are ignored.
+ * total_tokens == 0 or num_seqs == 0 is a no-op returning KDA_OK. */
+kda_status_t kda_chunk_fwd(const kda_shape_t* shape, int32_t chunk, int32_t total_tokens,
+                           int32_t num_seqs, const int32_t* cu_seqlens, const void* q,
+                           const void* k, const void* v, const float* g, const float* beta,
+                           float* states, int32_t num_slots, const int32_t* state_slots,
+                           uint32_t flags, void* o, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* One decode step: one new token per sequence against its resident state.
+ *
+ * For each b < batch and head h: S = states[slot(b), h] is faded by
+ * exp(g[b,h,:]) per key channel, read at k, corrected by beta (v - read),
+ * written back IN PLACE, and o[b,h,:] = S_new^T q (the recurrent form for
+ * decode: heqinghuang section 10; engineermaxxing ch. 02b and 06b).
+ *
+ * q, k     device [batch, H, dk], io dtype;  v, o: device [batch, H, dv], io dtype.
+ * g        device fp32 [batch, H, dk];       beta: device fp32 [batch, H].
+ * states   device fp32 pool [num_slots, H, dk, dv], updated in place.
+ * state_slots device int32 [batch] or NULL for slot b (num_slots >= batch).
+ *          Slots must be distinct within a call (two tokens of one sequence
+ *          are two calls).
+ * batch == 0 is a no-op returning KDA_OK.  Supported: dk, dv in
+ * {16, 32, 64, 128}, both dtypes. */
+kda_status_t kda_decode_step(const kda_shape_t* shape, int32_t batch, const void* q,
+                             const void* k, const void* v, const float* g, const float* beta,
+                             float* states, int32_t num_slots, const int32_t* state_slots,
+                             void* o, void* stream);
+
+/* Zero every state of a pool [num_slots, H, dk, dv] (fp32). */
+kda_status_t kda_state_init(const kda_shape_t* shape, float* states, int32_t num_slots,
+                            void* stream);
+
+/* Copy n dense states src [n, H, dk, dv] into pool slots slots[i] (or i when
+ * slots is NULL).  src and the pool must not overlap. */
+kda_status_t kda_state_load(const kda_shape_t* shape, float* states, int32_t num_slots,
+                            const int32_t* slots, int32_t n, const float* src, void* stream);
+
+/* Copy pool slots slots[i] (or i) into dense dst [n, H, dk, dv].  Entries with
+ * an out-of-range slot leave their dst rows unwritten. */
+kda_status_t kda_state_store(const kda_shape_t* shape, const float* states, int32_t num_slots,
+                             const int32_t* slots, int32_t n, float* dst, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

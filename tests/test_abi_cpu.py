@@ -1,0 +1,108 @@
+"""The C-ABI library loads and exports every entry point the header declares (CPU).
+
+No compute call is made here: only version/status queries and argument
+validation, which return before anything touches the GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s+(kda_[a-z0-9_]+)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from gated_delta_rule_08_amd import load_library, LIB_PATH
+    if not os.path.exists(LIB_PATH):
+        from gated_delta_rule_08_amd import build
+        build.build()
+    return load_library()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("kda_chunk_fwd", "kda_decode_step", "kda_state_init", "kda_state_load",
+                     "kda_state_store", "kda_chunk_fwd_workspace_bytes"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), f"libkda.so does not export {name}"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.kda_abi_version() == 1
+    assert lib.kda_status_string(0) == b"KDA_OK"
+    assert lib.kda_status_string(3) == b"KDA_ERR_WORKSPACE_TOO_SMALL"
+
+
+def _shape(H, dk, dv, io):
+    from gated_delta_rule_08_amd import _Shape
+    return _Shape(H, dk, dv, io)
+
+
+def test_supported_matrix(lib):
+    assert lib.kda_chunk_fwd_supported(128, 128, 64, 1) == 1
+    assert lib.kda_chunk_fwd_supported(128, 128, 64, 0) == 0   # fp32 at d=128 needs chunk <= 32
+    assert lib.kda_chunk_fwd_supported(128, 128, 32, 0) == 1
+    assert lib.kda_chunk_fwd_supported(16, 16, 16, 0) == 1
+    assert lib.kda_chunk_fwd_supported(96, 96, 64, 1) == 0
+    assert lib.kda_chunk_fwd_supported(16, 32, 16, 0) == 0
+
+
+def test_workspace_query(lib):
+    sh = _shape(16, 128, 128, 1)
+    n = lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(sh), 64, 4096, 1)
+    # one operand block set (~88 KiB) per (chunk, head), chunks <= T/C + N
+    assert 65 * 16 * 88 * 1024 <= n <= 65 * 16 * 92 * 1024 + 4096
+    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(_shape(2, 16, 16, 0)), 16, 64, 1) == 0
+
+
+def test_validation_errors_before_any_launch(lib):
+    P = ctypes.c_void_p
+    fake = P(0x1000)   # never dereferenced: every call below fails validation first
+    sh = _shape(16, 128, 128, 1)
+    args = lambda **kw: dict(dict(chunk=64, T=128, N=1, cu=fake, q=fake, k=fake, v=fake, g=fake,
+                                  beta=fake, states=None, ns=0, slots=None, flags=0, o=fake,
+                                  ws=None, wsb=0), **kw)
+
+    def call(shape, a):
+        return lib.kda_chunk_fwd(ctypes.byref(shape) if shape is not None else None, a["chunk"],
+                                 a["T"], a["N"], a["cu"], a["q"], a["k"], a["v"], a["g"], a["beta"],
+                                 a["states"], a["ns"], a["slots"], a["flags"], a["o"], a["ws"],
+                                 a["wsb"], None)
+
+    assert call(None, args()) == 1                                   # shape NULL
+    assert call(_shape(0, 128, 128, 1), args()) == 1                 # H = 0
+    assert call(_shape(16, 128, 128, 7), args()) == 1                # bad dtype
+    assert call(sh, args(chunk=48)) == 2                             # unsupported chunk
+    assert call(sh, args(flags=8)) == 1                              # unknown flag
+    assert call(sh, args(q=None)) == 1                               # NULL tensor
+    assert call(sh, args(flags=1)) == 1                              # state I/O without states
+    assert call(sh, args()) == 3                                     # workspace missing
+    assert b"workspace" in lib.kda_last_error()
+    assert call(sh, args(T=0)) == 0                                  # empty: no-op
+    assert call(sh, args(N=0)) == 0
+    # decode
+    assert lib.kda_decode_step(ctypes.byref(_shape(32, 96, 96, 1)), 4, fake, fake, fake, fake,
+                               fake, fake, 4, None, fake, None) == 2
+    assert lib.kda_decode_step(ctypes.byref(sh), 4, fake, fake, fake, fake, fake, fake, 2, None,
+                               fake, None) == 1                      # too few slots
+    assert lib.kda_decode_step(ctypes.byref(sh), 0, None, None, None, None, None, None, 0, None,
+                               None, None) == 0
+    # state helpers
+    assert lib.kda_state_init(ctypes.byref(sh), None, 3, None) == 1
+    assert lib.kda_state_load(ctypes.byref(sh), fake, 2, None, 3, fake, None) == 1
+    assert lib.kda_state_store(ctypes.byref(sh), fake, 4, None, 0, None, None) == 0
