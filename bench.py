@@ -1,0 +1,235 @@
+"""Benchmark of the KDA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Prefill: kda_chunk_fwd on the packed-sequence workload B=1, H=16, T=4096,
+dk=dv=128, chunk=64, bf16 I/O, fp32 state, zero initial state, final state
+written.  Decode: kda_decode_step on B=256 sequences x H=32 heads, d=128,
+against a 512 MiB resident fp32 state pool, updated in place.  Inputs are the
+seeded synthetic workloads of gated_delta_rule_08_amd.workloads, already
+resident in HBM before timing starts.
+
+Each timed step is one prefill pass (then, in its own loop, one decode step).
+Before every timed step a 1 GiB fill evicts the 256 MB Infinity Cache, so
+inputs come from HBM; the fill is outside the HIP events that time the step.
+`value` is prefill tokens/s = T / (mean event time of one kda_chunk_fwd call);
+decode steps/s is reported next to it with its own roofline.  The oracle
+(fp64, host threads) is timed on the same prefill input as a CPU baseline.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s (H=16,d=128,T=4096) + decode steps/s; % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+PREFILL_BYTES_PER_TOKEN_HEAD = 3 * 2 * 128 + 4 * 128 + 4 + 2 * 128   # q,k,v bf16 + g fp32 + beta + o bf16
+DECODE_BYTES_PER_HEAD = 2 * 128 * 128 * 4 + PREFILL_BYTES_PER_TOKEN_HEAD  # state read+write + token
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def _source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_delta_rule_08_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kind: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    when the kernel sources changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != _source_digest():
+        return None
+    return rec.get(kind)
+
+
+def _events_ms(pairs):
+    return [s.elapsed_time(e) for s, e in pairs]
+
+
+def bench_prefill(kda, torch, steps, warmup, flush):
+    from gated_delta_rule_08_amd import workloads
+    p = workloads.make_inputs(1)
+    cfg = p["config"]
+    dev = "cuda"
+    t = lambda a, dt: torch.from_numpy(a).to(dt).to(dev)
+    q, k, v = (t(p[n], torch.bfloat16) for n in ("q", "k", "v"))
+    g, beta = t(p["g"], torch.float32), t(p["beta"], torch.float32)
+    cu = t(p["cu_seqlens"], torch.int32)
+    T, H, d = q.shape
+    N = cu.numel() - 1
+    states = torch.zeros((N, H, d, d), dtype=torch.float32, device=dev)
+    o = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(kda.kda_chunk_fwd_workspace_bytes(H, d, d, torch.bfloat16, cfg.chunk, T, N),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        kda.kda_chunk_fwd(q, k, v, g, beta, cu, chunk=cfg.chunk, states=states, write_final=True,
+                          o=o, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        flush()
+        step()
+    torch.cuda.synchronize()
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s, e in pairs:
+        flush()
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = _events_ms(pairs)
+    # warm-cache figure (no eviction between steps), for context only
+    ws_pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(steps)]
+    for s, e in ws_pairs:
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize()
+    ms_warm = _events_ms(ws_pairs)
+    return dict(cfg=cfg, T=T, H=H, d=d, N=N, ms=ms, ms_warm=ms_warm, wall=wall, inputs=p)
+
+
+def bench_decode(kda, torch, steps, warmup, flush):
+    from gated_delta_rule_08_amd import workloads
+    p = workloads.make_inputs(2)
+    dev = "cuda"
+    t = lambda a, dt: torch.from_numpy(a).to(dt).to(dev)
+    q, k, v = (t(p[n], torch.bfloat16) for n in ("q", "k", "v"))
+    g, beta = t(p["g"], torch.float32), t(p["beta"], torch.float32)
+    states = t(p["s0"], torch.float32)
+    B, H, d = q.shape
+    o = torch.empty((B, H, d), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        kda.kda_decode_step(q, k, v, g, beta, states, o=o, stream=stream)
+
+    for _ in range(warmup):
+        flush()
+        step()
+    torch.cuda.synchronize()
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(steps)]
+    for s, e in pairs:
+        flush()
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize()
+    return dict(B=B, H=H, d=d, ms=_events_ms(pairs))
+
+
+def cpu_baseline(p, budget_s=10.0):
+    import oracle
+    nthreads = min(16, os.cpu_count() or 1, p["q"].shape[1])
+    T = p["q"].shape[0]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.run(p["q"], p["k"], p["v"], p["g"], p["beta"], p["cu_seqlens"], nthreads=nthreads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or el / reps * (reps + 1) > 3 * budget_s:
+            break
+    return {"value": reps * T / el, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"the full prefill input (T={T}, H={p['q'].shape[1]}, d=128), run {reps}x "
+                      f"in {el:.1f} s, fp64 sequential recurrence, one thread per head"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="run one leg only (for profiling)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path shards over "
+              "heads/sequences without communication, see DESIGN.md", file=sys.stderr)
+        return 2
+    import torch
+    import gated_delta_rule_08_amd as kda
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    kda.load_library()
+    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+    counter = [0]
+
+    def flush():
+        counter[0] += 1
+        flush_buf.fill_(float(counter[0] & 7))
+
+    out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic"}
+    if args.only in (None, "prefill"):
+        pr = bench_prefill(kda, torch, args.steps, args.warmup, flush)
+        ms = sum(pr["ms"]) / len(pr["ms"])
+        T, H = pr["T"], pr["H"]
+        bytes_ = PREFILL_BYTES_PER_TOKEN_HEAD * T * H + pr["N"] * H * 128 * 128 * 4
+        achieved = bytes_ / (ms * 1e-3) / 1e9
+        tr = _traffic("prefill_bytes")
+        out.update({
+            "value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+            "config": {"workload": pr["cfg"].name, "global_batch": 1, "seq_len": T,
+                       "num_heads": H, "head_dim": 128, "chunk": 64, "io": "bf16",
+                       "state": "fp32", "parallelism": "single-gpu"},
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                         "traffic": tr, "kernel": "kda_chunk_fwd (index + prep + scan launches)",
+                         "algorithmic_bytes": bytes_},
+            "prefill_ms": {"mean": ms, "min": min(pr["ms"]), "max": max(pr["ms"]),
+                           "warm_cache_mean": sum(pr["ms_warm"]) / len(pr["ms_warm"])},
+            "wall_s_timed_region": pr["wall"],
+        })
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline(pr["inputs"])
+        del pr
+    if args.only in (None, "decode"):
+        dc = bench_decode(kda, torch, args.steps, args.warmup, flush)
+        ms = sum(dc["ms"]) / len(dc["ms"])
+        bytes_ = DECODE_BYTES_PER_HEAD * dc["B"] * dc["H"]
+        achieved = bytes_ / (ms * 1e-3) / 1e9
+        out["decode"] = {
+            "value": 1e3 / ms, "unit": "steps/s", "ms_per_step": ms,
+            "tokens_per_s": dc["B"] * 1e3 / ms,
+            "workload": "decode_bf16_B256_H32_d128 (512 MiB fp32 state pool)",
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                         "traffic": _traffic("decode_bytes"), "kernel": "decode_kernel",
+                         "algorithmic_bytes": bytes_},
+        }
+        if args.only == "decode":
+            out.update({"value": 1e3 / ms, "unit": "steps/s", "ms_per_step": ms,
+                        "config": {"workload": "decode_bf16_B256_H32_d128"}})
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

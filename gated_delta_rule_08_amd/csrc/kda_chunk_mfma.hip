@@ -23,9 +23,10 @@
 //     gated Gram blocks, the triangular inverse (fp32), W, Ut, Q*Gam,
 //     (K*exp(G_C-G))^T, A_qk and Gam_C, and stores the MFMA operands in the
 //     exact per-lane order the scan consumes (one 16-byte load per lane).
-//  3. scan:  one wave per (sequence, head, 16 state columns).  The columns of
-//     S evolve independently given k, beta and g, so the state is split over
-//     8 waves per head.  Each wave keeps its 128 x 16 fp32 slice of S as MFMA
+//  3. scan:  one wave per (sequence, head, 16 state columns), four waves per
+//     workgroup sharing the chunk operands through LDS.  The columns of S
+//     evolve independently given k, beta and g, so the state is split over 8
+//     waves per head.  Each wave keeps its 128 x 16 fp32 slice of S as MFMA
 //     accumulators for the whole sequence and walks the chunks in order: the
 //     only loop-carried dependency of the method (heqinghuang section 10: the
 //     only sequential loop is over chunks).
@@ -71,15 +72,36 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 // accumulator pair converts to a B operand without moving data across lanes.
 __device__ __forceinline__ int kpos(int g, int q) { return q < 4 ? 4 * g + q : 12 + 4 * g + q; }
 
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
 __device__ __forceinline__ bf16x8 pack8(const float* f) {
-  u16x8 u;
+  f32x8 v;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) u[i] = f32_to_bf16(f[i]);
-  return __builtin_bit_cast(bf16x8, u);
+  for (int i = 0; i < 8; ++i) v[i] = f[i];
+  return __builtin_convertvector(v, bf16x8);  // v_cvt_pk_bf16_f32, round to nearest even
 }
 __device__ __forceinline__ bf16x8 pack_acc(f32x4 lo, f32x4 hi) {
-  float f[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return pack8(f);
+  const f32x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_convertvector(v, bf16x8);
+}
+
+// The 8 values a lane holds for K-block s: elements 32s+4g .. +3 and 32s+16+4g .. +3
+// of a padded LDS row (bf16 or fp32), read as two vector loads.
+__device__ __forceinline__ void runs_bf(const uint16_t* row, int s, int g, float out[8]) {
+  const uint2 a = *reinterpret_cast<const uint2*>(row + 32 * s + 4 * g);
+  const uint2 b = *reinterpret_cast<const uint2*>(row + 32 * s + 16 + 4 * g);
+  const uint32_t w[4] = {a.x, a.y, b.x, b.y};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void runs_f32(const float* row, int s, int g, float out[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(row + 32 * s + 4 * g);
+  const float4 b = *reinterpret_cast<const float4*>(row + 32 * s + 16 + 4 * g);
+  out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+  out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
 }
 
 struct Workspace {
@@ -161,7 +183,9 @@ struct PrepSmem {
 
 __device__ __forceinline__ float ld_bf(const uint16_t* row, int c) { return bf16_to_f32(row[c]); }
 
-__global__ __launch_bounds__(256) void prep_kernel(
+// LDS use allows one workgroup (one wave per SIMD) per CU: let the compiler
+// spend registers on batching loads instead of aiming for occupancy.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, int32_t N, int H, Workspace w) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
@@ -181,31 +205,49 @@ __global__ __launch_bounds__(256) void prep_kernel(
   const int c = min(C, w.seq_end[n] - t0);  // valid rows (>= 1)
   const size_t ci = (size_t)gc * H + h;
 
-  // ---- phase 0: stage the chunk in LDS (padded rows are neutral tokens)
-  for (int u = tid; u < C * 16; u += 256) {
-    const int r = u >> 4, cc = (u & 15) * 8;
-    uint4 kk = make_uint4(0, 0, 0, 0), qq = kk, vv = kk;
-    if (r < c) {
-      const size_t gi = ((size_t)(t0 + r) * H + h) * D + cc;
-      kk = *reinterpret_cast<const uint4*>(k + gi);
-      qq = *reinterpret_cast<const uint4*>(q + gi);
-      vv = *reinterpret_cast<const uint4*>(v + gi);
+  // ---- phase 0: stage the chunk in LDS (padded rows are neutral tokens).
+  // Every global load is issued before the first LDS write: rows past the end
+  // of the sequence read the last valid row and are zeroed afterwards.
+  {
+    uint4 kk[4], qq[4], vv[4];
+    float4 gg[8];
+    const size_t rowstride = (size_t)H * D;
+    const size_t base = ((size_t)t0 * H + h) * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = tid + 256 * i, r = u >> 4, cc = (u & 15) * 8;
+      const size_t gi = base + (size_t)min(r, c - 1) * rowstride + cc;
+      kk[i] = *reinterpret_cast<const uint4*>(k + gi);
+      qq[i] = *reinterpret_cast<const uint4*>(q + gi);
+      vv[i] = *reinterpret_cast<const uint4*>(v + gi);
     }
-    uint2* pk = reinterpret_cast<uint2*>(&sm.K[r][cc]);
-    uint2* pq = reinterpret_cast<uint2*>(&sm.Q[r][cc]);
-    uint2* pv = reinterpret_cast<uint2*>(&sm.V[r][cc]);
-    pk[0] = make_uint2(kk.x, kk.y); pk[1] = make_uint2(kk.z, kk.w);
-    pq[0] = make_uint2(qq.x, qq.y); pq[1] = make_uint2(qq.z, qq.w);
-    pv[0] = make_uint2(vv.x, vv.y); pv[1] = make_uint2(vv.z, vv.w);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int u = tid + 256 * i, r = u >> 5, cc = (u & 31) * 4;
+      gg[i] = *reinterpret_cast<const float4*>(g + base + (size_t)min(r, c - 1) * rowstride + cc);
+    }
+    const float bt = beta[(size_t)(t0 + min(tid & 63, c - 1)) * H + h];
+    const uint4 z4 = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = tid + 256 * i, r = u >> 4, cc = (u & 15) * 8;
+      const bool ok = r < c;
+      const uint4 a = ok ? kk[i] : z4, b = ok ? qq[i] : z4, d = ok ? vv[i] : z4;
+      uint2* pk = reinterpret_cast<uint2*>(&sm.K[r][cc]);
+      uint2* pq = reinterpret_cast<uint2*>(&sm.Q[r][cc]);
+      uint2* pv = reinterpret_cast<uint2*>(&sm.V[r][cc]);
+      pk[0] = make_uint2(a.x, a.y); pk[1] = make_uint2(a.z, a.w);
+      pq[0] = make_uint2(b.x, b.y); pq[1] = make_uint2(b.z, b.w);
+      pv[0] = make_uint2(d.x, d.y); pv[1] = make_uint2(d.z, d.w);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int u = tid + 256 * i, r = u >> 5, cc = (u & 31) * 4;
+      *reinterpret_cast<float4*>(&sm.G[r][cc]) = r < c ? gg[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (tid < C) sm.bs[tid] = tid < c ? bt : 0.f;
+    for (int u = tid; u < C * AP; u += 256) (&sm.Tm[0][0])[u] = 0.f;
   }
-  for (int u = tid; u < C * 32; u += 256) {
-    const int r = u >> 5, cc = (u & 31) * 4;
-    float4 gg = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (r < c) gg = *reinterpret_cast<const float4*>(g + ((size_t)(t0 + r) * H + h) * D + cc);
-    *reinterpret_cast<float4*>(&sm.G[r][cc]) = gg;
-  }
-  if (tid < C) sm.bs[tid] = tid < c ? beta[(size_t)(t0 + tid) * H + h] : 0.f;
-  for (int u = tid; u < C * AP; u += 256) (&sm.Tm[0][0])[u] = 0.f;
   __syncthreads();
 
   // ---- phase 1: running sum of the log-gates down each channel
@@ -241,44 +283,49 @@ __global__ __launch_bounds__(256) void prep_kernel(
     for (int off = 32; off >= 1; off >>= 1) sp = fmaxf(sp, __shfl_xor(sp, off, 64));
     const bool fast_diag = sp <= kMaxSpread;
 
-    // B operands: rows r of block R scaled by exp(G_r - G_s)  (<= 1)
+    // B operands: rows r of block R scaled by exp(G_r - G_s) (<= 1); the same
+    // rows scaled by exp(G_r) are Q*Gam, stored as the scan's A operand.
+    const int r = sR + li;
     bf16x8 bk[4], bq[4];
-    {
-      const int r = sR + li;
+    float gs[4][8];
+    uint16_t* qg_out = reinterpret_cast<uint16_t*>(w.qg + ci * kQgBytes);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        float fk[8], fq[8];
+    for (int s = 0; s < 4; ++s) {
+      float kr[8], qr[8], gr[8], fk[8], fq[8], fg[8];
+      runs_bf(sm.K[r], s, lg, kr);
+      runs_bf(sm.Q[r], s, lg, qr);
+      runs_f32(sm.G[r], s, lg, gr);
+      runs_f32(sm.G[sR], s, lg, gs[s]);
 #pragma unroll
-        for (int qq = 0; qq < 8; ++qq) {
-          const int cc = 32 * s + kpos(lg, qq);
-          const float f = fast_exp(sm.G[r][cc] - sm.G[sR][cc]);
-          fk[qq] = ld_bf(sm.K[r], cc) * f;
-          fq[qq] = ld_bf(sm.Q[r], cc) * f;
-        }
-        bk[s] = pack8(fk);
-        bq[s] = pack8(fq);
+      for (int i = 0; i < 8; ++i) {
+        const float f = fast_exp(gr[i] - gs[s][i]);
+        fk[i] = kr[i] * f;
+        fq[i] = qr[i] * f;
+        fg[i] = qr[i] * fast_exp(gr[i]);
       }
+      bk[s] = pack8(fk);
+      bq[s] = pack8(fq);
+      *reinterpret_cast<bf16x8*>(qg_out + ((size_t)(R * 4 + s) * 64 + lane) * 8) = pack8(fg);
     }
     uint16_t* aq_out = reinterpret_cast<uint16_t*>(w.aq + ci * kAqBytes);
     for (int J = 0; J < 4; ++J) {
       f32x4 acck = {0.f, 0.f, 0.f, 0.f}, accq = acck;
       if (J < R || (J == R && fast_diag)) {
+        // A operand: rows j of block J scaled by exp(G_s - G_j)
         const int j = 16 * J + li;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          float fa[8];
+          float kj[8], gj[8], fa[8];
+          runs_bf(sm.K[j], s, lg, kj);
+          runs_f32(sm.G[j], s, lg, gj);
 #pragma unroll
-          for (int qq = 0; qq < 8; ++qq) {
-            const int cc = 32 * s + kpos(lg, qq);
-            fa[qq] = ld_bf(sm.K[j], cc) * fast_exp(sm.G[sR][cc] - sm.G[j][cc]);
-          }
+          for (int i = 0; i < 8; ++i) fa[i] = kj[i] * fast_exp(gs[s][i] - gj[i]);
           const bf16x8 ak = pack8(fa);
           acck = mfma(ak, bk[s], acck);
           accq = mfma(ak, bq[s], accq);
         }
       } else if (J == R) {
         // extreme decay inside the block: exact element-wise fp32 sums
-        const int r = sR + li;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int j = sR + 4 * lg + jj;
@@ -296,23 +343,21 @@ __global__ __launch_bounds__(256) void prep_kernel(
         }
       }
       // lane holds raw A[r = sR + li][j = 16J + 4lg + jj]
-      const int r = sR + li;
       const float br = sm.bs[r];
       float4 arow;
-      uint16_t qv[4];
+      float qv[4];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int j = 16 * J + 4 * lg + jj;
-        const float akk = j < r ? br * acck[jj] : 0.f;
-        const float aqk = j <= r ? accq[jj] : 0.f;
-        (&arow.x)[jj] = akk;
-        qv[jj] = f32_to_bf16(aqk);
+        (&arow.x)[jj] = j < r ? br * acck[jj] : 0.f;
+        qv[jj] = j <= r ? accq[jj] : 0.f;
       }
       *reinterpret_cast<float4*>(&sm.A[r][16 * J + 4 * lg]) = arow;
       // A_qk as the scan's A operand: [m = R][s' = J / 2][lane][slots (J & 1) * 4 ..]
       uint16_t* dst = aq_out + ((size_t)(R * 2 + (J >> 1)) * 64 + lane) * 8 + (J & 1) * 4;
       *reinterpret_cast<uint2*>(dst) =
-          make_uint2((uint32_t)qv[0] | ((uint32_t)qv[1] << 16), (uint32_t)qv[2] | ((uint32_t)qv[3] << 16));
+          make_uint2((uint32_t)f32_to_bf16(qv[0]) | ((uint32_t)f32_to_bf16(qv[1]) << 16),
+                     (uint32_t)f32_to_bf16(qv[2]) | ((uint32_t)f32_to_bf16(qv[3]) << 16));
     }
   }
   __syncthreads();
@@ -447,40 +492,71 @@ __global__ __launch_bounds__(256) void prep_kernel(
       }
     }
 
-    // (c) Q*Gam as the scan's A operand: [m = wave][s][lane]
-    uint16_t* qg_out = reinterpret_cast<uint16_t*>(w.qg + ci * kQgBytes);
-    {
-      const int r = 16 * wave + li;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        float f[8];
-#pragma unroll
-        for (int qq = 0; qq < 8; ++qq) {
-          const int cc = 32 * s + kpos(lg, qq);
-          f[qq] = ld_bf(sm.Q[r], cc) * fast_exp(sm.G[r][cc]);
-        }
-        *reinterpret_cast<bf16x8*>(qg_out + ((size_t)(wave * 4 + s) * 64 + lane) * 8) = pack8(f);
-      }
-    }
     // (d) Gam_C
     if (tid < D) reinterpret_cast<float*>(w.gc + ci * kGcBytes)[tid] = fast_exp(sm.G[C - 1][tid]);
   }
 }
 
 // ------------------------------------------------------------------ 3. scan
-// One wave per (sequence n, head h, column block nb of 16 state columns).
-// Block index b -> head_lin = b % NH, nb = b / NH, so the 8 column blocks of a
-// head land on the same XCD (workgroups are dealt to XCDs round-robin) and
-// share its L2 for the per-chunk operands.
-__global__ __launch_bounds__(64) void scan_kernel(
+// One workgroup of 4 waves per (sequence n, head h, half of the state columns);
+// wave w owns 16 columns.  The per-chunk operands that all columns share (-W,
+// Q*Gam, Kd^T, A_qk), this half's Ut tiles and Gam_C are copied from the
+// workspace into LDS with direct global->LDS loads, double buffered: the copy
+// for chunk c+1 is in flight while chunk c is computed from the other buffer.
+// Block index b -> head_lin = b % NH, half = b / NH, so both halves of a head
+// land on the same XCD (workgroups are dealt to XCDs round-robin) and share
+// its L2.
+constexpr int kScanWaves = 4;
+
+struct ScanBuf {
+  bf16x8 wn[16][64];    // [m*4 + s][lane]
+  bf16x8 qg[16][64];    // [m*4 + s][lane]
+  bf16x8 kd[16][64];    // [t*2 + s'][lane]
+  bf16x8 aq[8][64];     // [m*2 + s'][lane]
+  f32x4 ut[4][4][64];   // [m][local column tile][lane]
+  f32x4 gc[32];         // Gam_C
+};
+
+__device__ __forceinline__ void dma16(const uint8_t* src, void* lds_dst) {
+  // each lane copies 16 bytes; lane i lands at lds_dst + 16 i
+  __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
+                                   (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+}
+
+__device__ __forceinline__ void issue_chunk(const Workspace& w, size_t ci, int half,
+                                            ScanBuf* dst, int wave, int lane) {
+  const uint8_t* wn = w.wn + ci * kWnBytes;
+  const uint8_t* qg = w.qg + ci * kQgBytes;
+  const uint8_t* kd = w.kd + ci * kKdBytes;
+  const uint8_t* aq = w.aq + ci * kAqBytes;
+  const uint8_t* ut = w.ut + ci * kUtBytes;
+  const int off = lane * 16;
+#pragma unroll
+  for (int i = 0; i < 18; ++i) {
+    const int p = wave + kScanWaves * i;  // 72 pieces of 1 KiB, wave-uniform
+    if (p < 16) dma16(wn + p * 1024 + off, &dst->wn[p][0]);
+    else if (p < 32) dma16(qg + (p - 16) * 1024 + off, &dst->qg[p - 16][0]);
+    else if (p < 48) dma16(kd + (p - 32) * 1024 + off, &dst->kd[p - 32][0]);
+    else if (p < 56) dma16(aq + (p - 48) * 1024 + off, &dst->aq[p - 48][0]);
+    else {
+      const int q = p - 56, m = q >> 2, nbl = q & 3;
+      dma16(ut + (size_t)((m * 8 + half * 4 + nbl) * 64) * 16 + off, &dst->ut[m][nbl][0]);
+    }
+  }
+  if (wave == 0 && lane < 32) dma16(w.gc + ci * kGcBytes + off, &dst->gc[0]);
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void scan_kernel(
     int32_t N, int H, Workspace w, float* __restrict__ states, int32_t num_slots,
     const int32_t* __restrict__ slots, uint32_t flags, uint16_t* __restrict__ o) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  ScanBuf* buf = reinterpret_cast<ScanBuf*>(smem_raw);
   const int NH = N * H;
   const int head_lin = blockIdx.x % NH;
-  const int nb = blockIdx.x / NH;
+  const int half = blockIdx.x / NH;
   const int n = head_lin / H, h = head_lin - n * H;
-  const int lane = threadIdx.x, li = lane & 15, lg = lane >> 4;
-  const int col = 16 * nb + li;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+  const int col = 16 * (half * kScanWaves + wave) + li;
 
   const int start = w.seq_start[n], end = w.seq_end[n], nch = w.seq_nch[n];
   const int cbase = w.chunk_off[n];
@@ -490,68 +566,107 @@ __global__ __launch_bounds__(64) void scan_kernel(
 
   // state slice: S[t] lane holds rows 16t + 4lg + jj of column col
   f32x4 S[8];
+  if (slot_ok && (flags & KDA_READ_INITIAL_STATE)) {  // uniform branch; all loads in flight
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < 8; ++t)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-      S[t][jj] = (slot_ok && (flags & KDA_READ_INITIAL_STATE))
-                     ? Sg[(size_t)(16 * t + 4 * lg + jj) * D + col] : 0.f;
+      for (int jj = 0; jj < 4; ++jj) S[t][jj] = Sg[(size_t)(16 * t + 4 * lg + jj) * D + col];
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
+  // Outputs of chunk c are stored right after the copies for chunk c+2 are
+  // issued, so the stores overlap the compute of chunk c+1 and have retired
+  // by the time the next wait for copies comes around.
+  f32x4 Oprev[4];
+  int prev_base = -1;
+  auto store_rows = [&](const f32x4* Ov, int base) {
+    if (base < 0) return;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int tok = base + 16 * m + 4 * lg + jj;
+        if (tok < end) o[((size_t)tok * H + h) * D + col] = f32_to_bf16(Ov[m][jj]);
+      }
+  };
+
+  if (nch > 0) issue_chunk(w, (size_t)cbase * H + h, half, &buf[0], wave, lane);
   for (int lc = 0; lc < nch; ++lc) {
-    const size_t ci = (size_t)(cbase + lc) * H + h;
-    const bf16x8* wn = reinterpret_cast<const bf16x8*>(w.wn + ci * kWnBytes);
-    const bf16x8* qg = reinterpret_cast<const bf16x8*>(w.qg + ci * kQgBytes);
-    const bf16x8* kd = reinterpret_cast<const bf16x8*>(w.kd + ci * kKdBytes);
-    const bf16x8* aq = reinterpret_cast<const bf16x8*>(w.aq + ci * kAqBytes);
-    const f32x4* ut = reinterpret_cast<const f32x4*>(w.ut + ci * kUtBytes);
-    const f32x4* gcv = reinterpret_cast<const f32x4*>(w.gc + ci * kGcBytes);
+    // chunk lc has landed (this wave's copies), then all waves' copies are
+    // visible and every wave is done with the buffer about to be refilled
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (lc + 1 < nch)
+      issue_chunk(w, (size_t)(cbase + lc + 1) * H + h, half, &buf[(lc + 1) & 1], wave, lane);
+    store_rows(Oprev, prev_base);
+    const ScanBuf& B = buf[lc & 1];
 
+    // Operands of this chunk: LDS -> registers in three batches, each issued
+    // ahead of the MFMAs that consume it (the scheduling barriers keep the
+    // compiler from interleaving one read per MFMA).
+    bf16x8 a_wn[16];
+    f32x4 U[4];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a_wn[i] = B.wn[i][lane];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) U[m] = B.ut[m][wave][lane];
     bf16x8 sb[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) sb[s] = pack_acc(S[2 * s], S[2 * s + 1]);
+    bf16x8 a_qg[16], a_aq[6];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a_qg[i] = B.qg[i][lane];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) a_aq[i] = B.aq[i < 2 ? 2 * i : i + 2][lane];  // [0],[2],[4],[5],[6],[7]
+    __builtin_amdgcn_sched_barrier(0);
 
     // U = Ut - W S
-    f32x4 U[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      U[m] = ut[(m * 8 + nb) * 64 + lane];
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) U[m] = mfma(wn[(m * 4 + s) * 64 + lane], sb[s], U[m]);
-    }
-    bf16x8 ub[2];
-    ub[0] = pack_acc(U[0], U[1]);
-    ub[1] = pack_acc(U[2], U[3]);
-
-    // O = (Q*Gam) S + A_qk U
+      for (int s = 0; s < 4; ++s) U[m] = mfma(a_wn[m * 4 + s], sb[s], U[m]);
+    // O, first part: (Q*Gam) S
     f32x4 O[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       O[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) O[m] = mfma(qg[(m * 4 + s) * 64 + lane], sb[s], O[m]);
-      O[m] = mfma(aq[(m * 2 + 0) * 64 + lane], ub[0], O[m]);
-      if (m >= 2) O[m] = mfma(aq[(m * 2 + 1) * 64 + lane], ub[1], O[m]);
+      for (int s = 0; s < 4; ++s) O[m] = mfma(a_qg[m * 4 + s], sb[s], O[m]);
     }
+    bf16x8 a_kd[16];
+    f32x4 gcv[8];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a_kd[i] = B.kd[i][lane];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) gcv[t] = B.gc[4 * t + lg];
+    __builtin_amdgcn_sched_barrier(0);
 
+    bf16x8 ub[2];
+    ub[0] = pack_acc(U[0], U[1]);
+    ub[1] = pack_acc(U[2], U[3]);
+    // O += A_qk U   (A_qk rows 0-31 have no entries in columns 32-63)
+    O[0] = mfma(a_aq[0], ub[0], O[0]);
+    O[1] = mfma(a_aq[1], ub[0], O[1]);
+    O[2] = mfma(a_aq[2], ub[0], O[2]);
+    O[2] = mfma(a_aq[3], ub[1], O[2]);
+    O[3] = mfma(a_aq[4], ub[0], O[3]);
+    O[3] = mfma(a_aq[5], ub[1], O[3]);
     // S' = Diag(Gam_C) S + Kd^T U
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const f32x4 gm = gcv[4 * t + lg];
-      S[t] = S[t] * gm;
-      S[t] = mfma(kd[(t * 2 + 0) * 64 + lane], ub[0], S[t]);
-      S[t] = mfma(kd[(t * 2 + 1) * 64 + lane], ub[1], S[t]);
+      S[t] = S[t] * gcv[t];
+      S[t] = mfma(a_kd[t * 2 + 0], ub[0], S[t]);
+      S[t] = mfma(a_kd[t * 2 + 1], ub[1], S[t]);
     }
 
-    // outputs of the valid rows of this chunk
-    const int tbase = start + lc * C;
+    // keep this chunk's outputs; they are stored early in the next iteration
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int tok = tbase + 16 * m + 4 * lg + jj;
-        if (tok < end) o[((size_t)tok * H + h) * D + col] = f32_to_bf16(O[m][jj]);
-      }
+    for (int m = 0; m < 4; ++m) Oprev[m] = O[m];
+    prev_base = start + lc * C;
   }
+  store_rows(Oprev, prev_base);
 
   if (slot_ok && (flags & KDA_WRITE_FINAL_STATE)) {
 #pragma unroll
@@ -591,6 +706,9 @@ kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, cons
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)sizeof(PrepSmem));
     if (e != hipSuccess) return hip_status(e, "hipFuncSetAttribute(prep)");
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(scan_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * sizeof(ScanBuf)));
+    if (e != hipSuccess) return hip_status(e, "hipFuncSetAttribute(scan)");
     attr_set = true;
   }
   hipLaunchKernelGGL(prep_kernel, dim3((unsigned)cap, (unsigned)H), dim3(256), sizeof(PrepSmem),
@@ -598,8 +716,9 @@ kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, cons
                      static_cast<const uint16_t*>(v), g, beta, N, H, w);
   st = check_launch("chunk_fwd prep");
   if (st != KDA_OK) return st;
-  hipLaunchKernelGGL(scan_kernel, dim3((unsigned)(N * H * (D / 16))), dim3(64), 0, stream, N, H, w,
-                     states, num_slots, slots, flags, static_cast<uint16_t*>(o));
+  hipLaunchKernelGGL(scan_kernel, dim3((unsigned)(N * H * (D / (16 * kScanWaves)))),
+                     dim3(64 * kScanWaves), 2 * sizeof(ScanBuf), stream, N, H, w, states,
+                     num_slots, slots, flags, static_cast<uint16_t*>(o));
   return check_launch("chunk_fwd scan");
 }
 
