@@ -23,13 +23,13 @@
 //     gated Gram blocks, the triangular inverse (fp32), W, Ut, Q*Gam,
 //     (K*exp(G_C-G))^T, A_qk and Gam_C, and stores the MFMA operands in the
 //     exact per-lane order the scan consumes (one 16-byte load per lane).
-//  3. scan:  one wave per (sequence, head, 16 state columns), four waves per
-//     workgroup sharing the chunk operands through LDS.  The columns of S
-//     evolve independently given k, beta and g, so the state is split over 8
-//     waves per head.  Each wave keeps its 128 x 16 fp32 slice of S as MFMA
+//  3. scan:  waves own tiles of 16 state columns of one (sequence, head); the
+//     columns of S evolve independently given k, beta and g, so the state is
+//     split over waves.  Each wave keeps its 128-row slice of S as MFMA
 //     accumulators for the whole sequence and walks the chunks in order: the
 //     only loop-carried dependency of the method (heqinghuang section 10: the
-//     only sequential loop is over chunks).
+//     only sequential loop is over chunks).  The waves of a workgroup share
+//     each chunk's operands through LDS.
 //
 // Numerics of the gated Gram products: exp(G_r - G_j) is split at the first
 // row s of the 16-row block of r as exp(G_r - G_s) * exp(G_s - G_j).  For j in
@@ -498,23 +498,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // ------------------------------------------------------------------ 3. scan
-// One workgroup of 4 waves per (sequence n, head h, half of the state columns);
-// wave w owns 16 columns.  The per-chunk operands that all columns share (-W,
-// Q*Gam, Kd^T, A_qk), this half's Ut tiles and Gam_C are copied from the
-// workspace into LDS with direct global->LDS loads, double buffered: the copy
-// for chunk c+1 is in flight while chunk c is computed from the other buffer.
-// Block index b -> head_lin = b % NH, half = b / NH, so both halves of a head
-// land on the same XCD (workgroups are dealt to XCDs round-robin) and share
-// its L2.
-constexpr int kScanWaves = 4;
-
+// A workgroup of WAVES waves owns 16 * NT * WAVES state columns of one
+// (sequence n, head h); each wave owns NT tiles of 16 columns.  The per-chunk
+// operands that every column needs (-W, Q*Gam, Kd^T, A_qk), the workgroup's
+// Ut tiles and Gam_C are copied from the workspace into LDS with direct
+// global->LDS loads, double buffered: the copy for chunk c+1 is in flight
+// while chunk c is computed from the other buffer.  More waves per workgroup
+// share one copy; more tiles per wave reuse each operand register for NT
+// MFMAs, so fewer LDS bytes are read per unit of work.
+//
+// Block index b -> head_lin = b % NH, group = b / NH, so the column groups of
+// a head land on the same XCD when NH is a multiple of 8 (workgroups are dealt
+// to XCDs round-robin) and share its L2.
+template <int WAVES, int NT>
 struct ScanBuf {
-  bf16x8 wn[16][64];    // [m*4 + s][lane]
-  bf16x8 qg[16][64];    // [m*4 + s][lane]
-  bf16x8 kd[16][64];    // [t*2 + s'][lane]
-  bf16x8 aq[8][64];     // [m*2 + s'][lane]
-  f32x4 ut[4][4][64];   // [m][local column tile][lane]
-  f32x4 gc[32];         // Gam_C
+  static constexpr int kTiles = WAVES * NT;  // 16-column tiles per workgroup
+  // Ut goes through LDS when both buffers fit; otherwise each wave loads its
+  // own Ut tiles into registers one chunk ahead.
+  static constexpr bool kUtInLds = kTiles <= 4;
+  bf16x8 wn[16][64];                        // [m*4 + s][lane]
+  bf16x8 qg[16][64];                        // [m*4 + s][lane]
+  bf16x8 kd[16][64];                        // [t*2 + s'][lane]
+  bf16x8 aq[8][64];                         // [m*2 + s'][lane]
+  f32x4 ut[4][kUtInLds ? kTiles : 1][64];   // [m][local column tile][lane]
+  f32x4 gc[32];                             // Gam_C
 };
 
 __device__ __forceinline__ void dma16(const uint8_t* src, void* lds_dst) {
@@ -523,8 +530,11 @@ __device__ __forceinline__ void dma16(const uint8_t* src, void* lds_dst) {
                                    (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
 }
 
-__device__ __forceinline__ void issue_chunk(const Workspace& w, size_t ci, int half,
-                                            ScanBuf* dst, int wave, int lane) {
+template <int WAVES, int NT>
+__device__ __forceinline__ void issue_chunk(const Workspace& w, size_t ci, int group,
+                                            ScanBuf<WAVES, NT>* dst, int wave, int lane) {
+  constexpr int kTiles = WAVES * NT;
+  constexpr int kPieces = 56 + (ScanBuf<WAVES, NT>::kUtInLds ? 4 * kTiles : 0);  // 1 KiB pieces
   const uint8_t* wn = w.wn + ci * kWnBytes;
   const uint8_t* qg = w.qg + ci * kQgBytes;
   const uint8_t* kd = w.kd + ci * kKdBytes;
@@ -532,31 +542,35 @@ __device__ __forceinline__ void issue_chunk(const Workspace& w, size_t ci, int h
   const uint8_t* ut = w.ut + ci * kUtBytes;
   const int off = lane * 16;
 #pragma unroll
-  for (int i = 0; i < 18; ++i) {
-    const int p = wave + kScanWaves * i;  // 72 pieces of 1 KiB, wave-uniform
+  for (int i = 0; i < (kPieces + WAVES - 1) / WAVES; ++i) {
+    const int p = wave + WAVES * i;  // wave-uniform
     if (p < 16) dma16(wn + p * 1024 + off, &dst->wn[p][0]);
     else if (p < 32) dma16(qg + (p - 16) * 1024 + off, &dst->qg[p - 16][0]);
     else if (p < 48) dma16(kd + (p - 32) * 1024 + off, &dst->kd[p - 32][0]);
     else if (p < 56) dma16(aq + (p - 48) * 1024 + off, &dst->aq[p - 48][0]);
-    else {
-      const int q = p - 56, m = q >> 2, nbl = q & 3;
-      dma16(ut + (size_t)((m * 8 + half * 4 + nbl) * 64) * 16 + off, &dst->ut[m][nbl][0]);
+    else if (p < kPieces) {
+      const int q = p - 56, m = q / kTiles, tl = q % kTiles;
+      dma16(ut + (size_t)((m * 8 + group * kTiles + tl) * 64) * 16 + off, &dst->ut[m][tl][0]);
     }
   }
-  if (wave == 0 && lane < 32) dma16(w.gc + ci * kGcBytes + off, &dst->gc[0]);
+  if (wave == WAVES - 1 && lane < 32) dma16(w.gc + ci * kGcBytes + off, &dst->gc[0]);
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void scan_kernel(
+template <int WAVES, int NT>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(1, 1))) void scan_kernel(
     int32_t N, int H, Workspace w, float* __restrict__ states, int32_t num_slots,
     const int32_t* __restrict__ slots, uint32_t flags, uint16_t* __restrict__ o) {
+  using Buf = ScanBuf<WAVES, NT>;
   extern __shared__ __align__(16) uint8_t smem_raw[];
-  ScanBuf* buf = reinterpret_cast<ScanBuf*>(smem_raw);
+  Buf* buf = reinterpret_cast<Buf*>(smem_raw);
   const int NH = N * H;
   const int head_lin = blockIdx.x % NH;
-  const int half = blockIdx.x / NH;
+  const int group = blockIdx.x / NH;
   const int n = head_lin / H, h = head_lin - n * H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
-  const int col = 16 * (half * kScanWaves + wave) + li;
+  int col[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) col[i] = 16 * (group * WAVES * NT + wave * NT + i) + li;
 
   const int start = w.seq_start[n], end = w.seq_end[n], nch = w.seq_nch[n];
   const int cbase = w.chunk_off[n];
@@ -564,116 +578,178 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const bool slot_ok = states != nullptr && slot >= 0 && slot < num_slots;
   float* Sg = slot_ok ? states + ((size_t)slot * H + h) * (size_t)(D * D) : nullptr;
 
-  // state slice: S[t] lane holds rows 16t + 4lg + jj of column col
-  f32x4 S[8];
+  // state slices: S[i][t] lane holds rows 16t + 4lg + jj of column col[i]
+  f32x4 S[NT][8];
   if (slot_ok && (flags & KDA_READ_INITIAL_STATE)) {  // uniform branch; all loads in flight
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int i = 0; i < NT; ++i)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) S[t][jj] = Sg[(size_t)(16 * t + 4 * lg + jj) * D + col];
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) S[i][t][jj] = Sg[(size_t)(16 * t + 4 * lg + jj) * D + col[i]];
   } else {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) S[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   // Outputs of chunk c are stored right after the copies for chunk c+2 are
   // issued, so the stores overlap the compute of chunk c+1 and have retired
   // by the time the next wait for copies comes around.
-  f32x4 Oprev[4];
+  f32x4 Oprev[NT][4];
   int prev_base = -1;
-  auto store_rows = [&](const f32x4* Ov, int base) {
+  auto store_rows = [&](int base) {
     if (base < 0) return;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int i = 0; i < NT; ++i)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int tok = base + 16 * m + 4 * lg + jj;
-        if (tok < end) o[((size_t)tok * H + h) * D + col] = f32_to_bf16(Ov[m][jj]);
-      }
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int tok = base + 16 * m + 4 * lg + jj;
+          if (tok < end) o[((size_t)tok * H + h) * D + col[i]] = f32_to_bf16(Oprev[i][m][jj]);
+        }
   };
 
-  if (nch > 0) issue_chunk(w, (size_t)cbase * H + h, half, &buf[0], wave, lane);
+  constexpr bool kUtInLds = Buf::kUtInLds;
+  f32x4 Unext[NT][4];
+  auto load_ut = [&](size_t ci) {  // this wave's Ut tiles, straight into registers
+    const f32x4* ut = reinterpret_cast<const f32x4*>(w.ut + ci * kUtBytes);
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) Unext[i][m] = ut[(m * 8 + (col[i] >> 4)) * 64 + lane];
+  };
+
+  if (nch > 0) {
+    issue_chunk<WAVES, NT>(w, (size_t)cbase * H + h, group, &buf[0], wave, lane);
+    if (!kUtInLds) load_ut((size_t)cbase * H + h);
+  }
   for (int lc = 0; lc < nch; ++lc) {
     // chunk lc has landed (this wave's copies), then all waves' copies are
     // visible and every wave is done with the buffer about to be refilled
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (lc + 1 < nch)
-      issue_chunk(w, (size_t)(cbase + lc + 1) * H + h, half, &buf[(lc + 1) & 1], wave, lane);
-    store_rows(Oprev, prev_base);
-    const ScanBuf& B = buf[lc & 1];
+      issue_chunk<WAVES, NT>(w, (size_t)(cbase + lc + 1) * H + h, group, &buf[(lc + 1) & 1], wave,
+                             lane);
+    f32x4 U[NT][4];
+    if (!kUtInLds) {
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) U[i][m] = Unext[i][m];
+      if (lc + 1 < nch) load_ut((size_t)(cbase + lc + 1) * H + h);
+    }
+    store_rows(prev_base);
+    const Buf& B = buf[lc & 1];
 
-    // Operands of this chunk: LDS -> registers in three batches, each issued
-    // ahead of the MFMAs that consume it (the scheduling barriers keep the
-    // compiler from interleaving one read per MFMA).
+    // Operands of this chunk: LDS -> registers in batches issued ahead of the
+    // MFMAs that consume them (the scheduling barriers keep the compiler from
+    // interleaving one read per MFMA).
     bf16x8 a_wn[16];
-    f32x4 U[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) a_wn[i] = B.wn[i][lane];
+    for (int x = 0; x < 16; ++x) a_wn[x] = B.wn[x][lane];
+    if (kUtInLds) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) U[m] = B.ut[m][wave][lane];
-    bf16x8 sb[4];
+      for (int i = 0; i < NT; ++i)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) sb[s] = pack_acc(S[2 * s], S[2 * s + 1]);
+        for (int m = 0; m < 4; ++m) U[i][m] = B.ut[m][kUtInLds ? wave * NT + i : 0][lane];
+    }
+    bf16x8 sb[NT][4];
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) sb[i][s] = pack_acc(S[i][2 * s], S[i][2 * s + 1]);
     bf16x8 a_qg[16], a_aq[6];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) a_qg[i] = B.qg[i][lane];
+    for (int x = 0; x < 16; ++x) a_qg[x] = B.qg[x][lane];
 #pragma unroll
-    for (int i = 0; i < 6; ++i) a_aq[i] = B.aq[i < 2 ? 2 * i : i + 2][lane];  // [0],[2],[4],[5],[6],[7]
+    for (int x = 0; x < 6; ++x) a_aq[x] = B.aq[x < 2 ? 2 * x : x + 2][lane];  // [0],[2],[4..7]
     __builtin_amdgcn_sched_barrier(0);
 
     // U = Ut - W S
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) U[m] = mfma(a_wn[m * 4 + s], sb[s], U[m]);
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < NT; ++i) U[i][m] = mfma(a_wn[m * 4 + s], sb[i][s], U[i][m]);
     // O, first part: (Q*Gam) S
-    f32x4 O[4];
+    f32x4 O[NT][4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      O[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) O[m] = mfma(a_qg[m * 4 + s], sb[s], O[m]);
-    }
+      for (int i = 0; i < NT; ++i) {
+        O[i][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) O[i][m] = mfma(a_qg[m * 4 + s], sb[i][s], O[i][m]);
+      }
     bf16x8 a_kd[16];
     f32x4 gcv[8];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) a_kd[i] = B.kd[i][lane];
+    for (int x = 0; x < 16; ++x) a_kd[x] = B.kd[x][lane];
 #pragma unroll
     for (int t = 0; t < 8; ++t) gcv[t] = B.gc[4 * t + lg];
     __builtin_amdgcn_sched_barrier(0);
 
-    bf16x8 ub[2];
-    ub[0] = pack_acc(U[0], U[1]);
-    ub[1] = pack_acc(U[2], U[3]);
-    // O += A_qk U   (A_qk rows 0-31 have no entries in columns 32-63)
-    O[0] = mfma(a_aq[0], ub[0], O[0]);
-    O[1] = mfma(a_aq[1], ub[0], O[1]);
-    O[2] = mfma(a_aq[2], ub[0], O[2]);
-    O[2] = mfma(a_aq[3], ub[1], O[2]);
-    O[3] = mfma(a_aq[4], ub[0], O[3]);
-    O[3] = mfma(a_aq[5], ub[1], O[3]);
-    // S' = Diag(Gam_C) S + Kd^T U
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      S[t] = S[t] * gcv[t];
-      S[t] = mfma(a_kd[t * 2 + 0], ub[0], S[t]);
-      S[t] = mfma(a_kd[t * 2 + 1], ub[1], S[t]);
+    for (int i = 0; i < NT; ++i) {
+      const bf16x8 ub0 = pack_acc(U[i][0], U[i][1]);
+      const bf16x8 ub1 = pack_acc(U[i][2], U[i][3]);
+      // O += A_qk U   (A_qk rows 0-31 have no entries in columns 32-63)
+      O[i][0] = mfma(a_aq[0], ub0, O[i][0]);
+      O[i][1] = mfma(a_aq[1], ub0, O[i][1]);
+      O[i][2] = mfma(a_aq[2], ub0, O[i][2]);
+      O[i][2] = mfma(a_aq[3], ub1, O[i][2]);
+      O[i][3] = mfma(a_aq[4], ub0, O[i][3]);
+      O[i][3] = mfma(a_aq[5], ub1, O[i][3]);
+      // S' = Diag(Gam_C) S + Kd^T U
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        S[i][t] = S[i][t] * gcv[t];
+        S[i][t] = mfma(a_kd[t * 2 + 0], ub0, S[i][t]);
+        S[i][t] = mfma(a_kd[t * 2 + 1], ub1, S[i][t]);
+      }
     }
 
     // keep this chunk's outputs; they are stored early in the next iteration
 #pragma unroll
-    for (int m = 0; m < 4; ++m) Oprev[m] = O[m];
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) Oprev[i][m] = O[i][m];
     prev_base = start + lc * C;
   }
-  store_rows(Oprev, prev_base);
+  store_rows(prev_base);
 
   if (slot_ok && (flags & KDA_WRITE_FINAL_STATE)) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int i = 0; i < NT; ++i)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) Sg[(size_t)(16 * t + 4 * lg + jj) * D + col] = S[t][jj];
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) Sg[(size_t)(16 * t + 4 * lg + jj) * D + col[i]] = S[i][t][jj];
   }
+}
+
+template <int WAVES, int NT>
+kda_status_t launch_scan(int32_t N, int H, const Workspace& w, float* states, int32_t num_slots,
+                         const int32_t* slots, uint32_t flags, void* o, hipStream_t stream) {
+  using Buf = ScanBuf<WAVES, NT>;
+  static bool attr_set = false;  // idempotent; set before the first launch of this variant
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(scan_kernel<WAVES, NT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)(2 * sizeof(Buf)));
+    if (e != hipSuccess) return hip_status(e, "hipFuncSetAttribute(scan)");
+    attr_set = true;
+  }
+  constexpr int kGroups = D / (16 * WAVES * NT);
+  hipLaunchKernelGGL((scan_kernel<WAVES, NT>), dim3((unsigned)(N * H * kGroups)), dim3(64 * WAVES),
+                     2 * sizeof(Buf), stream, N, H, w, states, num_slots, slots, flags,
+                     static_cast<uint16_t*>(o));
+  return check_launch("chunk_fwd scan");
 }
 
 }  // namespace
@@ -706,9 +782,6 @@ kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, cons
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)sizeof(PrepSmem));
     if (e != hipSuccess) return hip_status(e, "hipFuncSetAttribute(prep)");
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(scan_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * sizeof(ScanBuf)));
-    if (e != hipSuccess) return hip_status(e, "hipFuncSetAttribute(scan)");
     attr_set = true;
   }
   hipLaunchKernelGGL(prep_kernel, dim3((unsigned)cap, (unsigned)H), dim3(256), sizeof(PrepSmem),
@@ -716,10 +789,12 @@ kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, cons
                      static_cast<const uint16_t*>(v), g, beta, N, H, w);
   st = check_launch("chunk_fwd prep");
   if (st != KDA_OK) return st;
-  hipLaunchKernelGGL(scan_kernel, dim3((unsigned)(N * H * (D / (16 * kScanWaves)))),
-                     dim3(64 * kScanWaves), 2 * sizeof(ScanBuf), stream, N, H, w, states,
-                     num_slots, slots, flags, static_cast<uint16_t*>(o));
-  return check_launch("chunk_fwd scan");
+  // Few chains (sequence-heads): spread each head over 4 workgroups of 2 waves
+  // to shorten every step of the chain; many chains: one workgroup of 4 waves
+  // x 32 columns per head for throughput.
+  if ((size_t)N * H * 4 <= 512)
+    return launch_scan<2, 1>(N, H, w, states, num_slots, slots, flags, o, stream);
+  return launch_scan<4, 2>(N, H, w, states, num_slots, slots, flags, o, stream);
 }
 
 }  // namespace kda

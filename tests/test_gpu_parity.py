@@ -211,6 +211,22 @@ def test_prefill_mfma_ragged_varlen_slots():
     np.testing.assert_array_equal(got[untouched], pool[untouched])
 
 
+def test_prefill_mfma_many_chains():
+    """More than 128 (sequence, head) chains: the throughput layout of the scan
+    (one workgroup of 4 waves x 32 columns per head)."""
+    rng = np.random.default_rng(15)
+    lens = [int(x) for x in rng.integers(1, 200, size=40)]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    H, d, N = 4, 128, len(lens)
+    p = workloads.random_problem(rng, int(cu[-1]), H, d, d, io_dtype="bf16")
+    p["cu_seqlens"] = cu
+    s0 = (0.02 * rng.standard_normal((N, H, d, d))).astype(np.float32)
+    o, s = _prefill(p, "bf16", 64, s0=s0, read=True, write=True)
+    o_ref, s_ref = oracle.run(p["q"], p["k"], p["v"], p["g"], p["beta"], cu, s0=s0)
+    assert_close(o, o_ref, "bf16", "o")
+    assert_close(s, s_ref, "bf16", "state")
+
+
 @pytest.mark.parametrize("case", ["wipes", "deltanet", "beta0", "scalar_gate", "strong_decay"])
 def test_prefill_mfma_special_gates(case):
     """Extreme and degenerate gates, incl. the element-wise path for strong decay."""
