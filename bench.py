@@ -166,6 +166,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="run one leg only (for profiling)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run one plain device copy of MIB MiB (reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path shards over "
@@ -183,6 +186,15 @@ def main(argv=None):
     def flush():
         counter[0] += 1
         flush_buf.fill_(float(counter[0] & 7))
+
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        flush()
+        torch.mul(src, 1.0, out=dst)   # reads and writes exactly MIB MiB
+        torch.cuda.synchronize()
+        del src, dst
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
