@@ -115,6 +115,7 @@ struct Workspace {
   uint8_t* aq;
   uint8_t* ut;
   uint8_t* gc;
+  uint8_t* sink;       // 256 B target of stores for rows past a sequence's end
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -138,7 +139,8 @@ Workspace carve(void* base, int32_t T, int32_t N, int H) {
   w.kd = p; p += align256(ci * kKdBytes);
   w.aq = p; p += align256(ci * kAqBytes);
   w.ut = p; p += align256(ci * kUtBytes);
-  w.gc = p;
+  w.gc = p; p += align256(ci * kGcBytes);
+  w.sink = p;
   return w;
 }
 
@@ -169,331 +171,351 @@ __global__ void index_kernel(const int32_t* __restrict__ cu, int32_t N, int32_t 
 }
 
 // ------------------------------------------------------------------ 2. prep
+// Persistent workgroups of 8 waves; each walks (chunk, head) items with a
+// stride of the grid size.  The global loads of the next item are issued into
+// registers before the current item is computed, so they overlap its compute.
+constexpr int kPrepWaves = 8;
+constexpr int kPrepThreads = 64 * kPrepWaves;
+
 struct PrepSmem {
   uint16_t K[C][KP];
   uint16_t Q[C][KP];
   uint16_t V[C][KP];
   float G[C][GP];
-  float A[C][AP];    // beta-scaled strictly lower A_kk
-  float Tm[C][AP];   // (I + A_kk)^-1
-  float X[4][16][17];
-  float half_tot[D];
+  float A[C][AP];        // beta-scaled strictly lower A_kk
+  float Tm[C][AP];       // (I + A_kk)^-1
+  float X[4][16][20];    // scratch of the off-diagonal inverse blocks, one per wave
+  float tot[4][D];       // per-quarter column totals of the running gate sums
   float bs[C];
 };
 
-__device__ __forceinline__ float ld_bf(const uint16_t* row, int c) { return bf16_to_f32(row[c]); }
+// One item's inputs between the global loads and the LDS staging.
+struct PrepIn {
+  uint4 k[2], q[2], v[2];
+  float4 g[4];
+  float beta;
+};
 
-// LDS use allows one workgroup (one wave per SIMD) per CU: let the compiler
-// spend registers on batching loads instead of aiming for occupancy.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void prep_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, int32_t N, int H, Workspace w) {
-  extern __shared__ __align__(16) uint8_t smem_raw[];
-  PrepSmem& sm = *reinterpret_cast<PrepSmem*>(smem_raw);
-  const int gc = blockIdx.x;
-  const int h = blockIdx.y;
-  const int tid = threadIdx.x;
-  if (gc >= w.chunk_off[N]) return;  // uniform: capacity slack
-  // the sequence owning this chunk (binary search over chunk offsets)
-  int lo = 0, hi = N - 1;
+struct ItemPos {
+  int gc, h, t0, c;  // chunk, head, first token, valid rows (>= 1)
+};
+
+__device__ __forceinline__ ItemPos locate(const Workspace& w, int N, int H, int item) {
+  ItemPos p;
+  p.gc = item / H;
+  p.h = item - p.gc * H;
+  int lo = 0, hi = N - 1;  // the sequence owning chunk gc (largest n with chunk_off[n] <= gc)
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (w.chunk_off[mid] <= gc) lo = mid; else hi = mid - 1;
+    if (w.chunk_off[mid] <= p.gc) lo = mid; else hi = mid - 1;
   }
-  const int n = lo;
-  const int t0 = w.seq_start[n] + (gc - w.chunk_off[n]) * C;
-  const int c = min(C, w.seq_end[n] - t0);  // valid rows (>= 1)
-  const size_t ci = (size_t)gc * H + h;
+  p.t0 = w.seq_start[lo] + (p.gc - w.chunk_off[lo]) * C;
+  p.c = min(C, w.seq_end[lo] - p.t0);
+  return p;
+}
 
-  // ---- phase 0: stage the chunk in LDS (padded rows are neutral tokens).
-  // Every global load is issued before the first LDS write: rows past the end
-  // of the sequence read the last valid row and are zeroed afterwards.
-  {
-    uint4 kk[4], qq[4], vv[4];
-    float4 gg[8];
-    const size_t rowstride = (size_t)H * D;
-    const size_t base = ((size_t)t0 * H + h) * D;
+// Rows past the end of the sequence read the last valid row (zeroed at staging).
+__device__ __forceinline__ void prep_load(PrepIn& in, const ItemPos& p, const uint16_t* q,
+                                          const uint16_t* k, const uint16_t* v, const float* g,
+                                          const float* beta, int H, int tid) {
+  const size_t rowstride = (size_t)H * D;
+  const size_t base = ((size_t)p.t0 * H + p.h) * D;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int u = tid + 256 * i, r = u >> 4, cc = (u & 15) * 8;
-      const size_t gi = base + (size_t)min(r, c - 1) * rowstride + cc;
-      kk[i] = *reinterpret_cast<const uint4*>(k + gi);
-      qq[i] = *reinterpret_cast<const uint4*>(q + gi);
-      vv[i] = *reinterpret_cast<const uint4*>(v + gi);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int u = tid + 256 * i, r = u >> 5, cc = (u & 31) * 4;
-      gg[i] = *reinterpret_cast<const float4*>(g + base + (size_t)min(r, c - 1) * rowstride + cc);
-    }
-    const float bt = beta[(size_t)(t0 + min(tid & 63, c - 1)) * H + h];
-    const uint4 z4 = make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int u = tid + 256 * i, r = u >> 4, cc = (u & 15) * 8;
-      const bool ok = r < c;
-      const uint4 a = ok ? kk[i] : z4, b = ok ? qq[i] : z4, d = ok ? vv[i] : z4;
-      uint2* pk = reinterpret_cast<uint2*>(&sm.K[r][cc]);
-      uint2* pq = reinterpret_cast<uint2*>(&sm.Q[r][cc]);
-      uint2* pv = reinterpret_cast<uint2*>(&sm.V[r][cc]);
-      pk[0] = make_uint2(a.x, a.y); pk[1] = make_uint2(a.z, a.w);
-      pq[0] = make_uint2(b.x, b.y); pq[1] = make_uint2(b.z, b.w);
-      pv[0] = make_uint2(d.x, d.y); pv[1] = make_uint2(d.z, d.w);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int u = tid + 256 * i, r = u >> 5, cc = (u & 31) * 4;
-      *reinterpret_cast<float4*>(&sm.G[r][cc]) = r < c ? gg[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    if (tid < C) sm.bs[tid] = tid < c ? bt : 0.f;
-    for (int u = tid; u < C * AP; u += 256) (&sm.Tm[0][0])[u] = 0.f;
+  for (int i = 0; i < 2; ++i) {
+    const int u = tid + kPrepThreads * i, r = u >> 4, cc = (u & 15) * 8;
+    const size_t gi = base + (size_t)min(r, p.c - 1) * rowstride + cc;
+    in.k[i] = *reinterpret_cast<const uint4*>(k + gi);
+    in.q[i] = *reinterpret_cast<const uint4*>(q + gi);
+    in.v[i] = *reinterpret_cast<const uint4*>(v + gi);
   }
-  __syncthreads();
-
-  // ---- phase 1: running sum of the log-gates down each channel
-  {
-    const int col = tid & 127, half = tid >> 7;
-    float x[32];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) x[i] = sm.G[half * 32 + i][col];
-#pragma unroll
-    for (int i = 1; i < 32; ++i) x[i] += x[i - 1];
-    if (half == 0) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) sm.G[i][col] = x[i];
-      sm.half_tot[col] = x[31];
-    }
-    __syncthreads();
-    if (half == 1) {
-      const float base = sm.half_tot[col];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) sm.G[32 + i][col] = x[i] + base;
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int u = tid + kPrepThreads * i, r = u >> 5, cc = (u & 31) * 4;
+    in.g[i] = *reinterpret_cast<const float4*>(g + base + (size_t)min(r, p.c - 1) * rowstride + cc);
   }
-  __syncthreads();
+  in.beta = beta[(size_t)(p.t0 + min(tid & 63, p.c - 1)) * H + p.h];
+}
 
-  const int wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+__device__ __forceinline__ void prep_stage(PrepSmem& sm, const PrepIn& in, int c, int tid) {
+  const uint4 z4 = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int u = tid + kPrepThreads * i, r = u >> 4, cc = (u & 15) * 8;
+    const bool ok = r < c;
+    const uint4 a = ok ? in.k[i] : z4, b = ok ? in.q[i] : z4, d = ok ? in.v[i] : z4;
+    uint2* pk = reinterpret_cast<uint2*>(&sm.K[r][cc]);
+    uint2* pq = reinterpret_cast<uint2*>(&sm.Q[r][cc]);
+    uint2* pv = reinterpret_cast<uint2*>(&sm.V[r][cc]);
+    pk[0] = make_uint2(a.x, a.y); pk[1] = make_uint2(a.z, a.w);
+    pq[0] = make_uint2(b.x, b.y); pq[1] = make_uint2(b.z, b.w);
+    pv[0] = make_uint2(d.x, d.y); pv[1] = make_uint2(d.z, d.w);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int u = tid + kPrepThreads * i, r = u >> 5, cc = (u & 31) * 4;
+    *reinterpret_cast<float4*>(&sm.G[r][cc]) = r < c ? in.g[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if (tid < C) sm.bs[tid] = tid < c ? in.beta : 0.f;
+  for (int u = tid; u < C * AP; u += kPrepThreads) (&sm.Tm[0][0])[u] = 0.f;
+}
 
-  // ---- phase 2: gated Gram blocks; wave R owns block row R (rows 16R..16R+15)
-  {
-    const int R = wave, sR = 16 * R;
+__device__ __forceinline__ float ld_bf(const uint16_t* row, int c) { return bf16_to_f32(row[c]); }
+
+// LDS writes of this wave are visible to its later reads (no reordering by the
+// compiler across this point; the LDS serves one wave's requests in order).
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Gram block pair (R, J), J <= R: raw A[r][j] for r in block R (lane row li),
+// j = 16J + 4lg + jj, for keys (acck) and queries (accq).
+__device__ __forceinline__ void gram_pair(const PrepSmem& sm, int R, int J, int li, int lg,
+                                          f32x4& acck, f32x4& accq) {
+  const int sR = 16 * R, r = sR + li, j = 16 * J + li;
+  acck = f32x4{0.f, 0.f, 0.f, 0.f};
+  accq = acck;
+  bool fast = true;
+  if (J == R) {
+    const int lane = 16 * lg + li;
     float sp = fmaxf(sm.G[sR][lane] - sm.G[sR + 15][lane],
                      sm.G[sR][lane + 64] - sm.G[sR + 15][lane + 64]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) sp = fmaxf(sp, __shfl_xor(sp, off, 64));
-    const bool fast_diag = sp <= kMaxSpread;
-
-    // B operands: rows r of block R scaled by exp(G_r - G_s) (<= 1); the same
-    // rows scaled by exp(G_r) are Q*Gam, stored as the scan's A operand.
-    const int r = sR + li;
-    bf16x8 bk[4], bq[4];
-    float gs[4][8];
-    uint16_t* qg_out = reinterpret_cast<uint16_t*>(w.qg + ci * kQgBytes);
+    fast = sp <= kMaxSpread;
+  }
+  if (fast) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      float kr[8], qr[8], gr[8], fk[8], fq[8], fg[8];
+      float kr[8], qr[8], gr[8], gs[8], kj[8], gj[8], fk[8], fq[8], fa[8];
       runs_bf(sm.K[r], s, lg, kr);
       runs_bf(sm.Q[r], s, lg, qr);
       runs_f32(sm.G[r], s, lg, gr);
-      runs_f32(sm.G[sR], s, lg, gs[s]);
+      runs_f32(sm.G[sR], s, lg, gs);
+      runs_bf(sm.K[j], s, lg, kj);
+      runs_f32(sm.G[j], s, lg, gj);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float f = fast_exp(gr[i] - gs[s][i]);
+        const float f = fast_exp(gr[i] - gs[i]);      // rows r:  exp(G_r - G_s) <= 1
         fk[i] = kr[i] * f;
         fq[i] = qr[i] * f;
-        fg[i] = qr[i] * fast_exp(gr[i]);
+        fa[i] = kj[i] * fast_exp(gs[i] - gj[i]);     // rows j:  exp(G_s - G_j)
       }
-      bk[s] = pack8(fk);
-      bq[s] = pack8(fq);
-      *reinterpret_cast<bf16x8*>(qg_out + ((size_t)(R * 4 + s) * 64 + lane) * 8) = pack8(fg);
+      const bf16x8 ak = pack8(fa);
+      acck = mfma(ak, pack8(fk), acck);
+      accq = mfma(ak, pack8(fq), accq);
     }
-    uint16_t* aq_out = reinterpret_cast<uint16_t*>(w.aq + ci * kAqBytes);
-    for (int J = 0; J < 4; ++J) {
-      f32x4 acck = {0.f, 0.f, 0.f, 0.f}, accq = acck;
-      if (J < R || (J == R && fast_diag)) {
-        // A operand: rows j of block J scaled by exp(G_s - G_j)
-        const int j = 16 * J + li;
+  } else {
+    // extreme decay inside the block: exact element-wise fp32 sums
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          float kj[8], gj[8], fa[8];
-          runs_bf(sm.K[j], s, lg, kj);
-          runs_f32(sm.G[j], s, lg, gj);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) fa[i] = kj[i] * fast_exp(gs[s][i] - gj[i]);
-          const bf16x8 ak = pack8(fa);
-          acck = mfma(ak, bk[s], acck);
-          accq = mfma(ak, bq[s], accq);
-        }
-      } else if (J == R) {
-        // extreme decay inside the block: exact element-wise fp32 sums
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int j = sR + 4 * lg + jj;
-          float kk = 0.f, qk = 0.f;
-          if (j <= r) {
-            for (int cc = 0; cc < D; ++cc) {
-              const float e = fast_exp(sm.G[r][cc] - sm.G[j][cc]);
-              const float kj = ld_bf(sm.K[j], cc) * e;
-              kk += ld_bf(sm.K[r], cc) * kj;
-              qk += ld_bf(sm.Q[r], cc) * kj;
-            }
-          }
-          acck[jj] = kk;
-          accq[jj] = qk;
+    for (int jj = 0; jj < 4; ++jj) {
+      const int jd = sR + 4 * lg + jj;
+      float kk = 0.f, qk = 0.f;
+      if (jd <= r) {
+        for (int cc = 0; cc < D; ++cc) {
+          const float e = fast_exp(sm.G[r][cc] - sm.G[jd][cc]);
+          const float kv = ld_bf(sm.K[jd], cc) * e;
+          kk += ld_bf(sm.K[r], cc) * kv;
+          qk += ld_bf(sm.Q[r], cc) * kv;
         }
       }
-      // lane holds raw A[r = sR + li][j = 16J + 4lg + jj]
-      const float br = sm.bs[r];
-      float4 arow;
-      float qv[4];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int j = 16 * J + 4 * lg + jj;
-        (&arow.x)[jj] = j < r ? br * acck[jj] : 0.f;
-        qv[jj] = j <= r ? accq[jj] : 0.f;
-      }
-      *reinterpret_cast<float4*>(&sm.A[r][16 * J + 4 * lg]) = arow;
-      // A_qk as the scan's A operand: [m = R][s' = J / 2][lane][slots (J & 1) * 4 ..]
-      uint16_t* dst = aq_out + ((size_t)(R * 2 + (J >> 1)) * 64 + lane) * 8 + (J & 1) * 4;
-      *reinterpret_cast<uint2*>(dst) =
-          make_uint2((uint32_t)f32_to_bf16(qv[0]) | ((uint32_t)f32_to_bf16(qv[1]) << 16),
-                     (uint32_t)f32_to_bf16(qv[2]) | ((uint32_t)f32_to_bf16(qv[3]) << 16));
+      acck[jj] = kk;
+      accq[jj] = qk;
     }
   }
-  __syncthreads();
+}
 
-  // ---- phase 3: T = (I + A_kk)^-1, blocked forward substitution in fp32
-  {
-    const int R = wave, sR = 16 * R;
-    if (lane < 16) {  // diagonal block: lane = column
-      float x[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float acc = 0.f;
-#pragma unroll
-        for (int m = 0; m < i; ++m) acc += sm.A[sR + i][sR + m] * x[m];
-        x[i] = i < lane ? 0.f : (i == lane ? 1.f : -acc);
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sm.Tm[sR + i][sR + lane] = x[i];
+// LDS use (~124 KiB) allows one workgroup (two waves per SIMD) per CU.
+__global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prep_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, int32_t N, int H, Workspace w) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  PrepSmem& sm = *reinterpret_cast<PrepSmem*>(smem_raw);
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+  const int total = w.chunk_off[N] * H;
+  int item = blockIdx.x;
+  if (item >= total) return;  // uniform
+
+  PrepIn in;
+  ItemPos pos = locate(w, N, H, item);
+  prep_load(in, pos, q, k, v, g, beta, H, tid);
+
+  for (; item < total; item += gridDim.x) {
+    const size_t ci = (size_t)item;  // items are numbered chunk-major: ci = gc * H + h
+    const int c = pos.c;
+    __syncthreads();  // the previous item is done with LDS
+    prep_stage(sm, in, c, tid);
+    const int next = item + gridDim.x;
+    if (next < total) {  // next item's loads overlap this item's compute
+      pos = locate(w, N, H, next);
+      prep_load(in, pos, q, k, v, g, beta, H, tid);
     }
     __syncthreads();
-    // off-diagonal blocks by distance: T_RJ = -T_RR sum_{J<=K<R} A_RK T_KJ
-    const int rho = lane >> 2, c4 = (lane & 3) * 4;
-    for (int dist = 1; dist < 4; ++dist) {
-      const bool act = R >= dist;
-      const int J = R - dist;
-      if (act) {
+
+    // ---- running sum of the log-gates down each channel (four quarters of 16 rows)
+    {
+      const int col = tid & 127, qt = tid >> 7;
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = sm.G[16 * qt + i][col];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) x[i] += x[i - 1];
+      sm.tot[qt][col] = x[15];
+      __syncthreads();
+      float base = 0.f;
+      for (int j = 0; j < qt; ++j) base += sm.tot[j][col];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sm.G[16 * qt + i][col] = x[i] + base;
+    }
+    __syncthreads();
+
+    // ---- gated Gram blocks (10 block pairs over 8 waves) and Q*Gam
+    {
+      constexpr int kPairR[10] = {3, 3, 3, 3, 2, 2, 2, 1, 1, 0};
+      constexpr int kPairJ[10] = {3, 2, 1, 0, 2, 1, 0, 1, 0, 0};
+      uint16_t* aq_out = reinterpret_cast<uint16_t*>(w.aq + ci * kAqBytes);
+      for (int pi = wave; pi < 10; pi += kPrepWaves) {
+        const int R = kPairR[pi], J = kPairJ[pi];
+        f32x4 acck, accq;
+        gram_pair(sm, R, J, li, lg, acck, accq);
+        const int r = 16 * R + li;
+        const float br = sm.bs[r];
+        float4 arow;
+        float qv[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j = 16 * J + 4 * lg + jj;
+          (&arow.x)[jj] = j < r ? br * acck[jj] : 0.f;
+          qv[jj] = j <= r ? accq[jj] : 0.f;
+        }
+        *reinterpret_cast<float4*>(&sm.A[r][16 * J + 4 * lg]) = arow;
+        // A_qk as the scan's A operand: [m = R][s' = J / 2][lane][slots (J & 1) * 4 ..]
+        uint16_t* dst = aq_out + ((size_t)(R * 2 + (J >> 1)) * 64 + lane) * 8 + (J & 1) * 4;
+        *reinterpret_cast<uint2*>(dst) =
+            make_uint2((uint32_t)f32_to_bf16(qv[0]) | ((uint32_t)f32_to_bf16(qv[1]) << 16),
+                       (uint32_t)f32_to_bf16(qv[2]) | ((uint32_t)f32_to_bf16(qv[3]) << 16));
+      }
+      // blocks above the diagonal stored by the scan: (R, J) = (0,1), (2,3)
+      if (wave == 7) {
+        const uint2 z = make_uint2(0, 0);
+        *reinterpret_cast<uint2*>(aq_out + ((size_t)(0 * 2 + 0) * 64 + lane) * 8 + 4) = z;
+        *reinterpret_cast<uint2*>(aq_out + ((size_t)(2 * 2 + 1) * 64 + lane) * 8 + 4) = z;
+      }
+      // Q*Gam as the scan's A operand: wave -> row block m = wave / 2, K-blocks 2 (wave & 1) + {0, 1}
+      uint16_t* qg_out = reinterpret_cast<uint16_t*>(w.qg + ci * kQgBytes);
+      const int m = wave >> 1, r = 16 * m + li;
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss) {
+        const int s = 2 * (wave & 1) + ss;
+        float qr[8], gr[8], f[8];
+        runs_bf(sm.Q[r], s, lg, qr);
+        runs_f32(sm.G[r], s, lg, gr);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = qr[i] * fast_exp(gr[i]);
+        *reinterpret_cast<bf16x8*>(qg_out + ((size_t)(m * 4 + s) * 64 + lane) * 8) = pack8(f);
+      }
+    }
+    __syncthreads();
+
+    // ---- T = (I + A_kk)^-1: wave J owns column block J (waves 4-7 idle here)
+    if (wave < 4) {
+      const int J = wave, sJ = 16 * J;
+      if (lane < 16) {  // diagonal block by forward substitution, lane = column
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float acc = 0.f;
+#pragma unroll
+          for (int m = 0; m < i; ++m) acc += sm.A[sJ + i][sJ + m] * x[m];
+          x[i] = i < lane ? 0.f : (i == lane ? 1.f : -acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sm.Tm[sJ + i][sJ + lane] = x[i];
+      }
+    }
+    __syncthreads();
+    if (wave < 3) {
+      // T_RJ = -T_RR sum_{J<=K<R} A_RK T_KJ, for R = J+1 .. 3, by this wave alone
+      const int J = wave;
+      const int rho = lane >> 2, c4 = (lane & 3) * 4;
+      for (int R = J + 1; R < 4; ++R) {
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         for (int Kb = J; Kb < R; ++Kb) {
 #pragma unroll
           for (int m = 0; m < 16; ++m) {
-            const float a = sm.A[sR + rho][16 * Kb + m];
+            const float a = sm.A[16 * R + rho][16 * Kb + m];
             const float4 t = *reinterpret_cast<const float4*>(&sm.Tm[16 * Kb + m][16 * J + c4]);
             acc[0] += a * t.x; acc[1] += a * t.y; acc[2] += a * t.z; acc[3] += a * t.w;
           }
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sm.X[R][rho][c4 + i] = acc[i];
-      }
-      __syncthreads();
-      if (act) {
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<float4*>(&sm.X[J][rho][c4]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        wave_lds_sync();
+        float o4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
-          const float t = sm.Tm[sR + rho][sR + m];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i] += t * sm.X[R][m][c4 + i];
+          const float t = sm.Tm[16 * R + rho][16 * R + m];
+          const float4 x = *reinterpret_cast<const float4*>(&sm.X[J][m][c4]);
+          o4[0] += t * x.x; o4[1] += t * x.y; o4[2] += t * x.z; o4[3] += t * x.w;
         }
-        *reinterpret_cast<float4*>(&sm.Tm[sR + rho][16 * J + c4]) =
-            make_float4(-acc[0], -acc[1], -acc[2], -acc[3]);
+        *reinterpret_cast<float4*>(&sm.Tm[16 * R + rho][16 * J + c4]) =
+            make_float4(-o4[0], -o4[1], -o4[2], -o4[3]);
+        wave_lds_sync();
       }
-      __syncthreads();
     }
-  }
+    __syncthreads();
 
-  // ---- phase 4: W, Ut, Q*Gam, Kd^T, Gam_C in the scan's operand order
-  {
-    // T tiles, used as A operand (M = r) and as B operand of W^T (N = r)
-    bf16x8 tt[4][2];
+    // ---- W, Ut, Kd^T, Gam_C in the scan's operand order; wave = channel tile = value tile
+    {
+      bf16x8 tt[4][2];  // T tiles: A operand (M = r) of Ut and B operand (N = r) of W^T
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+      for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        if (m < 2 && s2 == 1) continue;  // T is lower triangular: zero block
-        const float* trow = &sm.Tm[16 * m + li][32 * s2 + 4 * lg];
-        const float4 a = *reinterpret_cast<const float4*>(trow);
-        const float4 b = *reinterpret_cast<const float4*>(trow + 16);
-        const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        tt[m][s2] = pack8(f);
-      }
-
-    // (a) W^T for channel tiles 2w, 2w+1 and Kd^T for the same channels
-    uint16_t* kd_out = reinterpret_cast<uint16_t*>(w.kd + ci * kKdBytes);
-    f32x4 wt[2][4];
-#pragma unroll
-    for (int tl = 0; tl < 2; ++tl) {
-      const int tile = 2 * wave + tl, ch = 16 * tile + li;
+        for (int s2 = 0; s2 < 2; ++s2) {
+          if (m < 2 && s2 == 1) continue;  // T is lower triangular: zero block
+          const float* trow = &sm.Tm[16 * m + li][32 * s2 + 4 * lg];
+          const float4 a = *reinterpret_cast<const float4*>(trow);
+          const float4 b = *reinterpret_cast<const float4*>(trow + 16);
+          const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+          tt[m][s2] = pack8(f);
+        }
+      const int tile = wave, ch = 16 * tile + li;
+      // (beta K Gam)^T (A operand of W^T) and Kd^T (stored) for channel tile `tile`
+      uint16_t* kd_out = reinterpret_cast<uint16_t*>(w.kd + ci * kKdBytes);
       const float gl = sm.G[C - 1][ch];
-      bf16x8 abkg[2];
+      bf16x8 abkg[2], bv[2];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        float fb[8], fd[8];
+        float fb[8], fd[8], fv[8];
 #pragma unroll
         for (int qq = 0; qq < 8; ++qq) {
           const int j = 32 * s2 + kpos(lg, qq);
-          const float kv = ld_bf(sm.K[j], ch), gv = sm.G[j][ch];
-          fb[qq] = sm.bs[j] * kv * fast_exp(gv);
+          const float kv = ld_bf(sm.K[j], ch), gv = sm.G[j][ch], bj = sm.bs[j];
+          fb[qq] = bj * kv * fast_exp(gv);
           fd[qq] = kv * fast_exp(gl - gv);
+          fv[qq] = bj * ld_bf(sm.V[j], ch);  // B operand of Ut for value tile `tile`
         }
-        abkg[s2] = pack8(fd);  // reuse the register for Kd^T first
-        *reinterpret_cast<bf16x8*>(kd_out + ((size_t)(tile * 2 + s2) * 64 + lane) * 8) = abkg[s2];
+        *reinterpret_cast<bf16x8*>(kd_out + ((size_t)(tile * 2 + s2) * 64 + lane) * 8) = pack8(fd);
         abkg[s2] = pack8(fb);
+        bv[s2] = pack8(fv);
       }
+      // -W: [m = nt][s = tile / 2][lane][slots (tile & 1) * 4 ..]
+      uint16_t* wn_out = reinterpret_cast<uint16_t*>(w.wn + ci * kWnBytes);
+      float* ut_out = reinterpret_cast<float*>(w.ut + ci * kUtBytes);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         acc = mfma(abkg[0], tt[nt][0], acc);
         if (nt >= 2) acc = mfma(abkg[1], tt[nt][1], acc);
-        wt[tl][nt] = acc;
+        uint16_t* dst = wn_out + ((size_t)(nt * 4 + (tile >> 1)) * 64 + lane) * 8 + (tile & 1) * 4;
+        *reinterpret_cast<uint2*>(dst) =
+            make_uint2((uint32_t)f32_to_bf16(-acc[0]) | ((uint32_t)f32_to_bf16(-acc[1]) << 16),
+                       (uint32_t)f32_to_bf16(-acc[2]) | ((uint32_t)f32_to_bf16(-acc[3]) << 16));
+        // Ut = T Diag(beta) V, value tile `tile`, accumulator layout
+        f32x4 u = {0.f, 0.f, 0.f, 0.f};
+        u = mfma(tt[nt][0], bv[0], u);
+        if (nt >= 2) u = mfma(tt[nt][1], bv[1], u);
+        *reinterpret_cast<f32x4*>(ut_out + ((size_t)(nt * 8 + tile) * 64 + lane) * 4) = u;
       }
+      if (tid < D) reinterpret_cast<float*>(w.gc + ci * kGcBytes)[tid] = fast_exp(sm.G[C - 1][tid]);
     }
-    // -W as the scan's A operand: [m = nt][s = wave][lane][slots tl*4 + jj]
-    uint16_t* wn_out = reinterpret_cast<uint16_t*>(w.wn + ci * kWnBytes);
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const float f[8] = {-wt[0][nt][0], -wt[0][nt][1], -wt[0][nt][2], -wt[0][nt][3],
-                          -wt[1][nt][0], -wt[1][nt][1], -wt[1][nt][2], -wt[1][nt][3]};
-      *reinterpret_cast<bf16x8*>(wn_out + ((size_t)(nt * 4 + wave) * 64 + lane) * 8) = pack8(f);
-    }
-
-    // (b) Ut = T Diag(beta) V for value tiles 2w, 2w+1 (accumulator layout, fp32)
-    float* ut_out = reinterpret_cast<float*>(w.ut + ci * kUtBytes);
-#pragma unroll
-    for (int nl = 0; nl < 2; ++nl) {
-      const int nb = 2 * wave + nl, col = 16 * nb + li;
-      bf16x8 bv[2];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        float f[8];
-#pragma unroll
-        for (int qq = 0; qq < 8; ++qq) {
-          const int j = 32 * s2 + kpos(lg, qq);
-          f[qq] = sm.bs[j] * ld_bf(sm.V[j], col);
-        }
-        bv[s2] = pack8(f);
-      }
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mfma(tt[m][0], bv[0], acc);
-        if (m >= 2) acc = mfma(tt[m][1], bv[1], acc);
-        *reinterpret_cast<f32x4*>(ut_out + ((size_t)(m * 8 + nb) * 64 + lane) * 4) = acc;
-      }
-    }
-
-    // (d) Gam_C
-    if (tid < D) reinterpret_cast<float*>(w.gc + ci * kGcBytes)[tid] = fast_exp(sm.G[C - 1][tid]);
   }
 }
 
@@ -530,30 +552,46 @@ __device__ __forceinline__ void dma16(const uint8_t* src, void* lds_dst) {
                                    (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
 }
 
-template <int WAVES, int NT>
+// Copies of chunk `ci` into `dst`, in two parts: part 0 = -W and Q*Gam, part 1 =
+// Kd^T, A_qk, Ut (when in LDS) and Gam_C.  Pieces of 1 KiB are dealt to waves.
+template <int WAVES, int NT, int PART>
 __device__ __forceinline__ void issue_chunk(const Workspace& w, size_t ci, int group,
                                             ScanBuf<WAVES, NT>* dst, int wave, int lane) {
   constexpr int kTiles = WAVES * NT;
-  constexpr int kPieces = 56 + (ScanBuf<WAVES, NT>::kUtInLds ? 4 * kTiles : 0);  // 1 KiB pieces
-  const uint8_t* wn = w.wn + ci * kWnBytes;
-  const uint8_t* qg = w.qg + ci * kQgBytes;
-  const uint8_t* kd = w.kd + ci * kKdBytes;
-  const uint8_t* aq = w.aq + ci * kAqBytes;
-  const uint8_t* ut = w.ut + ci * kUtBytes;
   const int off = lane * 16;
+  if (PART == 0) {
+    const uint8_t* wn = w.wn + ci * kWnBytes;
+    const uint8_t* qg = w.qg + ci * kQgBytes;
 #pragma unroll
-  for (int i = 0; i < (kPieces + WAVES - 1) / WAVES; ++i) {
-    const int p = wave + WAVES * i;  // wave-uniform
-    if (p < 16) dma16(wn + p * 1024 + off, &dst->wn[p][0]);
-    else if (p < 32) dma16(qg + (p - 16) * 1024 + off, &dst->qg[p - 16][0]);
-    else if (p < 48) dma16(kd + (p - 32) * 1024 + off, &dst->kd[p - 32][0]);
-    else if (p < 56) dma16(aq + (p - 48) * 1024 + off, &dst->aq[p - 48][0]);
-    else if (p < kPieces) {
-      const int q = p - 56, m = q / kTiles, tl = q % kTiles;
-      dma16(ut + (size_t)((m * 8 + group * kTiles + tl) * 64) * 16 + off, &dst->ut[m][tl][0]);
+    for (int i = 0; i < (32 + WAVES - 1) / WAVES; ++i) {
+      const int p = wave + WAVES * i;  // wave-uniform
+      if (p < 16) dma16(wn + p * 1024 + off, &dst->wn[p][0]);
+      else if (p < 32) dma16(qg + (p - 16) * 1024 + off, &dst->qg[p - 16][0]);
     }
+  } else {
+    constexpr int kPieces = 24 + (ScanBuf<WAVES, NT>::kUtInLds ? 4 * kTiles : 0);
+    const uint8_t* kd = w.kd + ci * kKdBytes;
+    const uint8_t* aq = w.aq + ci * kAqBytes;
+    const uint8_t* ut = w.ut + ci * kUtBytes;
+#pragma unroll
+    for (int i = 0; i < (kPieces + WAVES - 1) / WAVES; ++i) {
+      const int p = wave + WAVES * i;  // wave-uniform
+      if (p < 16) dma16(kd + p * 1024 + off, &dst->kd[p][0]);
+      else if (p < 24) dma16(aq + (p - 16) * 1024 + off, &dst->aq[p - 16][0]);
+      else if (p < kPieces) {
+        const int q = p - 24, m = q / kTiles, tl = q % kTiles;
+        dma16(ut + (size_t)((m * 8 + group * kTiles + tl) * 64) * 16 + off, &dst->ut[m][tl][0]);
+      }
+    }
+    if (wave == WAVES - 1 && lane < 32) dma16(w.gc + ci * kGcBytes + off, &dst->gc[0]);
   }
-  if (wave == WAVES - 1 && lane < 32) dma16(w.gc + ci * kGcBytes + off, &dst->gc[0]);
+}
+
+// Barrier for LDS traffic only: waits for this wave's LDS operations, not for
+// its outstanding global stores (which __syncthreads' fence would drain).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
 }
 
 template <int WAVES, int NT>
@@ -561,8 +599,12 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(1, 1
     int32_t N, int H, Workspace w, float* __restrict__ states, int32_t num_slots,
     const int32_t* __restrict__ slots, uint32_t flags, uint16_t* __restrict__ o) {
   using Buf = ScanBuf<WAVES, NT>;
-  extern __shared__ __align__(16) uint8_t smem_raw[];
-  Buf* buf = reinterpret_cast<Buf*>(smem_raw);
+  // Two separately declared buffers (not one indexed array): the compiler can
+  // then see that the copies into one never alias reads of the other and does
+  // not wait for the copies before unrelated LDS accesses.
+  constexpr int kCols = 16 * WAVES * NT;     // columns of this workgroup
+  __shared__ Buf buf0, buf1;
+  __shared__ uint16_t out0[C][kCols], out1[C][kCols];  // staged bf16 outputs of a chunk
   const int NH = N * H;
   const int head_lin = blockIdx.x % NH;
   const int group = blockIdx.x / NH;
@@ -594,22 +636,23 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(1, 1
       for (int t = 0; t < 8; ++t) S[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Outputs of chunk c are stored right after the copies for chunk c+2 are
-  // issued, so the stores overlap the compute of chunk c+1 and have retired
-  // by the time the next wait for copies comes around.
-  f32x4 Oprev[NT][4];
-  int prev_base = -1;
-  auto store_rows = [&](int base) {
-    if (base < 0) return;
+  // Outputs of chunk c are staged as bf16 in an LDS tile and stored, as whole
+  // 16-byte row pieces, early in chunk c + 1 so that they retire while it
+  // computes.  Pieces of rows past the sequence end go to the workspace sink,
+  // which keeps the stores free of branches.
+  constexpr int kRowPieces = kCols / 8;      // 16-byte pieces per row
+  constexpr int kStores = C * kRowPieces / (64 * WAVES);
+  static_assert(C * kRowPieces % (64 * WAVES) == 0, "store split");
+  auto store_rows = [&](const uint16_t (*ob)[kCols], int base) {
 #pragma unroll
-    for (int i = 0; i < NT; ++i)
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int tok = base + 16 * m + 4 * lg + jj;
-          if (tok < end) o[((size_t)tok * H + h) * D + col[i]] = f32_to_bf16(Oprev[i][m][jj]);
-        }
+    for (int x = 0; x < kStores; ++x) {
+      const int u = tid + 64 * WAVES * x;
+      const int r = u / kRowPieces, pc = u % kRowPieces, tok = base + r;
+      uint4* dst = tok < end
+          ? reinterpret_cast<uint4*>(o + ((size_t)tok * H + h) * D + 16 * group * WAVES * NT + 8 * pc)
+          : reinterpret_cast<uint4*>(w.sink) + (tid & 15);
+      *dst = *reinterpret_cast<const uint4*>(&ob[r][8 * pc]);
+    }
   };
 
   constexpr bool kUtInLds = Buf::kUtInLds;
@@ -622,32 +665,30 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(1, 1
       for (int m = 0; m < 4; ++m) Unext[i][m] = ut[(m * 8 + (col[i] >> 4)) * 64 + lane];
   };
 
-  if (nch > 0) {
-    issue_chunk<WAVES, NT>(w, (size_t)cbase * H + h, group, &buf[0], wave, lane);
-    if (!kUtInLds) load_ut((size_t)cbase * H + h);
-  }
-  for (int lc = 0; lc < nch; ++lc) {
-    // chunk lc has landed (this wave's copies), then all waves' copies are
-    // visible and every wave is done with the buffer about to be refilled
+  // One chunk: compute from B (copied during the previous chunk), copy the next
+  // chunk into Bn, store the outputs of the previous chunk (staged in Bn).
+  auto chunk_step = [&](const Buf& B, Buf& Bn, uint16_t (*ob)[kCols], const uint16_t (*obn)[kCols],
+                        int lc) {
+    // chunk lc has landed (this wave's copies; only the previous chunk's output
+    // stores may still be in flight), then all waves' copies are visible and
+    // every wave is done with Bn
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (lc + 1 < nch)
-      issue_chunk<WAVES, NT>(w, (size_t)(cbase + lc + 1) * H + h, group, &buf[(lc + 1) & 1], wave,
-                             lane);
+    lds_barrier();
+    const bool more = lc + 1 < nch;
+    const size_t ci_next = (size_t)(cbase + lc + 1) * H + h;
     f32x4 U[NT][4];
     if (!kUtInLds) {
 #pragma unroll
       for (int i = 0; i < NT; ++i)
 #pragma unroll
         for (int m = 0; m < 4; ++m) U[i][m] = Unext[i][m];
-      if (lc + 1 < nch) load_ut((size_t)(cbase + lc + 1) * H + h);
+      if (more) load_ut(ci_next);
     }
-    store_rows(prev_base);
-    const Buf& B = buf[lc & 1];
 
     // Operands of this chunk: LDS -> registers in batches issued ahead of the
     // MFMAs that consume them (the scheduling barriers keep the compiler from
-    // interleaving one read per MFMA).
+    // interleaving one read per MFMA); the copies for the next chunk are issued
+    // in two parts after each batch of reads.
     bf16x8 a_wn[16];
 #pragma unroll
     for (int x = 0; x < 16; ++x) a_wn[x] = B.wn[x][lane];
@@ -668,12 +709,16 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(1, 1
 #pragma unroll
     for (int x = 0; x < 6; ++x) a_aq[x] = B.aq[x < 2 ? 2 * x : x + 2][lane];  // [0],[2],[4..7]
     __builtin_amdgcn_sched_barrier(0);
+    // the previous chunk's outputs (staged in obn), early: they retire during this chunk
+    if (lc > 0) store_rows(obn, start + (lc - 1) * C);
+    if (more) issue_chunk<WAVES, NT, 0>(w, ci_next, group, &Bn, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // U = Ut - W S
+    // U = Ut - W S   (consecutive MFMAs go to different accumulators)
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+      for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int i = 0; i < NT; ++i) U[i][m] = mfma(a_wn[m * 4 + s], sb[i][s], U[i][m]);
     // O, first part: (Q*Gam) S
@@ -681,11 +726,13 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(1, 1
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        O[i][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < NT; ++i) O[i][m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) O[i][m] = mfma(a_qg[m * 4 + s], sb[i][s], O[i][m]);
-      }
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < NT; ++i) O[i][m] = mfma(a_qg[m * 4 + s], sb[i][s], O[i][m]);
     bf16x8 a_kd[16];
     f32x4 gcv[8];
 #pragma unroll
@@ -693,35 +740,61 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(1, 1
 #pragma unroll
     for (int t = 0; t < 8; ++t) gcv[t] = B.gc[4 * t + lg];
     __builtin_amdgcn_sched_barrier(0);
+    if (more) issue_chunk<WAVES, NT, 1>(w, ci_next, group, &Bn, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);
 
+    bf16x8 ub[NT][2];
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-      const bf16x8 ub0 = pack_acc(U[i][0], U[i][1]);
-      const bf16x8 ub1 = pack_acc(U[i][2], U[i][3]);
-      // O += A_qk U   (A_qk rows 0-31 have no entries in columns 32-63)
-      O[i][0] = mfma(a_aq[0], ub0, O[i][0]);
-      O[i][1] = mfma(a_aq[1], ub0, O[i][1]);
-      O[i][2] = mfma(a_aq[2], ub0, O[i][2]);
-      O[i][2] = mfma(a_aq[3], ub1, O[i][2]);
-      O[i][3] = mfma(a_aq[4], ub0, O[i][3]);
-      O[i][3] = mfma(a_aq[5], ub1, O[i][3]);
-      // S' = Diag(Gam_C) S + Kd^T U
+      ub[i][0] = pack_acc(U[i][0], U[i][1]);
+      ub[i][1] = pack_acc(U[i][2], U[i][3]);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        S[i][t] = S[i][t] * gcv[t];
-        S[i][t] = mfma(a_kd[t * 2 + 0], ub0, S[i][t]);
-        S[i][t] = mfma(a_kd[t * 2 + 1], ub1, S[i][t]);
-      }
+      for (int t = 0; t < 8; ++t) S[i][t] = S[i][t] * gcv[t];
+    }
+    // S' = Diag(Gam_C) S + Kd^T U  (the chain's critical path: issued first)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int i = 0; i < NT; ++i) S[i][t] = mfma(a_kd[t * 2 + s2], ub[i][s2], S[i][t]);
+    // O += A_qk U   (A_qk rows 0-31 have no entries in columns 32-63)
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      O[i][0] = mfma(a_aq[0], ub[i][0], O[i][0]);
+      O[i][1] = mfma(a_aq[1], ub[i][0], O[i][1]);
+      O[i][2] = mfma(a_aq[2], ub[i][0], O[i][2]);
+      O[i][3] = mfma(a_aq[4], ub[i][0], O[i][3]);
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      O[i][2] = mfma(a_aq[3], ub[i][1], O[i][2]);
+      O[i][3] = mfma(a_aq[5], ub[i][1], O[i][3]);
     }
 
-    // keep this chunk's outputs; they are stored early in the next iteration
+    // stage this chunk's outputs (bf16) in ob, stored during the next chunk
 #pragma unroll
     for (int i = 0; i < NT; ++i)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) Oprev[i][m] = O[i][m];
-    prev_base = start + lc * C;
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          ob[16 * m + 4 * lg + jj][16 * (wave * NT + i) + li] = f32_to_bf16(O[i][m][jj]);
+  };
+
+  if (nch > 0) {
+    issue_chunk<WAVES, NT, 0>(w, (size_t)cbase * H + h, group, &buf0, wave, lane);
+    issue_chunk<WAVES, NT, 1>(w, (size_t)cbase * H + h, group, &buf0, wave, lane);
+    if (!kUtInLds) load_ut((size_t)cbase * H + h);
   }
-  store_rows(prev_base);
+  for (int lc = 0; lc < nch; lc += 2) {
+    chunk_step(buf0, buf1, out0, out1, lc);
+    if (lc + 1 < nch) chunk_step(buf1, buf0, out1, out0, lc + 1);
+  }
+  if (nch > 0) {
+    lds_barrier();
+    store_rows((nch - 1) & 1 ? out1 : out0, start + (nch - 1) * C);
+  }
 
   if (slot_ok && (flags & KDA_WRITE_FINAL_STATE)) {
 #pragma unroll
@@ -736,19 +809,9 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(1, 1
 template <int WAVES, int NT>
 kda_status_t launch_scan(int32_t N, int H, const Workspace& w, float* states, int32_t num_slots,
                          const int32_t* slots, uint32_t flags, void* o, hipStream_t stream) {
-  using Buf = ScanBuf<WAVES, NT>;
-  static bool attr_set = false;  // idempotent; set before the first launch of this variant
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(scan_kernel<WAVES, NT>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)(2 * sizeof(Buf)));
-    if (e != hipSuccess) return hip_status(e, "hipFuncSetAttribute(scan)");
-    attr_set = true;
-  }
   constexpr int kGroups = D / (16 * WAVES * NT);
   hipLaunchKernelGGL((scan_kernel<WAVES, NT>), dim3((unsigned)(N * H * kGroups)), dim3(64 * WAVES),
-                     2 * sizeof(Buf), stream, N, H, w, states, num_slots, slots, flags,
-                     static_cast<uint16_t*>(o));
+                     0, stream, N, H, w, states, num_slots, slots, flags, static_cast<uint16_t*>(o));
   return check_launch("chunk_fwd scan");
 }
 
@@ -762,7 +825,7 @@ size_t chunk_mfma_workspace_bytes(int H, int32_t T, int32_t N) {
   const size_t ci = nchunks_max(T, N) * (size_t)H;
   return header_bytes(N) + align256(ci * kWnBytes) + align256(ci * kQgBytes) +
          align256(ci * kKdBytes) + align256(ci * kAqBytes) + align256(ci * kUtBytes) +
-         align256(ci * kGcBytes);
+         align256(ci * kGcBytes) + 256;
 }
 
 kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, const int32_t* cu,
@@ -784,8 +847,19 @@ kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, cons
     if (e != hipSuccess) return hip_status(e, "hipFuncSetAttribute(prep)");
     attr_set = true;
   }
-  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)cap, (unsigned)H), dim3(256), sizeof(PrepSmem),
-                     stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+  // persistent prep: one workgroup per CU, each walks items with a grid stride
+  int ncu = 256;
+  {
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess) {
+      int v = 0;
+      if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) ncu = v;
+    }
+  }
+  const size_t items = cap * (size_t)H;
+  const unsigned prep_grid = (unsigned)(items < (size_t)ncu ? items : (size_t)ncu);
+  hipLaunchKernelGGL(prep_kernel, dim3(prep_grid), dim3(kPrepThreads), sizeof(PrepSmem), stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), g, beta, N, H, w);
   st = check_launch("chunk_fwd prep");
   if (st != KDA_OK) return st;
