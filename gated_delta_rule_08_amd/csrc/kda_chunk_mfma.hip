@@ -65,6 +65,11 @@ constexpr size_t kGcBytes = D * 4;             // Gam_C   fp32
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// fp32 16x16x4: lane l supplies A[l%16][l/16] and B[l/16][l%16]; the result
+// layout is that of the bf16 instruction (rows 4(l/16)+jj, column l%16).
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
 // K index held in slot q (0..7) of lane group g of a 32-deep MFMA operand.
 // Slots 0-3 cover 4g..4g+3 and slots 4-7 cover 16+4g..16+4g+3: this is the row
@@ -170,6 +175,16 @@ __global__ void index_kernel(const int32_t* __restrict__ cu, int32_t N, int32_t 
   w.chunk_off[N] = run;
 }
 
+// Barrier for LDS traffic only: waits for this wave's LDS operations, not for
+// its outstanding global loads and stores (which __syncthreads' fence would
+// drain).  The empty asm after the barrier keeps the compiler from moving
+// later LDS accesses above it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ------------------------------------------------------------------ 2. prep
 // Persistent workgroups of 8 waves; each walks (chunk, head) items with a
 // stride of the grid size.  The global loads of the next item are issued into
@@ -184,7 +199,6 @@ struct PrepSmem {
   float G[C][GP];
   float A[C][AP];        // beta-scaled strictly lower A_kk
   float Tm[C][AP];       // (I + A_kk)^-1
-  float X[4][16][20];    // scratch of the off-diagonal inverse blocks, one per wave
   float tot[4][D];       // per-quarter column totals of the running gate sums
   float bs[C];
 };
@@ -260,10 +274,6 @@ __device__ __forceinline__ void prep_stage(PrepSmem& sm, const PrepIn& in, int c
 }
 
 __device__ __forceinline__ float ld_bf(const uint16_t* row, int c) { return bf16_to_f32(row[c]); }
-
-// LDS writes of this wave are visible to its later reads (no reordering by the
-// compiler across this point; the LDS serves one wave's requests in order).
-__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Gram block pair (R, J), J <= R: raw A[r][j] for r in block R (lane row li),
 // j = 16J + 4lg + jj, for keys (acck) and queries (accq).
@@ -341,14 +351,14 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2,
   for (; item < total; item += gridDim.x) {
     const size_t ci = (size_t)item;  // items are numbered chunk-major: ci = gc * H + h
     const int c = pos.c;
-    __syncthreads();  // the previous item is done with LDS
+    lds_barrier();  // the previous item is done with LDS
     prep_stage(sm, in, c, tid);
     const int next = item + gridDim.x;
     if (next < total) {  // next item's loads overlap this item's compute
       pos = locate(w, N, H, next);
       prep_load(in, pos, q, k, v, g, beta, H, tid);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- running sum of the log-gates down each channel (four quarters of 16 rows)
     {
@@ -359,13 +369,13 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
       for (int i = 1; i < 16; ++i) x[i] += x[i - 1];
       sm.tot[qt][col] = x[15];
-      __syncthreads();
+      lds_barrier();
       float base = 0.f;
       for (int j = 0; j < qt; ++j) base += sm.tot[j][col];
 #pragma unroll
       for (int i = 0; i < 16; ++i) sm.G[16 * qt + i][col] = x[i] + base;
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- gated Gram blocks (10 block pairs over 8 waves) and Q*Gam
     {
@@ -413,54 +423,47 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2,
         *reinterpret_cast<bf16x8*>(qg_out + ((size_t)(m * 4 + s) * 64 + lane) * 8) = pack8(f);
       }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // ---- T = (I + A_kk)^-1: wave J owns column block J (waves 4-7 idle here)
-    if (wave < 4) {
-      const int J = wave, sJ = 16 * J;
-      if (lane < 16) {  // diagonal block by forward substitution, lane = column
-        float x[16];
+    // ---- T = (I + A_kk)^-1 in 16x16 blocks.  Diagonal blocks: T_JJ = (I + A_JJ)^-1
+    // by right-looking forward substitution (wave J, lane = column): once x[m]
+    // is final it is eliminated from every later row at once, so the dependency
+    // chain is 15 steps deep.
+    if (wave < 4 && lane < 16) {
+      const int sJ = 16 * wave;
+      float x[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float acc = 0.f;
+      for (int i = 0; i < 16; ++i) x[i] = i == lane ? 1.f : 0.f;
 #pragma unroll
-          for (int m = 0; m < i; ++m) acc += sm.A[sJ + i][sJ + m] * x[m];
-          x[i] = i < lane ? 0.f : (i == lane ? 1.f : -acc);
-        }
+      for (int m = 0; m < 15; ++m)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sm.Tm[sJ + i][sJ + lane] = x[i];
-      }
+        for (int i = m + 1; i < 16; ++i) x[i] -= sm.A[sJ + i][sJ + m] * x[m];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sm.Tm[sJ + i][sJ + lane] = x[i];
     }
-    __syncthreads();
-    if (wave < 3) {
-      // T_RJ = -T_RR sum_{J<=K<R} A_RK T_KJ, for R = J+1 .. 3, by this wave alone
-      const int J = wave;
-      const int rho = lane >> 2, c4 = (lane & 3) * 4;
-      for (int R = J + 1; R < 4; ++R) {
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int Kb = J; Kb < R; ++Kb) {
+    lds_barrier();
+    // Off-diagonal blocks by distance L = R - J, the blocks of one distance in
+    // parallel (one wave each): T_RJ = -T_RR X with X = sum_{J<=K<R} A_RK T_KJ,
+    // both products on fp32 MFMA.  The second product takes X straight from the
+    // accumulators: at step jj lane group g contributes contraction index 4g+jj.
 #pragma unroll
-          for (int m = 0; m < 16; ++m) {
-            const float a = sm.A[16 * R + rho][16 * Kb + m];
-            const float4 t = *reinterpret_cast<const float4*>(&sm.Tm[16 * Kb + m][16 * J + c4]);
-            acc[0] += a * t.x; acc[1] += a * t.y; acc[2] += a * t.z; acc[3] += a * t.w;
-          }
-        }
-        *reinterpret_cast<float4*>(&sm.X[J][rho][c4]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        wave_lds_sync();
-        float o4[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int L = 1; L < 4; ++L) {
+      if (wave < 4 - L) {
+        const int J = wave, R = J + L;
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        for (int Kb = J; Kb < R; ++Kb)
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-          const float t = sm.Tm[16 * R + rho][16 * R + m];
-          const float4 x = *reinterpret_cast<const float4*>(&sm.X[J][m][c4]);
-          o4[0] += t * x.x; o4[1] += t * x.y; o4[2] += t * x.z; o4[3] += t * x.w;
-        }
-        *reinterpret_cast<float4*>(&sm.Tm[16 * R + rho][16 * J + c4]) =
-            make_float4(-o4[0], -o4[1], -o4[2], -o4[3]);
-        wave_lds_sync();
+          for (int kb = 0; kb < 4; ++kb)
+            x = mfma_f32(sm.A[16 * R + li][16 * Kb + 4 * kb + lg],
+                         sm.Tm[16 * Kb + 4 * kb + lg][16 * J + li], x);
+        f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) t = mfma_f32(sm.Tm[16 * R + li][16 * R + 4 * lg + jj], x[jj], t);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) sm.Tm[16 * R + 4 * lg + jj][16 * J + li] = -t[jj];
       }
+      lds_barrier();
     }
-    __syncthreads();
 
     // ---- W, Ut, Kd^T, Gam_C in the scan's operand order; wave = channel tile = value tile
     {
@@ -585,13 +588,6 @@ __device__ __forceinline__ void issue_chunk(const Workspace& w, size_t ci, int g
     }
     if (wave == WAVES - 1 && lane < 32) dma16(w.gc + ci * kGcBytes + off, &dst->gc[0]);
   }
-}
-
-// Barrier for LDS traffic only: waits for this wave's LDS operations, not for
-// its outstanding global stores (which __syncthreads' fence would drain).
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
 }
 
 template <int WAVES, int NT>
