@@ -29,7 +29,9 @@
 //     accumulators for the whole sequence and walks the chunks in order: the
 //     only loop-carried dependency of the method (heqinghuang section 10: the
 //     only sequential loop is over chunks).  The waves of a workgroup share
-//     each chunk's operands through LDS.
+//     each chunk's operands through LDS.  With few chains, dedicated loader
+//     waves copy the operands so the compute waves never wait on the copies;
+//     with many chains, one workgroup per head fetches them once per chunk.
 //
 // Numerics of the gated Gram products: exp(G_r - G_j) is split at the first
 // row s of the 16-row block of r as exp(G_r - G_s) * exp(G_s - G_j).  For j in
@@ -802,6 +804,243 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(1, 1
   }
 }
 
+// Warp-specialised scan: CW compute waves own the state columns (NT tiles of
+// 16 each) and touch only LDS and registers (plus their own Ut tiles, loaded
+// into registers one chunk ahead); LW loader waves copy the next chunk's shared
+// operands (-W, Q*Gam, Kd^T, A_qk, Gam_C) into LDS with direct global->LDS
+// loads and store the previous chunk's staged outputs.  The copy rate of a CU
+// grows with the number of waves issuing copies, and the compute waves never
+// stall on issuing them.  One LDS barrier per chunk separates the steps: in
+// step c the compute waves read buffer c % 2 and write staging tile c % 2,
+// while the loaders fill buffer (c + 1) % 2 and store staging tile (c - 1) % 2.
+template <int CW, int NT>
+struct ScanOperands {
+  bf16x8 wn[16][64];
+  bf16x8 qg[16][64];
+  bf16x8 kd[16][64];
+  bf16x8 aq[8][64];
+  f32x4 gc[32];
+};
+
+template <int CW, int NT, int LW>
+__global__ __launch_bounds__(64 * (CW + LW)) void scan_ws_kernel(
+    int32_t N, int H, Workspace w, float* __restrict__ states, int32_t num_slots,
+    const int32_t* __restrict__ slots, uint32_t flags, uint16_t* __restrict__ o) {
+  using Buf = ScanOperands<CW, NT>;
+  constexpr int kCols = 16 * CW * NT;  // columns of this workgroup
+  __shared__ Buf buf0, buf1;
+  __shared__ uint16_t out0[C][kCols], out1[C][kCols];
+  const int NH = N * H;
+  const int head_lin = blockIdx.x % NH;
+  const int group = blockIdx.x / NH;
+  const int n = head_lin / H, h = head_lin - n * H;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+  const int start = w.seq_start[n], end = w.seq_end[n], nch = w.seq_nch[n];
+  const int cbase = w.chunk_off[n];
+
+  if (wave >= CW) {
+    // ------------------------------------------------------------ loaders
+    const int lw = wave - CW, ltid = tid - 64 * CW;
+    const int off = lane * 16;
+    auto issue = [&](size_t ci, Buf* dst) {
+      const uint8_t* wn = w.wn + ci * kWnBytes;
+      const uint8_t* qg = w.qg + ci * kQgBytes;
+      const uint8_t* kd = w.kd + ci * kKdBytes;
+      const uint8_t* aq = w.aq + ci * kAqBytes;
+#pragma unroll
+      for (int i = 0; i < (56 + LW - 1) / LW; ++i) {
+        const int p = lw + LW * i;  // wave-uniform 1 KiB piece
+        if (p < 16) dma16(wn + p * 1024 + off, &dst->wn[p][0]);
+        else if (p < 32) dma16(qg + (p - 16) * 1024 + off, &dst->qg[p - 16][0]);
+        else if (p < 48) dma16(kd + (p - 32) * 1024 + off, &dst->kd[p - 32][0]);
+        else if (p < 56) dma16(aq + (p - 48) * 1024 + off, &dst->aq[p - 48][0]);
+      }
+      if (lw == LW - 1 && lane < 32) dma16(w.gc + ci * kGcBytes + off, &dst->gc[0]);
+    };
+    // Staged outputs, as whole 16-byte row pieces; pieces of rows past the
+    // sequence end go to the workspace sink, which keeps the stores free of
+    // branches on the data path.
+    constexpr int kRowPieces = kCols / 8;
+    constexpr int kPieces = C * kRowPieces;
+    auto store_rows = [&](const uint16_t (*ob)[kCols], int base) {
+#pragma unroll
+      for (int x = 0; x < (kPieces + 64 * LW - 1) / (64 * LW); ++x) {
+        const int u = ltid + 64 * LW * x;
+        if (kPieces % (64 * LW) == 0 || u < kPieces) {
+          const int r = u / kRowPieces, pc = u % kRowPieces, tok = base + r;
+          uint4* dst = tok < end
+              ? reinterpret_cast<uint4*>(o + ((size_t)tok * H + h) * D + kCols * group + 8 * pc)
+              : reinterpret_cast<uint4*>(w.sink) + (lane & 15);
+          *dst = *reinterpret_cast<const uint4*>(&ob[r][8 * pc]);
+        }
+      }
+    };
+    auto step_end = [&]() {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+      lds_barrier();
+    };
+    if (nch > 0) issue((size_t)cbase * H + h, &buf0);
+    step_end();
+    for (int lc = 0; lc < nch; lc += 2) {
+      if (lc + 1 < nch) issue((size_t)(cbase + lc + 1) * H + h, &buf1);
+      if (lc > 0) store_rows(out1, start + (lc - 1) * C);
+      step_end();
+      if (lc + 1 < nch) {
+        if (lc + 2 < nch) issue((size_t)(cbase + lc + 2) * H + h, &buf0);
+        store_rows(out0, start + lc * C);
+        step_end();
+      }
+    }
+    if (nch > 0) store_rows((nch - 1) & 1 ? out1 : out0, start + (nch - 1) * C);
+    return;
+  }
+
+  // -------------------------------------------------------------- compute
+  int col[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) col[i] = 16 * (group * CW * NT + wave * NT + i) + li;
+  const int slot = slots ? slots[n] : n;
+  const bool slot_ok = states != nullptr && slot >= 0 && slot < num_slots;
+  float* Sg = slot_ok ? states + ((size_t)slot * H + h) * (size_t)(D * D) : nullptr;
+
+  // state slices: S[i][t] lane holds rows 16t + 4lg + jj of column col[i]
+  f32x4 S[NT][8];
+  if (slot_ok && (flags & KDA_READ_INITIAL_STATE)) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) S[i][t][jj] = Sg[(size_t)(16 * t + 4 * lg + jj) * D + col[i]];
+  } else {
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) S[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  f32x4 Unext[NT][4];
+  auto load_ut = [&](size_t ci) {
+    const f32x4* ut = reinterpret_cast<const f32x4*>(w.ut + ci * kUtBytes);
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) Unext[i][m] = ut[(m * 8 + (col[i] >> 4)) * 64 + lane];
+  };
+  if (nch > 0) load_ut((size_t)cbase * H + h);
+  lds_barrier();
+
+  auto chunk_step = [&](const Buf& B, uint16_t (*ob)[kCols], int lc) {
+    f32x4 U[NT][4];
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) U[i][m] = Unext[i][m];
+    if (lc + 1 < nch) load_ut((size_t)(cbase + lc + 1) * H + h);
+
+    bf16x8 a_wn[16];
+#pragma unroll
+    for (int x = 0; x < 16; ++x) a_wn[x] = B.wn[x][lane];
+    bf16x8 sb[NT][4];
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) sb[i][s] = pack_acc(S[i][2 * s], S[i][2 * s + 1]);
+    bf16x8 a_qg[16], a_aq[6];
+#pragma unroll
+    for (int x = 0; x < 16; ++x) a_qg[x] = B.qg[x][lane];
+#pragma unroll
+    for (int x = 0; x < 6; ++x) a_aq[x] = B.aq[x < 2 ? 2 * x : x + 2][lane];  // [0],[2],[4..7]
+    __builtin_amdgcn_sched_barrier(0);
+
+    // U = Ut - W S   (consecutive MFMAs go to different accumulators)
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < NT; ++i) U[i][m] = mfma(a_wn[m * 4 + s], sb[i][s], U[i][m]);
+    // O, first part: (Q*Gam) S
+    f32x4 O[NT][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < NT; ++i) O[i][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < NT; ++i) O[i][m] = mfma(a_qg[m * 4 + s], sb[i][s], O[i][m]);
+    bf16x8 a_kd[16];
+    f32x4 gcv[8];
+#pragma unroll
+    for (int x = 0; x < 16; ++x) a_kd[x] = B.kd[x][lane];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) gcv[t] = B.gc[4 * t + lg];
+    __builtin_amdgcn_sched_barrier(0);
+
+    bf16x8 ub[NT][2];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      ub[i][0] = pack_acc(U[i][0], U[i][1]);
+      ub[i][1] = pack_acc(U[i][2], U[i][3]);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) S[i][t] = S[i][t] * gcv[t];
+    }
+    // S' = Diag(Gam_C) S + Kd^T U  (the chain's critical path: issued first)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int i = 0; i < NT; ++i) S[i][t] = mfma(a_kd[t * 2 + s2], ub[i][s2], S[i][t]);
+    // O += A_qk U   (A_qk rows 0-31 have no entries in columns 32-63)
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      O[i][0] = mfma(a_aq[0], ub[i][0], O[i][0]);
+      O[i][1] = mfma(a_aq[1], ub[i][0], O[i][1]);
+      O[i][2] = mfma(a_aq[2], ub[i][0], O[i][2]);
+      O[i][3] = mfma(a_aq[4], ub[i][0], O[i][3]);
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      O[i][2] = mfma(a_aq[3], ub[i][1], O[i][2]);
+      O[i][3] = mfma(a_aq[5], ub[i][1], O[i][3]);
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          ob[16 * m + 4 * lg + jj][16 * (wave * NT + i) + li] = f32_to_bf16(O[i][m][jj]);
+    lds_barrier();
+  };
+  for (int lc = 0; lc < nch; lc += 2) {
+    chunk_step(buf0, out0, lc);
+    if (lc + 1 < nch) chunk_step(buf1, out1, lc + 1);
+  }
+
+  if (slot_ok && (flags & KDA_WRITE_FINAL_STATE)) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) Sg[(size_t)(16 * t + 4 * lg + jj) * D + col[i]] = S[i][t][jj];
+  }
+}
+
+template <int CW, int NT, int LW>
+kda_status_t launch_scan_ws(int32_t N, int H, const Workspace& w, float* states, int32_t num_slots,
+                            const int32_t* slots, uint32_t flags, void* o, hipStream_t stream) {
+  constexpr int kGroups = D / (16 * CW * NT);
+  hipLaunchKernelGGL((scan_ws_kernel<CW, NT, LW>), dim3((unsigned)(N * H * kGroups)),
+                     dim3(64 * (CW + LW)), 0, stream, N, H, w, states, num_slots, slots, flags,
+                     static_cast<uint16_t*>(o));
+  return check_launch("chunk_fwd scan");
+}
+
 template <int WAVES, int NT>
 kda_status_t launch_scan(int32_t N, int H, const Workspace& w, float* states, int32_t num_slots,
                          const int32_t* slots, uint32_t flags, void* o, hipStream_t stream) {
@@ -859,11 +1098,12 @@ kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, cons
                      static_cast<const uint16_t*>(v), g, beta, N, H, w);
   st = check_launch("chunk_fwd prep");
   if (st != KDA_OK) return st;
-  // Few chains (sequence-heads): spread each head over 4 workgroups of 2 waves
-  // to shorten every step of the chain; many chains: one workgroup of 4 waves
-  // x 32 columns per head for throughput.
-  if ((size_t)N * H * 4 <= 512)
-    return launch_scan<2, 1>(N, H, w, states, num_slots, slots, flags, o, stream);
+  // Few chains (sequence-heads), one workgroup per CU at most: each head is
+  // split over 4 warp-specialised workgroups (2 compute + 6 loader waves) to
+  // shorten every step of the chains.  Many chains: one workgroup of 4 waves x
+  // 32 columns per head, which fetches each chunk's shared operands once.
+  if ((size_t)N * H * 4 <= (size_t)ncu)
+    return launch_scan_ws<2, 1, 6>(N, H, w, states, num_slots, slots, flags, o, stream);
   return launch_scan<4, 2>(N, H, w, states, num_slots, slots, flags, o, stream);
 }
 
