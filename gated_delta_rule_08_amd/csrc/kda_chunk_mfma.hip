@@ -202,7 +202,11 @@ struct PrepSmem {
   float A[C][AP];        // beta-scaled strictly lower A_kk
   float Tm[C][AP];       // (I + A_kk)^-1
   float tot[4][D];       // per-quarter column totals of the running gate sums
+  float es[4][D];        // exp(G) at the first row of each 16-row block
+  float spr[kPrepWaves]; // per-wave maxima of the in-block gate spread
   float bs[C];
+  bf16x8 rk[16][64];     // row-side Gram operands [R * 4 + s][lane]: k_r exp(G_r - G_sR)
+  bf16x8 rq[16][64];     //                                         q_r exp(G_r - G_sR)
 };
 
 // One item's inputs between the global loads and the LDS staging.
@@ -216,17 +220,26 @@ struct ItemPos {
   int gc, h, t0, c;  // chunk, head, first token, valid rows (>= 1)
 };
 
-__device__ __forceinline__ ItemPos locate(const Workspace& w, int N, int H, int item) {
+// The header arrays are read through const __restrict__ pointers with
+// wave-uniform indices, so the compiler uses scalar loads: their waits do not
+// include the workgroup's outstanding vector loads and stores.
+struct Header {
+  const int32_t* __restrict__ seq_start;
+  const int32_t* __restrict__ seq_end;
+  const int32_t* __restrict__ chunk_off;
+};
+
+__device__ __forceinline__ ItemPos locate(const Header& hd, int N, int H, int item) {
   ItemPos p;
   p.gc = item / H;
   p.h = item - p.gc * H;
   int lo = 0, hi = N - 1;  // the sequence owning chunk gc (largest n with chunk_off[n] <= gc)
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (w.chunk_off[mid] <= p.gc) lo = mid; else hi = mid - 1;
+    if (hd.chunk_off[mid] <= p.gc) lo = mid; else hi = mid - 1;
   }
-  p.t0 = w.seq_start[lo] + (p.gc - w.chunk_off[lo]) * C;
-  p.c = min(C, w.seq_end[lo] - p.t0);
+  p.t0 = hd.seq_start[lo] + (p.gc - hd.chunk_off[lo]) * C;
+  p.c = min(C, hd.seq_end[lo] - p.t0);
   return p;
 }
 
@@ -278,44 +291,29 @@ __device__ __forceinline__ void prep_stage(PrepSmem& sm, const PrepIn& in, int c
 __device__ __forceinline__ float ld_bf(const uint16_t* row, int c) { return bf16_to_f32(row[c]); }
 
 // Gram block pair (R, J), J <= R: raw A[r][j] for r in block R (lane row li),
-// j = 16J + 4lg + jj, for keys (acck) and queries (accq).
-__device__ __forceinline__ void gram_pair(const PrepSmem& sm, int R, int J, int li, int lg,
-                                          f32x4& acck, f32x4& accq) {
+// j = 16J + 4lg + jj, for keys (acck) and queries (accq).  The row side comes
+// scaled from LDS; the key side k_j exp(G_sR - G_j) is formed here.  `wide`:
+// the gate spread inside block R exceeds kMaxSpread, so the diagonal pair is
+// summed element by element in fp32 (exact, slow, only for extreme decay).
+__device__ __forceinline__ void gram_pair(const PrepSmem& sm, int R, int J, bool wide, int li,
+                                          int lg, int lane, f32x4& acck, f32x4& accq) {
   const int sR = 16 * R, r = sR + li, j = 16 * J + li;
   acck = f32x4{0.f, 0.f, 0.f, 0.f};
   accq = acck;
-  bool fast = true;
-  if (J == R) {
-    const int lane = 16 * lg + li;
-    float sp = fmaxf(sm.G[sR][lane] - sm.G[sR + 15][lane],
-                     sm.G[sR][lane + 64] - sm.G[sR + 15][lane + 64]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sp = fmaxf(sp, __shfl_xor(sp, off, 64));
-    fast = sp <= kMaxSpread;
-  }
-  if (fast) {
+  if (J != R || !wide) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      float kr[8], qr[8], gr[8], gs[8], kj[8], gj[8], fk[8], fq[8], fa[8];
-      runs_bf(sm.K[r], s, lg, kr);
-      runs_bf(sm.Q[r], s, lg, qr);
-      runs_f32(sm.G[r], s, lg, gr);
+      float gs[8], kj[8], gj[8], fa[8];
       runs_f32(sm.G[sR], s, lg, gs);
       runs_bf(sm.K[j], s, lg, kj);
       runs_f32(sm.G[j], s, lg, gj);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float f = fast_exp(gr[i] - gs[i]);      // rows r:  exp(G_r - G_s) <= 1
-        fk[i] = kr[i] * f;
-        fq[i] = qr[i] * f;
-        fa[i] = kj[i] * fast_exp(gs[i] - gj[i]);     // rows j:  exp(G_s - G_j)
-      }
+      for (int i = 0; i < 8; ++i) fa[i] = kj[i] * fast_exp(gs[i] - gj[i]);  // rows j: exp(G_s - G_j)
       const bf16x8 ak = pack8(fa);
-      acck = mfma(ak, pack8(fk), acck);
-      accq = mfma(ak, pack8(fq), accq);
+      acck = mfma(ak, sm.rk[R * 4 + s][lane], acck);
+      accq = mfma(ak, sm.rq[R * 4 + s][lane], accq);
     }
   } else {
-    // extreme decay inside the block: exact element-wise fp32 sums
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int jd = sR + 4 * lg + jj;
@@ -334,32 +332,34 @@ __device__ __forceinline__ void gram_pair(const PrepSmem& sm, int R, int J, int 
   }
 }
 
-// LDS use (~124 KiB) allows one workgroup (two waves per SIMD) per CU.
+// LDS use (~153 KiB) allows one workgroup (two waves per SIMD) per CU.
 __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, int32_t N, int H, Workspace w) {
+    const float* __restrict__ g, const float* __restrict__ beta, int32_t N, int H, Workspace w,
+    const int32_t* __restrict__ seq_start, const int32_t* __restrict__ seq_end,
+    const int32_t* __restrict__ chunk_off) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
+  const Header hd{seq_start, seq_end, chunk_off};
   PrepSmem& sm = *reinterpret_cast<PrepSmem*>(smem_raw);
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
-  const int total = w.chunk_off[N] * H;
+  const int total = hd.chunk_off[N] * H;
   int item = blockIdx.x;
   if (item >= total) return;  // uniform
 
   PrepIn in;
-  ItemPos pos = locate(w, N, H, item);
+  ItemPos pos = locate(hd, N, H, item);
   prep_load(in, pos, q, k, v, g, beta, H, tid);
+  // Wait for the first item here, so that inside the loop the wait for the
+  // prefetched registers only has to cover the loads, not the stores issued
+  // after them.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
   for (; item < total; item += gridDim.x) {
     const size_t ci = (size_t)item;  // items are numbered chunk-major: ci = gc * H + h
     const int c = pos.c;
     lds_barrier();  // the previous item is done with LDS
     prep_stage(sm, in, c, tid);
-    const int next = item + gridDim.x;
-    if (next < total) {  // next item's loads overlap this item's compute
-      pos = locate(w, N, H, next);
-      prep_load(in, pos, q, k, v, g, beta, H, tid);
-    }
     lds_barrier();
 
     // ---- running sum of the log-gates down each channel (four quarters of 16 rows)
@@ -376,18 +376,60 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2,
       for (int j = 0; j < qt; ++j) base += sm.tot[j][col];
 #pragma unroll
       for (int i = 0; i < 16; ++i) sm.G[16 * qt + i][col] = x[i] + base;
+      sm.es[qt][col] = fast_exp(x[0] + base);
+      float sp = x[0] - x[15];  // spread of this channel inside block qt
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) sp = fmaxf(sp, __shfl_xor(sp, off, 64));
+      if (lane == 0) sm.spr[wave] = sp;  // waves 2qt and 2qt + 1 cover block qt
+    }
+    // The next item's loads overlap this item's compute.  They are issued here
+    // rather than at the top of the item, where the previous item's output
+    // stores still occupy the memory pipeline.
+    const int next = item + gridDim.x;
+    if (next < total) {
+      pos = locate(hd, N, H, next);
+      prep_load(in, pos, q, k, v, g, beta, H, tid);
     }
     lds_barrier();
 
-    // ---- gated Gram blocks (10 block pairs over 8 waves) and Q*Gam
+    // ---- row-side Gram operands and Q*Gam, two (block R, K-block s) units per lane
     {
-      constexpr int kPairR[10] = {3, 3, 3, 3, 2, 2, 2, 1, 1, 0};
-      constexpr int kPairJ[10] = {3, 2, 1, 0, 2, 1, 0, 1, 0, 0};
+      uint16_t* qg_out = reinterpret_cast<uint16_t*>(w.qg + ci * kQgBytes);
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int R = (tid >> 8) + 2 * x, s = wave & 3, r = 16 * R + li;
+        float kr[8], qr[8], gr[8], gs[8], e0[8], fk[8], fq[8], fg[8];
+        runs_bf(sm.K[r], s, lg, kr);
+        runs_bf(sm.Q[r], s, lg, qr);
+        runs_f32(sm.G[r], s, lg, gr);
+        runs_f32(sm.G[16 * R], s, lg, gs);
+        runs_f32(sm.es[R], s, lg, e0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float f = fast_exp(gr[i] - gs[i]);  // exp(G_r - G_sR) <= 1
+          fk[i] = kr[i] * f;
+          fq[i] = qr[i] * f;
+          fg[i] = fq[i] * e0[i];                    // q_r exp(G_r)
+        }
+        sm.rk[R * 4 + s][lane] = pack8(fk);
+        sm.rq[R * 4 + s][lane] = pack8(fq);
+        *reinterpret_cast<bf16x8*>(qg_out + ((size_t)(R * 4 + s) * 64 + lane) * 8) = pack8(fg);
+      }
+    }
+    lds_barrier();
+
+    // ---- gated Gram blocks (10 block pairs over 8 waves)
+    {
       uint16_t* aq_out = reinterpret_cast<uint16_t*>(w.aq + ci * kAqBytes);
       for (int pi = wave; pi < 10; pi += kPrepWaves) {
-        const int R = kPairR[pi], J = kPairJ[pi];
+        // pairs in the order (3,3) (3,2) (3,1) (3,0) (2,2) (2,1) (2,0) (1,1) (1,0) (0,0),
+        // computed rather than read from a table (a memory read would wait for
+        // the next item's prefetched loads)
+        const int R = pi < 4 ? 3 : pi < 7 ? 2 : pi < 9 ? 1 : 0;
+        const int J = pi < 4 ? 3 - pi : pi < 7 ? 6 - pi : pi < 9 ? 8 - pi : 0;
         f32x4 acck, accq;
-        gram_pair(sm, R, J, li, lg, acck, accq);
+        const bool wide = fmaxf(sm.spr[2 * R], sm.spr[2 * R + 1]) > kMaxSpread;
+        gram_pair(sm, R, J, wide, li, lg, lane, acck, accq);
         const int r = 16 * R + li;
         const float br = sm.bs[r];
         float4 arow;
@@ -410,19 +452,6 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2,
         const uint2 z = make_uint2(0, 0);
         *reinterpret_cast<uint2*>(aq_out + ((size_t)(0 * 2 + 0) * 64 + lane) * 8 + 4) = z;
         *reinterpret_cast<uint2*>(aq_out + ((size_t)(2 * 2 + 1) * 64 + lane) * 8 + 4) = z;
-      }
-      // Q*Gam as the scan's A operand: wave -> row block m = wave / 2, K-blocks 2 (wave & 1) + {0, 1}
-      uint16_t* qg_out = reinterpret_cast<uint16_t*>(w.qg + ci * kQgBytes);
-      const int m = wave >> 1, r = 16 * m + li;
-#pragma unroll
-      for (int ss = 0; ss < 2; ++ss) {
-        const int s = 2 * (wave & 1) + ss;
-        float qr[8], gr[8], f[8];
-        runs_bf(sm.Q[r], s, lg, qr);
-        runs_f32(sm.G[r], s, lg, gr);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = qr[i] * fast_exp(gr[i]);
-        *reinterpret_cast<bf16x8*>(qg_out + ((size_t)(m * 4 + s) * 64 + lane) * 8) = pack8(f);
       }
     }
     lds_barrier();
@@ -1095,7 +1124,8 @@ kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, cons
   const unsigned prep_grid = (unsigned)(items < (size_t)ncu ? items : (size_t)ncu);
   hipLaunchKernelGGL(prep_kernel, dim3(prep_grid), dim3(kPrepThreads), sizeof(PrepSmem), stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), g, beta, N, H, w);
+                     static_cast<const uint16_t*>(v), g, beta, N, H, w, w.seq_start, w.seq_end,
+                     w.chunk_off);
   st = check_launch("chunk_fwd prep");
   if (st != KDA_OK) return st;
   // Few chains (sequence-heads), one workgroup per CU at most: each head is
