@@ -332,19 +332,16 @@ __device__ __forceinline__ void gram_pair(const PrepSmem& sm, int R, int J, bool
   }
 }
 
-// LDS use (~153 KiB) allows one workgroup (two waves per SIMD) per CU.
-__global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prep_kernel(
+// One workgroup of the prep: items wg, wg + nwg, ... in chunk-major order.
+__device__ __forceinline__ void prep_role(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, int32_t N, int H, Workspace w,
-    const int32_t* __restrict__ seq_start, const int32_t* __restrict__ seq_end,
-    const int32_t* __restrict__ chunk_off) {
-  extern __shared__ __align__(16) uint8_t smem_raw[];
-  const Header hd{seq_start, seq_end, chunk_off};
+    const float* __restrict__ g, const float* __restrict__ beta, int32_t N, int H,
+    const Workspace& w, const Header& hd, uint8_t* smem_raw, int wg, int nwg) {
   PrepSmem& sm = *reinterpret_cast<PrepSmem*>(smem_raw);
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
   const int total = hd.chunk_off[N] * H;
-  int item = blockIdx.x;
+  int item = wg;
   if (item >= total) return;  // uniform
 
   PrepIn in;
@@ -355,7 +352,7 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2,
   // after them.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-  for (; item < total; item += gridDim.x) {
+  for (; item < total; item += nwg) {
     const size_t ci = (size_t)item;  // items are numbered chunk-major: ci = gc * H + h
     const int c = pos.c;
     lds_barrier();  // the previous item is done with LDS
@@ -385,7 +382,7 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2,
     // The next item's loads overlap this item's compute.  They are issued here
     // rather than at the top of the item, where the previous item's output
     // stores still occupy the memory pipeline.
-    const int next = item + gridDim.x;
+    const int next = item + nwg;
     if (next < total) {
       pos = locate(hd, N, H, next);
       prep_load(in, pos, q, k, v, g, beta, H, tid);
@@ -551,6 +548,17 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2,
       if (tid < D) reinterpret_cast<float*>(w.gc + ci * kGcBytes)[tid] = fast_exp(sm.G[C - 1][tid]);
     }
   }
+}
+
+// LDS use (~153 KiB) allows one workgroup (two waves per SIMD) per CU.
+__global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prep_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, int32_t N, int H, Workspace w,
+    const int32_t* __restrict__ seq_start, const int32_t* __restrict__ seq_end,
+    const int32_t* __restrict__ chunk_off) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  const Header hd{seq_start, seq_end, chunk_off};
+  prep_role(q, k, v, g, beta, N, H, w, hd, smem_raw, blockIdx.x, gridDim.x);
 }
 
 // ------------------------------------------------------------------ 3. scan
@@ -834,34 +842,42 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(1, 1
 }
 
 // Warp-specialised scan: CW compute waves own the state columns (NT tiles of
-// 16 each) and touch only LDS and registers (plus their own Ut tiles, loaded
-// into registers one chunk ahead); LW loader waves copy the next chunk's shared
-// operands (-W, Q*Gam, Kd^T, A_qk, Gam_C) into LDS with direct global->LDS
-// loads and store the previous chunk's staged outputs.  The copy rate of a CU
-// grows with the number of waves issuing copies, and the compute waves never
-// stall on issuing them.  One LDS barrier per chunk separates the steps: in
-// step c the compute waves read buffer c % 2 and write staging tile c % 2,
-// while the loaders fill buffer (c + 1) % 2 and store staging tile (c - 1) % 2.
+// 16 each) and touch only LDS and registers; LW loader waves copy the next
+// chunk's operands (-W, Q*Gam, Kd^T, A_qk, the group's Ut tiles, Gam_C) into
+// LDS with direct global->LDS loads and store the previous chunk's staged
+// outputs.  The copy rate of a CU grows with the number of waves issuing
+// copies, and the compute waves never stall on issuing them.  One LDS barrier
+// per chunk separates the steps: in step c the compute waves read buffer c % 2
+// and write staging tile c % 2, while the loaders store staging tile (c-1) % 2
+// and fill buffer (c + 1) % 2.
 template <int CW, int NT>
-struct ScanOperands {
-  bf16x8 wn[16][64];
-  bf16x8 qg[16][64];
-  bf16x8 kd[16][64];
-  bf16x8 aq[8][64];
-  f32x4 gc[32];
+struct ScanLds {
+  static constexpr int kTiles = CW * NT;
+  static constexpr int kCols = 16 * kTiles;
+  struct Buf {
+    bf16x8 wn[16][64];         // [m*4 + s][lane]
+    bf16x8 qg[16][64];         // [m*4 + s][lane]
+    bf16x8 kd[16][64];         // [t*2 + s'][lane]
+    bf16x8 aq[8][64];          // [m*2 + s'][lane]
+    f32x4 ut[4][kTiles][64];   // [m][local column tile][lane]
+    f32x4 gc[32];              // Gam_C
+  };
+  Buf buf[2];
+  uint16_t out[2][C][kCols];   // staged bf16 outputs of a chunk
 };
 
 template <int CW, int NT, int LW>
-__global__ __launch_bounds__(64 * (CW + LW)) void scan_ws_kernel(
-    int32_t N, int H, Workspace w, float* __restrict__ states, int32_t num_slots,
-    const int32_t* __restrict__ slots, uint32_t flags, uint16_t* __restrict__ o) {
-  using Buf = ScanOperands<CW, NT>;
-  constexpr int kCols = 16 * CW * NT;  // columns of this workgroup
-  __shared__ Buf buf0, buf1;
-  __shared__ uint16_t out0[C][kCols], out1[C][kCols];
+__device__ __forceinline__ void scan_role(int b, uint8_t* smem, int32_t N, int H, const Workspace& w,
+                                          float* __restrict__ states, int32_t num_slots,
+                                          const int32_t* __restrict__ slots, uint32_t flags,
+                                          uint16_t* __restrict__ o) {
+  using L = ScanLds<CW, NT>;
+  using Buf = typename L::Buf;
+  constexpr int kTiles = L::kTiles, kCols = L::kCols;
+  L& sl = *reinterpret_cast<L*>(smem);
   const int NH = N * H;
-  const int head_lin = blockIdx.x % NH;
-  const int group = blockIdx.x / NH;
+  const int head_lin = b % NH;
+  const int group = b / NH;
   const int n = head_lin / H, h = head_lin - n * H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
   const int start = w.seq_start[n], end = w.seq_end[n], nch = w.seq_nch[n];
@@ -871,31 +887,39 @@ __global__ __launch_bounds__(64 * (CW + LW)) void scan_ws_kernel(
     // ------------------------------------------------------------ loaders
     const int lw = wave - CW, ltid = tid - 64 * CW;
     const int off = lane * 16;
+    constexpr int kPieces = 56 + 4 * kTiles;  // 1 KiB pieces of a chunk's operands
     auto issue = [&](size_t ci, Buf* dst) {
       const uint8_t* wn = w.wn + ci * kWnBytes;
       const uint8_t* qg = w.qg + ci * kQgBytes;
       const uint8_t* kd = w.kd + ci * kKdBytes;
       const uint8_t* aq = w.aq + ci * kAqBytes;
+      const uint8_t* ut = w.ut + ci * kUtBytes;
 #pragma unroll
-      for (int i = 0; i < (56 + LW - 1) / LW; ++i) {
-        const int p = lw + LW * i;  // wave-uniform 1 KiB piece
+      for (int i = 0; i < (kPieces + LW - 1) / LW; ++i) {
+        const int p = lw + LW * i;  // wave-uniform
         if (p < 16) dma16(wn + p * 1024 + off, &dst->wn[p][0]);
         else if (p < 32) dma16(qg + (p - 16) * 1024 + off, &dst->qg[p - 16][0]);
         else if (p < 48) dma16(kd + (p - 32) * 1024 + off, &dst->kd[p - 32][0]);
         else if (p < 56) dma16(aq + (p - 48) * 1024 + off, &dst->aq[p - 48][0]);
+        else if (p < kPieces) {
+          const int x = p - 56, m = x / kTiles, tl = x % kTiles;
+          dma16(ut + (size_t)((m * 8 + group * kTiles + tl) * 64) * 16 + off,
+                      &dst->ut[m][tl][0]);
+        }
       }
       if (lw == LW - 1 && lane < 32) dma16(w.gc + ci * kGcBytes + off, &dst->gc[0]);
     };
     // Staged outputs, as whole 16-byte row pieces; pieces of rows past the
     // sequence end go to the workspace sink, which keeps the stores free of
-    // branches on the data path.
+    // branches on the data path.  They are read before the next copies are
+    // issued, so no copy into LDS is outstanding when they are.
     constexpr int kRowPieces = kCols / 8;
-    constexpr int kPieces = C * kRowPieces;
+    constexpr int kOutPieces = C * kRowPieces;
     auto store_rows = [&](const uint16_t (*ob)[kCols], int base) {
 #pragma unroll
-      for (int x = 0; x < (kPieces + 64 * LW - 1) / (64 * LW); ++x) {
+      for (int x = 0; x < (kOutPieces + 64 * LW - 1) / (64 * LW); ++x) {
         const int u = ltid + 64 * LW * x;
-        if (kPieces % (64 * LW) == 0 || u < kPieces) {
+        if (kOutPieces % (64 * LW) == 0 || u < kOutPieces) {
           const int r = u / kRowPieces, pc = u % kRowPieces, tok = base + r;
           uint4* dst = tok < end
               ? reinterpret_cast<uint4*>(o + ((size_t)tok * H + h) * D + kCols * group + 8 * pc)
@@ -908,26 +932,26 @@ __global__ __launch_bounds__(64 * (CW + LW)) void scan_ws_kernel(
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
       lds_barrier();
     };
-    if (nch > 0) issue((size_t)cbase * H + h, &buf0);
+    if (nch > 0) issue((size_t)cbase * H + h, &sl.buf[0]);
     step_end();
     for (int lc = 0; lc < nch; lc += 2) {
-      if (lc + 1 < nch) issue((size_t)(cbase + lc + 1) * H + h, &buf1);
-      if (lc > 0) store_rows(out1, start + (lc - 1) * C);
+      if (lc > 0) store_rows(sl.out[1], start + (lc - 1) * C);
+      if (lc + 1 < nch) issue((size_t)(cbase + lc + 1) * H + h, &sl.buf[1]);
       step_end();
       if (lc + 1 < nch) {
-        if (lc + 2 < nch) issue((size_t)(cbase + lc + 2) * H + h, &buf0);
-        store_rows(out0, start + lc * C);
+        store_rows(sl.out[0], start + lc * C);
+        if (lc + 2 < nch) issue((size_t)(cbase + lc + 2) * H + h, &sl.buf[0]);
         step_end();
       }
     }
-    if (nch > 0) store_rows((nch - 1) & 1 ? out1 : out0, start + (nch - 1) * C);
+    if (nch > 0) store_rows(sl.out[(nch - 1) & 1], start + (nch - 1) * C);
     return;
   }
 
   // -------------------------------------------------------------- compute
   int col[NT];
 #pragma unroll
-  for (int i = 0; i < NT; ++i) col[i] = 16 * (group * CW * NT + wave * NT + i) + li;
+  for (int i = 0; i < NT; ++i) col[i] = 16 * (group * kTiles + wave * NT + i) + li;
   const int slot = slots ? slots[n] : n;
   const bool slot_ok = states != nullptr && slot >= 0 && slot < num_slots;
   float* Sg = slot_ok ? states + ((size_t)slot * H + h) * (size_t)(D * D) : nullptr;
@@ -947,25 +971,14 @@ __global__ __launch_bounds__(64 * (CW + LW)) void scan_ws_kernel(
 #pragma unroll
       for (int t = 0; t < 8; ++t) S[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  f32x4 Unext[NT][4];
-  auto load_ut = [&](size_t ci) {
-    const f32x4* ut = reinterpret_cast<const f32x4*>(w.ut + ci * kUtBytes);
-#pragma unroll
-    for (int i = 0; i < NT; ++i)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) Unext[i][m] = ut[(m * 8 + (col[i] >> 4)) * 64 + lane];
-  };
-  if (nch > 0) load_ut((size_t)cbase * H + h);
   lds_barrier();
 
-  auto chunk_step = [&](const Buf& B, uint16_t (*ob)[kCols], int lc) {
+  auto chunk_step = [&](const Buf& B, uint16_t (*ob)[kCols]) {
     f32x4 U[NT][4];
 #pragma unroll
     for (int i = 0; i < NT; ++i)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) U[i][m] = Unext[i][m];
-    if (lc + 1 < nch) load_ut((size_t)(cbase + lc + 1) * H + h);
-
+      for (int m = 0; m < 4; ++m) U[i][m] = B.ut[m][wave * NT + i][lane];
     bf16x8 a_wn[16];
 #pragma unroll
     for (int x = 0; x < 16; ++x) a_wn[x] = B.wn[x][lane];
@@ -1046,8 +1059,8 @@ __global__ __launch_bounds__(64 * (CW + LW)) void scan_ws_kernel(
     lds_barrier();
   };
   for (int lc = 0; lc < nch; lc += 2) {
-    chunk_step(buf0, out0, lc);
-    if (lc + 1 < nch) chunk_step(buf1, out1, lc + 1);
+    chunk_step(sl.buf[0], sl.out[0]);
+    if (lc + 1 < nch) chunk_step(sl.buf[1], sl.out[1]);
   }
 
   if (slot_ok && (flags & KDA_WRITE_FINAL_STATE)) {
@@ -1061,12 +1074,28 @@ __global__ __launch_bounds__(64 * (CW + LW)) void scan_ws_kernel(
 }
 
 template <int CW, int NT, int LW>
+__global__ __launch_bounds__(64 * (CW + LW)) void scan_ws_kernel(
+    int32_t N, int H, Workspace w, float* __restrict__ states, int32_t num_slots,
+    const int32_t* __restrict__ slots, uint32_t flags, uint16_t* __restrict__ o) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  scan_role<CW, NT, LW>(blockIdx.x, smem_raw, N, H, w, states, num_slots, slots, flags, o);
+}
+
+template <int CW, int NT, int LW>
 kda_status_t launch_scan_ws(int32_t N, int H, const Workspace& w, float* states, int32_t num_slots,
                             const int32_t* slots, uint32_t flags, void* o, hipStream_t stream) {
   constexpr int kGroups = D / (16 * CW * NT);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(scan_ws_kernel<CW, NT, LW>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)sizeof(ScanLds<CW, NT>));
+    if (e != hipSuccess) return hip_status(e, "hipFuncSetAttribute(scan)");
+    attr_set = true;
+  }
   hipLaunchKernelGGL((scan_ws_kernel<CW, NT, LW>), dim3((unsigned)(N * H * kGroups)),
-                     dim3(64 * (CW + LW)), 0, stream, N, H, w, states, num_slots, slots, flags,
-                     static_cast<uint16_t*>(o));
+                     dim3(64 * (CW + LW)), sizeof(ScanLds<CW, NT>), stream, N, H, w, states,
+                     num_slots, slots, flags, static_cast<uint16_t*>(o));
   return check_launch("chunk_fwd scan");
 }
 
@@ -1100,6 +1129,12 @@ kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, cons
   const int H = sh->num_heads;
   Workspace w = carve(workspace, T, N, H);
   const size_t cap = nchunks_max(T, N);
+  const size_t items = cap * (size_t)H;
+  int dev = 0, ncu = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int x = 0;
+    if (hipDeviceGetAttribute(&x, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && x > 0) ncu = x;
+  }
   hipLaunchKernelGGL(index_kernel, dim3(1), dim3(64), 0, stream, cu, N, T, (int32_t)cap, w);
   kda_status_t st = check_launch("chunk_fwd index");
   if (st != KDA_OK) return st;
@@ -1112,15 +1147,6 @@ kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, cons
     attr_set = true;
   }
   // persistent prep: one workgroup per CU, each walks items with a grid stride
-  int ncu = 256;
-  {
-    int dev = 0;
-    if (hipGetDevice(&dev) == hipSuccess) {
-      int v = 0;
-      if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) ncu = v;
-    }
-  }
-  const size_t items = cap * (size_t)H;
   const unsigned prep_grid = (unsigned)(items < (size_t)ncu ? items : (size_t)ncu);
   hipLaunchKernelGGL(prep_kernel, dim3(prep_grid), dim3(kPrepThreads), sizeof(PrepSmem), stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
@@ -1128,10 +1154,10 @@ kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, cons
                      w.chunk_off);
   st = check_launch("chunk_fwd prep");
   if (st != KDA_OK) return st;
-  // Few chains (sequence-heads), one workgroup per CU at most: each head is
-  // split over 4 warp-specialised workgroups (2 compute + 6 loader waves) to
-  // shorten every step of the chains.  Many chains: one workgroup of 4 waves x
-  // 32 columns per head, which fetches each chunk's shared operands once.
+  // Up to one workgroup per CU: each head split over 4 warp-specialised
+  // workgroups to shorten every step of the chains.  Many chains: one
+  // workgroup of 4 waves x 32 columns per head, which fetches each chunk's
+  // shared operands once.
   if ((size_t)N * H * 4 <= (size_t)ncu)
     return launch_scan_ws<2, 1, 6>(N, H, w, states, num_slots, slots, flags, o, stream);
   return launch_scan<4, 2>(N, H, w, states, num_slots, slots, flags, o, stream);
