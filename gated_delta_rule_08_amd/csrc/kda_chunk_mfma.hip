@@ -63,6 +63,15 @@ constexpr size_t kKdBytes = 8 * 2 * 64 * 16;   // Kd^T    A operand, M=dk,    K=
 constexpr size_t kAqBytes = 4 * 2 * 64 * 16;   // A_qk    A operand, M=rows,  K=rows
 constexpr size_t kUtBytes = 4 * 8 * 64 * 16;   // Ut      accumulator layout, fp32
 constexpr size_t kGcBytes = D * 4;             // Gam_C   fp32
+// Written by the state-only scan for the output kernel (few chains):
+constexpr size_t kScBytes = 8 * 4 * 64 * 16;   // S at chunk start, B operand (K=dk, N=dv), bf16
+constexpr size_t kUcBytes = 8 * 2 * 64 * 16;   // U, B operand (K=rows, N=dv), bf16
+
+// Chains (sequence-heads) up to which the scan only carries the state and a
+// separate, fully parallel kernel forms the outputs: with few chains the
+// serial chain of chunk steps is the critical path, so work is moved off it.
+constexpr int kSplitMaxChains = 32;
+bool split_outputs(int32_t N, int H) { return (int64_t)N * H <= kSplitMaxChains; }
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -122,6 +131,8 @@ struct Workspace {
   uint8_t* aq;
   uint8_t* ut;
   uint8_t* gc;
+  uint8_t* sc;         // split outputs only (else null)
+  uint8_t* uc;
   uint8_t* sink;       // 256 B target of stores for rows past a sequence's end
 };
 
@@ -147,6 +158,11 @@ Workspace carve(void* base, int32_t T, int32_t N, int H) {
   w.aq = p; p += align256(ci * kAqBytes);
   w.ut = p; p += align256(ci * kUtBytes);
   w.gc = p; p += align256(ci * kGcBytes);
+  w.sc = w.uc = nullptr;
+  if (split_outputs(N, H)) {
+    w.sc = p; p += align256(ci * kScBytes);
+    w.uc = p; p += align256(ci * kUcBytes);
+  }
   w.sink = p;
   return w;
 }
@@ -1081,6 +1097,272 @@ __global__ __launch_bounds__(64 * (CW + LW)) void scan_ws_kernel(
   scan_role<CW, NT, LW>(blockIdx.x, smem_raw, N, H, w, states, num_slots, slots, flags, o);
 }
 
+// State-only warp-specialised scan (few chains).  Per chunk only the state
+// recurrence is on the serial path: U = Ut - W S and S' = Diag(Gam_C) S +
+// Kd^T U.  The compute waves store the bf16 MFMA operands they form anyway,
+// S at the chunk start and U, for the output kernel, which then forms
+// O = (Q*Gam) S + A_qk U for all chunks in parallel.  The loaders copy -W,
+// Kd^T, the workgroup's Ut tiles and Gam_C.
+template <int CW, int NT>
+struct StateLds {
+  static constexpr int kTiles = CW * NT;
+  struct Buf {
+    bf16x8 wn[16][64];         // [m*4 + s][lane]
+    bf16x8 kd[16][64];         // [t*2 + s'][lane]
+    f32x4 ut[4][kTiles][64];   // [m][local column tile][lane]
+    f32x4 gc[32];              // Gam_C
+  };
+  Buf buf[2];
+};
+
+template <int CW, int NT, int LW>
+__global__ __launch_bounds__(64 * (CW + LW)) void scan_state_kernel(
+    int32_t N, int H, Workspace w, float* __restrict__ states, int32_t num_slots,
+    const int32_t* __restrict__ slots, uint32_t flags) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  using L = StateLds<CW, NT>;
+  using Buf = typename L::Buf;
+  constexpr int kTiles = L::kTiles;
+  L& sl = *reinterpret_cast<L*>(smem_raw);
+  const int NH = N * H;
+  const int head_lin = blockIdx.x % NH;
+  const int group = blockIdx.x / NH;
+  const int n = head_lin / H, h = head_lin - n * H;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+  const int nch = w.seq_nch[n];
+  const int cbase = w.chunk_off[n];
+
+  if (wave >= CW) {
+    // ------------------------------------------------------------ loaders
+    const int lw = wave - CW;
+    const int off = lane * 16;
+    constexpr int kPieces = 32 + 4 * kTiles;  // 1 KiB pieces of a chunk's operands
+    auto issue = [&](size_t ci, Buf* dst) {
+      const uint8_t* wn = w.wn + ci * kWnBytes;
+      const uint8_t* kd = w.kd + ci * kKdBytes;
+      const uint8_t* ut = w.ut + ci * kUtBytes;
+#pragma unroll
+      for (int i = 0; i < (kPieces + LW - 1) / LW; ++i) {
+        const int p = lw + LW * i;  // wave-uniform
+        if (p < 16) dma16(wn + p * 1024 + off, &dst->wn[p][0]);
+        else if (p < 32) dma16(kd + (p - 16) * 1024 + off, &dst->kd[p - 16][0]);
+        else if (p < kPieces) {
+          const int x = p - 32, m = x / kTiles, tl = x % kTiles;
+          dma16(ut + (size_t)((m * 8 + group * kTiles + tl) * 64) * 16 + off, &dst->ut[m][tl][0]);
+        }
+      }
+      if (lw == LW - 1 && lane < 32) dma16(w.gc + ci * kGcBytes + off, &dst->gc[0]);
+    };
+    auto step_end = [&]() {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+      lds_barrier();
+    };
+    if (nch > 0) issue((size_t)cbase * H + h, &sl.buf[0]);
+    step_end();
+    for (int lc = 0; lc < nch; lc += 2) {
+      if (lc + 1 < nch) issue((size_t)(cbase + lc + 1) * H + h, &sl.buf[1]);
+      step_end();
+      if (lc + 1 < nch) {
+        if (lc + 2 < nch) issue((size_t)(cbase + lc + 2) * H + h, &sl.buf[0]);
+        step_end();
+      }
+    }
+    return;
+  }
+
+  // -------------------------------------------------------------- compute
+  int ctile[NT], col[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    ctile[i] = group * kTiles + wave * NT + i;
+    col[i] = 16 * ctile[i] + li;
+  }
+  const int slot = slots ? slots[n] : n;
+  const bool slot_ok = states != nullptr && slot >= 0 && slot < num_slots;
+  float* Sg = slot_ok ? states + ((size_t)slot * H + h) * (size_t)(D * D) : nullptr;
+  f32x4 S[NT][8];
+  if (slot_ok && (flags & KDA_READ_INITIAL_STATE)) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) S[i][t][jj] = Sg[(size_t)(16 * t + 4 * lg + jj) * D + col[i]];
+  } else {
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) S[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  lds_barrier();
+
+  auto chunk_step = [&](const Buf& B, size_t ci) {
+    f32x4 U[NT][4];
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) U[i][m] = B.ut[m][wave * NT + i][lane];
+    bf16x8 a_wn[16];
+#pragma unroll
+    for (int x = 0; x < 16; ++x) a_wn[x] = B.wn[x][lane];
+    bf16x8 sb[NT][4];
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) sb[i][s] = pack_acc(S[i][2 * s], S[i][2 * s + 1]);
+    bf16x8 a_kd[16];
+    f32x4 gcv[8];
+#pragma unroll
+    for (int x = 0; x < 16; ++x) a_kd[x] = B.kd[x][lane];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) gcv[t] = B.gc[4 * t + lg];
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8* sc = reinterpret_cast<bf16x8*>(w.sc + ci * kScBytes);
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) sc[(ctile[i] * 4 + s) * 64 + lane] = sb[i][s];
+    // U = Ut - W S   (consecutive MFMAs go to different accumulators)
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < NT; ++i) U[i][m] = mfma(a_wn[m * 4 + s], sb[i][s], U[i][m]);
+    bf16x8 ub[NT][2];
+    bf16x8* uc = reinterpret_cast<bf16x8*>(w.uc + ci * kUcBytes);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      ub[i][0] = pack_acc(U[i][0], U[i][1]);
+      ub[i][1] = pack_acc(U[i][2], U[i][3]);
+      uc[(ctile[i] * 2 + 0) * 64 + lane] = ub[i][0];
+      uc[(ctile[i] * 2 + 1) * 64 + lane] = ub[i][1];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) S[i][t] = S[i][t] * gcv[t];
+    }
+    // S' = Diag(Gam_C) S + Kd^T U
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int i = 0; i < NT; ++i) S[i][t] = mfma(a_kd[t * 2 + s2], ub[i][s2], S[i][t]);
+    lds_barrier();
+  };
+  for (int lc = 0; lc < nch; lc += 2) {
+    chunk_step(sl.buf[0], (size_t)(cbase + lc) * H + h);
+    if (lc + 1 < nch) chunk_step(sl.buf[1], (size_t)(cbase + lc + 1) * H + h);
+  }
+
+  if (slot_ok && (flags & KDA_WRITE_FINAL_STATE)) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) Sg[(size_t)(16 * t + 4 * lg + jj) * D + col[i]] = S[i][t][jj];
+  }
+}
+
+// Outputs of every (chunk, head) in parallel from the operands stored by the
+// prep (Q*Gam, A_qk) and by the state-only scan (S at the chunk start, U):
+// O = (Q*Gam) S + A_qk U, with the MFMA sequence of the single-pass scan.
+// Four waves, each owning two 16-column tiles; the bf16 outputs are staged in
+// LDS and stored as whole 16-byte row pieces of the valid rows.
+constexpr int kOutThreads = 256;
+__global__ __launch_bounds__(kOutThreads) void out_kernel(
+    int32_t N, int H, Workspace w, const int32_t* __restrict__ seq_start,
+    const int32_t* __restrict__ seq_end, const int32_t* __restrict__ chunk_off,
+    uint16_t* __restrict__ o) {
+  __shared__ uint16_t ob[C][D + 8];
+  const Header hd{seq_start, seq_end, chunk_off};
+  const int item = blockIdx.x;
+  if (item >= hd.chunk_off[N] * H) return;  // uniform
+  const ItemPos pos = locate(hd, N, H, item);
+  const size_t ci = (size_t)item;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+  constexpr int NT = 2;
+  const bf16x8* qg = reinterpret_cast<const bf16x8*>(w.qg + ci * kQgBytes);
+  const bf16x8* aq = reinterpret_cast<const bf16x8*>(w.aq + ci * kAqBytes);
+  const bf16x8* sc = reinterpret_cast<const bf16x8*>(w.sc + ci * kScBytes);
+  const bf16x8* uc = reinterpret_cast<const bf16x8*>(w.uc + ci * kUcBytes);
+  bf16x8 sb[NT][4], ub[NT][2], a_qg[16], a_aq[6];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int t = wave * NT + i;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) sb[i][s] = sc[(t * 4 + s) * 64 + lane];
+    ub[i][0] = uc[(t * 2 + 0) * 64 + lane];
+    ub[i][1] = uc[(t * 2 + 1) * 64 + lane];
+  }
+#pragma unroll
+  for (int x = 0; x < 16; ++x) a_qg[x] = qg[x * 64 + lane];
+#pragma unroll
+  for (int x = 0; x < 6; ++x) a_aq[x] = aq[(x < 2 ? 2 * x : x + 2) * 64 + lane];  // [0],[2],[4..7]
+  f32x4 O[NT][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int i = 0; i < NT; ++i) O[i][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < NT; ++i) O[i][m] = mfma(a_qg[m * 4 + s], sb[i][s], O[i][m]);
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    O[i][0] = mfma(a_aq[0], ub[i][0], O[i][0]);
+    O[i][1] = mfma(a_aq[1], ub[i][0], O[i][1]);
+    O[i][2] = mfma(a_aq[2], ub[i][0], O[i][2]);
+    O[i][3] = mfma(a_aq[4], ub[i][0], O[i][3]);
+  }
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    O[i][2] = mfma(a_aq[3], ub[i][1], O[i][2]);
+    O[i][3] = mfma(a_aq[5], ub[i][1], O[i][3]);
+  }
+#pragma unroll
+  for (int i = 0; i < NT; ++i)
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        ob[16 * m + 4 * lg + jj][16 * (wave * NT + i) + li] = f32_to_bf16(O[i][m][jj]);
+  lds_barrier();
+  // 64 rows x 16 pieces of 16 bytes
+#pragma unroll
+  for (int x = 0; x < C * (D / 8) / kOutThreads; ++x) {
+    const int u = tid + kOutThreads * x, r = u >> 4, pc = u & 15;
+    if (r < pos.c)
+      *reinterpret_cast<uint4*>(o + ((size_t)(pos.t0 + r) * H + pos.h) * D + 8 * pc) =
+          *reinterpret_cast<const uint4*>(&ob[r][8 * pc]);
+  }
+}
+
+template <int CW, int NT, int LW>
+kda_status_t launch_split(int32_t N, int H, const Workspace& w, float* states, int32_t num_slots,
+                          const int32_t* slots, uint32_t flags, void* o, size_t items,
+                          hipStream_t stream) {
+  constexpr int kGroups = D / (16 * CW * NT);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(scan_state_kernel<CW, NT, LW>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)sizeof(StateLds<CW, NT>));
+    if (e != hipSuccess) return hip_status(e, "hipFuncSetAttribute(scan)");
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((scan_state_kernel<CW, NT, LW>), dim3((unsigned)(N * H * kGroups)),
+                     dim3(64 * (CW + LW)), sizeof(StateLds<CW, NT>), stream, N, H, w, states,
+                     num_slots, slots, flags);
+  kda_status_t st = check_launch("chunk_fwd scan");
+  if (st != KDA_OK) return st;
+  hipLaunchKernelGGL(out_kernel, dim3((unsigned)items), dim3(kOutThreads), 0, stream, N, H, w,
+                     w.seq_start, w.seq_end, w.chunk_off, static_cast<uint16_t*>(o));
+  return check_launch("chunk_fwd out");
+}
+
 template <int CW, int NT, int LW>
 kda_status_t launch_scan_ws(int32_t N, int H, const Workspace& w, float* states, int32_t num_slots,
                             const int32_t* slots, uint32_t flags, void* o, hipStream_t stream) {
@@ -1118,7 +1400,8 @@ size_t chunk_mfma_workspace_bytes(int H, int32_t T, int32_t N) {
   const size_t ci = nchunks_max(T, N) * (size_t)H;
   return header_bytes(N) + align256(ci * kWnBytes) + align256(ci * kQgBytes) +
          align256(ci * kKdBytes) + align256(ci * kAqBytes) + align256(ci * kUtBytes) +
-         align256(ci * kGcBytes) + 256;
+         align256(ci * kGcBytes) + 256 +
+         (split_outputs(N, H) ? align256(ci * kScBytes) + align256(ci * kUcBytes) : 0);
 }
 
 kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, const int32_t* cu,
@@ -1158,6 +1441,8 @@ kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, cons
   // workgroups to shorten every step of the chains.  Many chains: one
   // workgroup of 4 waves x 32 columns per head, which fetches each chunk's
   // shared operands once.
+  if (split_outputs(N, H))
+    return launch_split<2, 1, 6>(N, H, w, states, num_slots, slots, flags, o, items, stream);
   if ((size_t)N * H * 4 <= (size_t)ncu)
     return launch_scan_ws<2, 1, 6>(N, H, w, states, num_slots, slots, flags, o, stream);
   return launch_scan<4, 2>(N, H, w, states, num_slots, slots, flags, o, stream);
