@@ -213,7 +213,7 @@ def main(argv=None):
                        "state": "fp32", "parallelism": "single-gpu"},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                         "traffic": tr, "kernel": "kda_chunk_fwd (index + prep + scan launches)",
+                         "traffic": tr, "kernel": "kda_chunk_fwd (index, prep, scan and output launches)",
                          "algorithmic_bytes": bytes_},
             "prefill_ms": {"mean": ms, "min": min(pr["ms"]), "max": max(pr["ms"]),
                            "warm_cache_mean": sum(pr["ms_warm"]) / len(pr["ms_warm"])},

@@ -1437,12 +1437,14 @@ kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, cons
                      w.chunk_off);
   st = check_launch("chunk_fwd prep");
   if (st != KDA_OK) return st;
-  // Up to one workgroup per CU: each head split over 4 warp-specialised
-  // workgroups to shorten every step of the chains.  Many chains: one
-  // workgroup of 4 waves x 32 columns per head, which fetches each chunk's
-  // shared operands once.
+  // Few chains: the serial chain of chunk steps is the critical path; each
+  // head's state is split over 8 warp-specialised workgroups of 16 columns that
+  // carry only the state, and the outputs are formed afterwards in parallel.
+  // Up to one workgroup per CU at 4 per head: the single-pass warp-specialised
+  // scan.  Many chains: one workgroup of 4 waves x 32 columns per head, which
+  // fetches each chunk's shared operands once.
   if (split_outputs(N, H))
-    return launch_split<2, 1, 6>(N, H, w, states, num_slots, slots, flags, o, items, stream);
+    return launch_split<1, 1, 7>(N, H, w, states, num_slots, slots, flags, o, items, stream);
   if ((size_t)N * H * 4 <= (size_t)ncu)
     return launch_scan_ws<2, 1, 6>(N, H, w, states, num_slots, slots, flags, o, stream);
   return launch_scan<4, 2>(N, H, w, states, num_slots, slots, flags, o, stream);

@@ -8,7 +8,7 @@
 averages FETCH_SIZE and WRITE_SIZE (KiB per dispatch) per kernel, scales both
 by the factor that makes a plain device copy of a known size (an elementwise
 multiply by 1 of a 256 MiB tensor) read and write exactly that size, and writes the HBM bytes per launch of the prefill path
-(index + prep + scan kernels) and of the decode kernel, tagged with a digest
+(index, prep, scan and output kernels) and of the decode kernel, tagged with a digest
 of the kernel sources (bench.py reports the figures only while the sources are
 unchanged).
 """
@@ -25,12 +25,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _short(name: str) -> str:
-    for key in ("prep_kernel", "index_kernel", "decode_kernel", "chunk_small_kernel",
+    for key in ("prep_kernel", "index_kernel", "out_kernel", "decode_kernel", "chunk_small_kernel",
                 "zero_kernel", "gather_scatter_kernel"):
         if key in name:
             return key
-    if "scan_kernel" in name:
-        return "scan_kernel" + (name[name.index("<"):name.index(">") + 1] if "<" in name else "")
+    for key in ("scan_state_kernel", "scan_ws_kernel", "scan_kernel"):
+        if key in name:
+            return key + (name[name.index("<"):name.index(">") + 1] if "<" in name else "")
     if "MulFunctor" in name or "mul_kernel" in name:
         return "torch:mul"
     if "FillFunctor" in name:
@@ -84,7 +85,7 @@ def traffic(fetch_csv: str, write_csv: str, copy_mib: float, out: str) -> dict:
         wk = write.get(k, (0.0, 0))[0] * w_scale * 1024
         per[k] = {"fetch_bytes": fk, "write_bytes": wk}
     prefill = sum(per[k]["fetch_bytes"] + per[k]["write_bytes"] for k in per
-                  if k in ("index_kernel", "prep_kernel") or k.startswith("scan_kernel"))
+                  if k in ("index_kernel", "prep_kernel", "out_kernel") or k.startswith("scan_"))
     decode = sum(per[k]["fetch_bytes"] + per[k]["write_bytes"] for k in per if k == "decode_kernel")
     rec = {"source_digest": _source_digest(), "prefill_bytes": prefill or None,
            "decode_bytes": decode or None, "copy_calibration": {
