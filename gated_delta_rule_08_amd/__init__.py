@@ -28,6 +28,9 @@ KDA_OK = 0
 KDA_FP32, KDA_BF16 = 0, 1
 KDA_READ_INITIAL_STATE = 1
 KDA_WRITE_FINAL_STATE = 2
+KDA_GATE_SCALAR = 4
+KDA_GATE_NONE = 8
+KDA_ADDITIVE = 16
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
            3: "KDA_ERR_WORKSPACE_TOO_SMALL", 4: "KDA_ERR_HIP"}
 
@@ -69,6 +72,8 @@ def load_library(path: str | None = None):
     lib.kda_chunk_fwd.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [SH, I32, P, P, P, P, P, P, I32, P, P, P]
     lib.kda_decode_step.restype = ctypes.c_int
+    lib.kda_decode_step_ex.argtypes = [SH, I32, P, P, P, P, P, P, I32, P, U32, P, P]
+    lib.kda_decode_step_ex.restype = ctypes.c_int
     lib.kda_state_init.argtypes = [SH, P, I32, P]
     lib.kda_state_init.restype = ctypes.c_int
     lib.kda_state_load.argtypes = [SH, P, I32, P, I32, P, P]
@@ -116,6 +121,30 @@ def _need(t: torch.Tensor, name: str, shape, dtype) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+GATES = ("channel", "scalar", "none")
+
+
+def _variant_flags(gate: str, additive: bool) -> int:
+    if gate not in GATES:
+        raise ValueError(f"gate must be one of {GATES}, got {gate!r}")
+    return ({"channel": 0, "scalar": KDA_GATE_SCALAR, "none": KDA_GATE_NONE}[gate]
+            | (KDA_ADDITIVE if additive else 0))
+
+
+def _need_gate_beta(g, beta, lead, dk, gate, additive):
+    """g and beta as the variant reads them (see the flags in include/kda.h)."""
+    if gate == "channel":
+        _need(g, "g", lead + (dk,), torch.float32)
+    elif gate == "scalar":
+        _need(g, "g", lead, torch.float32)
+    elif g is not None:
+        raise ValueError("gate='none' reads no g: pass g=None")
+    if not additive:
+        _need(beta, "beta", lead, torch.float32)
+    elif beta is not None:
+        raise ValueError("additive=True reads no beta: pass beta=None")
+
+
 def kda_abi_version() -> int:
     return int(load_library().kda_abi_version())
 
@@ -134,11 +163,13 @@ def kda_chunk_fwd_workspace_bytes(num_heads: int, dk: int, dv: int, io_dtype: to
 
 def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens, chunk: int = 64, states=None, state_slots=None,
                   read_initial: bool = False, write_final: bool = False, o=None, workspace=None,
-                  stream=None):
+                  stream=None, gate: str = "channel", additive: bool = False):
     """Chunked prefill over packed sequences (see kda_chunk_fwd in include/kda.h).
 
-    q, k, g: [T, H, dk]; v: [T, H, dv]; beta: [T, H]; cu_seqlens: int32 [N+1] on
+    q, k: [T, H, dk]; v: [T, H, dv]; beta: [T, H]; cu_seqlens: int32 [N+1] on
     the device; states: fp32 pool [S, H, dk, dv]; state_slots: int32 [N] or None.
+    g: [T, H, dk] (gate="channel"), [T, H] (gate="scalar") or None (gate="none").
+    additive=True drops the delta correction (u = v) and takes beta=None.
     Returns o [T, H, dv] in the dtype of q.  ``workspace`` (uint8, device) is
     allocated here when not given.
     """
@@ -149,11 +180,11 @@ def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens, chunk: int = 64, states=None, st
     _need(q, "q", (T, H, dk), q.dtype)
     _need(k, "k", (T, H, dk), q.dtype)
     _need(v, "v", (T, H, dv), q.dtype)
-    _need(g, "g", (T, H, dk), torch.float32)
-    _need(beta, "beta", (T, H), torch.float32)
+    _need_gate_beta(g, beta, (T, H), dk, gate, additive)
     N = cu_seqlens.numel() - 1
     _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32)
-    flags = (KDA_READ_INITIAL_STATE if read_initial else 0) | (KDA_WRITE_FINAL_STATE if write_final else 0)
+    flags = ((KDA_READ_INITIAL_STATE if read_initial else 0)
+             | (KDA_WRITE_FINAL_STATE if write_final else 0) | _variant_flags(gate, additive))
     num_slots = 0
     if states is not None:
         _need(states, "states", (states.shape[0], H, dk, dv), torch.float32)
@@ -176,11 +207,15 @@ def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens, chunk: int = 64, states=None, st
     return o
 
 
-def kda_decode_step(q, k, v, g, beta, states, state_slots=None, o=None, stream=None):
+def kda_decode_step(q, k, v, g, beta, states, state_slots=None, o=None, stream=None,
+                    gate: str = "channel", additive: bool = False):
     """One token per sequence against resident states, updated in place.
 
-    q, k, g: [B, H, dk]; v: [B, H, dv]; beta: [B, H]; states: fp32 pool
-    [S, H, dk, dv]; state_slots: int32 [B] or None.  Returns o [B, H, dv].
+    q, k: [B, H, dk]; v: [B, H, dv]; beta: [B, H]; states: fp32 pool
+    [S, H, dk, dv]; state_slots: int32 [B] or None.  g: [B, H, dk]
+    (gate="channel"), [B, H] (gate="scalar") or None (gate="none");
+    additive=True drops the delta correction and takes beta=None.
+    Returns o [B, H, dv].
     """
     lib = load_library()
     B, H, dk = q.shape
@@ -189,8 +224,7 @@ def kda_decode_step(q, k, v, g, beta, states, state_slots=None, o=None, stream=N
     _need(q, "q", (B, H, dk), q.dtype)
     _need(k, "k", (B, H, dk), q.dtype)
     _need(v, "v", (B, H, dv), q.dtype)
-    _need(g, "g", (B, H, dk), torch.float32)
-    _need(beta, "beta", (B, H), torch.float32)
+    _need_gate_beta(g, beta, (B, H), dk, gate, additive)
     _need(states, "states", (states.shape[0], H, dk, dv), torch.float32)
     if state_slots is not None:
         _need(state_slots, "state_slots", (B,), torch.int32)
@@ -199,9 +233,9 @@ def kda_decode_step(q, k, v, g, beta, states, state_slots=None, o=None, stream=N
     else:
         _need(o, "o", (B, H, dv), q.dtype)
     sh = _Shape(H, dk, dv, io)
-    _check(lib.kda_decode_step(ctypes.byref(sh), B, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                               _ptr(beta), _ptr(states), states.shape[0], _ptr(state_slots),
-                               _ptr(o), _stream(stream)))
+    _check(lib.kda_decode_step_ex(ctypes.byref(sh), B, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                  _ptr(beta), _ptr(states), states.shape[0], _ptr(state_slots),
+                                  _variant_flags(gate, additive), _ptr(o), _stream(stream)))
     return o
 
 

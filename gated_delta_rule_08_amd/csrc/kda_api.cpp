@@ -19,7 +19,8 @@ kda_status_t launch_state_copy(bool to_pool, float* states, int32_t num_slots,
 bool decode_supported(int dk, int dv);
 kda_status_t launch_decode(const kda_shape_t* sh, int32_t batch, const void* q, const void* k,
                            const void* v, const float* g, const float* beta, float* states,
-                           int32_t num_slots, const int32_t* slots, void* o, hipStream_t stream);
+                           int32_t num_slots, const int32_t* slots, uint32_t flags, void* o,
+                           hipStream_t stream);
 bool chunk_small_supported(int dk, int dv, int chunk);
 kda_status_t launch_chunk_small(const kda_shape_t* sh, int32_t chunk, int32_t T, int32_t N,
                                 const int32_t* cu, const void* q, const void* k, const void* v,
@@ -80,6 +81,31 @@ kda_status_t check_shape(const kda_shape_t* sh, const char* what) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+constexpr uint32_t kStateFlags = KDA_READ_INITIAL_STATE | KDA_WRITE_FINAL_STATE;
+constexpr uint32_t kVariantFlags = KDA_GATE_SCALAR | KDA_GATE_NONE | KDA_ADDITIVE;
+
+// The variant bits: at most one gate bit.
+kda_status_t check_variant(uint32_t flags, const char* what) {
+  if ((flags & KDA_GATE_SCALAR) && (flags & KDA_GATE_NONE))
+    return invalid("%s: KDA_GATE_SCALAR and KDA_GATE_NONE are exclusive", what);
+  return KDA_OK;
+}
+
+// g and beta as the variant reads them: g not read with KDA_GATE_NONE, beta not
+// read with KDA_ADDITIVE; a per-channel g is read as 16-byte vectors.
+kda_status_t check_gate_beta(uint32_t flags, const float* g, const float* beta, const char* what) {
+  if (!(flags & KDA_GATE_NONE)) {
+    if (!g) return invalid("%s: g is NULL", what);
+    if (!aligned(g, (flags & KDA_GATE_SCALAR) ? 4 : 16))
+      return invalid("%s: g must be %d-byte aligned", what, (flags & KDA_GATE_SCALAR) ? 4 : 16);
+  }
+  if (!(flags & KDA_ADDITIVE)) {
+    if (!beta) return invalid("%s: beta is NULL", what);
+    if (!aligned(beta, 4)) return invalid("%s: beta must be 4-byte aligned", what);
+  }
+  return KDA_OK;
+}
+
 bool chunk_supported(const kda_shape_t* sh, int chunk) {
   return chunk_mfma_supported(sh->dk, sh->dv, chunk, sh->io_dtype) ||
          chunk_small_supported(sh->dk, sh->dv, chunk);
@@ -132,14 +158,18 @@ kda_status_t kda_chunk_fwd(const kda_shape_t* sh, int32_t chunk, int32_t total_t
   if (st != KDA_OK) return st;
   if (total_tokens < 0 || num_seqs < 0)
     return invalid("%s: total_tokens and num_seqs must be >= 0", W);
-  if (flags & ~(uint32_t)(KDA_READ_INITIAL_STATE | KDA_WRITE_FINAL_STATE))
-    return invalid("%s: unknown flag bits 0x%x", W, flags);
+  if (flags & ~(kStateFlags | kVariantFlags))
+    return invalid("%s: unknown flag bits 0x%x", W, flags & ~(kStateFlags | kVariantFlags));
+  st = check_variant(flags, W);
+  if (st != KDA_OK) return st;
   if (chunk <= 0) return invalid("%s: chunk must be >= 1 (got %d)", W, chunk);
   if (!chunk_supported(sh, chunk)) return unsupported(W, sh, chunk);
   if (total_tokens == 0 || num_seqs == 0) return KDA_OK;
   if (!cu_seqlens) return invalid("%s: cu_seqlens is NULL", W);
-  if (!q || !k || !v || !g || !beta || !o) return invalid("%s: a tensor pointer is NULL", W);
-  if (flags != 0) {
+  if (!q || !k || !v || !o) return invalid("%s: a tensor pointer is NULL", W);
+  st = check_gate_beta(flags, g, beta, W);
+  if (st != KDA_OK) return st;
+  if (flags & kStateFlags) {
     if (!states) return invalid("%s: states is NULL but flags request state I/O", W);
     if (num_slots <= 0) return invalid("%s: num_slots must be >= 1 with state I/O", W);
     if (!state_slots && num_slots < num_seqs)
@@ -148,8 +178,8 @@ kda_status_t kda_chunk_fwd(const kda_shape_t* sh, int32_t chunk, int32_t total_t
   }
   const size_t esz = sh->io_dtype == KDA_BF16 ? 2 : 4;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, esz) ||
-      !aligned(g, 16) || !aligned(beta, 4) || (states && !aligned(states, 16)))
-    return invalid("%s: q, k, v, g, states must be 16-byte aligned", W);
+      (states && !aligned(states, 16)))
+    return invalid("%s: q, k, v, states must be 16-byte aligned", W);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (chunk_mfma_supported(sh->dk, sh->dv, chunk, sh->io_dtype)) {
     const size_t need = chunk_mfma_workspace_bytes(sh->num_heads, total_tokens, num_seqs);
@@ -162,26 +192,40 @@ kda_status_t kda_chunk_fwd(const kda_shape_t* sh, int32_t chunk, int32_t total_t
                              num_slots, state_slots, flags, o, workspace, s);
   }
   return launch_chunk_small(sh, chunk, total_tokens, num_seqs, cu_seqlens, q, k, v, g, beta,
-                            flags ? states : nullptr, num_slots, state_slots, flags, o, s);
+                            (flags & kStateFlags) ? states : nullptr, num_slots, state_slots,
+                            flags, o, s);
 }
 
 kda_status_t kda_decode_step(const kda_shape_t* sh, int32_t batch, const void* q, const void* k,
                              const void* v, const float* g, const float* beta, float* states,
                              int32_t num_slots, const int32_t* state_slots, void* o,
                              void* stream) {
+  return kda_decode_step_ex(sh, batch, q, k, v, g, beta, states, num_slots, state_slots, 0u, o,
+                            stream);
+}
+
+kda_status_t kda_decode_step_ex(const kda_shape_t* sh, int32_t batch, const void* q,
+                                const void* k, const void* v, const float* g, const float* beta,
+                                float* states, int32_t num_slots, const int32_t* state_slots,
+                                uint32_t flags, void* o, void* stream) {
   const char* W = "kda_decode_step";
   kda_status_t st = check_shape(sh, W);
   if (st != KDA_OK) return st;
   if (batch < 0) return invalid("%s: batch must be >= 0", W);
+  if (flags & ~kVariantFlags)
+    return invalid("%s: unknown flag bits 0x%x", W, flags & ~kVariantFlags);
+  st = check_variant(flags, W);
+  if (st != KDA_OK) return st;
   if (!decode_supported(sh->dk, sh->dv)) return unsupported(W, sh, 0);
   if (batch == 0) return KDA_OK;
-  if (!q || !k || !v || !g || !beta || !o || !states)
-    return invalid("%s: a tensor pointer is NULL", W);
+  if (!q || !k || !v || !o || !states) return invalid("%s: a tensor pointer is NULL", W);
+  st = check_gate_beta(flags, g, beta, W);
+  if (st != KDA_OK) return st;
   if (num_slots <= 0) return invalid("%s: num_slots must be >= 1", W);
   if (!state_slots && num_slots < batch)
     return invalid("%s: num_slots (%d) < batch (%d) with implicit slots", W, num_slots, batch);
   if (!aligned(states, 16)) return invalid("%s: states must be 16-byte aligned", W);
-  return launch_decode(sh, batch, q, k, v, g, beta, states, num_slots, state_slots, o,
+  return launch_decode(sh, batch, q, k, v, g, beta, states, num_slots, state_slots, flags, o,
                        static_cast<hipStream_t>(stream));
 }
 

@@ -228,9 +228,13 @@ struct PrepSmem {
 // One item's inputs between the global loads and the LDS staging.
 struct PrepIn {
   uint4 k[2], q[2], v[2];
-  float4 g[4];
+  float4 g[4];   // per-channel gate; a scalar gate is read into .x and broadcast at staging
   float beta;
 };
+
+// Gate variants of the prep, fixed at compile time so that the prefetch of the
+// next item has no data-dependent register moves (which would wait for it).
+constexpr int kGateChannel = 0, kGateScalar = 1, kGateNone = 2;
 
 struct ItemPos {
   int gc, h, t0, c;  // chunk, head, first token, valid rows (>= 1)
@@ -260,6 +264,10 @@ __device__ __forceinline__ ItemPos locate(const Header& hd, int N, int H, int it
 }
 
 // Rows past the end of the sequence read the last valid row (zeroed at staging).
+// Variants: a scalar gate is read once per row and staged on every channel; no
+// gate reads nothing (G = 0); the additive write reads no beta (beta = 1, and
+// the correction is dropped later).
+template <int kGate, bool kAdd>
 __device__ __forceinline__ void prep_load(PrepIn& in, const ItemPos& p, const uint16_t* q,
                                           const uint16_t* k, const uint16_t* v, const float* g,
                                           const float* beta, int H, int tid) {
@@ -276,11 +284,15 @@ __device__ __forceinline__ void prep_load(PrepIn& in, const ItemPos& p, const ui
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int u = tid + kPrepThreads * i, r = u >> 5, cc = (u & 31) * 4;
-    in.g[i] = *reinterpret_cast<const float4*>(g + base + (size_t)min(r, p.c - 1) * rowstride + cc);
+    if (kGate == kGateScalar)
+      in.g[i].x = g[(size_t)(p.t0 + min(r, p.c - 1)) * H + p.h];
+    else if (kGate == kGateChannel)
+      in.g[i] = *reinterpret_cast<const float4*>(g + base + (size_t)min(r, p.c - 1) * rowstride + cc);
   }
-  in.beta = beta[(size_t)(p.t0 + min(tid & 63, p.c - 1)) * H + p.h];
+  if (!kAdd) in.beta = beta[(size_t)(p.t0 + min(tid & 63, p.c - 1)) * H + p.h];
 }
 
+template <int kGate, bool kAdd>
 __device__ __forceinline__ void prep_stage(PrepSmem& sm, const PrepIn& in, int c, int tid) {
   const uint4 z4 = make_uint4(0, 0, 0, 0);
 #pragma unroll
@@ -298,9 +310,12 @@ __device__ __forceinline__ void prep_stage(PrepSmem& sm, const PrepIn& in, int c
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int u = tid + kPrepThreads * i, r = u >> 5, cc = (u & 31) * 4;
-    *reinterpret_cast<float4*>(&sm.G[r][cc]) = r < c ? in.g[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 gv = kGate == kGateNone     ? make_float4(0.f, 0.f, 0.f, 0.f)
+                      : kGate == kGateScalar ? make_float4(in.g[i].x, in.g[i].x, in.g[i].x, in.g[i].x)
+                                             : in.g[i];
+    *reinterpret_cast<float4*>(&sm.G[r][cc]) = r < c ? gv : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  if (tid < C) sm.bs[tid] = tid < c ? in.beta : 0.f;
+  if (tid < C) sm.bs[tid] = tid < c ? (kAdd ? 1.f : in.beta) : 0.f;
   for (int u = tid; u < C * AP; u += kPrepThreads) (&sm.Tm[0][0])[u] = 0.f;
 }
 
@@ -349,10 +364,13 @@ __device__ __forceinline__ void gram_pair(const PrepSmem& sm, int R, int J, bool
 }
 
 // One workgroup of the prep: items wg, wg + nwg, ... in chunk-major order.
+template <int kGate, bool kAdd>
 __device__ __forceinline__ void prep_role(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, int32_t N, int H,
     const Workspace& w, const Header& hd, uint8_t* smem_raw, int wg, int nwg) {
+  // the additive write (u = v) has no correction: A_kk = 0, so T = I, W = 0, Ut = V
+  constexpr bool additive = kAdd;
   PrepSmem& sm = *reinterpret_cast<PrepSmem*>(smem_raw);
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
@@ -362,7 +380,7 @@ __device__ __forceinline__ void prep_role(
 
   PrepIn in;
   ItemPos pos = locate(hd, N, H, item);
-  prep_load(in, pos, q, k, v, g, beta, H, tid);
+  prep_load<kGate, kAdd>(in, pos, q, k, v, g, beta, H, tid);
   // Wait for the first item here, so that inside the loop the wait for the
   // prefetched registers only has to cover the loads, not the stores issued
   // after them.
@@ -372,7 +390,7 @@ __device__ __forceinline__ void prep_role(
     const size_t ci = (size_t)item;  // items are numbered chunk-major: ci = gc * H + h
     const int c = pos.c;
     lds_barrier();  // the previous item is done with LDS
-    prep_stage(sm, in, c, tid);
+    prep_stage<kGate, kAdd>(sm, in, c, tid);
     lds_barrier();
 
     // ---- running sum of the log-gates down each channel (four quarters of 16 rows)
@@ -401,7 +419,7 @@ __device__ __forceinline__ void prep_role(
     const int next = item + nwg;
     if (next < total) {
       pos = locate(hd, N, H, next);
-      prep_load(in, pos, q, k, v, g, beta, H, tid);
+      prep_load<kGate, kAdd>(in, pos, q, k, v, g, beta, H, tid);
     }
     lds_barrier();
 
@@ -450,7 +468,7 @@ __device__ __forceinline__ void prep_role(
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int j = 16 * J + 4 * lg + jj;
-          (&arow.x)[jj] = j < r ? br * acck[jj] : 0.f;
+          (&arow.x)[jj] = j < r && !additive ? br * acck[jj] : 0.f;
           qv[jj] = j <= r ? accq[jj] : 0.f;
         }
         *reinterpret_cast<float4*>(&sm.A[r][16 * J + 4 * lg]) = arow;
@@ -552,6 +570,7 @@ __device__ __forceinline__ void prep_role(
         acc = mfma(abkg[0], tt[nt][0], acc);
         if (nt >= 2) acc = mfma(abkg[1], tt[nt][1], acc);
         uint16_t* dst = wn_out + ((size_t)(nt * 4 + (tile >> 1)) * 64 + lane) * 8 + (tile & 1) * 4;
+        if (additive) acc = f32x4{0.f, 0.f, 0.f, 0.f};
         *reinterpret_cast<uint2*>(dst) =
             make_uint2((uint32_t)f32_to_bf16(-acc[0]) | ((uint32_t)f32_to_bf16(-acc[1]) << 16),
                        (uint32_t)f32_to_bf16(-acc[2]) | ((uint32_t)f32_to_bf16(-acc[3]) << 16));
@@ -567,6 +586,7 @@ __device__ __forceinline__ void prep_role(
 }
 
 // LDS use (~153 KiB) allows one workgroup (two waves per SIMD) per CU.
+template <int kGate, bool kAdd>
 __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, int32_t N, int H, Workspace w,
@@ -574,7 +594,26 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2,
     const int32_t* __restrict__ chunk_off) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   const Header hd{seq_start, seq_end, chunk_off};
-  prep_role(q, k, v, g, beta, N, H, w, hd, smem_raw, blockIdx.x, gridDim.x);
+  prep_role<kGate, kAdd>(q, k, v, g, beta, N, H, w, hd, smem_raw, blockIdx.x, gridDim.x);
+}
+
+template <int kGate, bool kAdd>
+kda_status_t launch_prep(unsigned grid, const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, int32_t N, int H, const Workspace& w,
+                         hipStream_t stream) {
+  static bool attr_set = false;  // idempotent; set before the first launch
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep_kernel<kGate, kAdd>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)sizeof(PrepSmem));
+    if (e != hipSuccess) return hip_status(e, "hipFuncSetAttribute(prep)");
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((prep_kernel<kGate, kAdd>), dim3(grid), dim3(kPrepThreads), sizeof(PrepSmem),
+                     stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), g, beta, N, H, w, w.seq_start, w.seq_end,
+                     w.chunk_off);
+  return check_launch("chunk_fwd prep");
 }
 
 // ------------------------------------------------------------------ 3. scan
@@ -1421,21 +1460,18 @@ kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, cons
   hipLaunchKernelGGL(index_kernel, dim3(1), dim3(64), 0, stream, cu, N, T, (int32_t)cap, w);
   kda_status_t st = check_launch("chunk_fwd index");
   if (st != KDA_OK) return st;
-  static bool attr_set = false;  // idempotent; set before first launch
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)sizeof(PrepSmem));
-    if (e != hipSuccess) return hip_status(e, "hipFuncSetAttribute(prep)");
-    attr_set = true;
-  }
   // persistent prep: one workgroup per CU, each walks items with a grid stride
-  const unsigned prep_grid = (unsigned)(items < (size_t)ncu ? items : (size_t)ncu);
-  hipLaunchKernelGGL(prep_kernel, dim3(prep_grid), dim3(kPrepThreads), sizeof(PrepSmem), stream,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), g, beta, N, H, w, w.seq_start, w.seq_end,
-                     w.chunk_off);
-  st = check_launch("chunk_fwd prep");
+  const unsigned grid = (unsigned)(items < (size_t)ncu ? items : (size_t)ncu);
+  const bool add = flags & KDA_ADDITIVE;
+  if (flags & KDA_GATE_SCALAR)
+    st = add ? launch_prep<kGateScalar, true>(grid, q, k, v, g, beta, N, H, w, stream)
+             : launch_prep<kGateScalar, false>(grid, q, k, v, g, beta, N, H, w, stream);
+  else if (flags & KDA_GATE_NONE)
+    st = add ? launch_prep<kGateNone, true>(grid, q, k, v, g, beta, N, H, w, stream)
+             : launch_prep<kGateNone, false>(grid, q, k, v, g, beta, N, H, w, stream);
+  else
+    st = add ? launch_prep<kGateChannel, true>(grid, q, k, v, g, beta, N, H, w, stream)
+             : launch_prep<kGateChannel, false>(grid, q, k, v, g, beta, N, H, w, stream);
   if (st != KDA_OK) return st;
   // Few chains: the serial chain of chunk steps is the critical path; each
   // head's state is split over 8 warp-specialised workgroups of 16 columns that

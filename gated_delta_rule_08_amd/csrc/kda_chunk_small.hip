@@ -20,6 +20,10 @@
 // serves the fp32 contract (1e-4 relative) and small heads, where launch
 // latency dominates.  A partial last chunk is padded with neutral tokens
 // (q = k = v = 0, beta = 0, g = 0), which leave state and outputs unchanged.
+//
+// Variants (flags): a scalar gate per (token, head) is staged as the same
+// value on every channel; without a gate G = 0; the additive write (u = v)
+// drops the correction, so A_kk = 0 (T = I) and the right-hand side is V.
 #include "kda_common.h"
 
 namespace kda {
@@ -55,6 +59,8 @@ __global__ __launch_bounds__(kSmallThreads) void chunk_small_kernel(
   for (int e = tid; e < D * D; e += kSmallThreads)
     Ss[e / D][e % D] = (slot_ok && (flags & KDA_READ_INITIAL_STATE)) ? Sg[e] : 0.f;
 
+  const bool gate_none = flags & KDA_GATE_NONE, gate_scalar = flags & KDA_GATE_SCALAR;
+  const bool additive = flags & KDA_ADDITIVE;
   for (int t0 = start; t0 < end; t0 += C) {
     const int c = min(C, end - t0);
     __syncthreads();
@@ -65,10 +71,10 @@ __global__ __launch_bounds__(kSmallThreads) void chunk_small_kernel(
       Qs[r][d] = ok ? io_traits<IO>::load(q, gi) : 0.f;
       Ks[r][d] = ok ? io_traits<IO>::load(k, gi) : 0.f;
       Vs[r][d] = ok ? io_traits<IO>::load(v, gi) : 0.f;
-      Gs[r][d] = ok ? g[gi] : 0.f;
+      Gs[r][d] = ok && !gate_none ? (gate_scalar ? g[(size_t)(t0 + r) * H + h] : g[gi]) : 0.f;
     }
     for (int r = tid; r < C; r += kSmallThreads)
-      bs[r] = r < c ? beta[(size_t)(t0 + r) * H + h] : 0.f;
+      bs[r] = r < c ? (additive ? 1.f : beta[(size_t)(t0 + r) * H + h]) : 0.f;
     __syncthreads();
 
     // running sum of the log-gates along the chunk, per key channel
@@ -91,7 +97,7 @@ __global__ __launch_bounds__(kSmallThreads) void chunk_small_kernel(
           qk += Qs[r][d] * kj;
         }
       }
-      Akk[r][j] = j < r ? bs[r] * kk : 0.f;
+      Akk[r][j] = j < r && !additive ? bs[r] * kk : 0.f;
       Aqk[r][j] = qk;
     }
     __syncthreads();
@@ -125,8 +131,10 @@ __global__ __launch_bounds__(kSmallThreads) void chunk_small_kernel(
     for (int e = tid; e < C * D; e += kSmallThreads) {
       const int r = e / D, col = e % D;
       float acc = 0.f;
-      for (int d = 0; d < D; ++d) acc += Gs[r][d] * Ss[d][col];
-      Vs[r][col] = bs[r] * (Vs[r][col] - acc);
+      if (!additive) {
+        for (int d = 0; d < D; ++d) acc += Gs[r][d] * Ss[d][col];
+        Vs[r][col] = bs[r] * (Vs[r][col] - acc);
+      }
     }
     __syncthreads();
 

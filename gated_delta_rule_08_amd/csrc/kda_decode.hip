@@ -10,6 +10,10 @@
 // faded state, one retention factor per key channel; heqinghuang "From GPT2 to
 // Kimi3, Explained", section 09: output read after the write.)
 //
+// Variants (flags, uniform per launch): a scalar gate per (sequence, head)
+// (Gated DeltaNet), no gate (DeltaNet), and the additive write u = v without
+// the correction (gated linear attention): engineermaxxing ch. 05c and 02g.
+//
 // The step is a streaming read-modify-write of the state: each state is read
 // from HBM once and written once, and the token vectors are tiny, so the kernel
 // is bound by HBM bandwidth (engineermaxxing ch. 02b: a decode step reads the
@@ -28,7 +32,8 @@ template <int DK, int DV, int BLOCK, typename IO>
 __global__ __launch_bounds__(BLOCK) void decode_kernel(
     const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ states,
-    int32_t num_slots, const int32_t* __restrict__ slots, IO* __restrict__ o, int H) {
+    int32_t num_slots, const int32_t* __restrict__ slots, uint32_t flags, IO* __restrict__ o,
+    int H) {
   constexpr int NCQ = DV / 4;      // column quads
   constexpr int RG = BLOCK / NCQ;  // row groups
   constexpr int RPT = DK / RG;     // rows per thread
@@ -59,10 +64,12 @@ __global__ __launch_bounds__(BLOCK) void decode_kernel(
 
   // 2. token vectors to LDS
   const size_t tk = (size_t)bh * DK, tv = (size_t)bh * DV;
+  const bool gate_none = flags & KDA_GATE_NONE, gate_scalar = flags & KDA_GATE_SCALAR;
+  const bool additive = flags & KDA_ADDITIVE;
   for (int i = tid; i < DK; i += BLOCK) {
     ks[i] = io_traits<IO>::load(k, tk + i);
     qs[i] = io_traits<IO>::load(q, tk + i);
-    as[i] = fast_exp(g[tk + i]);
+    as[i] = gate_none ? 1.f : fast_exp(gate_scalar ? g[bh] : g[tk + i]);
   }
   for (int i = tid; i < DV; i += BLOCK) vs[i] = io_traits<IO>::load(v, tv + i);
   __syncthreads();
@@ -99,10 +106,13 @@ __global__ __launch_bounds__(BLOCK) void decode_kernel(
       W.x += a.x; W.y += a.y; W.z += a.z; W.w += a.w;
       Y.x += c.x; Y.y += c.y; Y.z += c.z; Y.w += c.w;
     }
-    const float bt = beta[bh], kq = kq_sh;
+    const float kq = kq_sh;
     const int c0 = 4 * cq;
-    const float u0 = bt * (vs[c0 + 0] - W.x), u1 = bt * (vs[c0 + 1] - W.y);
-    const float u2 = bt * (vs[c0 + 2] - W.z), u3 = bt * (vs[c0 + 3] - W.w);
+    float u0 = vs[c0 + 0], u1 = vs[c0 + 1], u2 = vs[c0 + 2], u3 = vs[c0 + 3];
+    if (!additive) {  // the correction against the faded read
+      const float bt = beta[bh];
+      u0 = bt * (u0 - W.x); u1 = bt * (u1 - W.y); u2 = bt * (u2 - W.z); u3 = bt * (u3 - W.w);
+    }
     us[c0 + 0] = u0; us[c0 + 1] = u1; us[c0 + 2] = u2; us[c0 + 3] = u3;
     io_traits<IO>::store(o, tv + c0 + 0, Y.x + kq * u0);
     io_traits<IO>::store(o, tv + c0 + 1, Y.y + kq * u1);
@@ -126,10 +136,10 @@ __global__ __launch_bounds__(BLOCK) void decode_kernel(
 template <int D, int BLOCK, typename IO>
 kda_status_t launch_typed(int32_t batch, int H, const void* q, const void* k, const void* v,
                           const float* g, const float* beta, float* states, int32_t num_slots,
-                          const int32_t* slots, void* o, hipStream_t stream) {
+                          const int32_t* slots, uint32_t flags, void* o, hipStream_t stream) {
   hipLaunchKernelGGL((decode_kernel<D, D, BLOCK, IO>), dim3((unsigned)batch * H), dim3(BLOCK), 0,
                      stream, static_cast<const IO*>(q), static_cast<const IO*>(k),
-                     static_cast<const IO*>(v), g, beta, states, num_slots, slots,
+                     static_cast<const IO*>(v), g, beta, states, num_slots, slots, flags,
                      static_cast<IO*>(o), H);
   return check_launch("decode_step");
 }
@@ -137,12 +147,12 @@ kda_status_t launch_typed(int32_t batch, int H, const void* q, const void* k, co
 template <typename IO>
 kda_status_t launch_io(int d, int32_t batch, int H, const void* q, const void* k, const void* v,
                        const float* g, const float* beta, float* states, int32_t num_slots,
-                       const int32_t* slots, void* o, hipStream_t stream) {
+                       const int32_t* slots, uint32_t flags, void* o, hipStream_t stream) {
   switch (d) {
-    case 16: return launch_typed<16, 64, IO>(batch, H, q, k, v, g, beta, states, num_slots, slots, o, stream);
-    case 32: return launch_typed<32, 64, IO>(batch, H, q, k, v, g, beta, states, num_slots, slots, o, stream);
-    case 64: return launch_typed<64, 128, IO>(batch, H, q, k, v, g, beta, states, num_slots, slots, o, stream);
-    case 128: return launch_typed<128, 256, IO>(batch, H, q, k, v, g, beta, states, num_slots, slots, o, stream);
+    case 16: return launch_typed<16, 64, IO>(batch, H, q, k, v, g, beta, states, num_slots, slots, flags, o, stream);
+    case 32: return launch_typed<32, 64, IO>(batch, H, q, k, v, g, beta, states, num_slots, slots, flags, o, stream);
+    case 64: return launch_typed<64, 128, IO>(batch, H, q, k, v, g, beta, states, num_slots, slots, flags, o, stream);
+    case 128: return launch_typed<128, 256, IO>(batch, H, q, k, v, g, beta, states, num_slots, slots, flags, o, stream);
     default: return KDA_ERR_UNSUPPORTED;
   }
 }
@@ -155,12 +165,13 @@ bool decode_supported(int dk, int dv) {
 
 kda_status_t launch_decode(const kda_shape_t* sh, int32_t batch, const void* q, const void* k,
                            const void* v, const float* g, const float* beta, float* states,
-                           int32_t num_slots, const int32_t* slots, void* o, hipStream_t stream) {
+                           int32_t num_slots, const int32_t* slots, uint32_t flags, void* o,
+                           hipStream_t stream) {
   if (sh->io_dtype == KDA_BF16)
     return launch_io<uint16_t>(sh->dk, batch, sh->num_heads, q, k, v, g, beta, states, num_slots,
-                               slots, o, stream);
+                               slots, flags, o, stream);
   return launch_io<float>(sh->dk, batch, sh->num_heads, q, k, v, g, beta, states, num_slots,
-                          slots, o, stream);
+                          slots, flags, o, stream);
 }
 
 }  // namespace kda

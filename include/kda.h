@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum {
   KDA_OK = 0,
@@ -71,10 +71,21 @@ typedef struct {
   int32_t io_dtype;   /* kda_dtype_t                    */
 } kda_shape_t;
 
-/* flags of kda_chunk_fwd */
+/* flags of kda_chunk_fwd (bit-or); the last three also of kda_decode_step_ex.
+ *
+ * The variants are the special cases of the same recurrence that the pages
+ * name (engineermaxxing ch. 05c: a scalar gate is Gated DeltaNet, alpha = 1 is
+ * DeltaNet; heqinghuang section 07 and engineermaxxing ch. 02e-02g: without
+ * the delta correction the write is additive, u = v, which is (gated) linear
+ * attention).  They change what is read, not the layout of anything else. */
 enum {
   KDA_READ_INITIAL_STATE = 1u,  /* start each sequence from states[slot]; else from 0 */
-  KDA_WRITE_FINAL_STATE = 2u    /* store each sequence's final state to states[slot]  */
+  KDA_WRITE_FINAL_STATE = 2u,   /* store each sequence's final state to states[slot]  */
+  KDA_GATE_SCALAR = 4u,         /* g is [tokens, H]: one log-decay per token and head,
+                                   the same for every key channel                      */
+  KDA_GATE_NONE = 8u,           /* no decay (alpha = 1): g is not read and may be NULL  */
+  KDA_ADDITIVE = 16u            /* u = v (no delta correction): beta is not read and
+                                   may be NULL                                         */
 };
 
 /* Version of this interface (KDA_ABI_VERSION). */
@@ -114,10 +125,13 @@ size_t kda_chunk_fwd_workspace_bytes(const kda_shape_t* shape, int32_t chunk,
  *             be multiples of `chunk`; a zero-length sequence is allowed.
  * q, k        device [total_tokens, H, dk], io dtype.
  * v           device [total_tokens, H, dv], io dtype.
- * g           device fp32 [total_tokens, H, dk], log of the per-channel gate.
- * beta        device fp32 [total_tokens, H], write strengths.
+ * g           device fp32 [total_tokens, H, dk], log of the per-channel gate
+ *             (16-byte aligned); [total_tokens, H] with KDA_GATE_SCALAR;
+ *             unused (may be NULL) with KDA_GATE_NONE.
+ * beta        device fp32 [total_tokens, H], write strengths; unused (may be
+ *             NULL) with KDA_ADDITIVE.
  * states      device fp32 pool [num_slots, H, dk, dv] (may be NULL when
- *             flags == 0).  Read at the start of sequence n when
+ *             neither state flag is set).  Read at the start of sequence n when
  *             KDA_READ_INITIAL_STATE is set, overwritten with its final state
  *             when KDA_WRITE_FINAL_STATE is set.
  * state_slots device int32 [num_seqs] (slot of sequence n), or NULL for slot n
@@ -126,6 +140,9 @@ size_t kda_chunk_fwd_workspace_bytes(const kda_shape_t* shape, int32_t chunk,
  * o           device [total_tokens, H, dv], io dtype, fully overwritten.
  * workspace   device scratch of at least kda_chunk_fwd_workspace_bytes()
  *             bytes, 256-byte aligned; contents on entry are ignored.
+ * flags       KDA_READ_INITIAL_STATE | KDA_WRITE_FINAL_STATE | at most one of
+ *             KDA_GATE_SCALAR, KDA_GATE_NONE | KDA_ADDITIVE; other bits, or
+ *             both gate bits, are KDA_ERR_INVALID_ARGUMENT.
  * total_tokens == 0 or num_seqs == 0 is a no-op returning KDA_OK. */
 kda_status_t kda_chunk_fwd(const kda_shape_t* shape, int32_t chunk, int32_t total_tokens,
                            int32_t num_seqs, const int32_t* cu_seqlens, const void* q,
@@ -153,6 +170,17 @@ kda_status_t kda_decode_step(const kda_shape_t* shape, int32_t batch, const void
                              const void* k, const void* v, const float* g, const float* beta,
                              float* states, int32_t num_slots, const int32_t* state_slots,
                              void* o, void* stream);
+
+/* kda_decode_step for the variants: `flags` is a bit-or of at most one of
+ * KDA_GATE_SCALAR (g is [batch, H]) and KDA_GATE_NONE (g unused, may be NULL),
+ * and KDA_ADDITIVE (u = v; beta unused, may be NULL); flags == 0 is
+ * kda_decode_step.  Other bits, or both gate bits, are
+ * KDA_ERR_INVALID_ARGUMENT.  Same arguments, layouts and errors otherwise. */
+kda_status_t kda_decode_step_ex(const kda_shape_t* shape, int32_t batch, const void* q,
+                                const void* k, const void* v, const float* g,
+                                const float* beta, float* states, int32_t num_slots,
+                                const int32_t* state_slots, uint32_t flags, void* o,
+                                void* stream);
 
 /* Zero every state of a pool [num_slots, H, dk, dv] (fp32). */
 kda_status_t kda_state_init(const kda_shape_t* shape, float* states, int32_t num_slots,

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 1
+    assert lib.kda_abi_version() == 2
     assert lib.kda_status_string(0) == b"KDA_OK"
     assert lib.kda_status_string(3) == b"KDA_ERR_WORKSPACE_TOO_SMALL"
 
@@ -90,7 +90,16 @@ def test_validation_errors_before_any_launch(lib):
     assert call(_shape(0, 128, 128, 1), args()) == 1                 # H = 0
     assert call(_shape(16, 128, 128, 7), args()) == 1                # bad dtype
     assert call(sh, args(chunk=48)) == 2                             # unsupported chunk
-    assert call(sh, args(flags=8)) == 1                              # unknown flag
+    assert call(sh, args(flags=32)) == 1                             # unknown flag
+    assert call(sh, args(flags=4 | 8)) == 1                          # two gate variants
+    assert b"exclusive" in lib.kda_last_error()
+    assert call(sh, args(g=None)) == 1                               # per-channel gate needs g
+    assert call(sh, args(g=P(0x1004))) == 1                          # ... 16-byte aligned
+    assert call(sh, args(beta=None)) == 1                            # the delta rule needs beta
+    # variants that do not read g or beta pass validation (up to the missing workspace)
+    assert call(sh, args(flags=8, g=None)) == 3                      # KDA_GATE_NONE
+    assert call(sh, args(flags=4, g=P(0x1004))) == 3                 # scalar gate: 4-byte aligned
+    assert call(sh, args(flags=16, beta=None)) == 3                  # KDA_ADDITIVE
     assert call(sh, args(q=None)) == 1                               # NULL tensor
     assert call(sh, args(flags=1)) == 1                              # state I/O without states
     assert call(sh, args()) == 3                                     # workspace missing
@@ -104,6 +113,14 @@ def test_validation_errors_before_any_launch(lib):
                                fake, None) == 1                      # too few slots
     assert lib.kda_decode_step(ctypes.byref(sh), 0, None, None, None, None, None, None, 0, None,
                                None, None) == 0
+    dex = lambda flags, g, beta, ns: lib.kda_decode_step_ex(
+        ctypes.byref(sh), 4, fake, fake, fake, g, beta, fake, ns, None, flags, fake, None)
+    assert dex(1, fake, fake, 4) == 1                                # state flags are prefill-only
+    assert dex(4 | 8, fake, fake, 4) == 1                            # two gate variants
+    assert dex(0, None, fake, 4) == 1                                # g required
+    assert b"g is NULL" in lib.kda_last_error()
+    assert dex(8 | 16, None, None, 2) == 1                           # g, beta not read: next check
+    assert b"num_slots" in lib.kda_last_error()
     # state helpers
     assert lib.kda_state_init(ctypes.byref(sh), None, 3, None) == 1
     assert lib.kda_state_load(ctypes.byref(sh), fake, 2, None, 3, fake, None) == 1
