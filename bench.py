@@ -16,6 +16,9 @@ inputs come from HBM; the fill is outside the HIP events that time the step.
 decode steps/s is reported next to it with its own roofline.  The oracle
 (fp64, host threads) is timed on the same prefill input as a CPU baseline.
 
+The variant flags (scalar gate, no gate, additive write) are timed on the same
+prefill shape and reported under "variants", each with its own algorithmic bytes.
+
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -112,6 +115,61 @@ def bench_prefill(kda, torch, steps, warmup, flush):
     return dict(cfg=cfg, T=T, H=H, d=d, N=N, ms=ms, ms_warm=ms_warm, wall=wall, inputs=p)
 
 
+# Variants of the same path on the c1 shape: (flag arguments, bytes per token-head)
+VARIANTS = {
+    "gated_deltanet_scalar_gate": (dict(gate="scalar"), 3 * 2 * 128 + 4 + 4 + 2 * 128),
+    "deltanet_no_gate": (dict(gate="none"), 3 * 2 * 128 + 4 + 2 * 128),
+    "gated_linear_attention_additive": (dict(additive=True), 3 * 2 * 128 + 4 * 128 + 2 * 128),
+}
+
+
+def bench_variants(kda, torch, steps, warmup, flush):
+    """Prefill tokens/s of the variant flags on the c1 shape (same timing rules)."""
+    from gated_delta_rule_08_amd import workloads
+    p = workloads.make_inputs(1)
+    cfg = p["config"]
+    t = lambda a, dt: torch.from_numpy(a).to(dt).to("cuda")
+    q, k, v = (t(p[n], torch.bfloat16) for n in ("q", "k", "v"))
+    g, beta = t(p["g"], torch.float32), t(p["beta"], torch.float32)
+    cu = t(p["cu_seqlens"], torch.int32)
+    T, H, d = q.shape
+    N = cu.numel() - 1
+    g_scalar = g[..., 0].contiguous()      # one log-decay per (token, head)
+    states = torch.zeros((N, H, d, d), dtype=torch.float32, device="cuda")
+    o = torch.empty((T, H, d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(kda.kda_chunk_fwd_workspace_bytes(H, d, d, torch.bfloat16, cfg.chunk, T, N),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, (kw, per_token_head) in VARIANTS.items():
+        gate = kw.get("gate", "channel")
+        gg = {"channel": g, "scalar": g_scalar, "none": None}[gate]
+        bb = None if kw.get("additive") else beta
+
+        def step():
+            kda.kda_chunk_fwd(q, k, v, gg, bb, cu, chunk=cfg.chunk, states=states,
+                              write_final=True, o=o, workspace=ws, stream=stream, **kw)
+
+        for _ in range(warmup):
+            flush()
+            step()
+        torch.cuda.synchronize()
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(steps)]
+        for s_, e_ in pairs:
+            flush()
+            s_.record(stream)
+            step()
+            e_.record(stream)
+        torch.cuda.synchronize()
+        ms = sum(_events_ms(pairs)) / steps
+        bytes_ = per_token_head * T * H + N * H * d * d * 4
+        out[name] = {"tokens_per_s": T / (ms * 1e-3), "ms_per_call": ms,
+                     "algorithmic_bytes": bytes_,
+                     "roofline_frac": bytes_ / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    return out
+
+
 def bench_decode(kda, torch, steps, warmup, flush):
     from gated_delta_rule_08_amd import workloads
     p = workloads.make_inputs(2)
@@ -164,6 +222,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the prefill timings of the variant flags")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="run one leg only (for profiling)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -171,8 +231,9 @@ def main(argv=None):
                          "FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path shards over "
-              "heads/sequences without communication, see DESIGN.md", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the operator shards over "
+              "(sequence, head) pairs with no communication, so one GPU's share is what it "
+              "measures", file=sys.stderr)
         return 2
     import torch
     import gated_delta_rule_08_amd as kda
@@ -222,6 +283,8 @@ def main(argv=None):
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline(pr["inputs"])
         del pr
+        if not args.no_variants:
+            out["variants"] = bench_variants(kda, torch, max(5, args.steps // 2), 2, flush)
     if args.only in (None, "decode"):
         dc = bench_decode(kda, torch, args.steps, args.warmup, flush)
         ms = sum(dc["ms"]) / len(dc["ms"])
