@@ -17,29 +17,34 @@
 // The step is a streaming read-modify-write of the state: each state is read
 // from HBM once and written once, and the token vectors are tiny, so the kernel
 // is bound by HBM bandwidth (engineermaxxing ch. 02b: a decode step reads the
-// d x d state and writes it back).  Mapping: one workgroup per (b, h); thread
+// d x d state and writes it back).  Mapping: one workgroup per (b, h) and
+// slice of DVW state columns (the columns of S evolve independently given k,
+// q, beta and the gate, and the reductions run over rows, so slices need no
+// exchange; two 64-column slices per state at d = 128 stream best); thread
 // (row group rg, column quad cq) keeps rows rg, rg + RG, ... of columns
-// 4cq .. 4cq+3 in registers, so every wave load instruction covers whole
-// consecutive rows (coalesced 16-byte accesses).  The reductions over key
-// channels combine the row groups through LDS.
+// 4cq .. 4cq+3 of the slice in registers, so every wave load instruction
+// covers whole row segments (coalesced 16-byte accesses).  The reductions over
+// key channels combine the row groups through LDS.
 #include "kda_common.h"
 
 namespace kda {
 
 namespace {
 
-template <int DK, int DV, int BLOCK, typename IO>
+template <int DK, int DV, int BLOCK, typename IO, int DVW = DV>
 __global__ __launch_bounds__(BLOCK) void decode_kernel(
     const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ states,
     int32_t num_slots, const int32_t* __restrict__ slots, uint32_t flags, IO* __restrict__ o,
     int H) {
-  constexpr int NCQ = DV / 4;      // column quads
+  constexpr int NCQ = DVW / 4;     // column quads of this workgroup
   constexpr int RG = BLOCK / NCQ;  // row groups
   constexpr int RPT = DK / RG;     // rows per thread
   static_assert(DV % 4 == 0 && BLOCK % NCQ == 0 && DK % RG == 0, "bad decode tiling");
 
-  const int bh = blockIdx.x;  // b * H + h
+  constexpr int NSPLIT = DV / DVW;
+  const int bh = blockIdx.x / NSPLIT;  // b * H + h
+  const int c_base = (blockIdx.x - bh * NSPLIT) * DVW;
   const int b = bh / H;
   const int h = bh - b * H;
   const int tid = threadIdx.x;
@@ -60,7 +65,7 @@ __global__ __launch_bounds__(BLOCK) void decode_kernel(
 #pragma unroll
   for (int i = 0; i < RPT; ++i)
     s[i] = __builtin_nontemporal_load(
-        reinterpret_cast<const f32x4_t*>(S + (size_t)(rg + RG * i) * DV + 4 * cq));
+        reinterpret_cast<const f32x4_t*>(S + (size_t)(rg + RG * i) * DV + c_base + 4 * cq));
 
   // 2. token vectors to LDS
   const size_t tk = (size_t)bh * DK, tv = (size_t)bh * DV;
@@ -71,7 +76,7 @@ __global__ __launch_bounds__(BLOCK) void decode_kernel(
     qs[i] = io_traits<IO>::load(q, tk + i);
     as[i] = gate_none ? 1.f : fast_exp(gate_scalar ? g[bh] : g[tk + i]);
   }
-  for (int i = tid; i < DV; i += BLOCK) vs[i] = io_traits<IO>::load(v, tv + i);
+  for (int i = tid; i < DVW; i += BLOCK) vs[i] = io_traits<IO>::load(v, tv + c_base + i);
   __syncthreads();
 
   // k . q, reduced by the first wave
@@ -114,10 +119,10 @@ __global__ __launch_bounds__(BLOCK) void decode_kernel(
       u0 = bt * (u0 - W.x); u1 = bt * (u1 - W.y); u2 = bt * (u2 - W.z); u3 = bt * (u3 - W.w);
     }
     us[c0 + 0] = u0; us[c0 + 1] = u1; us[c0 + 2] = u2; us[c0 + 3] = u3;
-    io_traits<IO>::store(o, tv + c0 + 0, Y.x + kq * u0);
-    io_traits<IO>::store(o, tv + c0 + 1, Y.y + kq * u1);
-    io_traits<IO>::store(o, tv + c0 + 2, Y.z + kq * u2);
-    io_traits<IO>::store(o, tv + c0 + 3, Y.w + kq * u3);
+    io_traits<IO>::store(o, tv + c_base + c0 + 0, Y.x + kq * u0);
+    io_traits<IO>::store(o, tv + c_base + c0 + 1, Y.y + kq * u1);
+    io_traits<IO>::store(o, tv + c_base + c0 + 2, Y.z + kq * u2);
+    io_traits<IO>::store(o, tv + c_base + c0 + 3, Y.w + kq * u3);
   }
   __syncthreads();
 
@@ -129,15 +134,16 @@ __global__ __launch_bounds__(BLOCK) void decode_kernel(
     const float kr = ks[r];
     f32x4_t t = s[i];
     t[0] += kr * u4.x; t[1] += kr * u4.y; t[2] += kr * u4.z; t[3] += kr * u4.w;
-    __builtin_nontemporal_store(t, reinterpret_cast<f32x4_t*>(S + (size_t)r * DV + 4 * cq));
+    __builtin_nontemporal_store(t, reinterpret_cast<f32x4_t*>(S + (size_t)r * DV + c_base + 4 * cq));
   }
 }
 
-template <int D, int BLOCK, typename IO>
+template <int D, int BLOCK, typename IO, int DVW = D>
 kda_status_t launch_typed(int32_t batch, int H, const void* q, const void* k, const void* v,
                           const float* g, const float* beta, float* states, int32_t num_slots,
                           const int32_t* slots, uint32_t flags, void* o, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<D, D, BLOCK, IO>), dim3((unsigned)batch * H), dim3(BLOCK), 0,
+  hipLaunchKernelGGL((decode_kernel<D, D, BLOCK, IO, DVW>), dim3((unsigned)batch * H * (D / DVW)),
+                     dim3(BLOCK), 0,
                      stream, static_cast<const IO*>(q), static_cast<const IO*>(k),
                      static_cast<const IO*>(v), g, beta, states, num_slots, slots, flags,
                      static_cast<IO*>(o), H);
@@ -152,7 +158,7 @@ kda_status_t launch_io(int d, int32_t batch, int H, const void* q, const void* k
     case 16: return launch_typed<16, 64, IO>(batch, H, q, k, v, g, beta, states, num_slots, slots, flags, o, stream);
     case 32: return launch_typed<32, 64, IO>(batch, H, q, k, v, g, beta, states, num_slots, slots, flags, o, stream);
     case 64: return launch_typed<64, 128, IO>(batch, H, q, k, v, g, beta, states, num_slots, slots, flags, o, stream);
-    case 128: return launch_typed<128, 256, IO>(batch, H, q, k, v, g, beta, states, num_slots, slots, flags, o, stream);
+    case 128: return launch_typed<128, 256, IO, 64>(batch, H, q, k, v, g, beta, states, num_slots, slots, flags, o, stream);
     default: return KDA_ERR_UNSUPPORTED;
   }
 }
