@@ -115,3 +115,52 @@ def decode(q, k, v, g, beta, s):
     B = q.shape[0]
     cu = np.arange(B + 1, dtype=np.int32)
     return run(q, k, v, g, beta, cu_seqlens=cu, s0=s)
+
+
+def prepare_inputs(q_raw, k_raw, gate_logits=None, beta_logits=None, gate_min=-np.inf,
+                   gate="channel"):
+    """Input preparation from the raw projections, in float64.
+
+    q = normalize(silu(q_raw)), k = normalize(silu(k_raw)) over the key
+    dimension of each (token, head) (heqinghuang "From GPT2 to Kimi3,
+    Explained", section 09: unit-length queries and keys, F.normalize after
+    SiLU; normalize divides by max(norm, 1e-12)); beta = sigmoid(beta logit)
+    (same section: write strength in (0, 1)); alpha = sigmoid(gate logit) per
+    key channel (engineermaxxing "From GPT-2 to Kimi K3", ch. 06b) and
+    g = log(alpha), floored at gate_min (dev.to "From GPT-2 to Kimi K3",
+    block 5: the decay parameterisation is bounded for bf16 stability; the
+    pages give no value, so the floor is an argument, -inf = none).
+
+    q_raw, k_raw: [..., dk].  gate_logits: [..., dk] (gate="channel"), [...]
+    (gate="scalar", broadcast over dk) or None (gate="none": g = 0).
+    beta_logits: [...] or None (beta = 1, for the additive mode).
+    Returns (q, k, g, beta) in float64, g of shape [..., dk].
+    """
+    q_raw, k_raw = _f64(q_raw), _f64(k_raw)
+
+    def silu(x):
+        return x / (1.0 + np.exp(-x))
+
+    def normalize(x):
+        n = np.sqrt((x * x).sum(axis=-1, keepdims=True))
+        return x / np.maximum(n, 1e-12)
+
+    def log_sigmoid(x):
+        # log(1 / (1 + e^-x)) = min(x, 0) - log1p(e^-|x|): no overflow for any x
+        return np.minimum(x, 0.0) - np.log1p(np.exp(-np.abs(x)))
+
+    q = normalize(silu(q_raw))
+    k = normalize(silu(k_raw))
+    dk = q.shape[-1]
+    if gate == "none":
+        g = np.zeros(q.shape)
+    else:
+        a = _f64(gate_logits)
+        if gate == "scalar":
+            a = np.repeat(a[..., None], dk, axis=-1)
+        g = np.maximum(log_sigmoid(a), gate_min)
+    if beta_logits is None:
+        beta = np.ones(q.shape[:-1])
+    else:
+        beta = 1.0 / (1.0 + np.exp(-_f64(beta_logits)))
+    return q, k, g, beta

@@ -8,6 +8,7 @@ operations.  A plausible slip in the oracle (a dropped term, a wrong sign, the
 fade applied after the read, a transposed operand, the output read before the
 write) fails at least one of them.
 """
+import math
 from fractions import Fraction
 
 import numpy as np
@@ -439,3 +440,48 @@ def test_threads_do_not_change_results():
     o8, s8 = oracle.run(prob["q"], prob["k"], prob["v"], prob["g"], prob["beta"], cu, nthreads=8)
     np.testing.assert_array_equal(o1, o8)
     np.testing.assert_array_equal(s1, s8)
+
+
+# ------------------------------------------------- input preparation (from raw projections)
+
+def test_prepare_silu_normalize_closed_form():
+    """normalize(silu(x)): silu(1) = 1/(1+e^-1), silu(-1) = -e^-1/(1+e^-1); the row is
+    divided by its Euclidean norm; a zero row stays zero (the normaliser's floor)."""
+    s1 = 1.0 / (1.0 + math.exp(-1.0))
+    sm1 = -1.0 / (1.0 + math.exp(1.0))
+    n = math.hypot(s1, sm1)
+    q, k, g, beta = oracle.prepare_inputs(np.array([[1.0, -1.0], [0.0, 0.0]]),
+                                          np.array([[3.0, 4.0], [-2.0, 0.5]]), gate="none")
+    assert q[0, 0] == pytest.approx(s1 / n, rel=1e-15) and q[0, 1] == pytest.approx(sm1 / n, rel=1e-15)
+    assert np.all(q[1] == 0.0)
+    assert np.allclose(np.linalg.norm(k, axis=-1), 1.0, rtol=0, atol=1e-15)
+    assert np.all(g == 0.0) and np.all(beta == 1.0)
+
+
+def test_prepare_gates_closed_forms():
+    """sigmoid(ln 3) = 3/4 exactly; log-sigmoid(0) = -ln 2; log-sigmoid(-50) = -50 - log1p(e^-50)
+    and log-sigmoid(50) = -log1p(e^-50) without overflow or rounding to 0; the floor."""
+    logits = np.array([0.0, math.log(3.0), -50.0, 50.0])
+    _, _, g, beta = oracle.prepare_inputs(np.ones((4, 2)), np.ones((4, 2)),
+                                          gate_logits=np.repeat(logits[:, None], 2, axis=1),
+                                          beta_logits=logits)
+    assert beta[1] == pytest.approx(0.75, rel=1e-15) and beta[0] == 0.5
+    assert g[0, 0] == pytest.approx(-math.log(2.0), rel=1e-15)
+    assert g[1, 0] == pytest.approx(math.log(0.75), rel=1e-15)
+    assert g[2, 0] == pytest.approx(-50.0 - math.log1p(math.exp(-50.0)), rel=1e-15)
+    assert g[3, 0] == pytest.approx(-math.exp(-50.0), rel=1e-12) and g[3, 0] < 0.0
+    _, _, gf, _ = oracle.prepare_inputs(np.ones((4, 2)), np.ones((4, 2)),
+                                        gate_logits=np.repeat(logits[:, None], 2, axis=1),
+                                        beta_logits=logits, gate_min=-5.0)
+    assert np.all(gf >= -5.0) and gf[2, 0] == -5.0 and gf[0, 0] == g[0, 0]
+
+
+def test_prepare_scalar_gate_broadcasts():
+    """A scalar gate logit per (token, head) gives the same log-decay on every channel."""
+    rng = np.random.default_rng(5)
+    a = rng.standard_normal((6, 3))
+    _, _, g, _ = oracle.prepare_inputs(rng.standard_normal((6, 3, 4)), rng.standard_normal((6, 3, 4)),
+                                       gate_logits=a, beta_logits=a, gate="scalar")
+    for c in range(4):
+        assert np.array_equal(g[..., c], g[..., 0])
+    assert g[2, 1, 3] == pytest.approx(math.log(1.0 / (1.0 + math.exp(-a[2, 1]))), rel=1e-14)
