@@ -16,8 +16,9 @@ inputs come from HBM; the fill is outside the HIP events that time the step.
 decode steps/s is reported next to it with its own roofline.  The oracle
 (fp64, host threads) is timed on the same prefill input as a CPU baseline.
 
-The variant flags (scalar gate, no gate, additive write) are timed on the same
-prefill shape and reported under "variants", each with its own algorithmic bytes.
+The variant flags (scalar gate, no gate, additive write) and the prefill from raw
+bf16 projections (input preparation fused in) are timed on the same prefill
+shape and reported under "variants", each with its own algorithmic bytes.
 
 Prints one JSON line.
 """
@@ -120,6 +121,8 @@ VARIANTS = {
     "gated_deltanet_scalar_gate": (dict(gate="scalar"), 3 * 2 * 128 + 4 + 4 + 2 * 128),
     "deltanet_no_gate": (dict(gate="none"), 3 * 2 * 128 + 4 + 2 * 128),
     "gated_linear_attention_additive": (dict(additive=True), 3 * 2 * 128 + 4 * 128 + 2 * 128),
+    # raw bf16 projections: q, k, v, gate logits (bf16 per channel), write-strength logit, o
+    "kda_fused_input_preparation": (dict(raw=True), 3 * 2 * 128 + 2 * 128 + 2 + 2 * 128),
 }
 
 
@@ -135,6 +138,12 @@ def bench_variants(kda, torch, steps, warmup, flush):
     T, H, d = q.shape
     N = cu.numel() - 1
     g_scalar = g[..., 0].contiguous()      # one log-decay per (token, head)
+    # raw projections of the same shape (the prep normalises q, k and squashes the logits)
+    gen = torch.Generator(device="cuda").manual_seed(1001)
+    q_raw = torch.randn(q.shape, device="cuda", generator=gen).to(torch.bfloat16)
+    k_raw = torch.randn(k.shape, device="cuda", generator=gen).to(torch.bfloat16)
+    a_raw = (torch.randn(g.shape, device="cuda", generator=gen) + 3.0).to(torch.bfloat16)
+    b_raw = torch.randn(beta.shape, device="cuda", generator=gen).to(torch.bfloat16)
     states = torch.zeros((N, H, d, d), dtype=torch.float32, device="cuda")
     o = torch.empty((T, H, d), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(kda.kda_chunk_fwd_workspace_bytes(H, d, d, torch.bfloat16, cfg.chunk, T, N),
@@ -147,8 +156,13 @@ def bench_variants(kda, torch, steps, warmup, flush):
         bb = None if kw.get("additive") else beta
 
         def step():
-            kda.kda_chunk_fwd(q, k, v, gg, bb, cu, chunk=cfg.chunk, states=states,
-                              write_final=True, o=o, workspace=ws, stream=stream, **kw)
+            if kw.get("raw"):
+                kda.kda_chunk_fwd_raw(q_raw, k_raw, v, a_raw, b_raw, cu, chunk=cfg.chunk,
+                                      states=states, write_final=True, o=o, workspace=ws,
+                                      stream=stream)
+            else:
+                kda.kda_chunk_fwd(q, k, v, gg, bb, cu, chunk=cfg.chunk, states=states,
+                                  write_final=True, o=o, workspace=ws, stream=stream, **kw)
 
         for _ in range(warmup):
             flush()

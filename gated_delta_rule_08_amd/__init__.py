@@ -18,7 +18,8 @@ import torch
 __all__ = [
     "KdaError", "load_library", "kda_abi_version", "kda_chunk_fwd", "kda_chunk_fwd_supported",
     "kda_chunk_fwd_workspace_bytes", "kda_decode_step", "kda_state_init", "kda_state_load",
-    "kda_state_store", "KDA_READ_INITIAL_STATE", "KDA_WRITE_FINAL_STATE",
+    "kda_state_store", "KDA_READ_INITIAL_STATE", "KDA_WRITE_FINAL_STATE", "kda_chunk_fwd_raw",
+    "kda_decode_step_raw",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -74,6 +75,12 @@ def load_library(path: str | None = None):
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step_ex.argtypes = [SH, I32, P, P, P, P, P, P, I32, P, U32, P, P]
     lib.kda_decode_step_ex.restype = ctypes.c_int
+    F32 = ctypes.c_float
+    lib.kda_chunk_fwd_raw.argtypes = [SH, I32, I32, I32, P, P, P, P, P, P, F32, P, I32, P, U32, P,
+                                      P, SZ, P]
+    lib.kda_chunk_fwd_raw.restype = ctypes.c_int
+    lib.kda_decode_step_raw.argtypes = [SH, I32, P, P, P, P, P, F32, P, I32, P, U32, P, P]
+    lib.kda_decode_step_raw.restype = ctypes.c_int
     lib.kda_state_init.argtypes = [SH, P, I32, P]
     lib.kda_state_init.restype = ctypes.c_int
     lib.kda_state_load.argtypes = [SH, P, I32, P, I32, P, P]
@@ -236,6 +243,87 @@ def kda_decode_step(q, k, v, g, beta, states, state_slots=None, o=None, stream=N
     _check(lib.kda_decode_step_ex(ctypes.byref(sh), B, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                   _ptr(beta), _ptr(states), states.shape[0], _ptr(state_slots),
                                   _variant_flags(gate, additive), _ptr(o), _stream(stream)))
+    return o
+
+
+def _need_raw_gate_beta(gate_logits, beta_logits, lead, dk, gate, additive):
+    """bf16 logits as the variant reads them (see kda_chunk_fwd_raw in include/kda.h)."""
+    if gate == "channel":
+        _need(gate_logits, "gate_logits", lead + (dk,), torch.bfloat16)
+    elif gate == "scalar":
+        _need(gate_logits, "gate_logits", lead, torch.bfloat16)
+    elif gate_logits is not None:
+        raise ValueError("gate='none' reads no gate: pass gate_logits=None")
+    if not additive:
+        _need(beta_logits, "beta_logits", lead, torch.bfloat16)
+    elif beta_logits is not None:
+        raise ValueError("additive=True reads no beta: pass beta_logits=None")
+
+
+def kda_chunk_fwd_raw(q_raw, k_raw, v, gate_logits, beta_logits, cu_seqlens, chunk: int = 64,
+                      gate_min: float = float("-inf"), states=None, state_slots=None,
+                      read_initial: bool = False, write_final: bool = False, o=None,
+                      workspace=None, stream=None, gate: str = "channel", additive: bool = False):
+    """Prefill from raw bf16 projections with the input preparation fused in
+    (see kda_chunk_fwd_raw in include/kda.h): q = normalize(silu(q_raw)),
+    k = normalize(silu(k_raw)), beta = sigmoid(beta_logits),
+    g = max(log sigmoid(gate_logits), gate_min).  Returns o [T, H, dv] (bf16)."""
+    lib = load_library()
+    T, H, dk = q_raw.shape
+    dv = v.shape[2]
+    for t, name, shp in ((q_raw, "q_raw", (T, H, dk)), (k_raw, "k_raw", (T, H, dk)),
+                         (v, "v", (T, H, dv))):
+        _need(t, name, shp, torch.bfloat16)
+    _need_raw_gate_beta(gate_logits, beta_logits, (T, H), dk, gate, additive)
+    N = cu_seqlens.numel() - 1
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32)
+    flags = ((KDA_READ_INITIAL_STATE if read_initial else 0)
+             | (KDA_WRITE_FINAL_STATE if write_final else 0) | _variant_flags(gate, additive))
+    num_slots = 0
+    if states is not None:
+        _need(states, "states", (states.shape[0], H, dk, dv), torch.float32)
+        num_slots = states.shape[0]
+    if state_slots is not None:
+        _need(state_slots, "state_slots", (N,), torch.int32)
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=torch.bfloat16, device=q_raw.device)
+    else:
+        _need(o, "o", (T, H, dv), torch.bfloat16)
+    sh = _Shape(H, dk, dv, KDA_BF16)
+    need = int(lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(sh), chunk, T, N))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_raw.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.kda_chunk_fwd_raw(ctypes.byref(sh), chunk, T, N, _ptr(cu_seqlens), _ptr(q_raw),
+                                 _ptr(k_raw), _ptr(v), _ptr(gate_logits), _ptr(beta_logits),
+                                 float(gate_min), _ptr(states), num_slots, _ptr(state_slots),
+                                 flags, _ptr(o), _ptr(workspace), ws_bytes, _stream(stream)))
+    return o
+
+
+def kda_decode_step_raw(q_raw, k_raw, v, gate_logits, beta_logits, states, gate_min=float("-inf"),
+                        state_slots=None, o=None, stream=None, gate: str = "channel",
+                        additive: bool = False):
+    """kda_decode_step from raw bf16 projections (see kda_decode_step_raw)."""
+    lib = load_library()
+    B, H, dk = q_raw.shape
+    dv = v.shape[2]
+    for t, name, shp in ((q_raw, "q_raw", (B, H, dk)), (k_raw, "k_raw", (B, H, dk)),
+                         (v, "v", (B, H, dv))):
+        _need(t, name, shp, torch.bfloat16)
+    _need_raw_gate_beta(gate_logits, beta_logits, (B, H), dk, gate, additive)
+    _need(states, "states", (states.shape[0], H, dk, dv), torch.float32)
+    if state_slots is not None:
+        _need(state_slots, "state_slots", (B,), torch.int32)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=torch.bfloat16, device=q_raw.device)
+    else:
+        _need(o, "o", (B, H, dv), torch.bfloat16)
+    sh = _Shape(H, dk, dv, KDA_BF16)
+    _check(lib.kda_decode_step_raw(ctypes.byref(sh), B, _ptr(q_raw), _ptr(k_raw), _ptr(v),
+                                   _ptr(gate_logits), _ptr(beta_logits), float(gate_min),
+                                   _ptr(states), states.shape[0], _ptr(state_slots),
+                                   _variant_flags(gate, additive), _ptr(o), _stream(stream)))
     return o
 
 

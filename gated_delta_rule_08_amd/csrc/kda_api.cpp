@@ -18,9 +18,9 @@ kda_status_t launch_state_copy(bool to_pool, float* states, int32_t num_slots,
                                size_t per_state_floats, hipStream_t stream);
 bool decode_supported(int dk, int dv);
 kda_status_t launch_decode(const kda_shape_t* sh, int32_t batch, const void* q, const void* k,
-                           const void* v, const float* g, const float* beta, float* states,
-                           int32_t num_slots, const int32_t* slots, uint32_t flags, void* o,
-                           hipStream_t stream);
+                           const void* v, const void* g, const void* beta, bool raw,
+                           float gate_min, float* states, int32_t num_slots, const int32_t* slots,
+                           uint32_t flags, void* o, hipStream_t stream);
 bool chunk_small_supported(int dk, int dv, int chunk);
 kda_status_t launch_chunk_small(const kda_shape_t* sh, int32_t chunk, int32_t T, int32_t N,
                                 const int32_t* cu, const void* q, const void* k, const void* v,
@@ -30,10 +30,10 @@ kda_status_t launch_chunk_small(const kda_shape_t* sh, int32_t chunk, int32_t T,
 bool chunk_mfma_supported(int dk, int dv, int chunk, int io_dtype);
 size_t chunk_mfma_workspace_bytes(int H, int32_t T, int32_t N);
 kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, const int32_t* cu,
-                               const void* q, const void* k, const void* v, const float* g,
-                               const float* beta, float* states, int32_t num_slots,
-                               const int32_t* slots, uint32_t flags, void* o, void* workspace,
-                               hipStream_t stream);
+                               const void* q, const void* k, const void* v, const void* g,
+                               const void* beta, bool raw, float gate_min, float* states,
+                               int32_t num_slots, const int32_t* slots, uint32_t flags, void* o,
+                               void* workspace, hipStream_t stream);
 
 namespace {
 thread_local char g_last_error[512] = "";
@@ -92,16 +92,18 @@ kda_status_t check_variant(uint32_t flags, const char* what) {
 }
 
 // g and beta as the variant reads them: g not read with KDA_GATE_NONE, beta not
-// read with KDA_ADDITIVE; a per-channel g is read as 16-byte vectors.
-kda_status_t check_gate_beta(uint32_t flags, const float* g, const float* beta, const char* what) {
+// read with KDA_ADDITIVE; a per-channel g is read as 16-byte vectors of fp32
+// (8-byte vectors of bf16 logits when raw).
+kda_status_t check_gate_beta(uint32_t flags, const void* g, const void* beta, bool raw,
+                             const char* what) {
   if (!(flags & KDA_GATE_NONE)) {
-    if (!g) return invalid("%s: g is NULL", what);
-    if (!aligned(g, (flags & KDA_GATE_SCALAR) ? 4 : 16))
-      return invalid("%s: g must be %d-byte aligned", what, (flags & KDA_GATE_SCALAR) ? 4 : 16);
+    const int a = (flags & KDA_GATE_SCALAR) ? (raw ? 2 : 4) : (raw ? 8 : 16);
+    if (!g) return invalid("%s: %s is NULL", what, raw ? "gate_logits" : "g");
+    if (!aligned(g, a)) return invalid("%s: the gate must be %d-byte aligned", what, a);
   }
   if (!(flags & KDA_ADDITIVE)) {
-    if (!beta) return invalid("%s: beta is NULL", what);
-    if (!aligned(beta, 4)) return invalid("%s: beta must be 4-byte aligned", what);
+    if (!beta) return invalid("%s: %s is NULL", what, raw ? "beta_logits" : "beta");
+    if (!aligned(beta, raw ? 2 : 4)) return invalid("%s: beta is misaligned", what);
   }
   return KDA_OK;
 }
@@ -147,13 +149,14 @@ size_t kda_chunk_fwd_workspace_bytes(const kda_shape_t* sh, int32_t chunk, int32
   return 0;
 }
 
-kda_status_t kda_chunk_fwd(const kda_shape_t* sh, int32_t chunk, int32_t total_tokens,
-                           int32_t num_seqs, const int32_t* cu_seqlens, const void* q,
-                           const void* k, const void* v, const float* g, const float* beta,
-                           float* states, int32_t num_slots, const int32_t* state_slots,
-                           uint32_t flags, void* o, void* workspace, size_t workspace_bytes,
-                           void* stream) {
-  const char* W = "kda_chunk_fwd";
+namespace {
+
+kda_status_t chunk_fwd_impl(const char* W, const kda_shape_t* sh, int32_t chunk,
+                            int32_t total_tokens, int32_t num_seqs, const int32_t* cu_seqlens,
+                            const void* q, const void* k, const void* v, const void* g,
+                            const void* beta, bool raw, float gate_min, float* states,
+                            int32_t num_slots, const int32_t* state_slots, uint32_t flags,
+                            void* o, void* workspace, size_t workspace_bytes, void* stream) {
   kda_status_t st = check_shape(sh, W);
   if (st != KDA_OK) return st;
   if (total_tokens < 0 || num_seqs < 0)
@@ -163,11 +166,13 @@ kda_status_t kda_chunk_fwd(const kda_shape_t* sh, int32_t chunk, int32_t total_t
   st = check_variant(flags, W);
   if (st != KDA_OK) return st;
   if (chunk <= 0) return invalid("%s: chunk must be >= 1 (got %d)", W, chunk);
-  if (!chunk_supported(sh, chunk)) return unsupported(W, sh, chunk);
+  if (raw && gate_min != gate_min) return invalid("%s: gate_min is NaN", W);
+  if (raw ? !chunk_mfma_supported(sh->dk, sh->dv, chunk, sh->io_dtype) : !chunk_supported(sh, chunk))
+    return unsupported(W, sh, chunk);
   if (total_tokens == 0 || num_seqs == 0) return KDA_OK;
   if (!cu_seqlens) return invalid("%s: cu_seqlens is NULL", W);
   if (!q || !k || !v || !o) return invalid("%s: a tensor pointer is NULL", W);
-  st = check_gate_beta(flags, g, beta, W);
+  st = check_gate_beta(flags, g, beta, raw, W);
   if (st != KDA_OK) return st;
   if (flags & kStateFlags) {
     if (!states) return invalid("%s: states is NULL but flags request state I/O", W);
@@ -188,12 +193,63 @@ kda_status_t kda_chunk_fwd(const kda_shape_t* sh, int32_t chunk, int32_t total_t
       return KDA_ERR_WORKSPACE_TOO_SMALL;
     }
     if (!aligned(workspace, 256)) return invalid("%s: workspace must be 256-byte aligned", W);
-    return launch_chunk_mfma(sh, total_tokens, num_seqs, cu_seqlens, q, k, v, g, beta, states,
-                             num_slots, state_slots, flags, o, workspace, s);
+    return launch_chunk_mfma(sh, total_tokens, num_seqs, cu_seqlens, q, k, v, g, beta, raw,
+                             gate_min, states, num_slots, state_slots, flags, o, workspace, s);
   }
-  return launch_chunk_small(sh, chunk, total_tokens, num_seqs, cu_seqlens, q, k, v, g, beta,
+  return launch_chunk_small(sh, chunk, total_tokens, num_seqs, cu_seqlens, q, k, v,
+                            static_cast<const float*>(g), static_cast<const float*>(beta),
                             (flags & kStateFlags) ? states : nullptr, num_slots, state_slots,
                             flags, o, s);
+}
+
+kda_status_t decode_impl(const char* W, const kda_shape_t* sh, int32_t batch, const void* q,
+                         const void* k, const void* v, const void* g, const void* beta, bool raw,
+                         float gate_min, float* states, int32_t num_slots,
+                         const int32_t* state_slots, uint32_t flags, void* o, void* stream) {
+  kda_status_t st = check_shape(sh, W);
+  if (st != KDA_OK) return st;
+  if (batch < 0) return invalid("%s: batch must be >= 0", W);
+  if (flags & ~kVariantFlags)
+    return invalid("%s: unknown flag bits 0x%x", W, flags & ~kVariantFlags);
+  st = check_variant(flags, W);
+  if (st != KDA_OK) return st;
+  if (raw && gate_min != gate_min) return invalid("%s: gate_min is NaN", W);
+  if (!decode_supported(sh->dk, sh->dv) || (raw && sh->io_dtype != KDA_BF16))
+    return unsupported(W, sh, 0);
+  if (batch == 0) return KDA_OK;
+  if (!q || !k || !v || !o || !states) return invalid("%s: a tensor pointer is NULL", W);
+  st = check_gate_beta(flags, g, beta, raw, W);
+  if (st != KDA_OK) return st;
+  if (num_slots <= 0) return invalid("%s: num_slots must be >= 1", W);
+  if (!state_slots && num_slots < batch)
+    return invalid("%s: num_slots (%d) < batch (%d) with implicit slots", W, num_slots, batch);
+  if (!aligned(states, 16)) return invalid("%s: states must be 16-byte aligned", W);
+  return launch_decode(sh, batch, q, k, v, g, beta, raw, gate_min, states, num_slots, state_slots,
+                       flags, o, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+kda_status_t kda_chunk_fwd(const kda_shape_t* sh, int32_t chunk, int32_t total_tokens,
+                           int32_t num_seqs, const int32_t* cu_seqlens, const void* q,
+                           const void* k, const void* v, const float* g, const float* beta,
+                           float* states, int32_t num_slots, const int32_t* state_slots,
+                           uint32_t flags, void* o, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return chunk_fwd_impl("kda_chunk_fwd", sh, chunk, total_tokens, num_seqs, cu_seqlens, q, k, v,
+                        g, beta, false, 0.f, states, num_slots, state_slots, flags, o, workspace,
+                        workspace_bytes, stream);
+}
+
+kda_status_t kda_chunk_fwd_raw(const kda_shape_t* sh, int32_t chunk, int32_t total_tokens,
+                               int32_t num_seqs, const int32_t* cu_seqlens, const void* q_raw,
+                               const void* k_raw, const void* v, const void* gate_logits,
+                               const void* beta_logits, float gate_min, float* states,
+                               int32_t num_slots, const int32_t* state_slots, uint32_t flags,
+                               void* o, void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_fwd_impl("kda_chunk_fwd_raw", sh, chunk, total_tokens, num_seqs, cu_seqlens, q_raw,
+                        k_raw, v, gate_logits, beta_logits, true, gate_min, states, num_slots,
+                        state_slots, flags, o, workspace, workspace_bytes, stream);
 }
 
 kda_status_t kda_decode_step(const kda_shape_t* sh, int32_t batch, const void* q, const void* k,
@@ -208,25 +264,17 @@ kda_status_t kda_decode_step_ex(const kda_shape_t* sh, int32_t batch, const void
                                 const void* k, const void* v, const float* g, const float* beta,
                                 float* states, int32_t num_slots, const int32_t* state_slots,
                                 uint32_t flags, void* o, void* stream) {
-  const char* W = "kda_decode_step";
-  kda_status_t st = check_shape(sh, W);
-  if (st != KDA_OK) return st;
-  if (batch < 0) return invalid("%s: batch must be >= 0", W);
-  if (flags & ~kVariantFlags)
-    return invalid("%s: unknown flag bits 0x%x", W, flags & ~kVariantFlags);
-  st = check_variant(flags, W);
-  if (st != KDA_OK) return st;
-  if (!decode_supported(sh->dk, sh->dv)) return unsupported(W, sh, 0);
-  if (batch == 0) return KDA_OK;
-  if (!q || !k || !v || !o || !states) return invalid("%s: a tensor pointer is NULL", W);
-  st = check_gate_beta(flags, g, beta, W);
-  if (st != KDA_OK) return st;
-  if (num_slots <= 0) return invalid("%s: num_slots must be >= 1", W);
-  if (!state_slots && num_slots < batch)
-    return invalid("%s: num_slots (%d) < batch (%d) with implicit slots", W, num_slots, batch);
-  if (!aligned(states, 16)) return invalid("%s: states must be 16-byte aligned", W);
-  return launch_decode(sh, batch, q, k, v, g, beta, states, num_slots, state_slots, flags, o,
-                       static_cast<hipStream_t>(stream));
+  return decode_impl("kda_decode_step", sh, batch, q, k, v, g, beta, false, 0.f, states,
+                     num_slots, state_slots, flags, o, stream);
+}
+
+kda_status_t kda_decode_step_raw(const kda_shape_t* sh, int32_t batch, const void* q_raw,
+                                 const void* k_raw, const void* v, const void* gate_logits,
+                                 const void* beta_logits, float gate_min, float* states,
+                                 int32_t num_slots, const int32_t* state_slots, uint32_t flags,
+                                 void* o, void* stream) {
+  return decode_impl("kda_decode_step_raw", sh, batch, q_raw, k_raw, v, gate_logits, beta_logits,
+                     true, gate_min, states, num_slots, state_slots, flags, o, stream);
 }
 
 kda_status_t kda_state_init(const kda_shape_t* sh, float* states, int32_t num_slots,

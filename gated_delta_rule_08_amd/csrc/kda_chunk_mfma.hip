@@ -228,8 +228,12 @@ struct PrepSmem {
 // One item's inputs between the global loads and the LDS staging.
 struct PrepIn {
   uint4 k[2], q[2], v[2];
-  float4 g[4];   // per-channel gate; a scalar gate is read into .x and broadcast at staging
+  float4 g[4];        // per-channel gate; a scalar gate is read into .x and broadcast at staging
   float beta;
+  // raw projections (kRaw): bf16 logits kept as loaded, converted at staging
+  uint2 gl[4];        // 4 per-channel gate logits
+  uint16_t gs16[4];   // scalar gate logit
+  uint16_t b16;       // write-strength logit
 };
 
 // Gate variants of the prep, fixed at compile time so that the prefetch of the
@@ -266,11 +270,16 @@ __device__ __forceinline__ ItemPos locate(const Header& hd, int N, int H, int it
 // Rows past the end of the sequence read the last valid row (zeroed at staging).
 // Variants: a scalar gate is read once per row and staged on every channel; no
 // gate reads nothing (G = 0); the additive write reads no beta (beta = 1, and
-// the correction is dropped later).
-template <int kGate, bool kAdd>
+// the correction is dropped later).  kRaw: q, k are raw projections and the
+// gate and write strength are bf16 logits (prepared at staging).
+template <int kGate, bool kAdd, bool kRaw>
 __device__ __forceinline__ void prep_load(PrepIn& in, const ItemPos& p, const uint16_t* q,
-                                          const uint16_t* k, const uint16_t* v, const float* g,
-                                          const float* beta, int H, int tid) {
+                                          const uint16_t* k, const uint16_t* v, const void* gp,
+                                          const void* bp, int H, int tid) {
+  const float* g = static_cast<const float*>(gp);
+  const float* beta = static_cast<const float*>(bp);
+  const uint16_t* g16 = static_cast<const uint16_t*>(gp);
+  const uint16_t* b16 = static_cast<const uint16_t*>(bp);
   const size_t rowstride = (size_t)H * D;
   const size_t base = ((size_t)p.t0 * H + p.h) * D;
 #pragma unroll
@@ -284,22 +293,57 @@ __device__ __forceinline__ void prep_load(PrepIn& in, const ItemPos& p, const ui
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int u = tid + kPrepThreads * i, r = u >> 5, cc = (u & 31) * 4;
-    if (kGate == kGateScalar)
-      in.g[i].x = g[(size_t)(p.t0 + min(r, p.c - 1)) * H + p.h];
-    else if (kGate == kGateChannel)
-      in.g[i] = *reinterpret_cast<const float4*>(g + base + (size_t)min(r, p.c - 1) * rowstride + cc);
+    const size_t row = (size_t)min(r, p.c - 1);
+    if (kGate == kGateScalar) {
+      if (kRaw) in.gs16[i] = g16[(p.t0 + row) * H + p.h];
+      else in.g[i].x = g[(p.t0 + row) * H + p.h];
+    } else if (kGate == kGateChannel) {
+      if (kRaw) in.gl[i] = *reinterpret_cast<const uint2*>(g16 + base + row * rowstride + cc);
+      else in.g[i] = *reinterpret_cast<const float4*>(g + base + row * rowstride + cc);
+    }
   }
-  if (!kAdd) in.beta = beta[(size_t)(p.t0 + min(tid & 63, p.c - 1)) * H + p.h];
+  if (!kAdd) {
+    const size_t bi = (size_t)(p.t0 + min(tid & 63, p.c - 1)) * H + p.h;
+    if (kRaw) in.b16 = b16[bi];
+    else in.beta = beta[bi];
+  }
 }
 
-template <int kGate, bool kAdd>
-__device__ __forceinline__ void prep_stage(PrepSmem& sm, const PrepIn& in, int c, int tid) {
+// normalize(silu(x)) of one row held by the 16 lanes of a lane group, 8 channels
+// per lane (bf16 in, bf16 out)
+__device__ __forceinline__ uint4 prepare_row8(uint4 raw) {
+  const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+  float f[8];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f[2 * j] = silu(__uint_as_float(wv[j] << 16));
+    f[2 * j + 1] = silu(__uint_as_float(wv[j] & 0xffff0000u));
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ss += f[j] * f[j];
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  const float inv = inv_norm(ss);
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    o[j] = (uint32_t)f32_to_bf16(f[2 * j] * inv) | ((uint32_t)f32_to_bf16(f[2 * j + 1] * inv) << 16);
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+template <int kGate, bool kAdd, bool kRaw>
+__device__ __forceinline__ void prep_stage(PrepSmem& sm, const PrepIn& in, int c, int tid,
+                                           float gate_min) {
   const uint4 z4 = make_uint4(0, 0, 0, 0);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int u = tid + kPrepThreads * i, r = u >> 4, cc = (u & 15) * 8;
     const bool ok = r < c;
-    const uint4 a = ok ? in.k[i] : z4, b = ok ? in.q[i] : z4, d = ok ? in.v[i] : z4;
+    // kRaw: the 16 lanes of a row group hold one row (every lane takes part in the sum)
+    const uint4 kk = kRaw ? prepare_row8(in.k[i]) : in.k[i];
+    const uint4 qq = kRaw ? prepare_row8(in.q[i]) : in.q[i];
+    const uint4 a = ok ? kk : z4, b = ok ? qq : z4, d = ok ? in.v[i] : z4;
     uint2* pk = reinterpret_cast<uint2*>(&sm.K[r][cc]);
     uint2* pq = reinterpret_cast<uint2*>(&sm.Q[r][cc]);
     uint2* pv = reinterpret_cast<uint2*>(&sm.V[r][cc]);
@@ -310,12 +354,25 @@ __device__ __forceinline__ void prep_stage(PrepSmem& sm, const PrepIn& in, int c
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int u = tid + kPrepThreads * i, r = u >> 5, cc = (u & 31) * 4;
-    const float4 gv = kGate == kGateNone     ? make_float4(0.f, 0.f, 0.f, 0.f)
-                      : kGate == kGateScalar ? make_float4(in.g[i].x, in.g[i].x, in.g[i].x, in.g[i].x)
-                                             : in.g[i];
+    float4 gv;
+    if (kGate == kGateNone) {
+      gv = make_float4(0.f, 0.f, 0.f, 0.f);
+    } else if (kGate == kGateScalar) {
+      const float x = kRaw ? fmaxf(log_sigmoid(bf16_to_f32(in.gs16[i])), gate_min) : in.g[i].x;
+      gv = make_float4(x, x, x, x);
+    } else if (kRaw) {
+      const uint2 l = in.gl[i];
+      gv = make_float4(fmaxf(log_sigmoid(__uint_as_float(l.x << 16)), gate_min),
+                       fmaxf(log_sigmoid(__uint_as_float(l.x & 0xffff0000u)), gate_min),
+                       fmaxf(log_sigmoid(__uint_as_float(l.y << 16)), gate_min),
+                       fmaxf(log_sigmoid(__uint_as_float(l.y & 0xffff0000u)), gate_min));
+    } else {
+      gv = in.g[i];
+    }
     *reinterpret_cast<float4*>(&sm.G[r][cc]) = r < c ? gv : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  if (tid < C) sm.bs[tid] = tid < c ? (kAdd ? 1.f : in.beta) : 0.f;
+  const float bt = kAdd ? 1.f : kRaw ? sigmoid(bf16_to_f32(in.b16)) : in.beta;
+  if (tid < C) sm.bs[tid] = tid < c ? bt : 0.f;
   for (int u = tid; u < C * AP; u += kPrepThreads) (&sm.Tm[0][0])[u] = 0.f;
 }
 
@@ -364,10 +421,10 @@ __device__ __forceinline__ void gram_pair(const PrepSmem& sm, int R, int J, bool
 }
 
 // One workgroup of the prep: items wg, wg + nwg, ... in chunk-major order.
-template <int kGate, bool kAdd>
+template <int kGate, bool kAdd, bool kRaw>
 __device__ __forceinline__ void prep_role(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, int32_t N, int H,
+    const void* __restrict__ g, const void* __restrict__ beta, float gate_min, int32_t N, int H,
     const Workspace& w, const Header& hd, uint8_t* smem_raw, int wg, int nwg) {
   // the additive write (u = v) has no correction: A_kk = 0, so T = I, W = 0, Ut = V
   constexpr bool additive = kAdd;
@@ -380,7 +437,7 @@ __device__ __forceinline__ void prep_role(
 
   PrepIn in;
   ItemPos pos = locate(hd, N, H, item);
-  prep_load<kGate, kAdd>(in, pos, q, k, v, g, beta, H, tid);
+  prep_load<kGate, kAdd, kRaw>(in, pos, q, k, v, g, beta, H, tid);
   // Wait for the first item here, so that inside the loop the wait for the
   // prefetched registers only has to cover the loads, not the stores issued
   // after them.
@@ -390,7 +447,7 @@ __device__ __forceinline__ void prep_role(
     const size_t ci = (size_t)item;  // items are numbered chunk-major: ci = gc * H + h
     const int c = pos.c;
     lds_barrier();  // the previous item is done with LDS
-    prep_stage<kGate, kAdd>(sm, in, c, tid);
+    prep_stage<kGate, kAdd, kRaw>(sm, in, c, tid, gate_min);
     lds_barrier();
 
     // ---- running sum of the log-gates down each channel (four quarters of 16 rows)
@@ -419,7 +476,7 @@ __device__ __forceinline__ void prep_role(
     const int next = item + nwg;
     if (next < total) {
       pos = locate(hd, N, H, next);
-      prep_load<kGate, kAdd>(in, pos, q, k, v, g, beta, H, tid);
+      prep_load<kGate, kAdd, kRaw>(in, pos, q, k, v, g, beta, H, tid);
     }
     lds_barrier();
 
@@ -586,34 +643,50 @@ __device__ __forceinline__ void prep_role(
 }
 
 // LDS use (~153 KiB) allows one workgroup (two waves per SIMD) per CU.
-template <int kGate, bool kAdd>
+template <int kGate, bool kAdd, bool kRaw>
 __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, int32_t N, int H, Workspace w,
-    const int32_t* __restrict__ seq_start, const int32_t* __restrict__ seq_end,
+    const void* __restrict__ g, const void* __restrict__ beta, float gate_min, int32_t N, int H,
+    Workspace w, const int32_t* __restrict__ seq_start, const int32_t* __restrict__ seq_end,
     const int32_t* __restrict__ chunk_off) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   const Header hd{seq_start, seq_end, chunk_off};
-  prep_role<kGate, kAdd>(q, k, v, g, beta, N, H, w, hd, smem_raw, blockIdx.x, gridDim.x);
+  prep_role<kGate, kAdd, kRaw>(q, k, v, g, beta, gate_min, N, H, w, hd, smem_raw, blockIdx.x,
+                               gridDim.x);
 }
 
-template <int kGate, bool kAdd>
-kda_status_t launch_prep(unsigned grid, const void* q, const void* k, const void* v, const float* g,
-                         const float* beta, int32_t N, int H, const Workspace& w,
+template <int kGate, bool kAdd, bool kRaw>
+kda_status_t launch_prep(unsigned grid, const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, float gate_min, int32_t N, int H, const Workspace& w,
                          hipStream_t stream) {
   static bool attr_set = false;  // idempotent; set before the first launch
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep_kernel<kGate, kAdd>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep_kernel<kGate, kAdd, kRaw>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)sizeof(PrepSmem));
     if (e != hipSuccess) return hip_status(e, "hipFuncSetAttribute(prep)");
     attr_set = true;
   }
-  hipLaunchKernelGGL((prep_kernel<kGate, kAdd>), dim3(grid), dim3(kPrepThreads), sizeof(PrepSmem),
-                     stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), g, beta, N, H, w, w.seq_start, w.seq_end,
-                     w.chunk_off);
+  hipLaunchKernelGGL((prep_kernel<kGate, kAdd, kRaw>), dim3(grid), dim3(kPrepThreads),
+                     sizeof(PrepSmem), stream, static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), g, beta,
+                     gate_min, N, H, w, w.seq_start, w.seq_end, w.chunk_off);
   return check_launch("chunk_fwd prep");
+}
+
+template <bool kRaw>
+kda_status_t launch_prep_variant(uint32_t flags, unsigned grid, const void* q, const void* k,
+                                 const void* v, const void* g, const void* beta, float gate_min,
+                                 int32_t N, int H, const Workspace& w, hipStream_t s) {
+  const bool add = flags & KDA_ADDITIVE;
+  if (flags & KDA_GATE_SCALAR)
+    return add ? launch_prep<kGateScalar, true, kRaw>(grid, q, k, v, g, beta, gate_min, N, H, w, s)
+               : launch_prep<kGateScalar, false, kRaw>(grid, q, k, v, g, beta, gate_min, N, H, w, s);
+  if (flags & KDA_GATE_NONE)
+    return add ? launch_prep<kGateNone, true, kRaw>(grid, q, k, v, g, beta, gate_min, N, H, w, s)
+               : launch_prep<kGateNone, false, kRaw>(grid, q, k, v, g, beta, gate_min, N, H, w, s);
+  return add ? launch_prep<kGateChannel, true, kRaw>(grid, q, k, v, g, beta, gate_min, N, H, w, s)
+             : launch_prep<kGateChannel, false, kRaw>(grid, q, k, v, g, beta, gate_min, N, H, w, s);
 }
 
 // ------------------------------------------------------------------ 3. scan
@@ -1444,10 +1517,10 @@ size_t chunk_mfma_workspace_bytes(int H, int32_t T, int32_t N) {
 }
 
 kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, const int32_t* cu,
-                               const void* q, const void* k, const void* v, const float* g,
-                               const float* beta, float* states, int32_t num_slots,
-                               const int32_t* slots, uint32_t flags, void* o, void* workspace,
-                               hipStream_t stream) {
+                               const void* q, const void* k, const void* v, const void* g,
+                               const void* beta, bool raw, float gate_min, float* states,
+                               int32_t num_slots, const int32_t* slots, uint32_t flags, void* o,
+                               void* workspace, hipStream_t stream) {
   const int H = sh->num_heads;
   Workspace w = carve(workspace, T, N, H);
   const size_t cap = nchunks_max(T, N);
@@ -1462,16 +1535,8 @@ kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, cons
   if (st != KDA_OK) return st;
   // persistent prep: one workgroup per CU, each walks items with a grid stride
   const unsigned grid = (unsigned)(items < (size_t)ncu ? items : (size_t)ncu);
-  const bool add = flags & KDA_ADDITIVE;
-  if (flags & KDA_GATE_SCALAR)
-    st = add ? launch_prep<kGateScalar, true>(grid, q, k, v, g, beta, N, H, w, stream)
-             : launch_prep<kGateScalar, false>(grid, q, k, v, g, beta, N, H, w, stream);
-  else if (flags & KDA_GATE_NONE)
-    st = add ? launch_prep<kGateNone, true>(grid, q, k, v, g, beta, N, H, w, stream)
-             : launch_prep<kGateNone, false>(grid, q, k, v, g, beta, N, H, w, stream);
-  else
-    st = add ? launch_prep<kGateChannel, true>(grid, q, k, v, g, beta, N, H, w, stream)
-             : launch_prep<kGateChannel, false>(grid, q, k, v, g, beta, N, H, w, stream);
+  st = raw ? launch_prep_variant<true>(flags, grid, q, k, v, g, beta, gate_min, N, H, w, stream)
+           : launch_prep_variant<false>(flags, grid, q, k, v, g, beta, gate_min, N, H, w, stream);
   if (st != KDA_OK) return st;
   // Few chains: the serial chain of chunk steps is the critical path; each
   // head's state is split over 8 warp-specialised workgroups of 16 columns that

@@ -34,6 +34,22 @@ template <> struct io_traits<uint16_t> {
 
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
 
+// Input preparation from raw projections (heqinghuang "From GPT2 to Kimi3,
+// Explained", section 09: SiLU then unit length for queries and keys, sigmoid
+// write strength; engineermaxxing ch. 06b: the per-channel gate is a sigmoid).
+// Hardware reciprocal, exponential and logarithm (about 1 ulp): their error is
+// far below the bf16 rounding of the prepared operands.
+__device__ __forceinline__ float sigmoid(float x) {
+  return __builtin_amdgcn_rcpf(1.f + fast_exp(-x));
+}
+__device__ __forceinline__ float silu(float x) { return x * sigmoid(x); }
+// log(sigmoid(x)) = min(x, 0) - log(1 + e^-|x|), finite for every finite x
+__device__ __forceinline__ float log_sigmoid(float x) {
+  return fminf(x, 0.f) - __logf(1.f + fast_exp(-fabsf(x)));
+}
+// reciprocal of the normaliser max(norm, 1e-12) applied to a row
+__device__ __forceinline__ float inv_norm(float sumsq) { return rsqrtf(fmaxf(sumsq, 1e-24f)); }
+
 // Sanitised sequence bounds, shared by every prefill kernel: offsets are
 // clamped to [0, T] and made nondecreasing so that no access leaves [0, T).
 __device__ __forceinline__ int clamp_tok(int x, int T) { return x < 0 ? 0 : (x > T ? T : x); }

@@ -31,12 +31,19 @@ namespace kda {
 
 namespace {
 
-template <int DK, int DV, int BLOCK, typename IO, int DVW = DV>
+// kRaw: q and k are raw projections (SiLU, then unit length), the gate and the
+// write strength are bf16 logits (log-decay = max(log sigmoid, gate_min),
+// beta = sigmoid): the input preparation fused into the step.
+template <int DK, int DV, int BLOCK, typename IO, int DVW = DV, bool kRaw = false>
 __global__ __launch_bounds__(BLOCK) void decode_kernel(
     const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ states,
-    int32_t num_slots, const int32_t* __restrict__ slots, uint32_t flags, IO* __restrict__ o,
-    int H) {
+    const void* __restrict__ gp, const void* __restrict__ bp, float gate_min,
+    float* __restrict__ states, int32_t num_slots, const int32_t* __restrict__ slots,
+    uint32_t flags, IO* __restrict__ o, int H) {
+  const float* g = static_cast<const float*>(gp);
+  const float* beta = static_cast<const float*>(bp);
+  const uint16_t* g16 = static_cast<const uint16_t*>(gp);
+  const uint16_t* b16 = static_cast<const uint16_t*>(bp);
   constexpr int NCQ = DVW / 4;     // column quads of this workgroup
   constexpr int RG = BLOCK / NCQ;  // row groups
   constexpr int RPT = DK / RG;     // rows per thread
@@ -72,12 +79,30 @@ __global__ __launch_bounds__(BLOCK) void decode_kernel(
   const bool gate_none = flags & KDA_GATE_NONE, gate_scalar = flags & KDA_GATE_SCALAR;
   const bool additive = flags & KDA_ADDITIVE;
   for (int i = tid; i < DK; i += BLOCK) {
-    ks[i] = io_traits<IO>::load(k, tk + i);
-    qs[i] = io_traits<IO>::load(q, tk + i);
-    as[i] = gate_none ? 1.f : fast_exp(gate_scalar ? g[bh] : g[tk + i]);
+    const float kv = io_traits<IO>::load(k, tk + i), qv = io_traits<IO>::load(q, tk + i);
+    ks[i] = kRaw ? silu(kv) : kv;
+    qs[i] = kRaw ? silu(qv) : qv;
+    const size_t gi = gate_scalar ? (size_t)bh : tk + i;
+    as[i] = gate_none ? 1.f
+          : kRaw      ? fast_exp(fmaxf(log_sigmoid(bf16_to_f32(g16[gi])), gate_min))
+                      : fast_exp(g[gi]);
   }
   for (int i = tid; i < DVW; i += BLOCK) vs[i] = io_traits<IO>::load(v, tv + c_base + i);
   __syncthreads();
+  if (kRaw) {  // unit-length q and k (the first wave), seen by all after the barrier
+    if (tid < 64) {
+      float sk = 0.f, sq = 0.f;
+      for (int i = tid; i < DK; i += 64) { sk += ks[i] * ks[i]; sq += qs[i] * qs[i]; }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        sk += __shfl_xor(sk, off, 64);
+        sq += __shfl_xor(sq, off, 64);
+      }
+      const float ik = inv_norm(sk), iq = inv_norm(sq);
+      for (int i = tid; i < DK; i += 64) { ks[i] *= ik; qs[i] *= iq; }
+    }
+    __syncthreads();
+  }
 
   // k . q, reduced by the first wave
   if (tid < 64) {
@@ -115,7 +140,7 @@ __global__ __launch_bounds__(BLOCK) void decode_kernel(
     const int c0 = 4 * cq;
     float u0 = vs[c0 + 0], u1 = vs[c0 + 1], u2 = vs[c0 + 2], u3 = vs[c0 + 3];
     if (!additive) {  // the correction against the faded read
-      const float bt = beta[bh];
+      const float bt = kRaw ? sigmoid(bf16_to_f32(b16[bh])) : beta[bh];
       u0 = bt * (u0 - W.x); u1 = bt * (u1 - W.y); u2 = bt * (u2 - W.z); u3 = bt * (u3 - W.w);
     }
     us[c0 + 0] = u0; us[c0 + 1] = u1; us[c0 + 2] = u2; us[c0 + 3] = u3;
@@ -140,25 +165,33 @@ __global__ __launch_bounds__(BLOCK) void decode_kernel(
 
 template <int D, int BLOCK, typename IO, int DVW = D>
 kda_status_t launch_typed(int32_t batch, int H, const void* q, const void* k, const void* v,
-                          const float* g, const float* beta, float* states, int32_t num_slots,
-                          const int32_t* slots, uint32_t flags, void* o, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<D, D, BLOCK, IO, DVW>), dim3((unsigned)batch * H * (D / DVW)),
-                     dim3(BLOCK), 0,
-                     stream, static_cast<const IO*>(q), static_cast<const IO*>(k),
-                     static_cast<const IO*>(v), g, beta, states, num_slots, slots, flags,
-                     static_cast<IO*>(o), H);
+                          const void* g, const void* beta, bool raw, float gate_min, float* states,
+                          int32_t num_slots, const int32_t* slots, uint32_t flags, void* o,
+                          hipStream_t stream) {
+  const dim3 grid((unsigned)batch * H * (D / DVW));
+  if (raw)
+    hipLaunchKernelGGL((decode_kernel<D, D, BLOCK, IO, DVW, true>), grid, dim3(BLOCK), 0, stream,
+                       static_cast<const IO*>(q), static_cast<const IO*>(k),
+                       static_cast<const IO*>(v), g, beta, gate_min, states, num_slots, slots,
+                       flags, static_cast<IO*>(o), H);
+  else
+    hipLaunchKernelGGL((decode_kernel<D, D, BLOCK, IO, DVW, false>), grid, dim3(BLOCK), 0, stream,
+                       static_cast<const IO*>(q), static_cast<const IO*>(k),
+                       static_cast<const IO*>(v), g, beta, gate_min, states, num_slots, slots,
+                       flags, static_cast<IO*>(o), H);
   return check_launch("decode_step");
 }
 
 template <typename IO>
 kda_status_t launch_io(int d, int32_t batch, int H, const void* q, const void* k, const void* v,
-                       const float* g, const float* beta, float* states, int32_t num_slots,
-                       const int32_t* slots, uint32_t flags, void* o, hipStream_t stream) {
+                       const void* g, const void* beta, bool raw, float gate_min, float* states,
+                       int32_t num_slots, const int32_t* slots, uint32_t flags, void* o,
+                       hipStream_t stream) {
   switch (d) {
-    case 16: return launch_typed<16, 64, IO>(batch, H, q, k, v, g, beta, states, num_slots, slots, flags, o, stream);
-    case 32: return launch_typed<32, 64, IO>(batch, H, q, k, v, g, beta, states, num_slots, slots, flags, o, stream);
-    case 64: return launch_typed<64, 128, IO>(batch, H, q, k, v, g, beta, states, num_slots, slots, flags, o, stream);
-    case 128: return launch_typed<128, 256, IO, 64>(batch, H, q, k, v, g, beta, states, num_slots, slots, flags, o, stream);
+    case 16: return launch_typed<16, 64, IO>(batch, H, q, k, v, g, beta, raw, gate_min, states, num_slots, slots, flags, o, stream);
+    case 32: return launch_typed<32, 64, IO>(batch, H, q, k, v, g, beta, raw, gate_min, states, num_slots, slots, flags, o, stream);
+    case 64: return launch_typed<64, 128, IO>(batch, H, q, k, v, g, beta, raw, gate_min, states, num_slots, slots, flags, o, stream);
+    case 128: return launch_typed<128, 256, IO, 64>(batch, H, q, k, v, g, beta, raw, gate_min, states, num_slots, slots, flags, o, stream);
     default: return KDA_ERR_UNSUPPORTED;
   }
 }
@@ -170,14 +203,15 @@ bool decode_supported(int dk, int dv) {
 }
 
 kda_status_t launch_decode(const kda_shape_t* sh, int32_t batch, const void* q, const void* k,
-                           const void* v, const float* g, const float* beta, float* states,
-                           int32_t num_slots, const int32_t* slots, uint32_t flags, void* o,
-                           hipStream_t stream) {
+                           const void* v, const void* g, const void* beta, bool raw,
+                           float gate_min, float* states, int32_t num_slots, const int32_t* slots,
+                           uint32_t flags, void* o, hipStream_t stream) {
   if (sh->io_dtype == KDA_BF16)
-    return launch_io<uint16_t>(sh->dk, batch, sh->num_heads, q, k, v, g, beta, states, num_slots,
-                               slots, flags, o, stream);
-  return launch_io<float>(sh->dk, batch, sh->num_heads, q, k, v, g, beta, states, num_slots,
-                          slots, flags, o, stream);
+    return launch_io<uint16_t>(sh->dk, batch, sh->num_heads, q, k, v, g, beta, raw, gate_min,
+                               states, num_slots, slots, flags, o, stream);
+  if (raw) return KDA_ERR_UNSUPPORTED;  // raw projections are bf16
+  return launch_io<float>(sh->dk, batch, sh->num_heads, q, k, v, g, beta, false, gate_min, states,
+                          num_slots, slots, flags, o, stream);
 }
 
 }  // namespace kda

@@ -182,6 +182,43 @@ kda_status_t kda_decode_step_ex(const kda_shape_t* shape, int32_t batch, const v
                                 const int32_t* state_slots, uint32_t flags, void* o,
                                 void* stream);
 
+/* Prefill and decode from the raw projection outputs, with the input
+ * preparation fused into the path (heqinghuang section 09: q and k pass through
+ * SiLU and are scaled to unit length, beta is a sigmoid; engineermaxxing
+ * ch. 06b: the per-channel decay is a sigmoid of its own projection; dev.to
+ * block 5: K3 bounds the decay parameterisation for bf16 stability):
+ *
+ *   q = normalize(silu(q_raw)),  k = normalize(silu(k_raw))   over dk, per (token, head),
+ *                                normalize(x) = x / max(|x|_2, 1e-12)
+ *   beta = sigmoid(beta_logits)                               per (token, head)
+ *   g = log(alpha) = max(log(sigmoid(gate_logits)), gate_min)  per key channel
+ *
+ * then exactly kda_chunk_fwd / kda_decode_step_ex on (q, k, v, g, beta).
+ * Reading bf16 logits instead of fp32 log-decays moves 1,282 instead of 1,540
+ * bytes per token and head.
+ *
+ * q_raw, k_raw  device bf16 [tokens, H, dk];  v: device bf16 [tokens, H, dv].
+ * gate_logits   device bf16 [tokens, H, dk] (8-byte aligned); [tokens, H] with
+ *               KDA_GATE_SCALAR; unused (may be NULL) with KDA_GATE_NONE.
+ * beta_logits   device bf16 [tokens, H]; unused (may be NULL) with KDA_ADDITIVE.
+ * gate_min      floor of the log-decay (-INFINITY: none; NaN is an error).
+ * Everything else (flags, states, slots, o, workspace, errors) as in
+ * kda_chunk_fwd / kda_decode_step_ex.  Supported: io_dtype KDA_BF16; the
+ * prefill for dk = dv = 128 with chunk 64 (else KDA_ERR_UNSUPPORTED), the
+ * decode for the dims kda_decode_step supports. */
+kda_status_t kda_chunk_fwd_raw(const kda_shape_t* shape, int32_t chunk, int32_t total_tokens,
+                               int32_t num_seqs, const int32_t* cu_seqlens, const void* q_raw,
+                               const void* k_raw, const void* v, const void* gate_logits,
+                               const void* beta_logits, float gate_min, float* states,
+                               int32_t num_slots, const int32_t* state_slots, uint32_t flags,
+                               void* o, void* workspace, size_t workspace_bytes, void* stream);
+
+kda_status_t kda_decode_step_raw(const kda_shape_t* shape, int32_t batch, const void* q_raw,
+                                 const void* k_raw, const void* v, const void* gate_logits,
+                                 const void* beta_logits, float gate_min, float* states,
+                                 int32_t num_slots, const int32_t* state_slots, uint32_t flags,
+                                 void* o, void* stream);
+
 /* Zero every state of a pool [num_slots, H, dk, dv] (fp32). */
 kda_status_t kda_state_init(const kda_shape_t* shape, float* states, int32_t num_slots,
                             void* stream);

@@ -121,6 +121,16 @@ def test_validation_errors_before_any_launch(lib):
     assert b"g is NULL" in lib.kda_last_error()
     assert dex(8 | 16, None, None, 2) == 1                           # g, beta not read: next check
     assert b"num_slots" in lib.kda_last_error()
+    # raw projections: bf16 only, the MFMA prefill shape only, gate_min not NaN
+    raw = lambda shape, chunk, gmin: lib.kda_chunk_fwd_raw(
+        ctypes.byref(shape), chunk, 128, 1, fake, fake, fake, fake, fake, fake, gmin, None, 0,
+        None, 0, fake, None, 0, None)
+    assert raw(_shape(16, 128, 128, 0), 64, 0.0) == 2               # fp32 io
+    assert raw(sh, 32, 0.0) == 2                                     # chunk 32
+    assert raw(sh, 64, float("nan")) == 1
+    assert raw(sh, 64, float("-inf")) == 3                           # valid up to the workspace
+    assert lib.kda_decode_step_raw(ctypes.byref(_shape(32, 64, 64, 0)), 4, fake, fake, fake, fake,
+                                   fake, 0.0, fake, 4, None, 0, fake, None) == 2
     # state helpers
     assert lib.kda_state_init(ctypes.byref(sh), None, 3, None) == 1
     assert lib.kda_state_load(ctypes.byref(sh), fake, 2, None, 3, fake, None) == 1
