@@ -19,7 +19,7 @@ __all__ = [
     "KdaError", "load_library", "kda_abi_version", "kda_chunk_fwd", "kda_chunk_fwd_supported",
     "kda_chunk_fwd_workspace_bytes", "kda_decode_step", "kda_state_init", "kda_state_load",
     "kda_state_store", "KDA_READ_INITIAL_STATE", "KDA_WRITE_FINAL_STATE", "kda_chunk_fwd_raw",
-    "kda_decode_step_raw",
+    "kda_decode_step_raw", "kda_state_affine",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -81,6 +81,8 @@ def load_library(path: str | None = None):
     lib.kda_chunk_fwd_raw.restype = ctypes.c_int
     lib.kda_decode_step_raw.argtypes = [SH, I32, P, P, P, P, P, F32, P, I32, P, U32, P, P]
     lib.kda_decode_step_raw.restype = ctypes.c_int
+    lib.kda_state_affine.argtypes = [SH, I32, P, P, P, P, P]
+    lib.kda_state_affine.restype = ctypes.c_int
     lib.kda_state_init.argtypes = [SH, P, I32, P]
     lib.kda_state_init.restype = ctypes.c_int
     lib.kda_state_load.argtypes = [SH, P, I32, P, I32, P, P]
@@ -325,6 +327,25 @@ def kda_decode_step_raw(q_raw, k_raw, v, gate_logits, beta_logits, states, gate_
                                    _ptr(states), states.shape[0], _ptr(state_slots),
                                    _variant_flags(gate, additive), _ptr(o), _stream(stream)))
     return o
+
+
+def kda_state_affine(M, S_in, B, out=None, stream=None):
+    """out[i] = M[i] @ S_in[i] + B[i] per head (see kda_state_affine in include/kda.h).
+
+    M: fp32 [n, H, dk, dk]; S_in, B: fp32 [n, H, dk, dv].  ``out`` may be B."""
+    lib = load_library()
+    n, H, dk, dv = S_in.shape
+    _need(M, "M", (n, H, dk, dk), torch.float32)
+    _need(S_in, "S_in", (n, H, dk, dv), torch.float32)
+    _need(B, "B", (n, H, dk, dv), torch.float32)
+    if out is None:
+        out = torch.empty_like(B)
+    else:
+        _need(out, "out", (n, H, dk, dv), torch.float32)
+    sh = _Shape(H, dk, dv, KDA_FP32)
+    _check(lib.kda_state_affine(ctypes.byref(sh), n, _ptr(M), _ptr(S_in), _ptr(B), _ptr(out),
+                                _stream(stream)))
+    return out
 
 
 def _pool_shape(states):

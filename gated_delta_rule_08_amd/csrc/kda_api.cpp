@@ -16,6 +16,9 @@ kda_status_t launch_state_init(float* states, size_t n_floats, hipStream_t strea
 kda_status_t launch_state_copy(bool to_pool, float* states, int32_t num_slots,
                                const int32_t* slots, int32_t n, float* dense,
                                size_t per_state_floats, hipStream_t stream);
+kda_status_t launch_state_affine(int32_t n, int H, int dk, int dv, const float* M,
+                                 const float* S_in, const float* B, float* S_out,
+                                 hipStream_t stream);
 bool decode_supported(int dk, int dv);
 kda_status_t launch_decode(const kda_shape_t* sh, int32_t batch, const void* q, const void* k,
                            const void* v, const void* g, const void* beta, bool raw,
@@ -318,6 +321,30 @@ kda_status_t kda_state_store(const kda_shape_t* sh, const float* states, int32_t
                              const int32_t* slots, int32_t n, float* dst, void* stream) {
   return state_copy("kda_state_store", false, sh, const_cast<float*>(states), num_slots, slots, n,
                     dst, stream);
+}
+
+kda_status_t kda_state_affine(const kda_shape_t* sh, int32_t n, const float* M,
+                              const float* S_in, const float* B, float* S_out, void* stream) {
+  const char* W = "kda_state_affine";
+  kda_status_t st = check_shape(sh, W);
+  if (st != KDA_OK) return st;
+  if (n < 0) return invalid("%s: n must be >= 0", W);
+  if (sh->dk > 256) return unsupported(W, sh, 0);
+  if (n == 0) return KDA_OK;
+  if (!M || !S_in || !B || !S_out) return invalid("%s: a tensor pointer is NULL", W);
+  if (!aligned(M, 4) || !aligned(S_in, 4) || !aligned(B, 4) || !aligned(S_out, 4))
+    return invalid("%s: tensors must be 4-byte aligned", W);
+  const size_t per = (size_t)sh->num_heads * sh->dk * sh->dv * sizeof(float);
+  const size_t perm = (size_t)sh->num_heads * sh->dk * sh->dk * sizeof(float);
+  const uintptr_t o0 = reinterpret_cast<uintptr_t>(S_out), o1 = o0 + (size_t)n * per;
+  auto overlaps = [&](const void* p, size_t bytes) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), a1 = a0 + (size_t)n * bytes;
+    return a0 < o1 && o0 < a1;
+  };
+  if (overlaps(M, perm) || overlaps(S_in, per) || (B != S_out && overlaps(B, per)))
+    return invalid("%s: S_out overlaps M or S_in (only S_out == B is allowed)", W);
+  return launch_state_affine(n, sh->num_heads, sh->dk, sh->dv, M, S_in, B, S_out,
+                             static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -39,6 +39,42 @@ __global__ __launch_bounds__(kThreads) void gather_scatter_kernel(
   }
 }
 
+// S_out = M S_in + B for one (entry, head) and a block of kAffCols columns:
+// the effect of a segment on its incoming state is affine, and composing it is
+// the exchange step of context-parallel prefill (heqinghuang "From GPT2 to
+// Kimi3, Explained", section 10: the state is the only thing one chunk passes to
+// the next; a run of chunks passes it through a product of transition matrices
+// plus the state written inside it).  fp32 FMAs in key order; the S_in block is
+// staged in LDS, rows of M are read by all column lanes at once.
+constexpr int kAffCols = 32;
+__global__ __launch_bounds__(kThreads) void affine_kernel(const float* __restrict__ M,
+                                                          const float* __restrict__ S_in,
+                                                          const float* B, float* S_out, int dk,
+                                                          int dv, int col_blocks) {
+  extern __shared__ float sin_blk[];  // [dk][kAffCols]
+  const int cb = blockIdx.x % col_blocks;
+  const size_t eh = blockIdx.x / col_blocks;  // entry * H + head
+  const int c0 = cb * kAffCols;
+  const int ncols = min(kAffCols, dv - c0);
+  const float* Sm = S_in + eh * (size_t)dk * dv;
+  const float* Mm = M + eh * (size_t)dk * dk;
+  for (int e = threadIdx.x; e < dk * kAffCols; e += kThreads) {
+    const int r = e / kAffCols, c = e - r * kAffCols;
+    sin_blk[e] = c < ncols ? Sm[(size_t)r * dv + c0 + c] : 0.f;
+  }
+  __syncthreads();
+  const int c = threadIdx.x % kAffCols;
+  for (int r = threadIdx.x / kAffCols; r < dk; r += kThreads / kAffCols) {
+    float acc = 0.f;
+    const float* mrow = Mm + (size_t)r * dk;
+    for (int kk = 0; kk < dk; ++kk) acc = fmaf(mrow[kk], sin_blk[kk * kAffCols + c], acc);
+    if (c < ncols) {
+      const size_t i = eh * (size_t)dk * dv + (size_t)r * dv + c0 + c;
+      S_out[i] = acc + B[i];
+    }
+  }
+}
+
 int grid_for(size_t n4) {
   size_t blocks = (n4 + kThreads - 1) / kThreads;
   if (blocks > 8192) blocks = 8192;
@@ -53,6 +89,16 @@ kda_status_t launch_state_init(float* states, size_t n_floats, hipStream_t strea
   hipLaunchKernelGGL(zero_kernel, dim3(grid_for(n4)), dim3(kThreads), 0, stream,
                      reinterpret_cast<float4*>(states), n4);
   return check_launch("state_init");
+}
+
+kda_status_t launch_state_affine(int32_t n, int H, int dk, int dv, const float* M,
+                                 const float* S_in, const float* B, float* S_out,
+                                 hipStream_t stream) {
+  const int col_blocks = (dv + kAffCols - 1) / kAffCols;
+  hipLaunchKernelGGL(affine_kernel, dim3((unsigned)((size_t)n * H * col_blocks)), dim3(kThreads),
+                     (size_t)dk * kAffCols * sizeof(float), stream, M, S_in, B, S_out, dk, dv,
+                     col_blocks);
+  return check_launch("state_affine");
 }
 
 kda_status_t launch_state_copy(bool to_pool, float* states, int32_t num_slots,

@@ -219,6 +219,27 @@ kda_status_t kda_decode_step_raw(const kda_shape_t* shape, int32_t batch, const 
                                  int32_t num_slots, const int32_t* state_slots, uint32_t flags,
                                  void* o, void* stream);
 
+/* Composition of a segment's effect on its incoming state, for context-parallel
+ * prefill of one long sequence split into segments (one per GPU):
+ *
+ *   S_out[i] = M[i] S_in[i] + B[i]      for i < n and every head,
+ *
+ * where a segment's M is its state-transition matrix, prod_t (I - beta_t k_t
+ * k_t^T) Diag(alpha_t), and B the state it writes from the zero state; each
+ * segment is affine in its incoming state because the state is all one chunk
+ * passes to the next (heqinghuang section 10; engineermaxxing ch. 04f).  Both
+ * come from kda_chunk_fwd on the segment (KDA_WRITE_FINAL_STATE): M with v = 0
+ * from the identity (KDA_READ_INITIAL_STATE; needs dk = dv), B from the zero
+ * state.  An exclusive scan of the segments' maps with this call gives every
+ * segment its incoming state for the final kda_chunk_fwd; across GPUs the maps
+ * (dk x dk + dk x dv fp32 per head) are what is exchanged.
+ *
+ * M     device fp32 dense [n, H, dk, dk];
+ * S_in, B, S_out  device fp32 dense [n, H, dk, dv].  S_out may be B (in place)
+ *       but must not overlap M or S_in.  fp32 arithmetic.  Supported: dk <= 256. */
+kda_status_t kda_state_affine(const kda_shape_t* shape, int32_t n, const float* M,
+                              const float* S_in, const float* B, float* S_out, void* stream);
+
 /* Zero every state of a pool [num_slots, H, dk, dv] (fp32). */
 kda_status_t kda_state_init(const kda_shape_t* shape, float* states, int32_t num_slots,
                             void* stream);

@@ -135,3 +135,16 @@ def test_validation_errors_before_any_launch(lib):
     assert lib.kda_state_init(ctypes.byref(sh), None, 3, None) == 1
     assert lib.kda_state_load(ctypes.byref(sh), fake, 2, None, 3, fake, None) == 1
     assert lib.kda_state_store(ctypes.byref(sh), fake, 4, None, 0, None, None) == 0
+    # affine composition: n, size, NULL and overlap checks
+    aff = lambda shape, n, M, S, B, O: lib.kda_state_affine(ctypes.byref(shape), n, M, S, B, O,
+                                                             None)
+    per = 16 * 128 * 128 * 4
+    assert aff(sh, -1, fake, fake, fake, fake) == 1
+    assert aff(sh, 0, None, None, None, None) == 0                   # empty: no-op
+    assert aff(_shape(16, 512, 512, 0), 1, fake, fake, fake, fake) == 2
+    assert aff(sh, 1, None, fake, fake, fake) == 1
+    assert aff(sh, 1, P(0x10000), P(0x10000 + 2 * per), P(0x10000 + 4 * per),
+               P(0x10000 + 2 * per + 64)) == 1                       # S_out inside S_in
+    assert b"overlaps" in lib.kda_last_error()
+    assert aff(sh, 2, P(0x10000), P(0x10000 + 8 * per), P(0x10000 + 4 * per),
+               P(0x10000 + 4 * per + 4)) == 1                        # partial overlap with B

@@ -485,3 +485,38 @@ def test_prepare_scalar_gate_broadcasts():
     for c in range(4):
         assert np.array_equal(g[..., c], g[..., 0])
     assert g[2, 1, 3] == pytest.approx(math.log(1.0 / (1.0 + math.exp(-a[2, 1]))), rel=1e-14)
+
+
+# ------------------------------------------------- affine maps of segments (context parallelism)
+
+def test_segment_is_an_affine_map_of_its_incoming_state():
+    """A segment acts on its incoming state as S_out = M S_in + B, with M the run of the
+    segment with v = 0 from the identity (dk = dv) and B its run from the zero state; the
+    maps of consecutive segments compose, so a sequence split into segments gives the final
+    state of the unsplit run (the exchange step of context-parallel prefill)."""
+    rng = np.random.default_rng(17)
+    T, H, d, P = 48, 2, 8, 3
+    p = workloads.random_problem(rng, T, H, d, d)
+    s0 = rng.standard_normal((1, H, d, d))
+    _, s_ref = oracle.run(p["q"], p["k"], p["v"], p["g"], p["beta"], np.array([0, T], np.int32),
+                          s0=s0)
+    bounds = [0, 11, 30, T]
+    eye = np.broadcast_to(np.eye(d), (P, H, d, d)).copy()
+    cu = np.array(bounds, np.int32)
+    _, M = oracle.run(p["q"], p["k"], np.zeros_like(p["v"]), p["g"], p["beta"], cu, s0=eye)
+    _, B = oracle.run(p["q"], p["k"], p["v"], p["g"], p["beta"], cu, s0=np.zeros((P, H, d, d)))
+    s = s0[0]
+    for i in range(P):
+        s = M[i] @ s + B[i]
+    np.testing.assert_allclose(s, s_ref[0], rtol=0, atol=1e-12 * np.abs(s_ref).max())
+    # the same holds for the additive write
+    _, s_ref = oracle.run(p["q"], p["k"], p["v"], p["g"], p["beta"], np.array([0, T], np.int32),
+                          s0=s0, mode=oracle.MODE_ADDITIVE)
+    _, M = oracle.run(p["q"], p["k"], np.zeros_like(p["v"]), p["g"], p["beta"], cu, s0=eye,
+                      mode=oracle.MODE_ADDITIVE)
+    _, B = oracle.run(p["q"], p["k"], p["v"], p["g"], p["beta"], cu, s0=np.zeros((P, H, d, d)),
+                      mode=oracle.MODE_ADDITIVE)
+    s = s0[0]
+    for i in range(P):
+        s = M[i] @ s + B[i]
+    np.testing.assert_allclose(s, s_ref[0], rtol=0, atol=1e-12 * np.abs(s_ref).max())
