@@ -46,6 +46,9 @@ def _load():
         lib.kda_oracle_run.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(ctypes.c_int32)] + \
             [dp] * 8 + [ctypes.c_int]
         lib.kda_oracle_run.restype = ctypes.c_int
+        lib.kda_oracle_bwd.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(ctypes.c_int32)] + \
+            [dp] * 14 + [ctypes.c_int]
+        lib.kda_oracle_bwd.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -102,6 +105,46 @@ def run(q, k, v, g, beta, cu_seqlens=None, s0=None, mode: int = MODE_DELTA,
     if rc != 0:
         raise RuntimeError("kda_oracle_run failed")
     return o, sf
+
+
+def run_bwd(q, k, v, g, beta, d_o, cu_seqlens=None, s0=None, ds_final=None,
+            mode: int = MODE_DELTA, nthreads: int | None = None):
+    """Gradients of a scalar loss through the recurrence (reverse-mode, token by
+    token; the derivation is in the header of ``kda_oracle.c``).
+
+    d_o: dL/do [T, H, dv]; ds_final: dL/dS_final [N, H, dk, dv] or None (zero).
+    Returns a dict of float64 arrays: dq, dk, dg [T, H, dk], dv [T, H, dv],
+    dbeta [T, H], ds0 [N, H, dk, dv] (dL/dS0).
+    """
+    lib = _load()
+    q, k, v, g, beta, d_o = map(_f64, (q, k, v, g, beta, d_o))
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    assert k.shape == (T, H, dk) and g.shape == (T, H, dk)
+    assert v.shape == (T, H, dv) and beta.shape == (T, H) and d_o.shape == (T, H, dv)
+    if cu_seqlens is None:
+        cu = np.array([0, T], dtype=np.int32)
+    else:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    N = len(cu) - 1
+    assert cu[0] == 0 and cu[-1] == T and np.all(np.diff(cu) >= 0)
+    s0, ds_final = _f64(s0), _f64(ds_final)
+    for a in (s0, ds_final):
+        if a is not None:
+            assert a.shape == (N, H, dk, dv)
+    out = dict(dq=np.zeros((T, H, dk)), dk=np.zeros((T, H, dk)), dv=np.zeros((T, H, dv)),
+               dg=np.zeros((T, H, dk)), dbeta=np.zeros((T, H)), ds0=np.zeros((N, H, dk, dv)))
+    if nthreads is None:
+        nthreads = min(16, os.cpu_count() or 1)
+    rc = lib.kda_oracle_bwd(int(mode), H, dk, dv, N,
+                            cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0),
+                            _ptr(d_o), _ptr(ds_final), _ptr(out["dq"]), _ptr(out["dk"]),
+                            _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
+                            _ptr(out["ds0"]), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_bwd failed")
+    return out
 
 
 def decode(q, k, v, g, beta, s):

@@ -71,3 +71,87 @@ def chunk_forward(q, k, v, g, beta, C, cu_seqlens=None, s0=None):
             o[sl, h], s[n, h] = chunk_forward_head(q[sl, h], k[sl, h], v[sl, h], g[sl, h],
                                                    beta[sl, h], C, S0)
     return o, s
+
+
+def chunk_backward_head(q, k, v, g, beta, C, d_o, S0=None, dS_final=None):
+    """Gradients through the chunk algebra above, chunk by chunk (fp64 mirror of
+    the GPU backward).  Per chunk, with S the incoming state, S' the outgoing one
+    and dS' its cotangent (from the later chunks):
+
+      reverse state pass   dU  = A_qk^T dO + Kd dS'
+                           dS  = (Q*Gam)^T dO + Diag(Gam_c) dS' - W^T dU
+      solve                U = (I + A_kk)^-1 R with R = Diag(beta)(V - (K*Gam) S), so
+                           dR = T^T dU,  dA_kk = -dR U^T (strictly lower)
+      R                    dV = Diag(beta) dR,  Z = dR S^T,  d(K*Gam) = -Diag(beta) Z,
+                           dbeta += rowsum(dR * V) - rowsum((K*Gam) * Z)
+      A_kk = Diag(beta) M  dbeta += rowsum(dA_kk * M),  dM = Diag(beta) dA_kk
+      A_qk, M (decayed)    dA_qk = tril(dO U^T); each decayed product
+                           X[r, j] = sum_c a_r[c] b_j[c] exp(G_r[c] - G_j[c]) sends
+                           dX[r, j] b_j exp(G_r - G_j) to a_r, dX[r, j] a_r exp(..) to b_j,
+                           and +a_r * (that) to dG_r, -b_j * (..) to dG_j
+      O, S' (state side)   d(Q*Gam) = dO S^T, dKd = U dS'^T, dGam_c = rowsum(dS' * S)
+      gates                G = cumsum(g), so dg = reverse cumsum of dG
+    Returns dq, dk, dv, dg [L, d], dbeta [L], dS0 [dk, dv].
+    """
+    q, k, v, g, beta, d_o = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g, beta, d_o))
+    L, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    starts = list(range(0, L, C))
+    S_in = []
+    for s in starts:   # forward state pass: the state entering every chunk
+        S_in.append(S.copy())
+        e = min(s + C, L)
+        _, S = chunk_forward_head(q[s:e], k[s:e], v[s:e], g[s:e], beta[s:e], C, S)
+    dq, dk_, dv_, dg = (np.zeros_like(a) for a in (q, k, v, g))
+    db = np.zeros(L)
+    dS = np.zeros((dk, dv)) if dS_final is None else np.array(dS_final, dtype=np.float64)
+    for ci in reversed(range(len(starts))):
+        s = starts[ci]
+        e = min(s + C, L)
+        Q, K, V, b, dO, Sc = q[s:e], k[s:e], v[s:e], beta[s:e], d_o[s:e], S_in[ci]
+        G = np.cumsum(g[s:e], axis=0)
+        c = e - s
+        lower = np.tril(np.ones((c, c), dtype=bool))
+        strict = np.tril(np.ones((c, c), dtype=bool), -1)
+        E = np.exp(np.where(lower[:, :, None], G[:, None, :] - G[None, :, :], -np.inf))
+        M = np.where(strict, np.einsum("rc,jc,rjc->rj", K, K, E), 0.0)
+        A_qk = np.where(lower, np.einsum("rc,jc,rjc->rj", Q, K, E), 0.0)
+        T = np.linalg.inv(np.eye(c) + b[:, None] * M)
+        Gam = np.exp(G)
+        Kg = K * Gam
+        U = T @ (b[:, None] * (V - Kg @ Sc))
+        Kd = K * np.exp(G[-1] - G)
+        # reverse state pass
+        dU = A_qk.T @ dO + Kd @ dS
+        dS_in = (Q * Gam).T @ dO + Gam[-1][:, None] * dS - (T @ (b[:, None] * Kg)).T @ dU
+        # gradients inside the chunk
+        dR = T.T @ dU
+        dA_kk = np.where(strict, -dR @ U.T, 0.0)
+        Z = dR @ Sc.T
+        dv_[s:e] = b[:, None] * dR
+        db[s:e] = (dR * V).sum(1) - (Kg * Z).sum(1) + (dA_kk * M).sum(1)
+        dM = b[:, None] * dA_kk
+        dA_qk = np.where(lower, dO @ U.T, 0.0)
+        dQg = dO @ Sc.T
+        dKg = -b[:, None] * Z
+        dKd = U @ dS.T
+        dGc = (dS * Sc).sum(1) * Gam[-1]
+        dQ = dQg * Gam
+        dK = dKg * Gam + dKd * np.exp(G[-1] - G)
+        dG = dQg * Q * Gam + dKg * K * Gam - dKd * Kd
+        dG[-1] += (dKd * Kd).sum(0) + dGc
+        # decayed products: A_qk (a = q, b = k) and M (a = k, b = k)
+        for dX, A_side in ((dA_qk, Q), (dM, K)):
+            row = np.einsum("rj,jc,rjc->rc", dX, K, E)     # to a_r
+            col = np.einsum("rj,rc,rjc->jc", dX, A_side, E)  # to b_j = k_j
+            if A_side is Q:
+                dQ += row
+            else:
+                dK += row
+            dK += col
+            dG += A_side * row - K * col
+        dq[s:e], dk_[s:e] = dQ, dK
+        dg[s:e] = np.cumsum(dG[::-1], axis=0)[::-1]
+        dS = dS_in
+    return dq, dk_, dv_, dg, db, dS

@@ -520,3 +520,110 @@ def test_segment_is_an_affine_map_of_its_incoming_state():
     for i in range(P):
         s = M[i] @ s + B[i]
     np.testing.assert_allclose(s, s_ref[0], rtol=0, atol=1e-12 * np.abs(s_ref).max())
+
+
+# ---------------------------------------------------------------- gradients
+# The pages stop at the forward pass, so the backward oracle is a derivation;
+# it is pinned to finite differences of the forward oracle, and to closed forms
+# of the gradient in the cases where the recurrence has one.
+
+def _bwd_problem(seed, T, H, dk, dv, N_cu=None, gate=-0.3):
+    rng = np.random.default_rng(seed)
+    q, k = rng.standard_normal((T, H, dk)), rng.standard_normal((T, H, dk))
+    g = gate * np.abs(rng.standard_normal((T, H, dk)))
+    v = rng.standard_normal((T, H, dv))
+    beta = rng.random((T, H))
+    cu = np.array([0, T] if N_cu is None else N_cu, dtype=np.int32)
+    N = len(cu) - 1
+    s0 = rng.standard_normal((N, H, dk, dv))
+    do = rng.standard_normal((T, H, dv))
+    dsf = rng.standard_normal((N, H, dk, dv))
+    return dict(q=q, k=k, v=v, g=g, beta=beta, cu=cu, s0=s0, do=do, dsf=dsf)
+
+
+def _loss(p, mode, **over):
+    a = dict(p, **over)
+    o, s = oracle.run(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], s0=a["s0"], mode=mode)
+    return float((o * a["do"]).sum() + (s * a["dsf"]).sum())
+
+
+@pytest.mark.parametrize("mode", [oracle.MODE_DELTA, oracle.MODE_ADDITIVE])
+def test_gradients_match_central_differences(mode):
+    """Every input's gradient, entry by entry, against (L(x+h) - L(x-h)) / 2h."""
+    p = _bwd_problem(3, 9, 2, 3, 4, N_cu=[0, 4, 4, 9])   # a zero-length sequence in the middle
+    r = oracle.run_bwd(p["q"], p["k"], p["v"], p["g"], p["beta"], p["do"], p["cu"], s0=p["s0"],
+                       ds_final=p["dsf"], mode=mode)
+    h = 1e-6
+    for name, key in [("q", "dq"), ("k", "dk"), ("v", "dv"), ("g", "dg"), ("beta", "dbeta"),
+                      ("s0", "ds0")]:
+        x = p[name]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            fd[idx] = (_loss(p, mode, **{name: xp}) - _loss(p, mode, **{name: xm})) / (2 * h)
+        assert np.abs(fd - r[key]).max() <= 1e-7 * max(1.0, np.abs(fd).max()), name
+    if mode == oracle.MODE_ADDITIVE:
+        assert not r["dbeta"].any()
+
+
+def test_gradient_directional_derivative_across_checkpoints():
+    """Longer ragged sequences (the backward recomputes states from copies taken
+    every 64 tokens): <grad, d> equals the central difference along d."""
+    p = _bwd_problem(4, 230, 2, 8, 6, N_cu=[0, 70, 200, 230], gate=-0.05)
+    r = oracle.run_bwd(p["q"], p["k"], p["v"], p["g"], p["beta"], p["do"], p["cu"], s0=p["s0"],
+                       ds_final=p["dsf"])
+    rng = np.random.default_rng(5)
+    keys = [("q", "dq"), ("k", "dk"), ("v", "dv"), ("g", "dg"), ("beta", "dbeta"), ("s0", "ds0")]
+    d = {name: rng.standard_normal(p[name].shape) for name, _ in keys}
+    h = 1e-5
+    plus = {name: p[name] + h * d[name] for name, _ in keys}
+    minus = {name: p[name] - h * d[name] for name, _ in keys}
+    fd = (_loss(p, oracle.MODE_DELTA, **plus) - _loss(p, oracle.MODE_DELTA, **minus)) / (2 * h)
+    an = sum(float((r[key] * d[name]).sum()) for name, key in keys)
+    assert abs(fd - an) <= 1e-6 * max(1.0, abs(an))
+
+
+def test_gradient_beta_zero_closed_form():
+    """beta = 0 and q = 0: the state only fades, S_T = Diag(exp(sum g)) S0, so
+    dS0 = Diag(exp(sum g)) dS_T, every token's dg = rowsum(dS_T * S_T), dq_t = S_t do_t
+    (S_t the faded state), dk = dv = 0, and dbeta_t = (G_t^T k_t) . (v_t - S_a,t^T k_t) with the cotangent
+    G_t = Diag(exp(sum_{s>t} g_s)) dS_T and the faded state S_a,t = Diag(exp(sum_{s<=t} g_s)) S0."""
+    p = _bwd_problem(6, 12, 1, 4, 3)
+    p["beta"][:] = 0.0
+    p["q"][:] = 0.0
+    r = oracle.run_bwd(p["q"], p["k"], p["v"], p["g"], p["beta"], p["do"], p["cu"], s0=p["s0"],
+                       ds_final=p["dsf"])
+    g, S0, W = p["g"][:, 0], p["s0"][0, 0], p["dsf"][0, 0]
+    tot = g.sum(axis=0)
+    ST = np.exp(tot)[:, None] * S0
+    np.testing.assert_allclose(r["ds0"][0, 0], np.exp(tot)[:, None] * W, rtol=1e-12)
+    for t in range(12):
+        np.testing.assert_allclose(r["dg"][t, 0], (W * ST).sum(axis=1), rtol=1e-12)
+        G = np.exp(g[t + 1:].sum(axis=0))[:, None] * W
+        Sa = np.exp(g[:t + 1].sum(axis=0))[:, None] * S0
+        kt, vt = p["k"][t, 0], p["v"][t, 0]
+        np.testing.assert_allclose(r["dbeta"][t, 0], (G.T @ kt) @ (vt - Sa.T @ kt), rtol=1e-10)
+        np.testing.assert_allclose(r["dq"][t, 0], Sa @ p["do"][t, 0], rtol=1e-10)
+    for key in ("dk", "dv"):
+        assert np.abs(r[key]).max() <= 1e-12
+
+
+def test_gradient_linear_attention_closed_form():
+    """Additive write, no fade: o = tril(Q K^T) V + Q S0 and S_T = S0 + K^T V, so
+    with P = tril(Q K^T): dV = P^T dO + K dS_T, dP = tril(dO V^T), dQ = dP K + dO S0^T,
+    dK = dP^T Q + V dS_T^T, dS0 = Q^T dO + dS_T (explicit T x T matrices)."""
+    p = _bwd_problem(7, 10, 1, 5, 3)
+    p["g"][:] = 0.0
+    r = oracle.run_bwd(p["q"], p["k"], p["v"], p["g"], p["beta"], p["do"], p["cu"], s0=p["s0"],
+                       ds_final=p["dsf"], mode=oracle.MODE_ADDITIVE)
+    Q, K, V, dO = p["q"][:, 0], p["k"][:, 0], p["v"][:, 0], p["do"][:, 0]
+    S0, dST = p["s0"][0, 0], p["dsf"][0, 0]
+    mask = np.tril(np.ones((10, 10)))
+    P = mask * (Q @ K.T)
+    dP = mask * (dO @ V.T)
+    np.testing.assert_allclose(r["dv"][:, 0], P.T @ dO + K @ dST, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(r["dq"][:, 0], dP @ K + dO @ S0.T, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(r["dk"][:, 0], dP.T @ Q + V @ dST.T, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(r["ds0"][0, 0], Q.T @ dO + dST, rtol=1e-10, atol=1e-12)
