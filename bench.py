@@ -184,6 +184,52 @@ def bench_variants(kda, torch, steps, warmup, flush):
     return out
 
 
+# Backward on the c1 shape: reads q, k, v, g, beta, dO; writes dq, dk, dv, dg, dbeta.
+BACKWARD_BYTES_PER_TOKEN_HEAD = (3 * 2 * 128 + 4 * 128 + 4 + 2 * 128) + (3 * 2 * 128 + 4 * 128 + 4)
+
+
+def bench_backward(kda, torch, steps, warmup, flush):
+    """kda_chunk_bwd tokens/s on the c1 shape (same timing rules as the prefill)."""
+    from gated_delta_rule_08_amd import workloads
+    p = workloads.make_inputs(1)
+    cfg = p["config"]
+    t = lambda a, dt: torch.from_numpy(a).to(dt).to("cuda")
+    q, k, v = (t(p[n], torch.bfloat16) for n in ("q", "k", "v"))
+    g, beta = t(p["g"], torch.float32), t(p["beta"], torch.float32)
+    cu = t(p["cu_seqlens"], torch.int32)
+    T, H, d = q.shape
+    N = cu.numel() - 1
+    gen = torch.Generator(device="cuda").manual_seed(1002)
+    do = torch.randn(q.shape, device="cuda", generator=gen).to(torch.bfloat16)
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+               dg=torch.empty_like(g), dbeta=torch.empty_like(beta), d_initial=None)
+    ws = torch.empty(kda.kda_chunk_bwd_workspace_bytes(H, d, d, torch.bfloat16, cfg.chunk, T, N),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        kda.kda_chunk_bwd(q, k, v, g, beta, cu, do, chunk=cfg.chunk, workspace=ws, stream=stream,
+                          out=out)
+
+    for _ in range(warmup):
+        flush()
+        step()
+    torch.cuda.synchronize()
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(steps)]
+    for s_, e_ in pairs:
+        flush()
+        s_.record(stream)
+        step()
+        e_.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(_events_ms(pairs)) / steps
+    bytes_ = BACKWARD_BYTES_PER_TOKEN_HEAD * T * H
+    return {"tokens_per_s": T / (ms * 1e-3), "ms_per_call": ms, "algorithmic_bytes": bytes_,
+            "roofline_frac": bytes_ / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "workload": "backward_bf16_B1_H16_T4096_d128_C64 (dL/do given, zero initial state)"}
+
+
 def bench_decode(kda, torch, steps, warmup, flush):
     from gated_delta_rule_08_amd import workloads
     p = workloads.make_inputs(2)
@@ -299,6 +345,7 @@ def main(argv=None):
         del pr
         if not args.no_variants:
             out["variants"] = bench_variants(kda, torch, max(5, args.steps // 2), 2, flush)
+            out["backward"] = bench_backward(kda, torch, max(5, args.steps // 2), 2, flush)
     if args.only in (None, "decode"):
         dc = bench_decode(kda, torch, args.steps, args.warmup, flush)
         ms = sum(dc["ms"]) / len(dc["ms"])

@@ -19,7 +19,7 @@ __all__ = [
     "KdaError", "load_library", "kda_abi_version", "kda_chunk_fwd", "kda_chunk_fwd_supported",
     "kda_chunk_fwd_workspace_bytes", "kda_decode_step", "kda_state_init", "kda_state_load",
     "kda_state_store", "KDA_READ_INITIAL_STATE", "KDA_WRITE_FINAL_STATE", "kda_chunk_fwd_raw",
-    "kda_decode_step_raw", "kda_state_affine",
+    "kda_decode_step_raw", "kda_state_affine", "kda_chunk_bwd",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -81,6 +81,11 @@ def load_library(path: str | None = None):
     lib.kda_chunk_fwd_raw.restype = ctypes.c_int
     lib.kda_decode_step_raw.argtypes = [SH, I32, P, P, P, P, P, F32, P, I32, P, U32, P, P]
     lib.kda_decode_step_raw.restype = ctypes.c_int
+    lib.kda_chunk_bwd_workspace_bytes.argtypes = [SH, I32, I32, I32]
+    lib.kda_chunk_bwd_workspace_bytes.restype = SZ
+    lib.kda_chunk_bwd.argtypes = [SH, I32, I32, I32, P, P, P, P, P, P, P, I32, P, U32, P, P, P, P,
+                                  P, P, P, P, P, SZ, P]
+    lib.kda_chunk_bwd.restype = ctypes.c_int
     lib.kda_state_affine.argtypes = [SH, I32, P, P, P, P, P]
     lib.kda_state_affine.restype = ctypes.c_int
     lib.kda_state_init.argtypes = [SH, P, I32, P]
@@ -170,6 +175,13 @@ def kda_chunk_fwd_workspace_bytes(num_heads: int, dk: int, dv: int, io_dtype: to
                                                             total_tokens, num_seqs))
 
 
+def kda_chunk_bwd_workspace_bytes(num_heads: int, dk: int, dv: int, io_dtype: torch.dtype,
+                                  chunk: int, total_tokens: int, num_seqs: int) -> int:
+    sh = _Shape(num_heads, dk, dv, KDA_BF16 if io_dtype == torch.bfloat16 else KDA_FP32)
+    return int(load_library().kda_chunk_bwd_workspace_bytes(ctypes.byref(sh), chunk,
+                                                            total_tokens, num_seqs))
+
+
 def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens, chunk: int = 64, states=None, state_slots=None,
                   read_initial: bool = False, write_final: bool = False, o=None, workspace=None,
                   stream=None, gate: str = "channel", additive: bool = False):
@@ -214,6 +226,63 @@ def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens, chunk: int = 64, states=None, st
                              _ptr(state_slots), flags, _ptr(o), _ptr(workspace), ws_bytes,
                              _stream(stream)))
     return o
+
+
+def kda_chunk_bwd(q, k, v, g, beta, cu_seqlens, d_o, chunk: int = 64, states=None,
+                  state_slots=None, read_initial: bool = False, d_final=None,
+                  want_d_initial: bool = False, workspace=None, stream=None, out=None):
+    """Gradients through kda_chunk_fwd (see kda_chunk_bwd in include/kda.h).
+
+    Same inputs as the forward call (per-channel gate, delta rule) plus
+    d_o [T, H, dv] and, optionally, d_final: fp32 [N, H, dk, dv] (dL/dS_final).
+    Returns a dict with dq, dk, dv (dtype of q), dg, dbeta (fp32) and d_initial
+    (fp32 [N, H, dk, dv], dL/dS0) when want_d_initial; ``out`` may hold those
+    tensors already (they are checked and overwritten).
+    """
+    lib = load_library()
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    io = _io_dtype(q)
+    for t, name, d in ((q, "q", dk), (k, "k", dk), (v, "v", dv), (d_o, "d_o", dv)):
+        _need(t, name, (T, H, d), q.dtype)
+    _need(g, "g", (T, H, dk), torch.float32)
+    _need(beta, "beta", (T, H), torch.float32)
+    N = cu_seqlens.numel() - 1
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32)
+    num_slots = 0
+    if states is not None:
+        _need(states, "states", (states.shape[0], H, dk, dv), torch.float32)
+        num_slots = states.shape[0]
+    if state_slots is not None:
+        _need(state_slots, "state_slots", (N,), torch.int32)
+    if d_final is not None:
+        _need(d_final, "d_final", (N, H, dk, dv), torch.float32)
+    if out is None:
+        out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+                   dg=torch.empty((T, H, dk), dtype=torch.float32, device=q.device),
+                   dbeta=torch.empty((T, H), dtype=torch.float32, device=q.device))
+        out["d_initial"] = (torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+                            if want_d_initial else None)
+    else:
+        for name, shape, dt in (("dq", (T, H, dk), q.dtype), ("dk", (T, H, dk), q.dtype),
+                                ("dv", (T, H, dv), q.dtype), ("dg", (T, H, dk), torch.float32),
+                                ("dbeta", (T, H), torch.float32)):
+            _need(out.get(name), name, shape, dt)
+        if out.get("d_initial") is not None:
+            _need(out["d_initial"], "d_initial", (N, H, dk, dv), torch.float32)
+    sh = _Shape(H, dk, dv, io)
+    need = int(lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(sh), chunk, T, N))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    flags = KDA_READ_INITIAL_STATE if read_initial else 0
+    _check(lib.kda_chunk_bwd(ctypes.byref(sh), chunk, T, N, _ptr(cu_seqlens), _ptr(q), _ptr(k),
+                             _ptr(v), _ptr(g), _ptr(beta), _ptr(states), num_slots,
+                             _ptr(state_slots), flags, _ptr(d_o), _ptr(d_final), _ptr(out["dq"]),
+                             _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+                             _ptr(out["dbeta"]), _ptr(out["d_initial"]), _ptr(workspace),
+                             ws_bytes, _stream(stream)))
+    return out
 
 
 def kda_decode_step(q, k, v, g, beta, states, state_slots=None, o=None, stream=None,

@@ -38,6 +38,15 @@ kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, cons
                                int32_t num_slots, const int32_t* slots, uint32_t flags, void* o,
                                void* workspace, hipStream_t stream);
 
+size_t chunk_mfma_bwd_workspace_bytes(int H, int32_t T, int32_t N);
+kda_status_t launch_chunk_mfma_bwd(const kda_shape_t* sh, int32_t T, int32_t N, const int32_t* cu,
+                                   const void* q, const void* k, const void* v, const float* g,
+                                   const float* beta, const float* states, int32_t num_slots,
+                                   const int32_t* slots, uint32_t flags, const void* d_o,
+                                   const float* d_final, void* dq, void* dk, void* dv, float* dg,
+                                   float* dbeta, float* d_initial, void* workspace,
+                                   hipStream_t stream);
+
 namespace {
 thread_local char g_last_error[512] = "";
 }
@@ -345,6 +354,59 @@ kda_status_t kda_state_affine(const kda_shape_t* sh, int32_t n, const float* M,
     return invalid("%s: S_out overlaps M or S_in (only S_out == B is allowed)", W);
   return launch_state_affine(n, sh->num_heads, sh->dk, sh->dv, M, S_in, B, S_out,
                              static_cast<hipStream_t>(stream));
+}
+
+size_t kda_chunk_bwd_workspace_bytes(const kda_shape_t* sh, int32_t chunk, int32_t total_tokens,
+                                     int32_t num_seqs) {
+  if (!sh || sh->num_heads <= 0 || total_tokens < 0 || num_seqs < 0) return 0;
+  if (!chunk_mfma_supported(sh->dk, sh->dv, chunk, sh->io_dtype)) return 0;
+  return chunk_mfma_bwd_workspace_bytes(sh->num_heads, total_tokens, num_seqs);
+}
+
+kda_status_t kda_chunk_bwd(const kda_shape_t* sh, int32_t chunk, int32_t total_tokens,
+                           int32_t num_seqs, const int32_t* cu_seqlens, const void* q,
+                           const void* k, const void* v, const float* g, const float* beta,
+                           const float* states, int32_t num_slots, const int32_t* state_slots,
+                           uint32_t flags, const void* d_o, const float* d_final_state, void* dq,
+                           void* dk, void* dv, float* dg, float* dbeta, float* d_initial_state,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  const char* W = "kda_chunk_bwd";
+  kda_status_t st = check_shape(sh, W);
+  if (st != KDA_OK) return st;
+  if (total_tokens < 0 || num_seqs < 0)
+    return invalid("%s: total_tokens and num_seqs must be >= 0", W);
+  if (flags & ~(uint32_t)KDA_READ_INITIAL_STATE)
+    return invalid("%s: flags other than KDA_READ_INITIAL_STATE (0x%x)", W,
+                   flags & ~(uint32_t)KDA_READ_INITIAL_STATE);
+  if (chunk <= 0) return invalid("%s: chunk must be >= 1 (got %d)", W, chunk);
+  if (!chunk_mfma_supported(sh->dk, sh->dv, chunk, sh->io_dtype)) return unsupported(W, sh, chunk);
+  if (total_tokens == 0 || num_seqs == 0) return KDA_OK;
+  if (!cu_seqlens) return invalid("%s: cu_seqlens is NULL", W);
+  if (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta)
+    return invalid("%s: a tensor pointer is NULL", W);
+  if (flags & KDA_READ_INITIAL_STATE) {
+    if (!states) return invalid("%s: states is NULL but KDA_READ_INITIAL_STATE is set", W);
+    if (num_slots <= 0) return invalid("%s: num_slots must be >= 1 with initial states", W);
+    if (!state_slots && num_slots < num_seqs)
+      return invalid("%s: num_slots (%d) < num_seqs (%d) with implicit slots", W, num_slots,
+                     num_seqs);
+  }
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 2) || !aligned(g, 16) ||
+      !aligned(beta, 4) || !aligned(d_o, 16) || !aligned(dq, 16) || !aligned(dk, 16) ||
+      !aligned(dv, 2) || !aligned(dg, 4) || !aligned(dbeta, 4) ||
+      (states && !aligned(states, 16)) || (d_final_state && !aligned(d_final_state, 4)) ||
+      (d_initial_state && !aligned(d_initial_state, 4)))
+    return invalid("%s: q, k, g, d_o, dq, dk, states must be 16-byte aligned, the rest "
+                   "element-aligned", W);
+  const size_t need = chunk_mfma_bwd_workspace_bytes(sh->num_heads, total_tokens, num_seqs);
+  if (!workspace || workspace_bytes < need) {
+    set_error("%s: workspace of %zu bytes needed, %zu given", W, need, workspace_bytes);
+    return KDA_ERR_WORKSPACE_TOO_SMALL;
+  }
+  if (!aligned(workspace, 256)) return invalid("%s: workspace must be 256-byte aligned", W);
+  return launch_chunk_mfma_bwd(sh, total_tokens, num_seqs, cu_seqlens, q, k, v, g, beta, states,
+                               num_slots, state_slots, flags, d_o, d_final_state, dq, dk, dv, dg,
+                               dbeta, d_initial_state, workspace, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -66,6 +66,13 @@ constexpr size_t kGcBytes = D * 4;             // Gam_C   fp32
 // Written by the state-only scan for the output kernel (few chains):
 constexpr size_t kScBytes = 8 * 4 * 64 * 16;   // S at chunk start, B operand (K=dk, N=dv), bf16
 constexpr size_t kUcBytes = 8 * 2 * 64 * 16;   // U, B operand (K=rows, N=dv), bf16
+// Backward only (the reverse scan's A operands use the Kd^T / A_qk block sizes;
+// the gradient kernel reads M_kk and T as plain fp32 [64][64]):
+//   kdr  Kd        A operand, M=rows, K=dk      wt   -W^T    A operand, M=dk, K=rows
+//   qgt  (Q*Gam)^T A operand, M=dk,   K=rows    aqt  A_qk^T  A operand, M=rows j, K=rows r
+//   dsc  dL/dS at chunk end and duc dL/dU, laid out as S and U above.
+constexpr size_t kMkBytes = C * C * 4;
+constexpr size_t kTmBytes = C * C * 4;
 
 // Chains (sequence-heads) up to which the scan only carries the state and a
 // separate, fully parallel kernel forms the outputs: with few chains the
@@ -131,9 +138,18 @@ struct Workspace {
   uint8_t* aq;
   uint8_t* ut;
   uint8_t* gc;
-  uint8_t* sc;         // split outputs only (else null)
+  uint8_t* sc;         // split outputs and backward only (else null)
   uint8_t* uc;
   uint8_t* sink;       // 256 B target of stores for rows past a sequence's end
+  // backward only (else null)
+  uint8_t* kdr;
+  uint8_t* wt;
+  uint8_t* qgt;
+  uint8_t* aqt;
+  uint8_t* mkk;
+  uint8_t* tm;
+  uint8_t* dsc;
+  uint8_t* duc;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -142,7 +158,7 @@ size_t header_bytes(int32_t N) { return align256(sizeof(int32_t) * (size_t)(4 * 
 
 size_t nchunks_max(int32_t T, int32_t N) { return (size_t)T / C + (size_t)N; }
 
-Workspace carve(void* base, int32_t T, int32_t N, int H) {
+Workspace carve(void* base, int32_t T, int32_t N, int H, bool bwd = false) {
   Workspace w;
   uint8_t* p = static_cast<uint8_t*>(base);
   int32_t* hdr = reinterpret_cast<int32_t*>(p);
@@ -159,9 +175,20 @@ Workspace carve(void* base, int32_t T, int32_t N, int H) {
   w.ut = p; p += align256(ci * kUtBytes);
   w.gc = p; p += align256(ci * kGcBytes);
   w.sc = w.uc = nullptr;
-  if (split_outputs(N, H)) {
+  w.kdr = w.wt = w.qgt = w.aqt = w.mkk = w.tm = w.dsc = w.duc = nullptr;
+  if (bwd || split_outputs(N, H)) {
     w.sc = p; p += align256(ci * kScBytes);
     w.uc = p; p += align256(ci * kUcBytes);
+  }
+  if (bwd) {
+    w.kdr = p; p += align256(ci * kKdBytes);
+    w.wt = p; p += align256(ci * kKdBytes);
+    w.qgt = p; p += align256(ci * kKdBytes);
+    w.aqt = p; p += align256(ci * kAqBytes);
+    w.mkk = p; p += align256(ci * kMkBytes);
+    w.tm = p; p += align256(ci * kTmBytes);
+    w.dsc = p; p += align256(ci * kScBytes);
+    w.duc = p; p += align256(ci * kUcBytes);
   }
   w.sink = p;
   return w;
@@ -421,7 +448,7 @@ __device__ __forceinline__ void gram_pair(const PrepSmem& sm, int R, int J, bool
 }
 
 // One workgroup of the prep: items wg, wg + nwg, ... in chunk-major order.
-template <int kGate, bool kAdd, bool kRaw>
+template <int kGate, bool kAdd, bool kRaw, bool kBwd>
 __device__ __forceinline__ void prep_role(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const void* __restrict__ g, const void* __restrict__ beta, float gate_min, int32_t N, int H,
@@ -507,6 +534,7 @@ __device__ __forceinline__ void prep_role(
     lds_barrier();
 
     // ---- gated Gram blocks (10 block pairs over 8 waves)
+    float aq_keep[2][4];  // backward: A_qk of this wave's pairs, transposed through LDS below
     {
       uint16_t* aq_out = reinterpret_cast<uint16_t*>(w.aq + ci * kAqBytes);
       for (int pi = wave; pi < 10; pi += kPrepWaves) {
@@ -529,6 +557,15 @@ __device__ __forceinline__ void prep_role(
           qv[jj] = j <= r ? accq[jj] : 0.f;
         }
         *reinterpret_cast<float4*>(&sm.A[r][16 * J + 4 * lg]) = arow;
+        if constexpr (kBwd) {
+          // M_kk (unscaled, strictly lower) for the gradient of beta
+          float4 mrow;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) (&mrow.x)[jj] = 16 * J + 4 * lg + jj < r ? acck[jj] : 0.f;
+          *reinterpret_cast<float4*>(w.mkk + ci * kMkBytes + (size_t)(r * C + 16 * J + 4 * lg) * 4) = mrow;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) aq_keep[pi >= kPrepWaves][jj] = qv[jj];
+        }
         // A_qk as the scan's A operand: [m = R][s' = J / 2][lane][slots (J & 1) * 4 ..]
         uint16_t* dst = aq_out + ((size_t)(R * 2 + (J >> 1)) * 64 + lane) * 8 + (J & 1) * 4;
         *reinterpret_cast<uint2*>(dst) =
@@ -543,6 +580,16 @@ __device__ __forceinline__ void prep_role(
       }
     }
     lds_barrier();
+    if constexpr (kBwd) {
+      // A_qk into the row-side operand space (free after the Gram phase): [r][j]
+      float(*aqs)[AP] = reinterpret_cast<float(*)[AP]>(&sm.rk[0][0]);
+      for (int pi = wave, x = 0; pi < 10; pi += kPrepWaves, ++x) {
+        const int R = pi < 4 ? 3 : pi < 7 ? 2 : pi < 9 ? 1 : 0;
+        const int J = pi < 4 ? 3 - pi : pi < 7 ? 6 - pi : pi < 9 ? 8 - pi : 0;
+        *reinterpret_cast<float4*>(&aqs[16 * R + li][16 * J + 4 * lg]) =
+            make_float4(aq_keep[x][0], aq_keep[x][1], aq_keep[x][2], aq_keep[x][3]);
+      }
+    }
 
     // ---- T = (I + A_kk)^-1 in 16x16 blocks.  Diagonal blocks: T_JJ = (I + A_JJ)^-1
     // by right-looking forward substitution (wave J, lane = column): once x[m]
@@ -584,6 +631,16 @@ __device__ __forceinline__ void prep_role(
       lds_barrier();
     }
 
+    if constexpr (kBwd) {
+      // T for the gradient kernel, plain [j][r] fp32 (upper blocks are zero)
+      float* tm_out = reinterpret_cast<float*>(w.tm + ci * kTmBytes);
+#pragma unroll
+      for (int x = 0; x < C * C / 4 / kPrepThreads; ++x) {
+        const int u = tid + kPrepThreads * x, r = u >> 4, c4 = (u & 15) * 4;
+        *reinterpret_cast<float4*>(tm_out + r * C + c4) = *reinterpret_cast<const float4*>(&sm.Tm[r][c4]);
+      }
+    }
+
     // ---- W, Ut, Kd^T, Gam_C in the scan's operand order; wave = channel tile = value tile
     {
       bf16x8 tt[4][2];  // T tiles: A operand (M = r) of Ut and B operand (N = r) of W^T
@@ -617,6 +674,56 @@ __device__ __forceinline__ void prep_role(
         *reinterpret_cast<bf16x8*>(kd_out + ((size_t)(tile * 2 + s2) * 64 + lane) * 8) = pack8(fd);
         abkg[s2] = pack8(fb);
         bv[s2] = pack8(fv);
+        if constexpr (kBwd) {
+          // (Q*Gam)^T as the reverse scan's A operand (M = channel, K = row)
+          float fq[8];
+#pragma unroll
+          for (int qq = 0; qq < 8; ++qq) {
+            const int j = 32 * s2 + kpos(lg, qq);
+            fq[qq] = ld_bf(sm.Q[j], ch) * fast_exp(sm.G[j][ch]);
+          }
+          *reinterpret_cast<bf16x8*>(w.qgt + ci * kKdBytes + ((size_t)(tile * 2 + s2) * 64 + lane) * 16) =
+              pack8(fq);
+        }
+      }
+      if constexpr (kBwd) {
+        // -W^T (M = channel, K = row): W tiles with rows in the accumulator, packed in pairs
+        f32x4 wr[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          wr[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          wr[nt] = mfma(tt[nt][0], abkg[0], wr[nt]);
+          if (nt >= 2) wr[nt] = mfma(tt[nt][1], abkg[1], wr[nt]);
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+          *reinterpret_cast<bf16x8*>(w.wt + ci * kKdBytes + ((size_t)(tile * 2 + s2) * 64 + lane) * 16) =
+              pack_acc(-wr[2 * s2], -wr[2 * s2 + 1]);
+        // Kd as an A operand (M = row, K = channel) and A_qk^T (M = column j, K = row r),
+        // two operand tiles of each per wave
+        const float(*aqs)[AP] = reinterpret_cast<const float(*)[AP]>(&sm.rk[0][0]);
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int opi = wave * 2 + x, m = opi >> 2, sk = opi & 3, r = 16 * m + li;
+          float fk[8];
+#pragma unroll
+          for (int qq = 0; qq < 8; ++qq) {
+            const int cc = 32 * sk + kpos(lg, qq);
+            fk[qq] = ld_bf(sm.K[r], cc) * fast_exp(sm.G[C - 1][cc] - sm.G[r][cc]);
+          }
+          *reinterpret_cast<bf16x8*>(w.kdr + ci * kKdBytes + ((size_t)opi * 64 + lane) * 16) = pack8(fk);
+        }
+        {
+          const int m = wave >> 1, s2 = wave & 1, j = 16 * m + li;
+          float fa[8];
+#pragma unroll
+          for (int qq = 0; qq < 8; ++qq) {
+            const int rr = 32 * s2 + kpos(lg, qq);
+            fa[qq] = (rr >> 4) >= m ? aqs[rr][j] : 0.f;  // blocks above the diagonal are zero
+          }
+          *reinterpret_cast<bf16x8*>(w.aqt + ci * kAqBytes + ((size_t)(m * 2 + s2) * 64 + lane) * 16) =
+              pack8(fa);
+        }
       }
       // -W: [m = nt][s = tile / 2][lane][slots (tile & 1) * 4 ..]
       uint16_t* wn_out = reinterpret_cast<uint16_t*>(w.wn + ci * kWnBytes);
@@ -643,7 +750,7 @@ __device__ __forceinline__ void prep_role(
 }
 
 // LDS use (~153 KiB) allows one workgroup (two waves per SIMD) per CU.
-template <int kGate, bool kAdd, bool kRaw>
+template <int kGate, bool kAdd, bool kRaw, bool kBwd>
 __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const void* __restrict__ g, const void* __restrict__ beta, float gate_min, int32_t N, int H,
@@ -651,23 +758,23 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2,
     const int32_t* __restrict__ chunk_off) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   const Header hd{seq_start, seq_end, chunk_off};
-  prep_role<kGate, kAdd, kRaw>(q, k, v, g, beta, gate_min, N, H, w, hd, smem_raw, blockIdx.x,
+  prep_role<kGate, kAdd, kRaw, kBwd>(q, k, v, g, beta, gate_min, N, H, w, hd, smem_raw, blockIdx.x,
                                gridDim.x);
 }
 
-template <int kGate, bool kAdd, bool kRaw>
+template <int kGate, bool kAdd, bool kRaw, bool kBwd = false>
 kda_status_t launch_prep(unsigned grid, const void* q, const void* k, const void* v, const void* g,
                          const void* beta, float gate_min, int32_t N, int H, const Workspace& w,
                          hipStream_t stream) {
   static bool attr_set = false;  // idempotent; set before the first launch
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep_kernel<kGate, kAdd, kRaw>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep_kernel<kGate, kAdd, kRaw, kBwd>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)sizeof(PrepSmem));
     if (e != hipSuccess) return hip_status(e, "hipFuncSetAttribute(prep)");
     attr_set = true;
   }
-  hipLaunchKernelGGL((prep_kernel<kGate, kAdd, kRaw>), dim3(grid), dim3(kPrepThreads),
+  hipLaunchKernelGGL((prep_kernel<kGate, kAdd, kRaw, kBwd>), dim3(grid), dim3(kPrepThreads),
                      sizeof(PrepSmem), stream, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), g, beta,
                      gate_min, N, H, w, w.seq_start, w.seq_end, w.chunk_off);
@@ -1502,6 +1609,608 @@ kda_status_t launch_scan(int32_t N, int H, const Workspace& w, float* states, in
   return check_launch("chunk_fwd scan");
 }
 
+// ------------------------------------------------------------------ 4. backward
+// The pages stop at the forward pass; the gradient is reverse-mode
+// differentiation of the chunk algebra above.  With X = dL/dS at a chunk's end,
+//   reverse pass   dU = A_qk^T dO + Kd X,   X <- (Q*Gam)^T dO + Diag(Gam_C) X - W^T dU
+// (the transpose of the forward pass U = Ut - W S, S <- Diag(Gam_C) S + Kd^T U), and
+// inside a chunk, with R = Diag(beta)(V - (K*Gam) S) and U = (I + A_kk)^-1 R:
+//   dR = T^T dU,  dA_kk = -dR U^T,  dV = Diag(beta) dR,  Z = dR S^T,
+//   dA_qk = dO U^T,  d(Q*Gam) = dO S^T,  dKd = U X^T,  dGam_C = rowsum(X * S),
+// and the decayed products A_qk, M_kk send their cotangents to q, k and the
+// cumulative gates.  The forward state pass runs first (the state-only scan
+// stores S at every chunk start and U); the reverse pass stores X and dU; the
+// gradient kernel then handles every (chunk, head) independently.
+
+// Reverse pass: 8 workgroups of 16 value columns per (sequence, head), one
+// compute wave and LW loader waves copying the chunk's operands (Kd, -W^T,
+// (Q*Gam)^T, A_qk^T, dO rows, Gam_C) into LDS, double buffered, chunks walked
+// from the last to the first.
+struct GradScanLds {
+  struct Buf {
+    bf16x8 kdr[16][64];   // Kd      [m*4 + s][lane]   (M = rows, K = dk)
+    bf16x8 wt[16][64];    // -W^T    [t*2 + s2][lane]  (M = dk, K = rows)
+    bf16x8 qgt[16][64];   // (Q*Gam)^T
+    bf16x8 aqt[8][64];    // A_qk^T  [m*2 + s2][lane]  (M = rows j, K = rows r)
+    uint16_t dob[C][16];  // dO rows, this workgroup's 16 columns
+    f32x4 gc[32];         // Gam_C
+  };
+  Buf buf[2];
+};
+
+template <int LW>
+__global__ __launch_bounds__(64 * (1 + LW)) void scan_grad_kernel(
+    int32_t N, int H, Workspace w, const uint16_t* __restrict__ d_o,
+    const float* __restrict__ d_final, float* __restrict__ d_initial) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  using Buf = GradScanLds::Buf;
+  GradScanLds& sl = *reinterpret_cast<GradScanLds*>(smem_raw);
+  const int NH = N * H;
+  const int head_lin = blockIdx.x % NH;
+  const int group = blockIdx.x / NH;
+  const int n = head_lin / H, h = head_lin - n * H;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+  const int nch = w.seq_nch[n];
+  const int cbase = w.chunk_off[n];
+  const int s_start = w.seq_start[n], s_end = w.seq_end[n];
+
+  if (wave >= 1) {
+    // ------------------------------------------------------------ loaders
+    const int lw = wave - 1;
+    const int off = lane * 16;
+    constexpr int kPieces = 58;  // 1 KiB pieces: Kd 16, -W^T 16, (Q*Gam)^T 16, A_qk^T 8, dO 2
+    auto issue = [&](int lc, Buf* dst) {
+      const size_t ci = (size_t)(cbase + lc) * H + h;
+      const uint8_t* kdr = w.kdr + ci * kKdBytes;
+      const uint8_t* wt = w.wt + ci * kKdBytes;
+      const uint8_t* qgt = w.qgt + ci * kKdBytes;
+      const uint8_t* aqt = w.aqt + ci * kAqBytes;
+      const int t0 = s_start + lc * C;
+      const int last = min(C, s_end - t0) - 1;  // rows past the end re-read the last row
+#pragma unroll
+      for (int i = 0; i < (kPieces + LW - 1) / LW; ++i) {
+        const int p = lw + LW * i;  // wave-uniform
+        if (p < 16) dma16(kdr + p * 1024 + off, &dst->kdr[p][0]);
+        else if (p < 32) dma16(wt + (p - 16) * 1024 + off, &dst->wt[p - 16][0]);
+        else if (p < 48) dma16(qgt + (p - 32) * 1024 + off, &dst->qgt[p - 32][0]);
+        else if (p < 56) dma16(aqt + (p - 48) * 1024 + off, &dst->aqt[p - 48][0]);
+        else if (p < kPieces) {
+          const int row = min(32 * (p - 56) + (lane >> 1), last);
+          const uint16_t* src = d_o + ((size_t)(t0 + row) * H + h) * D + 16 * group + 8 * (lane & 1);
+          dma16(reinterpret_cast<const uint8_t*>(src), &dst->dob[32 * (p - 56)][0]);
+        }
+      }
+      if (lw == LW - 1 && lane < 32) dma16(w.gc + ci * kGcBytes + off, &dst->gc[0]);
+    };
+    auto step_end = [&]() {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+      lds_barrier();
+    };
+    // the k-th chunk processed is chunk nch - 1 - k, in buffer k & 1
+    if (nch > 0) issue(nch - 1, &sl.buf[0]);
+    step_end();
+    for (int kx = 0; kx < nch; kx += 2) {
+      if (kx + 1 < nch) issue(nch - 2 - kx, &sl.buf[1]);
+      step_end();
+      if (kx + 1 < nch) {
+        if (kx + 2 < nch) issue(nch - 3 - kx, &sl.buf[0]);
+        step_end();
+      }
+    }
+    return;
+  }
+
+  // -------------------------------------------------------------- compute
+  const int col = 16 * group + li;
+  f32x4 X[8];
+  const size_t sb = ((size_t)n * H + h) * (size_t)(D * D);
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      X[t][jj] = d_final ? d_final[sb + (size_t)(16 * t + 4 * lg + jj) * D + col] : 0.f;
+  lds_barrier();
+
+  auto chunk_step = [&](const Buf& B, size_t ci) {
+    bf16x8 xb[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) xb[s] = pack_acc(X[2 * s], X[2 * s + 1]);
+    bf16x8* dsc = reinterpret_cast<bf16x8*>(w.dsc + ci * kScBytes);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) dsc[(group * 4 + s) * 64 + lane] = xb[s];
+    // dO as a B operand: K = row (kpos order), N = column li
+    bf16x8 dob[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      u16x8 t;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t[e] = B.dob[32 * s2 + kpos(lg, e)][li];
+      dob[s2] = __builtin_bit_cast(bf16x8, t);
+    }
+    // dU = A_qk^T dO + Kd X   (A_qk^T is zero for K rows 0..31 of row tiles 2, 3)
+    f32x4 dU[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) dU[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) dU[m] = mfma(B.kdr[m * 4 + s][lane], xb[s], dU[m]);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) dU[m] = mfma(B.aqt[m * 2 + 1][lane], dob[1], dU[m]);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) dU[m] = mfma(B.aqt[m * 2][lane], dob[0], dU[m]);
+    bf16x8 ub[2];
+    bf16x8* duc = reinterpret_cast<bf16x8*>(w.duc + ci * kUcBytes);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      ub[s2] = pack_acc(dU[2 * s2], dU[2 * s2 + 1]);
+      duc[(group * 2 + s2) * 64 + lane] = ub[s2];
+    }
+    // X <- Diag(Gam_C) X + (Q*Gam)^T dO - W^T dU
+#pragma unroll
+    for (int t = 0; t < 8; ++t) X[t] = X[t] * B.gc[4 * t + lg];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) X[t] = mfma(B.qgt[t * 2 + s2][lane], dob[s2], X[t]);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) X[t] = mfma(B.wt[t * 2 + s2][lane], ub[s2], X[t]);
+    lds_barrier();
+  };
+  for (int kx = 0; kx < nch; kx += 2) {
+    chunk_step(sl.buf[0], (size_t)(cbase + nch - 1 - kx) * H + h);
+    if (kx + 1 < nch) chunk_step(sl.buf[1], (size_t)(cbase + nch - 2 - kx) * H + h);
+  }
+  if (d_initial) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) d_initial[sb + (size_t)(16 * t + 4 * lg + jj) * D + col] = X[t][jj];
+  }
+}
+
+// Gradient kernel: one workgroup of 8 waves per (chunk, head).  Phases:
+//  0  stage K, Q, the gates (running sums), beta and T; T^T operands to registers
+//  1  two halves of 64 value columns: dR = T^T dU (-> dV, dbeta), then
+//     Z = dR S^T, d(Q*Gam) = dO S^T, dKd = U X^T, dA_qk = dO U^T, dR U^T, dGam_C
+//  2  elementwise terms of dq, dk, dG; dbeta terms; dA_qk and dM = beta dA_kk to LDS
+//  3  the decayed products: blocks below the diagonal on MFMA with the decay split
+//     at a block boundary (both factors <= 1), diagonal blocks on MFMA when the
+//     block's gate spread allows it, else element by element
+//  4  reverse running sum of dG (the gates are running sums), stores.
+// Lane layout of the per-element results: rows 16m + 4lg + jj (m = 0..3),
+// channel 16 * wave + li.
+constexpr int kGradThreads = 512;
+constexpr int KB = D + 8;  // bf16 row pitch of K, Q (16-byte aligned rows)
+constexpr int HB = 72;     // bf16 row pitch of 64-column tiles
+
+struct GradSmem {
+  uint16_t K[C][KB];   // k (phase 4: dk staging)
+  uint16_t Q[C][KB];   // q (phase 4: dq staging)
+  float G[C][GP];      // running gate sums (phase 4: dG)
+  float bs[C];
+  float db[C];         // dbeta
+  float dgl[D];        // dG of the chunk's last row from Gam_C
+  float spr[kGradThreads / 64];
+  union {
+    float T[C][AP];       // phase 0
+    uint16_t dR[C][HB];   // phase 1
+  } x;
+  union {
+    struct {
+      uint16_t dO[C][HB];
+      uint16_t U[C][HB];
+      uint16_t S[D][HB];
+      uint16_t dS[D][HB];
+    } h;                  // phase 1
+    struct {
+      uint16_t dAq[C][HB];
+      uint16_t dAqT[C][HB];
+      uint16_t dM[C][HB];
+      uint16_t dMT[C][HB];
+    } a;                  // phases 2-3
+    float tot[4][D];      // running sums (phases 0 and 4)
+  } y;
+};
+
+__device__ __forceinline__ bf16x8 lds8(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ float bfv(uint16_t b) { return bf16_to_f32(b); }
+
+__global__ __launch_bounds__(kGradThreads) void grad_kernel(
+    int32_t N, int H, Workspace w, const int32_t* __restrict__ seq_start,
+    const int32_t* __restrict__ seq_end, const int32_t* __restrict__ chunk_off,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, const uint16_t* __restrict__ d_o,
+    uint16_t* __restrict__ dq, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+    float* __restrict__ dg, float* __restrict__ dbeta) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  GradSmem& sm = *reinterpret_cast<GradSmem*>(smem_raw);
+  const Header hd{seq_start, seq_end, chunk_off};
+  const int item = blockIdx.x;
+  if (item >= hd.chunk_off[N] * H) return;  // uniform
+  const ItemPos pos = locate(hd, N, H, item);
+  const size_t ci = (size_t)item;
+  const int c = pos.c;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+  const size_t row0 = (size_t)pos.t0 * H + pos.h;  // token-row of the chunk's first row
+  const size_t rs = (size_t)H;                     // token-row stride
+
+  // ---- 0. staging (rows past the end are zero)
+  const uint4 z4 = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int u = tid + kGradThreads * x, r = u >> 4, cc = (u & 15) * 8;
+    const size_t gi = (row0 + r * rs) * D + cc;
+    *reinterpret_cast<uint4*>(&sm.K[r][cc]) = r < c ? *reinterpret_cast<const uint4*>(k + gi) : z4;
+    *reinterpret_cast<uint4*>(&sm.Q[r][cc]) = r < c ? *reinterpret_cast<const uint4*>(q + gi) : z4;
+  }
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int u = tid + kGradThreads * x, r = u >> 5, cc = (u & 31) * 4;
+    *reinterpret_cast<float4*>(&sm.G[r][cc]) =
+        r < c ? *reinterpret_cast<const float4*>(g + (row0 + r * rs) * D + cc)
+              : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if (tid < C) {
+    sm.bs[tid] = tid < c ? beta[row0 + tid * rs] : 0.f;
+    sm.db[tid] = 0.f;
+  }
+  if (tid < D) sm.dgl[tid] = 0.f;
+  {
+    const float* tm = reinterpret_cast<const float*>(w.tm + ci * kTmBytes);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int u = tid + kGradThreads * x, r = u >> 4, c4 = (u & 15) * 4;
+      *reinterpret_cast<float4*>(&sm.x.T[r][c4]) = *reinterpret_cast<const float4*>(tm + r * C + c4);
+    }
+  }
+  __syncthreads();
+  {
+    const int col = tid & 127, qt = tid >> 7;
+    float xs[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) xs[i] = sm.G[16 * qt + i][col];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) xs[i] += xs[i - 1];
+    sm.y.tot[qt][col] = xs[15];
+    __syncthreads();
+    float base = 0.f;
+    for (int j = 0; j < qt; ++j) base += sm.y.tot[j][col];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sm.G[16 * qt + i][col] = xs[i] + base;
+    float sp = xs[0] - xs[15];  // gate spread of this channel inside block qt
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sp = fmaxf(sp, __shfl_xor(sp, off, 64));
+    if (lane == 0) sm.spr[wave] = sp;  // waves 2qt and 2qt + 1 cover block qt
+  }
+  // T^T as the A operand of dR = T^T dU (M = row r, K = row j, kpos order):
+  // this wave's dR tiles are column tile ct of a half and row tiles mb, mb + 1.
+  const int ct = wave & 3, mb = (wave >> 2) * 2;
+  bf16x8 tT[2][2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = sm.x.T[32 * s2 + kpos(lg, e)][16 * (mb + mi) + li];
+      tT[mi][s2] = pack8(f);
+    }
+  __syncthreads();  // T is read; its space holds dR from here
+
+  // ---- 1. the two halves of the value columns
+  f32x4 aZ[4], aQ[4], aK[4], aAq[2], aAk[2];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) aZ[m] = aQ[m] = aK[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  aAq[0] = aAq[1] = aAk[0] = aAk[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float dgc = 0.f;  // rowsum(X * S) for channel tid >> 2, over this thread's columns
+  const u16x8* uc = reinterpret_cast<const u16x8*>(w.uc + ci * kUcBytes);
+  const u16x8* sc = reinterpret_cast<const u16x8*>(w.sc + ci * kScBytes);
+  const u16x8* dsc = reinterpret_cast<const u16x8*>(w.dsc + ci * kScBytes);
+  const bf16x8* duc = reinterpret_cast<const bf16x8*>(w.duc + ci * kUcBytes);
+  for (int hf = 0; hf < 2; ++hf) {
+    const int ctg = 4 * hf + ct;  // dR column tile in the whole row
+    const bf16x8 dub0 = duc[(ctg * 2 + 0) * 64 + lane], dub1 = duc[(ctg * 2 + 1) * 64 + lane];
+    {
+      const int r = tid >> 3, cc = (tid & 7) * 8;
+      *reinterpret_cast<uint4*>(&sm.y.h.dO[r][cc]) =
+          r < c ? *reinterpret_cast<const uint4*>(d_o + (row0 + r * rs) * D + 64 * hf + cc) : z4;
+    }
+    {
+      // U from the B-operand layout: [column tile][row half][lane], rows in kpos order
+      const int ctl = tid >> 7, s2 = (tid >> 6) & 1, ln = tid & 63;
+      const u16x8 u8 = uc[((4 * hf + ctl) * 2 + s2) * 64 + ln];
+      const int cl = 16 * ctl + (ln & 15), g4 = ln >> 4;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm.y.h.U[32 * s2 + kpos(g4, e)][cl] = u8[e];
+    }
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      // S and X from [column tile][row block of 32][lane], rows in kpos order
+      const int u = tid + kGradThreads * x, ctl = u >> 8, s = (u >> 6) & 3, ln = u & 63;
+      const size_t idx = (size_t)((4 * hf + ctl) * 4 + s) * 64 + ln;
+      const u16x8 s8 = sc[idx], d8 = dsc[idx];
+      const int cl = 16 * ctl + (ln & 15), g4 = ln >> 4;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 32 * s + kpos(g4, e);
+        sm.y.h.S[r][cl] = s8[e];
+        sm.y.h.dS[r][cl] = d8[e];
+      }
+    }
+    __syncthreads();
+    // dR = T^T dU (T^T is zero for K rows 0..31 of row tiles 2, 3)
+    {
+      f32x4 r2[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        r2[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (mb + mi < 2) r2[mi] = mfma(tT[mi][0], dub0, r2[mi]);
+        r2[mi] = mfma(tT[mi][1], dub1, r2[mi]);
+      }
+      const int cl = 16 * ct + li, cg = 64 * hf + cl;
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int r = 16 * (mb + mi) + 4 * lg + jj;
+          const float x = r2[mi][jj];
+          sm.x.dR[r][cl] = f32_to_bf16(x);
+          float p = 0.f;
+          if (r < c) {
+            const size_t gi = (row0 + r * rs) * D + cg;
+            dv[gi] = f32_to_bf16(sm.bs[r] * x);
+            p = x * bf16_to_f32(v[gi]);
+          }
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) p += __shfl_xor(p, o, 64);
+          if (li == 0) atomicAdd(&sm.db[r], p);
+        }
+    }
+    __syncthreads();
+    // products over the half's 64 columns; plain operands, K = column
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int cc = 32 * ks + 8 * lg;
+      const bf16x8 bS = lds8(&sm.y.h.S[16 * wave + li][cc]);
+      const bf16x8 bX = lds8(&sm.y.h.dS[16 * wave + li][cc]);
+      bf16x8 aR[4], aO[4], aU[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        aR[m] = lds8(&sm.x.dR[16 * m + li][cc]);
+        aO[m] = lds8(&sm.y.h.dO[16 * m + li][cc]);
+        aU[m] = lds8(&sm.y.h.U[16 * m + li][cc]);
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        aZ[m] = mfma(aR[m], bS, aZ[m]);
+        aQ[m] = mfma(aO[m], bS, aQ[m]);
+        aK[m] = mfma(aU[m], bX, aK[m]);
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int tt = wave + 8 * x, R = tt >> 2, J = tt & 3;
+        if (J <= R) {
+          aAq[x] = mfma(aO[R], aU[J], aAq[x]);
+          aAk[x] = mfma(aR[R], aU[J], aAk[x]);
+        }
+      }
+    }
+    {
+      const int i = tid >> 2, c0 = (tid & 3) * 16;
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s += bfv(sm.y.h.S[i][c0 + e]) * bfv(sm.y.h.dS[i][c0 + e]);
+      dgc += s;
+    }
+    __syncthreads();  // the tiles are read before the next half (or phase 2) overwrites them
+  }
+  dgc += __shfl_xor(dgc, 1, 64);
+  dgc += __shfl_xor(dgc, 2, 64);
+  if ((tid & 3) == 0) atomicAdd(&sm.dgl[tid >> 2], dgc * fast_exp(sm.G[C - 1][tid >> 2]));
+
+  // ---- 2. elementwise terms
+  const int ich = 16 * wave + li;
+  const float GC = sm.G[C - 1][ich];
+  f32x4 oq[4], okk[4], oG[4];
+  float kdsum = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int r = 16 * m + 4 * lg + jj;
+      const float Gr = sm.G[r][ich], gam = fast_exp(Gr), ed = fast_exp(GC - Gr);
+      const float kr = bfv(sm.K[r][ich]), qr = bfv(sm.Q[r][ich]), br = sm.bs[r];
+      const float z = aZ[m][jj], dqg = aQ[m][jj], dkd = aK[m][jj];
+      const float dkg = -br * z;
+      const float kdv = kr * ed;
+      oq[m][jj] = dqg * gam;
+      okk[m][jj] = dkg * gam + dkd * ed;
+      oG[m][jj] = (dqg * qr + dkg * kr) * gam - dkd * kdv;
+      kdsum += dkd * kdv;
+      float p = kr * gam * z;  // dbeta_r -= sum_i (K*Gam)[r,i] Z[r,i]
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) p += __shfl_xor(p, o, 64);
+      if (li == 0) atomicAdd(&sm.db[r], -p);
+    }
+  kdsum += __shfl_xor(kdsum, 16, 64);
+  kdsum += __shfl_xor(kdsum, 32, 64);
+  if (lg == 0) atomicAdd(&sm.dgl[ich], kdsum);
+  {
+    const float* mk = reinterpret_cast<const float*>(w.mkk + ci * kMkBytes);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int tt = wave + 8 * x, R = tt >> 2, J = tt & 3, j = 16 * J + li;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = 16 * R + 4 * lg + jj;
+        const bool low = J <= R;
+        const float aq = low && j <= r ? aAq[x][jj] : 0.f;
+        const float ak = low && j < r ? -aAk[x][jj] : 0.f;   // dA_kk = -(dR U^T)
+        const float mv = low && j < r ? mk[r * C + j] : 0.f;
+        float p = ak * mv;  // dbeta_r += sum_j dA_kk[r,j] M_kk[r,j]
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) p += __shfl_xor(p, o, 64);
+        if (li == 0) atomicAdd(&sm.db[r], p);
+        const uint16_t bq = f32_to_bf16(aq), bm = f32_to_bf16(sm.bs[r] * ak);
+        sm.y.a.dAq[r][j] = bq;
+        sm.y.a.dAqT[j][r] = bq;
+        sm.y.a.dM[r][j] = bm;
+        sm.y.a.dMT[j][r] = bm;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 3. decayed products
+  // Row side: out row r of block R gets sum_j dA[r,j] k_j exp(G_r - G_j); split at
+  // ref = 16R: exp(G_r - G_ref) <= 1 and exp(G_ref - G_j) <= 1 for j < ref, <= the
+  // block's spread for the diagonal block (included only when that is safe).
+#pragma unroll
+  for (int R = 0; R < 4; ++R) {
+    const int ref = 16 * R;
+    const bool diag = fmaxf(sm.spr[2 * R], sm.spr[2 * R + 1]) <= kMaxSpread;
+    const int jend = diag ? ref + 16 : ref;
+    if (jend == 0) continue;
+    f32x4 accq = {0.f, 0.f, 0.f, 0.f}, acck = {0.f, 0.f, 0.f, 0.f};
+    const float Gref = sm.G[ref][ich];
+    for (int ks = 0; 32 * ks < jend; ++ks) {
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = 32 * ks + 8 * lg + e;
+        const float ex = fast_exp(Gref - sm.G[j][ich]);
+        f[e] = j < jend ? bfv(sm.K[j][ich]) * ex : 0.f;
+      }
+      const bf16x8 b = pack8(f);
+      accq = mfma(lds8(&sm.y.a.dAq[16 * R + li][32 * ks + 8 * lg]), b, accq);
+      acck = mfma(lds8(&sm.y.a.dM[16 * R + li][32 * ks + 8 * lg]), b, acck);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int r = ref + 4 * lg + jj;
+      const float fr = fast_exp(sm.G[r][ich] - Gref);
+      const float xq = accq[jj] * fr, xk = acck[jj] * fr;
+      oq[R][jj] += xq;
+      okk[R][jj] += xk;
+      oG[R][jj] += bfv(sm.Q[r][ich]) * xq + bfv(sm.K[r][ich]) * xk;
+    }
+  }
+  // Column side: out row j of block J gets sum_r (dA_qk[r,j] q_r + dM[r,j] k_r)
+  // exp(G_r - G_j); split at ref = 16J + 15.
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    const int ref = 16 * J + 15;
+    const bool diag = fmaxf(sm.spr[2 * J], sm.spr[2 * J + 1]) <= kMaxSpread;
+    const int rbeg = diag ? 16 * J : ref + 1;
+    if (rbeg >= C) continue;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const float Gref = sm.G[ref][ich];
+    for (int ks = rbeg / 32; ks < 2; ++ks) {
+      float fq[8], fk[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 32 * ks + 8 * lg + e;
+        const bool ok = r >= rbeg;
+        const float ex = ok ? fast_exp(sm.G[r][ich] - Gref) : 0.f;
+        fq[e] = ok ? bfv(sm.Q[r][ich]) * ex : 0.f;
+        fk[e] = ok ? bfv(sm.K[r][ich]) * ex : 0.f;
+      }
+      acc = mfma(lds8(&sm.y.a.dAqT[16 * J + li][32 * ks + 8 * lg]), pack8(fq), acc);
+      acc = mfma(lds8(&sm.y.a.dMT[16 * J + li][32 * ks + 8 * lg]), pack8(fk), acc);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int j = 16 * J + 4 * lg + jj;
+      const float x = acc[jj] * fast_exp(Gref - sm.G[j][ich]);
+      okk[J][jj] += x;
+      oG[J][jj] -= bfv(sm.K[j][ich]) * x;
+    }
+  }
+  // Diagonal blocks with a gate spread too wide for the split: exact decay per element.
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    if (fmaxf(sm.spr[2 * m], sm.spr[2 * m + 1]) <= kMaxSpread) continue;  // uniform
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int r = 16 * m + 4 * lg + jj;
+      const float Gr = sm.G[r][ich], kr = bfv(sm.K[r][ich]), qr = bfv(sm.Q[r][ich]);
+      float sq = 0.f, sk = 0.f, scol = 0.f;
+      for (int x = 0; x < 16; ++x) {
+        const int j = 16 * m + x;
+        const float Gj = sm.G[j][ich];
+        // row side (j <= r) and column side (this lane's row as the column, x >= its row)
+        const float er = fast_exp(fminf(Gr - Gj, 0.f));
+        const float ec = fast_exp(fminf(Gj - Gr, 0.f));
+        const float kj = bfv(sm.K[j][ich]), qj = bfv(sm.Q[j][ich]);
+        if (j <= r) {
+          sq += bfv(sm.y.a.dAq[r][j]) * kj * er;
+          sk += bfv(sm.y.a.dM[r][j]) * kj * er;
+        } else {
+          scol += (bfv(sm.y.a.dAq[j][r]) * qj + bfv(sm.y.a.dM[j][r]) * kj) * ec;
+        }
+      }
+      scol += bfv(sm.y.a.dAq[r][r]) * qr;  // the diagonal entry (exp(0) = 1)
+      oq[m][jj] += sq;
+      okk[m][jj] += sk + scol;
+      oG[m][jj] += qr * sq + kr * sk - kr * scol;
+    }
+  }
+  __syncthreads();  // every read of K, Q, G and the dA tiles is done
+
+  // ---- 4. dG -> dg by a reverse running sum; dq, dk staged for row stores
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int r = 16 * m + 4 * lg + jj;
+      sm.G[r][ich] = oG[m][jj] + (r == C - 1 ? sm.dgl[ich] : 0.f);
+      sm.K[r][ich] = f32_to_bf16(okk[m][jj]);
+      sm.Q[r][ich] = f32_to_bf16(oq[m][jj]);
+    }
+  __syncthreads();
+  {
+    const int col = tid & 127, qt = tid >> 7;
+    float xs[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) xs[i] = sm.G[16 * qt + i][col];
+#pragma unroll
+    for (int i = 14; i >= 0; --i) xs[i] += xs[i + 1];
+    sm.y.tot[qt][col] = xs[0];
+    __syncthreads();
+    float base = 0.f;
+    for (int j = qt + 1; j < 4; ++j) base += sm.y.tot[j][col];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 16 * qt + i;
+      if (r < c) dg[(row0 + r * rs) * D + col] = xs[i] + base;
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int u = tid + kGradThreads * x, r = u >> 4, cc = (u & 15) * 8;
+    if (r < c) {
+      const size_t gi = (row0 + r * rs) * D + cc;
+      *reinterpret_cast<uint4*>(dk + gi) = *reinterpret_cast<const uint4*>(&sm.K[r][cc]);
+      *reinterpret_cast<uint4*>(dq + gi) = *reinterpret_cast<const uint4*>(&sm.Q[r][cc]);
+    }
+  }
+  if (tid < c) dbeta[row0 + tid * rs] = sm.db[tid];
+}
+
+// Sets the dynamic LDS limit of a kernel once (before its first launch).
+kda_status_t allow_lds(const void* fn, size_t bytes, bool& done, const char* what) {
+  if (done) return KDA_OK;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess) return hip_status(e, what);
+  done = true;
+  return KDA_OK;
+}
+
 }  // namespace
 
 bool chunk_mfma_supported(int dk, int dv, int chunk, int io_dtype) {
@@ -1549,6 +2258,71 @@ kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, cons
   if ((size_t)N * H * 4 <= (size_t)ncu)
     return launch_scan_ws<2, 1, 6>(N, H, w, states, num_slots, slots, flags, o, stream);
   return launch_scan<4, 2>(N, H, w, states, num_slots, slots, flags, o, stream);
+}
+
+size_t chunk_mfma_bwd_workspace_bytes(int H, int32_t T, int32_t N) {
+  const size_t ci = nchunks_max(T, N) * (size_t)H;
+  return header_bytes(N) + align256(ci * kWnBytes) + align256(ci * kQgBytes) +
+         align256(ci * kKdBytes) + align256(ci * kAqBytes) + align256(ci * kUtBytes) +
+         align256(ci * kGcBytes) + align256(ci * kScBytes) + align256(ci * kUcBytes) +
+         3 * align256(ci * kKdBytes) + align256(ci * kAqBytes) + align256(ci * kMkBytes) +
+         align256(ci * kTmBytes) + align256(ci * kScBytes) + align256(ci * kUcBytes) + 256;
+}
+
+kda_status_t launch_chunk_mfma_bwd(const kda_shape_t* sh, int32_t T, int32_t N, const int32_t* cu,
+                                   const void* q, const void* k, const void* v, const float* g,
+                                   const float* beta, const float* states, int32_t num_slots,
+                                   const int32_t* slots, uint32_t flags, const void* d_o,
+                                   const float* d_final, void* dq, void* dk, void* dv, float* dg,
+                                   float* dbeta, float* d_initial, void* workspace,
+                                   hipStream_t stream) {
+  const int H = sh->num_heads;
+  Workspace w = carve(workspace, T, N, H, true);
+  const size_t cap = nchunks_max(T, N);
+  const size_t items = cap * (size_t)H;
+  int dev = 0, ncu = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int x = 0;
+    if (hipDeviceGetAttribute(&x, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && x > 0) ncu = x;
+  }
+  hipLaunchKernelGGL(index_kernel, dim3(1), dim3(64), 0, stream, cu, N, T, (int32_t)cap, w);
+  kda_status_t st = check_launch("chunk_bwd index");
+  if (st != KDA_OK) return st;
+  // chunk operands of the forward pass plus the transposed ones of the reverse pass
+  const unsigned grid = (unsigned)(items < (size_t)ncu ? items : (size_t)ncu);
+  st = launch_prep<kGateChannel, false, false, true>(grid, q, k, v, g, beta, 0.f, N, H, w, stream);
+  if (st != KDA_OK) return st;
+  // forward state pass: S at every chunk start and U
+  constexpr int kGroups = D / 16;
+  static bool lds_state = false, lds_scan = false, lds_grad = false;
+  st = allow_lds(reinterpret_cast<const void*>(scan_state_kernel<1, 1, 7>), sizeof(StateLds<1, 1>),
+                 lds_state, "hipFuncSetAttribute(scan)");
+  if (st != KDA_OK) return st;
+  hipLaunchKernelGGL((scan_state_kernel<1, 1, 7>), dim3((unsigned)(N * H * kGroups)), dim3(64 * 8),
+                     sizeof(StateLds<1, 1>), stream, N, H, w, const_cast<float*>(states), num_slots,
+                     slots, flags & KDA_READ_INITIAL_STATE);
+  st = check_launch("chunk_bwd state scan");
+  if (st != KDA_OK) return st;
+  // reverse pass: dL/dS at every chunk end and dL/dU
+  st = allow_lds(reinterpret_cast<const void*>(scan_grad_kernel<7>), sizeof(GradScanLds), lds_scan,
+                 "hipFuncSetAttribute(reverse scan)");
+  if (st != KDA_OK) return st;
+  hipLaunchKernelGGL((scan_grad_kernel<7>), dim3((unsigned)(N * H * kGroups)), dim3(64 * 8),
+                     sizeof(GradScanLds), stream, N, H, w, static_cast<const uint16_t*>(d_o),
+                     d_final, d_initial);
+  st = check_launch("chunk_bwd reverse scan");
+  if (st != KDA_OK) return st;
+  // gradients of every (chunk, head)
+  st = allow_lds(reinterpret_cast<const void*>(grad_kernel), sizeof(GradSmem), lds_grad,
+                 "hipFuncSetAttribute(grad)");
+  if (st != KDA_OK) return st;
+  hipLaunchKernelGGL(grad_kernel, dim3((unsigned)items), dim3(kGradThreads), sizeof(GradSmem),
+                     stream, N, H, w, w.seq_start, w.seq_end, w.chunk_off,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), g, beta, static_cast<const uint16_t*>(d_o),
+                     static_cast<uint16_t*>(dq), static_cast<uint16_t*>(dk),
+                     static_cast<uint16_t*>(dv), dg, dbeta);
+  return check_launch("chunk_bwd grad");
 }
 
 }  // namespace kda

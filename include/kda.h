@@ -219,6 +219,45 @@ kda_status_t kda_decode_step_raw(const kda_shape_t* shape, int32_t batch, const 
                                  int32_t num_slots, const int32_t* state_slots, uint32_t flags,
                                  void* o, void* stream);
 
+/* Device workspace bytes that kda_chunk_bwd needs (0 for invalid or
+ * unsupported arguments; kda_chunk_bwd reports those). */
+size_t kda_chunk_bwd_workspace_bytes(const kda_shape_t* shape, int32_t chunk,
+                                     int32_t total_tokens, int32_t num_seqs);
+
+/* Gradients of a scalar loss through kda_chunk_fwd (training).
+ *
+ * The chunked form exists for training (engineermaxxing ch. 04; heqinghuang
+ * section 10); the pages give no gradient, so this is reverse-mode
+ * differentiation of the same chunk algebra: a forward pass over the chunks
+ * recomputes the state at every chunk start, a reverse pass carries dL/dS from
+ * the last chunk to the first, and every (chunk, head) then forms its
+ * gradients in parallel.  Results equal the gradients of the token-by-token
+ * recurrence up to rounding.
+ *
+ * Inputs are those of the forward call (same layouts; the per-channel gate,
+ * the delta rule): q, k, v, g, beta, cu_seqlens, and with
+ * KDA_READ_INITIAL_STATE the initial states[slot] (else zero).  g must be <= 0
+ * (alpha <= 1), as for the forward.
+ * d_o            device io dtype [total_tokens, H, dv]: dL/do.
+ * d_final_state  device fp32 dense [num_seqs, H, dk, dv]: dL/dS_final, or NULL (0).
+ * dq, dk         device io dtype [total_tokens, H, dk] (16-byte aligned);
+ * dv             device io dtype [total_tokens, H, dv];
+ * dg             device fp32 [total_tokens, H, dk];  dbeta: device fp32 [total_tokens, H].
+ *                All fully overwritten.
+ * d_initial_state  device fp32 dense [num_seqs, H, dk, dv]: dL/dS0, or NULL (not formed).
+ * flags          0 or KDA_READ_INITIAL_STATE; other bits are KDA_ERR_INVALID_ARGUMENT.
+ * workspace      device scratch of kda_chunk_bwd_workspace_bytes() bytes, 256-byte
+ *                aligned (about 345 KiB per chunk and head).
+ * Supported: io_dtype KDA_BF16, dk = dv = 128, chunk 64 (else KDA_ERR_UNSUPPORTED).
+ * total_tokens == 0 or num_seqs == 0 is a no-op returning KDA_OK. */
+kda_status_t kda_chunk_bwd(const kda_shape_t* shape, int32_t chunk, int32_t total_tokens,
+                           int32_t num_seqs, const int32_t* cu_seqlens, const void* q,
+                           const void* k, const void* v, const float* g, const float* beta,
+                           const float* states, int32_t num_slots, const int32_t* state_slots,
+                           uint32_t flags, const void* d_o, const float* d_final_state, void* dq,
+                           void* dk, void* dv, float* dg, float* dbeta, float* d_initial_state,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Composition of a segment's effect on its incoming state, for context-parallel
  * prefill of one long sequence split into segments (one per GPU):
  *

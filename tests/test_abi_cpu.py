@@ -148,3 +148,15 @@ def test_validation_errors_before_any_launch(lib):
     assert b"overlaps" in lib.kda_last_error()
     assert aff(sh, 2, P(0x10000), P(0x10000 + 8 * per), P(0x10000 + 4 * per),
                P(0x10000 + 4 * per + 4)) == 1                        # partial overlap with B
+    # backward: bf16 d=128 chunk 64 only; state flags other than READ_INITIAL rejected
+    bwd = lambda shape, chunk, flags, ptr, states=None, ws=None, wsb=0: lib.kda_chunk_bwd(
+        ctypes.byref(shape), chunk, 128, 1, fake, ptr, fake, fake, fake, fake, states, 1, None,
+        flags, fake, None, fake, fake, fake, fake, fake, None, ws, wsb, None)
+    assert bwd(_shape(16, 128, 128, 0), 64, 0, fake) == 2           # fp32 io
+    assert bwd(sh, 32, 0, fake) == 2
+    assert bwd(sh, 64, 2, fake) == 1                                 # WRITE_FINAL is forward-only
+    assert bwd(sh, 64, 0, None) == 1                                 # q NULL
+    assert bwd(sh, 64, 1, fake) == 1                                 # initial state without states
+    assert bwd(sh, 64, 0, fake) == 3                                 # workspace missing
+    assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(sh), 64, 4096, 1) > 0
+    assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(_shape(16, 64, 64, 1)), 64, 4096, 1) == 0
