@@ -1796,7 +1796,7 @@ struct GradSmem {
   float spr[kGradThreads / 64];
   union {
     float T[C][AP];       // phase 0
-    uint16_t dR[C][HB];   // phase 1
+    uint16_t dR[C][KB];   // phase 1: all 128 value columns
   } x;
   union {
     struct {
@@ -1815,13 +1815,47 @@ struct GradSmem {
   } y;
 };
 
+// Workspace blocks the gradient kernel reads.
+struct GradWs {
+  const uint8_t* tm;
+  const uint8_t* mkk;
+  const uint8_t* sc;
+  const uint8_t* uc;
+  const uint8_t* dsc;
+  const uint8_t* duc;
+};
+
+// v[i] summed over the 16 lanes of a row group (lanes li = 0..15); lane li
+// returns the sum of index li.  A butterfly that halves the values carried at
+// every step: 15 shuffles instead of 64.
+__device__ __forceinline__ float row_sum16_transposed(const float (&v)[16], int li) {
+  float a[8], b[4], c2[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bool hi = li & 8;
+    a[i] = (hi ? v[i + 8] : v[i]) + __shfl_xor(hi ? v[i] : v[i + 8], 8, 64);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool hi = li & 4;
+    b[i] = (hi ? a[i + 4] : a[i]) + __shfl_xor(hi ? a[i] : a[i + 4], 4, 64);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const bool hi = li & 2;
+    c2[i] = (hi ? b[i + 2] : b[i]) + __shfl_xor(hi ? b[i] : b[i + 2], 2, 64);
+  }
+  const bool hi = li & 1;
+  return (hi ? c2[1] : c2[0]) + __shfl_xor(hi ? c2[0] : c2[1], 1, 64);
+}
+
 __device__ __forceinline__ bf16x8 lds8(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 __device__ __forceinline__ float bfv(uint16_t b) { return bf16_to_f32(b); }
 
 __global__ __launch_bounds__(kGradThreads) void grad_kernel(
-    int32_t N, int H, Workspace w, const int32_t* __restrict__ seq_start,
+    int32_t N, int H, GradWs w, const int32_t* __restrict__ seq_start,
     const int32_t* __restrict__ seq_end, const int32_t* __restrict__ chunk_off,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const uint16_t* __restrict__ d_o,
@@ -1829,6 +1863,9 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
     float* __restrict__ dg, float* __restrict__ dbeta) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   GradSmem& sm = *reinterpret_cast<GradSmem*>(smem_raw);
+  float pb[16];  // dbeta partials of rows 16m + 4lg + jj at [4m + jj], over this lane's columns
+#pragma unroll
+  for (int i = 0; i < 16; ++i) pb[i] = 0.f;
   const Header hd{seq_start, seq_end, chunk_off};
   const int item = blockIdx.x;
   if (item >= hd.chunk_off[N] * H) return;  // uniform
@@ -1887,22 +1924,47 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
     for (int off = 32; off >= 1; off >>= 1) sp = fmaxf(sp, __shfl_xor(sp, off, 64));
     if (lane == 0) sm.spr[wave] = sp;  // waves 2qt and 2qt + 1 cover block qt
   }
-  // T^T as the A operand of dR = T^T dU (M = row r, K = row j, kpos order):
-  // this wave's dR tiles are column tile ct of a half and row tiles mb, mb + 1.
-  const int ct = wave & 3, mb = (wave >> 2) * 2;
-  bf16x8 tT[2][2];
+  // T^T as the A operand of dR = T^T dU (M = row r, K = row j, kpos order); T^T is
+  // zero for K rows 0..31 of row tiles 2 and 3.
+  bf16x8 tT[4][2];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
+      if (m >= 2 && s2 == 0) continue;
       float f[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = sm.x.T[32 * s2 + kpos(lg, e)][16 * (mb + mi) + li];
-      tT[mi][s2] = pack8(f);
+      for (int e = 0; e < 8; ++e) f[e] = sm.x.T[32 * s2 + kpos(lg, e)][16 * m + li];
+      tT[m][s2] = pack8(f);
     }
   __syncthreads();  // T is read; its space holds dR from here
 
-  // ---- 1. the two halves of the value columns
+  // ---- 1. dR = T^T dU for value column tile `wave` (dU straight from the reverse
+  // pass), then dV = Diag(beta) dR and the dbeta term rowsum(dR * V)
+  {
+    const bf16x8* duc = reinterpret_cast<const bf16x8*>(w.duc + ci * kUcBytes);
+    const bf16x8 dub0 = duc[(wave * 2 + 0) * 64 + lane], dub1 = duc[(wave * 2 + 1) * 64 + lane];
+    const int cg = 16 * wave + li;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      f32x4 r2 = {0.f, 0.f, 0.f, 0.f};
+      if (m < 2) r2 = mfma(tT[m][0], dub0, r2);
+      r2 = mfma(tT[m][1], dub1, r2);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = 16 * m + 4 * lg + jj;
+        const float x = r2[jj];
+        sm.x.dR[r][cg] = f32_to_bf16(x);
+        if (r < c) {
+          const size_t gi = (row0 + r * rs) * D + cg;
+          dv[gi] = f32_to_bf16(sm.bs[r] * x);
+          pb[4 * m + jj] += x * bf16_to_f32(v[gi]);  // dbeta_r += sum_c dR V
+        }
+      }
+    }
+  }
+
+  // the two halves of the value columns
   f32x4 aZ[4], aQ[4], aK[4], aAq[2], aAk[2];
 #pragma unroll
   for (int m = 0; m < 4; ++m) aZ[m] = aQ[m] = aK[m] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1911,10 +1973,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
   const u16x8* uc = reinterpret_cast<const u16x8*>(w.uc + ci * kUcBytes);
   const u16x8* sc = reinterpret_cast<const u16x8*>(w.sc + ci * kScBytes);
   const u16x8* dsc = reinterpret_cast<const u16x8*>(w.dsc + ci * kScBytes);
-  const bf16x8* duc = reinterpret_cast<const bf16x8*>(w.duc + ci * kUcBytes);
   for (int hf = 0; hf < 2; ++hf) {
-    const int ctg = 4 * hf + ct;  // dR column tile in the whole row
-    const bf16x8 dub0 = duc[(ctg * 2 + 0) * 64 + lane], dub1 = duc[(ctg * 2 + 1) * 64 + lane];
     {
       const int r = tid >> 3, cc = (tid & 7) * 8;
       *reinterpret_cast<uint4*>(&sm.y.h.dO[r][cc]) =
@@ -1943,60 +2002,25 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
       }
     }
     __syncthreads();
-    // dR = T^T dU (T^T is zero for K rows 0..31 of row tiles 2, 3)
-    {
-      f32x4 r2[2];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
-        r2[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (mb + mi < 2) r2[mi] = mfma(tT[mi][0], dub0, r2[mi]);
-        r2[mi] = mfma(tT[mi][1], dub1, r2[mi]);
-      }
-      const int cl = 16 * ct + li, cg = 64 * hf + cl;
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int r = 16 * (mb + mi) + 4 * lg + jj;
-          const float x = r2[mi][jj];
-          sm.x.dR[r][cl] = f32_to_bf16(x);
-          float p = 0.f;
-          if (r < c) {
-            const size_t gi = (row0 + r * rs) * D + cg;
-            dv[gi] = f32_to_bf16(sm.bs[r] * x);
-            p = x * bf16_to_f32(v[gi]);
-          }
-#pragma unroll
-          for (int o = 1; o < 16; o <<= 1) p += __shfl_xor(p, o, 64);
-          if (li == 0) atomicAdd(&sm.db[r], p);
-        }
-    }
-    __syncthreads();
     // products over the half's 64 columns; plain operands, K = column
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int cc = 32 * ks + 8 * lg;
+      const int cc = 32 * ks + 8 * lg, ccg = 64 * hf + cc;
       const bf16x8 bS = lds8(&sm.y.h.S[16 * wave + li][cc]);
       const bf16x8 bX = lds8(&sm.y.h.dS[16 * wave + li][cc]);
-      bf16x8 aR[4], aO[4], aU[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        aR[m] = lds8(&sm.x.dR[16 * m + li][cc]);
-        aO[m] = lds8(&sm.y.h.dO[16 * m + li][cc]);
-        aU[m] = lds8(&sm.y.h.U[16 * m + li][cc]);
-      }
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        aZ[m] = mfma(aR[m], bS, aZ[m]);
-        aQ[m] = mfma(aO[m], bS, aQ[m]);
-        aK[m] = mfma(aU[m], bX, aK[m]);
+        aZ[m] = mfma(lds8(&sm.x.dR[16 * m + li][ccg]), bS, aZ[m]);
+        aQ[m] = mfma(lds8(&sm.y.h.dO[16 * m + li][cc]), bS, aQ[m]);
+        aK[m] = mfma(lds8(&sm.y.h.U[16 * m + li][cc]), bX, aK[m]);
       }
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int tt = wave + 8 * x, R = tt >> 2, J = tt & 3;
         if (J <= R) {
-          aAq[x] = mfma(aO[R], aU[J], aAq[x]);
-          aAk[x] = mfma(aR[R], aU[J], aAk[x]);
+          const bf16x8 bU = lds8(&sm.y.h.U[16 * J + li][cc]);
+          aAq[x] = mfma(lds8(&sm.y.h.dO[16 * R + li][cc]), bU, aAq[x]);
+          aAk[x] = mfma(lds8(&sm.x.dR[16 * R + li][ccg]), bU, aAk[x]);
         }
       }
     }
@@ -2032,10 +2056,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
       okk[m][jj] = dkg * gam + dkd * ed;
       oG[m][jj] = (dqg * qr + dkg * kr) * gam - dkd * kdv;
       kdsum += dkd * kdv;
-      float p = kr * gam * z;  // dbeta_r -= sum_i (K*Gam)[r,i] Z[r,i]
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) p += __shfl_xor(p, o, 64);
-      if (li == 0) atomicAdd(&sm.db[r], -p);
+      pb[4 * m + jj] -= kr * gam * z;  // dbeta_r -= sum_i (K*Gam)[r,i] Z[r,i]
     }
   kdsum += __shfl_xor(kdsum, 16, 64);
   kdsum += __shfl_xor(kdsum, 32, 64);
@@ -2052,10 +2073,10 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
         const float aq = low && j <= r ? aAq[x][jj] : 0.f;
         const float ak = low && j < r ? -aAk[x][jj] : 0.f;   // dA_kk = -(dR U^T)
         const float mv = low && j < r ? mk[r * C + j] : 0.f;
-        float p = ak * mv;  // dbeta_r += sum_j dA_kk[r,j] M_kk[r,j]
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) p += __shfl_xor(p, o, 64);
-        if (li == 0) atomicAdd(&sm.db[r], p);
+        // dbeta_r += sum_j dA_kk[r,j] M_kk[r,j]; R is 0 or 1 (x = 0), 2 or 3 (x = 1)
+        const float add = ak * mv;
+        pb[8 * x + jj] += (R & 1) ? 0.f : add;
+        pb[8 * x + 4 + jj] += (R & 1) ? add : 0.f;
         const uint16_t bq = f32_to_bf16(aq), bm = f32_to_bf16(sm.bs[r] * ak);
         sm.y.a.dAq[r][j] = bq;
         sm.y.a.dAqT[j][r] = bq;
@@ -2064,6 +2085,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
       }
     }
   }
+  atomicAdd(&sm.db[16 * (li >> 2) + 4 * lg + (li & 3)], row_sum16_transposed(pb, li));
   __syncthreads();
 
   // ---- 3. decayed products
@@ -2140,6 +2162,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
       const int r = 16 * m + 4 * lg + jj;
       const float Gr = sm.G[r][ich], kr = bfv(sm.K[r][ich]), qr = bfv(sm.Q[r][ich]);
       float sq = 0.f, sk = 0.f, scol = 0.f;
+#pragma unroll 1
       for (int x = 0; x < 16; ++x) {
         const int j = 16 * m + x;
         const float Gj = sm.G[j][ich];
@@ -2317,7 +2340,8 @@ kda_status_t launch_chunk_mfma_bwd(const kda_shape_t* sh, int32_t T, int32_t N, 
                  "hipFuncSetAttribute(grad)");
   if (st != KDA_OK) return st;
   hipLaunchKernelGGL(grad_kernel, dim3((unsigned)items), dim3(kGradThreads), sizeof(GradSmem),
-                     stream, N, H, w, w.seq_start, w.seq_end, w.chunk_off,
+                     stream, N, H, GradWs{w.tm, w.mkk, w.sc, w.uc, w.dsc, w.duc}, w.seq_start,
+                     w.seq_end, w.chunk_off,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), g, beta, static_cast<const uint16_t*>(d_o),
                      static_cast<uint16_t*>(dq), static_cast<uint16_t*>(dk),
