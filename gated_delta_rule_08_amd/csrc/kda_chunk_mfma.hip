@@ -534,7 +534,6 @@ __device__ __forceinline__ void prep_role(
     lds_barrier();
 
     // ---- gated Gram blocks (10 block pairs over 8 waves)
-    float aq_keep[2][4];  // backward: A_qk of this wave's pairs, transposed through LDS below
     {
       uint16_t* aq_out = reinterpret_cast<uint16_t*>(w.aq + ci * kAqBytes);
       for (int pi = wave; pi < 10; pi += kPrepWaves) {
@@ -563,8 +562,14 @@ __device__ __forceinline__ void prep_role(
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) (&mrow.x)[jj] = 16 * J + 4 * lg + jj < r ? acck[jj] : 0.f;
           *reinterpret_cast<float4*>(w.mkk + ci * kMkBytes + (size_t)(r * C + 16 * J + 4 * lg) * 4) = mrow;
+          // A_qk^T as the reverse scan's A operand (M = column j, K = row r, kpos
+          // order): every value lands in another lane's slot, so 2-byte stores
+          const int ro = 16 * (R & 1) + li;  // row inside the 32-row K block R / 2
+          const int slot = (ro & 3) + 4 * (ro >> 4), lgd = (ro & 15) >> 2;
+          uint16_t* at = reinterpret_cast<uint16_t*>(w.aqt + ci * kAqBytes) +
+                         ((size_t)(J * 2 + (R >> 1)) * 64 + lgd * 16) * 8 + slot;
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) aq_keep[pi >= kPrepWaves][jj] = qv[jj];
+          for (int jj = 0; jj < 4; ++jj) at[(4 * lg + jj) * 8] = f32_to_bf16(qv[jj]);
         }
         // A_qk as the scan's A operand: [m = R][s' = J / 2][lane][slots (J & 1) * 4 ..]
         uint16_t* dst = aq_out + ((size_t)(R * 2 + (J >> 1)) * 64 + lane) * 8 + (J & 1) * 4;
@@ -581,13 +586,16 @@ __device__ __forceinline__ void prep_role(
     }
     lds_barrier();
     if constexpr (kBwd) {
-      // A_qk into the row-side operand space (free after the Gram phase): [r][j]
-      float(*aqs)[AP] = reinterpret_cast<float(*)[AP]>(&sm.rk[0][0]);
-      for (int pi = wave, x = 0; pi < 10; pi += kPrepWaves, ++x) {
-        const int R = pi < 4 ? 3 : pi < 7 ? 2 : pi < 9 ? 1 : 0;
-        const int J = pi < 4 ? 3 - pi : pi < 7 ? 6 - pi : pi < 9 ? 8 - pi : 0;
-        *reinterpret_cast<float4*>(&aqs[16 * R + li][16 * J + 4 * lg]) =
-            make_float4(aq_keep[x][0], aq_keep[x][1], aq_keep[x][2], aq_keep[x][3]);
+      // zeros of A_qk^T where A_qk is above the diagonal: pairs (R, J), J > R
+      if (wave < 6) {
+        const int R = wave < 3 ? 0 : wave < 5 ? 1 : 2;
+        const int J = wave < 3 ? wave + 1 : wave < 5 ? wave - 1 : 3;
+        const int ro = 16 * (R & 1) + li;
+        const int slot = (ro & 3) + 4 * (ro >> 4), lgd = (ro & 15) >> 2;
+        uint16_t* at = reinterpret_cast<uint16_t*>(w.aqt + ci * kAqBytes) +
+                       ((size_t)(J * 2 + (R >> 1)) * 64 + lgd * 16) * 8 + slot;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) at[(4 * lg + jj) * 8] = 0;
       }
     }
 
@@ -674,56 +682,6 @@ __device__ __forceinline__ void prep_role(
         *reinterpret_cast<bf16x8*>(kd_out + ((size_t)(tile * 2 + s2) * 64 + lane) * 8) = pack8(fd);
         abkg[s2] = pack8(fb);
         bv[s2] = pack8(fv);
-        if constexpr (kBwd) {
-          // (Q*Gam)^T as the reverse scan's A operand (M = channel, K = row)
-          float fq[8];
-#pragma unroll
-          for (int qq = 0; qq < 8; ++qq) {
-            const int j = 32 * s2 + kpos(lg, qq);
-            fq[qq] = ld_bf(sm.Q[j], ch) * fast_exp(sm.G[j][ch]);
-          }
-          *reinterpret_cast<bf16x8*>(w.qgt + ci * kKdBytes + ((size_t)(tile * 2 + s2) * 64 + lane) * 16) =
-              pack8(fq);
-        }
-      }
-      if constexpr (kBwd) {
-        // -W^T (M = channel, K = row): W tiles with rows in the accumulator, packed in pairs
-        f32x4 wr[4];
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          wr[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-          wr[nt] = mfma(tt[nt][0], abkg[0], wr[nt]);
-          if (nt >= 2) wr[nt] = mfma(tt[nt][1], abkg[1], wr[nt]);
-        }
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-          *reinterpret_cast<bf16x8*>(w.wt + ci * kKdBytes + ((size_t)(tile * 2 + s2) * 64 + lane) * 16) =
-              pack_acc(-wr[2 * s2], -wr[2 * s2 + 1]);
-        // Kd as an A operand (M = row, K = channel) and A_qk^T (M = column j, K = row r),
-        // two operand tiles of each per wave
-        const float(*aqs)[AP] = reinterpret_cast<const float(*)[AP]>(&sm.rk[0][0]);
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          const int opi = wave * 2 + x, m = opi >> 2, sk = opi & 3, r = 16 * m + li;
-          float fk[8];
-#pragma unroll
-          for (int qq = 0; qq < 8; ++qq) {
-            const int cc = 32 * sk + kpos(lg, qq);
-            fk[qq] = ld_bf(sm.K[r], cc) * fast_exp(sm.G[C - 1][cc] - sm.G[r][cc]);
-          }
-          *reinterpret_cast<bf16x8*>(w.kdr + ci * kKdBytes + ((size_t)opi * 64 + lane) * 16) = pack8(fk);
-        }
-        {
-          const int m = wave >> 1, s2 = wave & 1, j = 16 * m + li;
-          float fa[8];
-#pragma unroll
-          for (int qq = 0; qq < 8; ++qq) {
-            const int rr = 32 * s2 + kpos(lg, qq);
-            fa[qq] = (rr >> 4) >= m ? aqs[rr][j] : 0.f;  // blocks above the diagonal are zero
-          }
-          *reinterpret_cast<bf16x8*>(w.aqt + ci * kAqBytes + ((size_t)(m * 2 + s2) * 64 + lane) * 16) =
-              pack8(fa);
-        }
       }
       // -W: [m = nt][s = tile / 2][lane][slots (tile & 1) * 4 ..]
       uint16_t* wn_out = reinterpret_cast<uint16_t*>(w.wn + ci * kWnBytes);
@@ -745,6 +703,50 @@ __device__ __forceinline__ void prep_role(
         *reinterpret_cast<f32x4*>(ut_out + ((size_t)(nt * 8 + tile) * 64 + lane) * 4) = u;
       }
       if (tid < D) reinterpret_cast<float*>(w.gc + ci * kGcBytes)[tid] = fast_exp(sm.G[C - 1][tid]);
+      if constexpr (kBwd) {
+        // -W^T (M = channel, K = row): W tiles with rows in the accumulator, packed in pairs
+        f32x4 wr[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          wr[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          wr[nt] = mfma(tt[nt][0], abkg[0], wr[nt]);
+          if (nt >= 2) wr[nt] = mfma(tt[nt][1], abkg[1], wr[nt]);
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+          *reinterpret_cast<bf16x8*>(w.wt + ci * kKdBytes + ((size_t)(tile * 2 + s2) * 64 + lane) * 16) =
+              pack_acc(-wr[2 * s2], -wr[2 * s2 + 1]);
+      }
+    }
+    if constexpr (kBwd) {
+      // the reverse pass's other operands, from LDS only
+      {
+        // (Q*Gam)^T as the reverse scan's A operand (M = channel, K = row)
+        const int ch = 16 * wave + li;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          float fq[8];
+#pragma unroll
+          for (int qq = 0; qq < 8; ++qq) {
+            const int j = 32 * s2 + kpos(lg, qq);
+            fq[qq] = ld_bf(sm.Q[j], ch) * fast_exp(sm.G[j][ch]);
+          }
+          *reinterpret_cast<bf16x8*>(w.qgt + ci * kKdBytes +
+                                     ((size_t)(wave * 2 + s2) * 64 + lane) * 16) = pack8(fq);
+        }
+      }
+      // Kd as an A operand (M = row, K = channel), two operand tiles per wave
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int opi = wave * 2 + x, m = opi >> 2, sk = opi & 3, r = 16 * m + li;
+        float fk[8];
+#pragma unroll
+        for (int qq = 0; qq < 8; ++qq) {
+          const int cc = 32 * sk + kpos(lg, qq);
+          fk[qq] = ld_bf(sm.K[r], cc) * fast_exp(sm.G[C - 1][cc] - sm.G[r][cc]);
+        }
+        *reinterpret_cast<bf16x8*>(w.kdr + ci * kKdBytes + ((size_t)opi * 64 + lane) * 16) = pack8(fk);
+      }
     }
   }
 }
@@ -1849,6 +1851,14 @@ __device__ __forceinline__ float row_sum16_transposed(const float (&v)[16], int 
   return (hi ? c2[1] : c2[0]) + __shfl_xor(hi ? c2[0] : c2[1], 1, 64);
 }
 
+// Workgroup barrier after which every LDS value is re-read: the empty asm keeps
+// the compiler from carrying values loaded before it (which would only raise
+// register pressure: LDS reads are cheap).
+__device__ __forceinline__ void block_sync() {
+  __syncthreads();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ bf16x8 lds8(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
@@ -1905,7 +1915,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
       *reinterpret_cast<float4*>(&sm.x.T[r][c4]) = *reinterpret_cast<const float4*>(tm + r * C + c4);
     }
   }
-  __syncthreads();
+  block_sync();
   {
     const int col = tid & 127, qt = tid >> 7;
     float xs[16];
@@ -1914,7 +1924,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
 #pragma unroll
     for (int i = 1; i < 16; ++i) xs[i] += xs[i - 1];
     sm.y.tot[qt][col] = xs[15];
-    __syncthreads();
+    block_sync();
     float base = 0.f;
     for (int j = 0; j < qt; ++j) base += sm.y.tot[j][col];
 #pragma unroll
@@ -1937,7 +1947,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
       for (int e = 0; e < 8; ++e) f[e] = sm.x.T[32 * s2 + kpos(lg, e)][16 * m + li];
       tT[m][s2] = pack8(f);
     }
-  __syncthreads();  // T is read; its space holds dR from here
+  block_sync();  // T is read; its space holds dR from here
 
   // ---- 1. dR = T^T dU for value column tile `wave` (dU straight from the reverse
   // pass), then dV = Diag(beta) dR and the dbeta term rowsum(dR * V)
@@ -2001,7 +2011,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
         sm.y.h.dS[r][cl] = d8[e];
       }
     }
-    __syncthreads();
+    block_sync();
     // products over the half's 64 columns; plain operands, K = column
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -2031,7 +2041,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
       for (int e = 0; e < 16; ++e) s += bfv(sm.y.h.S[i][c0 + e]) * bfv(sm.y.h.dS[i][c0 + e]);
       dgc += s;
     }
-    __syncthreads();  // the tiles are read before the next half (or phase 2) overwrites them
+    block_sync();  // the tiles are read before the next half (or phase 2) overwrites them
   }
   dgc += __shfl_xor(dgc, 1, 64);
   dgc += __shfl_xor(dgc, 2, 64);
@@ -2086,7 +2096,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
     }
   }
   atomicAdd(&sm.db[16 * (li >> 2) + 4 * lg + (li & 3)], row_sum16_transposed(pb, li));
-  __syncthreads();
+  block_sync();
 
   // ---- 3. decayed products
   // Row side: out row r of block R gets sum_j dA[r,j] k_j exp(G_r - G_j); split at
@@ -2153,10 +2163,13 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
       oG[J][jj] -= bfv(sm.K[j][ich]) * x;
     }
   }
-  // Diagonal blocks with a gate spread too wide for the split: exact decay per element.
-#pragma unroll
+  // Diagonal blocks with a gate spread too wide for the split: exact decay per
+  // element (rare; kept rolled so that it does not add to the register load of
+  // the common path).
+#pragma unroll 1
   for (int m = 0; m < 4; ++m) {
     if (fmaxf(sm.spr[2 * m], sm.spr[2 * m + 1]) <= kMaxSpread) continue;  // uniform
+    float aq4[4], ak4[4], ag4[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int r = 16 * m + 4 * lg + jj;
@@ -2166,7 +2179,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
       for (int x = 0; x < 16; ++x) {
         const int j = 16 * m + x;
         const float Gj = sm.G[j][ich];
-        // row side (j <= r) and column side (this lane's row as the column, x >= its row)
+        // row side (j <= r) and column side (this lane's row as the column, j > r)
         const float er = fast_exp(fminf(Gr - Gj, 0.f));
         const float ec = fast_exp(fminf(Gj - Gr, 0.f));
         const float kj = bfv(sm.K[j][ich]), qj = bfv(sm.Q[j][ich]);
@@ -2178,12 +2191,22 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
         }
       }
       scol += bfv(sm.y.a.dAq[r][r]) * qr;  // the diagonal entry (exp(0) = 1)
-      oq[m][jj] += sq;
-      okk[m][jj] += sk + scol;
-      oG[m][jj] += qr * sq + kr * sk - kr * scol;
+      aq4[jj] = sq;
+      ak4[jj] = sk + scol;
+      ag4[jj] = qr * sq + kr * sk - kr * scol;
     }
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm)
+      if (mm == m) {  // uniform branch: compile-time register indices
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          oq[mm][jj] += aq4[jj];
+          okk[mm][jj] += ak4[jj];
+          oG[mm][jj] += ag4[jj];
+        }
+      }
   }
-  __syncthreads();  // every read of K, Q, G and the dA tiles is done
+  block_sync();  // every read of K, Q, G and the dA tiles is done
 
   // ---- 4. dG -> dg by a reverse running sum; dq, dk staged for row stores
 #pragma unroll
@@ -2195,7 +2218,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
       sm.K[r][ich] = f32_to_bf16(okk[m][jj]);
       sm.Q[r][ich] = f32_to_bf16(oq[m][jj]);
     }
-  __syncthreads();
+  block_sync();
   {
     const int col = tid & 127, qt = tid >> 7;
     float xs[16];
@@ -2204,7 +2227,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
 #pragma unroll
     for (int i = 14; i >= 0; --i) xs[i] += xs[i + 1];
     sm.y.tot[qt][col] = xs[0];
-    __syncthreads();
+    block_sync();
     float base = 0.f;
     for (int j = qt + 1; j < 4; ++j) base += sm.y.tot[j][col];
 #pragma unroll
