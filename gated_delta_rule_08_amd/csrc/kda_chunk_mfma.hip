@@ -1859,6 +1859,13 @@ __device__ __forceinline__ void block_sync() {
   asm volatile("" ::: "memory");
 }
 
+// x where ok, else all-zero bits: a per-component mask (a select of whole vectors
+// can be lowered through private memory).
+__device__ __forceinline__ uint4 keep_if(uint4 x, bool ok) {
+  const uint32_t m = ok ? 0xFFFFFFFFu : 0u;
+  return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
+}
+
 __device__ __forceinline__ bf16x8 lds8(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
@@ -1886,24 +1893,39 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
   const size_t row0 = (size_t)pos.t0 * H + pos.h;  // token-row of the chunk's first row
   const size_t rs = (size_t)H;                     // token-row stride
 
-  // ---- 0. staging (rows past the end are zero)
-  const uint4 z4 = make_uint4(0, 0, 0, 0);
+  // ---- 0. staging (rows past the end are zero).  Loads are issued for every
+  // row (rows past the end re-read the last row) and the zeros are selected
+  // afterwards, so that no load sits behind a branch and they overlap.
+  {
+    uint4 kx[2], qx[2];
+    uint4 gx[4];
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int u = tid + kGradThreads * x, r = u >> 4, cc = (u & 15) * 8;
-    const size_t gi = (row0 + r * rs) * D + cc;
-    *reinterpret_cast<uint4*>(&sm.K[r][cc]) = r < c ? *reinterpret_cast<const uint4*>(k + gi) : z4;
-    *reinterpret_cast<uint4*>(&sm.Q[r][cc]) = r < c ? *reinterpret_cast<const uint4*>(q + gi) : z4;
-  }
+    for (int x = 0; x < 2; ++x) {
+      const int u = tid + kGradThreads * x, r = min(u >> 4, c - 1), cc = (u & 15) * 8;
+      const size_t gi = (row0 + r * rs) * D + cc;
+      kx[x] = *reinterpret_cast<const uint4*>(k + gi);
+      qx[x] = *reinterpret_cast<const uint4*>(q + gi);
+    }
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int u = tid + kGradThreads * x, r = u >> 5, cc = (u & 31) * 4;
-    *reinterpret_cast<float4*>(&sm.G[r][cc]) =
-        r < c ? *reinterpret_cast<const float4*>(g + (row0 + r * rs) * D + cc)
-              : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int x = 0; x < 4; ++x) {
+      const int u = tid + kGradThreads * x, r = min(u >> 5, c - 1), cc = (u & 31) * 4;
+      gx[x] = *reinterpret_cast<const uint4*>(g + (row0 + r * rs) * D + cc);
+    }
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int u = tid + kGradThreads * x, r = u >> 4, cc = (u & 15) * 8;
+      *reinterpret_cast<uint4*>(&sm.K[r][cc]) = keep_if(kx[x], r < c);
+      *reinterpret_cast<uint4*>(&sm.Q[r][cc]) = keep_if(qx[x], r < c);
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int u = tid + kGradThreads * x, r = u >> 5, cc = (u & 31) * 4;
+      *reinterpret_cast<uint4*>(&sm.G[r][cc]) = keep_if(gx[x], r < c);
+    }
   }
   if (tid < C) {
-    sm.bs[tid] = tid < c ? beta[row0 + tid * rs] : 0.f;
+    const float bt = beta[row0 + min(tid, c - 1) * rs];
+    sm.bs[tid] = tid < c ? bt : 0.f;
     sm.db[tid] = 0.f;
   }
   if (tid < D) sm.dgl[tid] = 0.f;
@@ -1955,6 +1977,12 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
     const bf16x8* duc = reinterpret_cast<const bf16x8*>(w.duc + ci * kUcBytes);
     const bf16x8 dub0 = duc[(wave * 2 + 0) * 64 + lane], dub1 = duc[(wave * 2 + 1) * 64 + lane];
     const int cg = 16 * wave + li;
+    uint16_t vx[4][4];  // V at this lane's dR positions, loaded before any is used
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        vx[m][jj] = v[(row0 + min(16 * m + 4 * lg + jj, c - 1) * rs) * D + cg];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       f32x4 r2 = {0.f, 0.f, 0.f, 0.f};
@@ -1965,11 +1993,8 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
         const int r = 16 * m + 4 * lg + jj;
         const float x = r2[jj];
         sm.x.dR[r][cg] = f32_to_bf16(x);
-        if (r < c) {
-          const size_t gi = (row0 + r * rs) * D + cg;
-          dv[gi] = f32_to_bf16(sm.bs[r] * x);
-          pb[4 * m + jj] += x * bf16_to_f32(v[gi]);  // dbeta_r += sum_c dR V
-        }
+        pb[4 * m + jj] += r < c ? x * bf16_to_f32(vx[m][jj]) : 0.f;  // dbeta_r += sum_c dR V
+        if (r < c) dv[(row0 + r * rs) * D + cg] = f32_to_bf16(sm.bs[r] * x);
       }
     }
   }
@@ -1986,8 +2011,9 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
   for (int hf = 0; hf < 2; ++hf) {
     {
       const int r = tid >> 3, cc = (tid & 7) * 8;
-      *reinterpret_cast<uint4*>(&sm.y.h.dO[r][cc]) =
-          r < c ? *reinterpret_cast<const uint4*>(d_o + (row0 + r * rs) * D + 64 * hf + cc) : z4;
+      const uint4 x = *reinterpret_cast<const uint4*>(d_o + (row0 + min(r, c - 1) * rs) * D +
+                                                      64 * hf + cc);
+      *reinterpret_cast<uint4*>(&sm.y.h.dO[r][cc]) = keep_if(x, r < c);
     }
     {
       // U from the B-operand layout: [column tile][row half][lane], rows in kpos order
@@ -2114,9 +2140,10 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
       float f[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int j = 32 * ks + 8 * lg + e;
-        const float ex = fast_exp(Gref - sm.G[j][ich]);
-        f[e] = j < jend ? bfv(sm.K[j][ich]) * ex : 0.f;
+        const int j = 32 * ks + 8 * lg + e;  // < 64: loaded for every lane, masked after
+        const float kj = bfv(sm.K[j][ich]);
+        const float ex = fast_exp(fminf(Gref - sm.G[j][ich], 88.f));
+        f[e] = j < jend ? kj * ex : 0.f;
       }
       const bf16x8 b = pack8(f);
       accq = mfma(lds8(&sm.y.a.dAq[16 * R + li][32 * ks + 8 * lg]), b, accq);
@@ -2146,11 +2173,12 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
       float fq[8], fk[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int r = 32 * ks + 8 * lg + e;
+        const int r = 32 * ks + 8 * lg + e;  // < 64: loaded for every lane, masked after
         const bool ok = r >= rbeg;
-        const float ex = ok ? fast_exp(sm.G[r][ich] - Gref) : 0.f;
-        fq[e] = ok ? bfv(sm.Q[r][ich]) * ex : 0.f;
-        fk[e] = ok ? bfv(sm.K[r][ich]) * ex : 0.f;
+        const float qr = bfv(sm.Q[r][ich]), kr = bfv(sm.K[r][ich]);
+        const float ex = fast_exp(fminf(sm.G[r][ich] - Gref, 88.f));
+        fq[e] = ok ? qr * ex : 0.f;
+        fk[e] = ok ? kr * ex : 0.f;
       }
       acc = mfma(lds8(&sm.y.a.dAqT[16 * J + li][32 * ks + 8 * lg]), pack8(fq), acc);
       acc = mfma(lds8(&sm.y.a.dMT[16 * J + li][32 * ks + 8 * lg]), pack8(fk), acc);
