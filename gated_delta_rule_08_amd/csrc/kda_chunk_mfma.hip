@@ -2132,11 +2132,12 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
   for (int R = 0; R < 4; ++R) {
     const int ref = 16 * R;
     const bool diag = fmaxf(sm.spr[2 * R], sm.spr[2 * R + 1]) <= kMaxSpread;
-    const int jend = diag ? ref + 16 : ref;
-    if (jend == 0) continue;
+    const int jend = diag ? ref + 16 : ref;  // K rows j < jend (R = 0 without diag: none)
     f32x4 accq = {0.f, 0.f, 0.f, 0.f}, acck = {0.f, 0.f, 0.f, 0.f};
     const float Gref = sm.G[ref][ich];
-    for (int ks = 0; 32 * ks < jend; ++ks) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (32 * ks >= ref + 16) continue;  // compile-time: no row of this K step is used
       float f[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -2165,11 +2166,12 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
   for (int J = 0; J < 4; ++J) {
     const int ref = 16 * J + 15;
     const bool diag = fmaxf(sm.spr[2 * J], sm.spr[2 * J + 1]) <= kMaxSpread;
-    const int rbeg = diag ? 16 * J : ref + 1;
-    if (rbeg >= C) continue;
+    const int rbeg = diag ? 16 * J : ref + 1;  // K rows r >= rbeg (J = 3 without diag: none)
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const float Gref = sm.G[ref][ich];
-    for (int ks = rbeg / 32; ks < 2; ++ks) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (32 * ks + 32 <= 16 * J) continue;  // compile-time: no row of this K step is used
       float fq[8], fk[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
