@@ -40,6 +40,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 PREFILL_BYTES_PER_TOKEN_HEAD = 3 * 2 * 128 + 4 * 128 + 4 + 2 * 128   # q,k,v bf16 + g fp32 + beta + o bf16
 DECODE_BYTES_PER_HEAD = 2 * 128 * 128 * 4 + PREFILL_BYTES_PER_TOKEN_HEAD  # state read+write + token
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+TRAFFIC_BACKWARD_FILE = os.path.join(ROOT, "profiles", "traffic_backward.json")
 
 
 def _source_digest() -> str:
@@ -51,11 +52,11 @@ def _source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic(kind: str):
+def _traffic(kind: str, path: str = TRAFFIC_FILE):
     """HBM bytes per launch from the committed rocprofv3 counter runs, or None
     when the kernel sources changed since they were taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
@@ -227,6 +228,7 @@ def bench_backward(kda, torch, steps, warmup, flush):
     bytes_ = BACKWARD_BYTES_PER_TOKEN_HEAD * T * H
     return {"tokens_per_s": T / (ms * 1e-3), "ms_per_call": ms, "algorithmic_bytes": bytes_,
             "roofline_frac": bytes_ / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "traffic": _traffic("backward_bytes", TRAFFIC_BACKWARD_FILE),
             "workload": "backward_bf16_B1_H16_T4096_d128_C64 (dL/do given, zero initial state)"}
 
 
@@ -284,7 +286,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the prefill timings of the variant flags")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "backward"], default=None,
                     help="run one leg only (for profiling)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one plain device copy of MIB MiB (reference for the "
@@ -346,6 +348,10 @@ def main(argv=None):
         if not args.no_variants:
             out["variants"] = bench_variants(kda, torch, max(5, args.steps // 2), 2, flush)
             out["backward"] = bench_backward(kda, torch, max(5, args.steps // 2), 2, flush)
+    if args.only == "backward":
+        bw = bench_backward(kda, torch, args.steps, args.warmup, flush)
+        out.update({"value": bw["tokens_per_s"], "unit": "tokens/s", "ms_per_step": bw["ms_per_call"],
+                    "config": {"workload": bw["workload"]}, "backward": bw})
     if args.only in (None, "decode"):
         dc = bench_decode(kda, torch, args.steps, args.warmup, flush)
         ms = sum(dc["ms"]) / len(dc["ms"])

@@ -7,8 +7,9 @@
 `stats` prints a table of per-kernel call counts and durations.  `traffic`
 averages FETCH_SIZE and WRITE_SIZE (KiB per dispatch) per kernel, scales both
 by the factor that makes a plain device copy of a known size (an elementwise
-multiply by 1 of a 256 MiB tensor) read and write exactly that size, and writes the HBM bytes per launch of the prefill path
-(index, prep, scan and output kernels) and of the decode kernel, tagged with a digest
+multiply by 1 of a 256 MiB tensor) read and write exactly that size, and writes the HBM bytes
+per launch of the prefill path (index, prep, scan and output kernels) and of the decode kernel
+(or, for a backward-only run, of the backward's launches), tagged with a digest
 of the kernel sources (bench.py reports the figures only while the sources are
 unchanged).
 """
@@ -26,7 +27,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def _short(name: str) -> str:
     for key in ("prep_kernel", "index_kernel", "out_kernel", "decode_kernel", "chunk_small_kernel",
-                "zero_kernel", "gather_scatter_kernel"):
+                "zero_kernel", "gather_scatter_kernel", "scan_grad_kernel", "grad_kernel"):
         if key in name:
             return key
     for key in ("scan_state_kernel", "scan_ws_kernel", "scan_kernel"):
@@ -84,11 +85,15 @@ def traffic(fetch_csv: str, write_csv: str, copy_mib: float, out: str) -> dict:
         fk = fetch.get(k, (0.0, 0))[0] * f_scale * 1024
         wk = write.get(k, (0.0, 0))[0] * w_scale * 1024
         per[k] = {"fetch_bytes": fk, "write_bytes": wk}
-    prefill = sum(per[k]["fetch_bytes"] + per[k]["write_bytes"] for k in per
+    both = lambda k: per[k]["fetch_bytes"] + per[k]["write_bytes"]
+    prefill = sum(both(k) for k in per
                   if k in ("index_kernel", "prep_kernel", "out_kernel") or k.startswith("scan_"))
-    decode = sum(per[k]["fetch_bytes"] + per[k]["write_bytes"] for k in per if k == "decode_kernel")
-    rec = {"source_digest": _source_digest(), "prefill_bytes": prefill or None,
-           "decode_bytes": decode or None, "copy_calibration": {
+    decode = sum(both(k) for k in per if k == "decode_kernel")
+    # a backward-only run (bench.py --only backward): its index, prep and scans are the backward's
+    backward = sum(both(k) for k in per if k in ("index_kernel", "prep_kernel", "grad_kernel")
+                   or k.startswith("scan_")) if "grad_kernel" in per else 0
+    rec = {"source_digest": _source_digest(), "prefill_bytes": (prefill or None) if not backward else None,
+           "decode_bytes": decode or None, "backward_bytes": backward or None, "copy_calibration": {
                "copy_mib": copy_mib, "fetch_scale": f_scale, "write_scale": w_scale},
            "per_kernel": per}
     with open(out, "w") as f:
