@@ -230,14 +230,16 @@ def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens, chunk: int = 64, states=None, st
 
 def kda_chunk_bwd(q, k, v, g, beta, cu_seqlens, d_o, chunk: int = 64, states=None,
                   state_slots=None, read_initial: bool = False, d_final=None,
-                  want_d_initial: bool = False, workspace=None, stream=None, out=None):
+                  want_d_initial: bool = False, workspace=None, stream=None, out=None,
+                  gate: str = "channel", additive: bool = False):
     """Gradients through kda_chunk_fwd (see kda_chunk_bwd in include/kda.h).
 
-    Same inputs as the forward call (per-channel gate, delta rule) plus
-    d_o [T, H, dv] and, optionally, d_final: fp32 [N, H, dk, dv] (dL/dS_final).
-    Returns a dict with dq, dk, dv (dtype of q), dg, dbeta (fp32) and d_initial
-    (fp32 [N, H, dk, dv], dL/dS0) when want_d_initial; ``out`` may hold those
-    tensors already (they are checked and overwritten).
+    Same inputs and variant arguments as the forward call plus d_o [T, H, dv] and,
+    optionally, d_final: fp32 [N, H, dk, dv] (dL/dS_final).  Returns a dict with
+    dq, dk, dv (dtype of q), dg (fp32, shaped like g; None for gate="none"), dbeta
+    (fp32; None when additive) and d_initial (fp32 [N, H, dk, dv], dL/dS0) when
+    want_d_initial; ``out`` may hold those tensors already (they are checked and
+    overwritten).
     """
     lib = load_library()
     T, H, dk = q.shape
@@ -245,8 +247,7 @@ def kda_chunk_bwd(q, k, v, g, beta, cu_seqlens, d_o, chunk: int = 64, states=Non
     io = _io_dtype(q)
     for t, name, d in ((q, "q", dk), (k, "k", dk), (v, "v", dv), (d_o, "d_o", dv)):
         _need(t, name, (T, H, d), q.dtype)
-    _need(g, "g", (T, H, dk), torch.float32)
-    _need(beta, "beta", (T, H), torch.float32)
+    _need_gate_beta(g, beta, (T, H), dk, gate, additive)
     N = cu_seqlens.numel() - 1
     _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32)
     num_slots = 0
@@ -257,17 +258,21 @@ def kda_chunk_bwd(q, k, v, g, beta, cu_seqlens, d_o, chunk: int = 64, states=Non
         _need(state_slots, "state_slots", (N,), torch.int32)
     if d_final is not None:
         _need(d_final, "d_final", (N, H, dk, dv), torch.float32)
+    g_shape = {"channel": (T, H, dk), "scalar": (T, H), "none": None}[gate]
     if out is None:
         out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
-                   dg=torch.empty((T, H, dk), dtype=torch.float32, device=q.device),
-                   dbeta=torch.empty((T, H), dtype=torch.float32, device=q.device))
+                   dg=None if g_shape is None else torch.empty(g_shape, dtype=torch.float32,
+                                                               device=q.device),
+                   dbeta=None if additive else torch.empty((T, H), dtype=torch.float32,
+                                                           device=q.device))
         out["d_initial"] = (torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
                             if want_d_initial else None)
     else:
         for name, shape, dt in (("dq", (T, H, dk), q.dtype), ("dk", (T, H, dk), q.dtype),
-                                ("dv", (T, H, dv), q.dtype), ("dg", (T, H, dk), torch.float32),
-                                ("dbeta", (T, H), torch.float32)):
-            _need(out.get(name), name, shape, dt)
+                                ("dv", (T, H, dv), q.dtype), ("dg", g_shape, torch.float32),
+                                ("dbeta", None if additive else (T, H), torch.float32)):
+            if shape is not None:
+                _need(out.get(name), name, shape, dt)
         if out.get("d_initial") is not None:
             _need(out["d_initial"], "d_initial", (N, H, dk, dv), torch.float32)
     sh = _Shape(H, dk, dv, io)
@@ -275,12 +280,12 @@ def kda_chunk_bwd(q, k, v, g, beta, cu_seqlens, d_o, chunk: int = 64, states=Non
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    flags = KDA_READ_INITIAL_STATE if read_initial else 0
+    flags = (KDA_READ_INITIAL_STATE if read_initial else 0) | _variant_flags(gate, additive)
     _check(lib.kda_chunk_bwd(ctypes.byref(sh), chunk, T, N, _ptr(cu_seqlens), _ptr(q), _ptr(k),
                              _ptr(v), _ptr(g), _ptr(beta), _ptr(states), num_slots,
                              _ptr(state_slots), flags, _ptr(d_o), _ptr(d_final), _ptr(out["dq"]),
-                             _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
-                             _ptr(out["dbeta"]), _ptr(out["d_initial"]), _ptr(workspace),
+                             _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out.get("dg")),
+                             _ptr(out.get("dbeta")), _ptr(out.get("d_initial")), _ptr(workspace),
                              ws_bytes, _stream(stream)))
     return out
 

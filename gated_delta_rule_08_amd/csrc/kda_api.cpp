@@ -375,15 +375,21 @@ kda_status_t kda_chunk_bwd(const kda_shape_t* sh, int32_t chunk, int32_t total_t
   if (st != KDA_OK) return st;
   if (total_tokens < 0 || num_seqs < 0)
     return invalid("%s: total_tokens and num_seqs must be >= 0", W);
-  if (flags & ~(uint32_t)KDA_READ_INITIAL_STATE)
-    return invalid("%s: flags other than KDA_READ_INITIAL_STATE (0x%x)", W,
-                   flags & ~(uint32_t)KDA_READ_INITIAL_STATE);
+  const uint32_t allowed = KDA_READ_INITIAL_STATE | kVariantFlags;
+  if (flags & ~allowed)
+    return invalid("%s: flags other than KDA_READ_INITIAL_STATE and the variant bits (0x%x)", W,
+                   flags & ~allowed);
+  st = check_variant(flags, W);
+  if (st != KDA_OK) return st;
   if (chunk <= 0) return invalid("%s: chunk must be >= 1 (got %d)", W, chunk);
   if (!chunk_mfma_supported(sh->dk, sh->dv, chunk, sh->io_dtype)) return unsupported(W, sh, chunk);
   if (total_tokens == 0 || num_seqs == 0) return KDA_OK;
   if (!cu_seqlens) return invalid("%s: cu_seqlens is NULL", W);
-  if (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta)
-    return invalid("%s: a tensor pointer is NULL", W);
+  if (!q || !k || !v || !d_o || !dq || !dk || !dv) return invalid("%s: a tensor pointer is NULL", W);
+  st = check_gate_beta(flags, g, beta, false, W);
+  if (st != KDA_OK) return st;
+  if (!(flags & KDA_GATE_NONE) && !dg) return invalid("%s: dg is NULL", W);
+  if (!(flags & KDA_ADDITIVE) && !dbeta) return invalid("%s: dbeta is NULL", W);
   if (flags & KDA_READ_INITIAL_STATE) {
     if (!states) return invalid("%s: states is NULL but KDA_READ_INITIAL_STATE is set", W);
     if (num_slots <= 0) return invalid("%s: num_slots must be >= 1 with initial states", W);
@@ -391,8 +397,8 @@ kda_status_t kda_chunk_bwd(const kda_shape_t* sh, int32_t chunk, int32_t total_t
       return invalid("%s: num_slots (%d) < num_seqs (%d) with implicit slots", W, num_slots,
                      num_seqs);
   }
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 2) || !aligned(g, 16) ||
-      !aligned(beta, 4) || !aligned(d_o, 16) || !aligned(dq, 16) || !aligned(dk, 16) ||
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 2) || !aligned(d_o, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) ||
       !aligned(dv, 2) || !aligned(dg, 4) || !aligned(dbeta, 4) ||
       (states && !aligned(states, 16)) || (d_final_state && !aligned(d_final_state, 4)) ||
       (d_initial_state && !aligned(d_initial_state, 4)))

@@ -712,6 +712,7 @@ __device__ __forceinline__ void prep_role(
           wr[nt] = mfma(tt[nt][0], abkg[0], wr[nt]);
           if (nt >= 2) wr[nt] = mfma(tt[nt][1], abkg[1], wr[nt]);
         }
+        if (additive) wr[0] = wr[1] = wr[2] = wr[3] = f32x4{0.f, 0.f, 0.f, 0.f};  // W = 0
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
           *reinterpret_cast<bf16x8*>(w.wt + ci * kKdBytes + ((size_t)(tile * 2 + s2) * 64 + lane) * 16) =
@@ -1871,6 +1872,11 @@ __device__ __forceinline__ bf16x8 lds8(const uint16_t* p) {
 }
 __device__ __forceinline__ float bfv(uint16_t b) { return bf16_to_f32(b); }
 
+// Variants (compile time): kGate = kGateScalar reads a [T, H] gate and returns dg
+// [T, H] (the channel sum of the per-channel gradient: the gate is broadcast over
+// channels); kGateNone reads and returns no gate; kAdd (u = v, no beta): U = V,
+// so T = I, W = 0, dV = dU, and the terms through (K*Gam) S and A_kk vanish.
+template <int kGate, bool kAdd>
 __global__ __launch_bounds__(kGradThreads) void grad_kernel(
     int32_t N, int H, GradWs w, const int32_t* __restrict__ seq_start,
     const int32_t* __restrict__ seq_end, const int32_t* __restrict__ chunk_off,
@@ -1909,7 +1915,14 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int u = tid + kGradThreads * x, r = min(u >> 5, c - 1), cc = (u & 31) * 4;
-      gx[x] = *reinterpret_cast<const uint4*>(g + (row0 + r * rs) * D + cc);
+      if (kGate == kGateChannel) {
+        gx[x] = *reinterpret_cast<const uint4*>(g + (row0 + r * rs) * D + cc);
+      } else if (kGate == kGateScalar) {
+        const uint32_t b = __float_as_uint(g[row0 + r * rs]);
+        gx[x] = make_uint4(b, b, b, b);
+      } else {
+        gx[x] = make_uint4(0, 0, 0, 0);
+      }
     }
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
@@ -1924,7 +1937,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
     }
   }
   if (tid < C) {
-    const float bt = beta[row0 + min(tid, c - 1) * rs];
+    const float bt = kAdd ? 1.f : beta[row0 + min(tid, c - 1) * rs];
     sm.bs[tid] = tid < c ? bt : 0.f;
     sm.db[tid] = 0.f;
   }
@@ -1993,7 +2006,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
         const int r = 16 * m + 4 * lg + jj;
         const float x = r2[jj];
         sm.x.dR[r][cg] = f32_to_bf16(x);
-        pb[4 * m + jj] += r < c ? x * bf16_to_f32(vx[m][jj]) : 0.f;  // dbeta_r += sum_c dR V
+        if (!kAdd) pb[4 * m + jj] += r < c ? x * bf16_to_f32(vx[m][jj]) : 0.f;  // += dR V
         if (r < c) dv[(row0 + r * rs) * D + cg] = f32_to_bf16(sm.bs[r] * x);
       }
     }
@@ -2086,13 +2099,13 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
       const float Gr = sm.G[r][ich], gam = fast_exp(Gr), ed = fast_exp(GC - Gr);
       const float kr = bfv(sm.K[r][ich]), qr = bfv(sm.Q[r][ich]), br = sm.bs[r];
       const float z = aZ[m][jj], dqg = aQ[m][jj], dkd = aK[m][jj];
-      const float dkg = -br * z;
+      const float dkg = kAdd ? 0.f : -br * z;  // no (K*Gam) S term in the additive write
       const float kdv = kr * ed;
       oq[m][jj] = dqg * gam;
       okk[m][jj] = dkg * gam + dkd * ed;
       oG[m][jj] = (dqg * qr + dkg * kr) * gam - dkd * kdv;
       kdsum += dkd * kdv;
-      pb[4 * m + jj] -= kr * gam * z;  // dbeta_r -= sum_i (K*Gam)[r,i] Z[r,i]
+      if (!kAdd) pb[4 * m + jj] -= kr * gam * z;  // dbeta_r -= sum_i (K*Gam)[r,i] Z[r,i]
     }
   kdsum += __shfl_xor(kdsum, 16, 64);
   kdsum += __shfl_xor(kdsum, 32, 64);
@@ -2107,8 +2120,8 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
         const int r = 16 * R + 4 * lg + jj;
         const bool low = J <= R;
         const float aq = low && j <= r ? aAq[x][jj] : 0.f;
-        const float ak = low && j < r ? -aAk[x][jj] : 0.f;   // dA_kk = -(dR U^T)
-        const float mv = low && j < r ? mk[r * C + j] : 0.f;
+        const float ak = !kAdd && low && j < r ? -aAk[x][jj] : 0.f;   // dA_kk = -(dR U^T)
+        const float mv = !kAdd && low && j < r ? mk[r * C + j] : 0.f;
         // dbeta_r += sum_j dA_kk[r,j] M_kk[r,j]; R is 0 or 1 (x = 0), 2 or 3 (x = 1)
         const float add = ak * mv;
         pb[8 * x + jj] += (R & 1) ? 0.f : add;
@@ -2249,7 +2262,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
       sm.Q[r][ich] = f32_to_bf16(oq[m][jj]);
     }
   block_sync();
-  {
+  if (kGate == kGateChannel) {
     const int col = tid & 127, qt = tid >> 7;
     float xs[16];
 #pragma unroll
@@ -2265,6 +2278,27 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
       const int r = 16 * qt + i;
       if (r < c) dg[(row0 + r * rs) * D + col] = xs[i] + base;
     }
+  } else if (kGate == kGateScalar) {
+    // the channel sum of dG per row (8 threads per row), then the reverse running sum
+    // over the 64 rows in one wave
+    const int r = tid >> 3, part = tid & 7;
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += sm.G[r][16 * part + i];
+    sum += __shfl_xor(sum, 1, 64);
+    sum += __shfl_xor(sum, 2, 64);
+    sum += __shfl_xor(sum, 4, 64);
+    if (part == 0) sm.y.tot[0][r] = sum;
+    block_sync();
+    if (wave == 0) {
+      float x = sm.y.tot[0][lane];
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {  // suffix sum: lane l adds lane l + o
+        const float y = __shfl_down(x, o, 64);
+        if (lane + o < 64) x += y;
+      }
+      if (lane < c) dg[row0 + lane * rs] = x;
+    }
   }
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
@@ -2275,7 +2309,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
       *reinterpret_cast<uint4*>(dq + gi) = *reinterpret_cast<const uint4*>(&sm.Q[r][cc]);
     }
   }
-  if (tid < c) dbeta[row0 + tid * rs] = sm.db[tid];
+  if (!kAdd && tid < c) dbeta[row0 + tid * rs] = sm.db[tid];
 }
 
 // Sets the dynamic LDS limit of a kernel once (before its first launch).
@@ -2366,11 +2400,18 @@ kda_status_t launch_chunk_mfma_bwd(const kda_shape_t* sh, int32_t T, int32_t N, 
   if (st != KDA_OK) return st;
   // chunk operands of the forward pass plus the transposed ones of the reverse pass
   const unsigned grid = (unsigned)(items < (size_t)ncu ? items : (size_t)ncu);
-  st = launch_prep<kGateChannel, false, false, true>(grid, q, k, v, g, beta, 0.f, N, H, w, stream);
+  const bool add = flags & KDA_ADDITIVE;
+  const int gate = (flags & KDA_GATE_SCALAR) ? kGateScalar : (flags & KDA_GATE_NONE) ? kGateNone
+                                                                                    : kGateChannel;
+#define KDA_BWD_PREP(G, A) launch_prep<G, A, false, true>(grid, q, k, v, g, beta, 0.f, N, H, w, stream)
+  st = gate == kGateScalar ? (add ? KDA_BWD_PREP(kGateScalar, true) : KDA_BWD_PREP(kGateScalar, false))
+     : gate == kGateNone   ? (add ? KDA_BWD_PREP(kGateNone, true) : KDA_BWD_PREP(kGateNone, false))
+                           : (add ? KDA_BWD_PREP(kGateChannel, true) : KDA_BWD_PREP(kGateChannel, false));
+#undef KDA_BWD_PREP
   if (st != KDA_OK) return st;
   // forward state pass: S at every chunk start and U
   constexpr int kGroups = D / 16;
-  static bool lds_state = false, lds_scan = false, lds_grad = false;
+  static bool lds_state = false, lds_scan = false;
   st = allow_lds(reinterpret_cast<const void*>(scan_state_kernel<1, 1, 7>), sizeof(StateLds<1, 1>),
                  lds_state, "hipFuncSetAttribute(scan)");
   if (st != KDA_OK) return st;
@@ -2389,16 +2430,26 @@ kda_status_t launch_chunk_mfma_bwd(const kda_shape_t* sh, int32_t T, int32_t N, 
   st = check_launch("chunk_bwd reverse scan");
   if (st != KDA_OK) return st;
   // gradients of every (chunk, head)
-  st = allow_lds(reinterpret_cast<const void*>(grad_kernel), sizeof(GradSmem), lds_grad,
-                 "hipFuncSetAttribute(grad)");
+  auto launch_grad = [&](auto kern, bool& done) -> kda_status_t {
+    kda_status_t e = allow_lds(reinterpret_cast<const void*>(kern), sizeof(GradSmem), done,
+                               "hipFuncSetAttribute(grad)");
+    if (e != KDA_OK) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)items), dim3(kGradThreads), sizeof(GradSmem), stream, N,
+                       H, GradWs{w.tm, w.mkk, w.sc, w.uc, w.dsc, w.duc}, w.seq_start, w.seq_end,
+                       w.chunk_off, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), g, beta, static_cast<const uint16_t*>(d_o),
+                       static_cast<uint16_t*>(dq), static_cast<uint16_t*>(dk),
+                       static_cast<uint16_t*>(dv), dg, dbeta);
+    return KDA_OK;
+  };
+  static bool lg[6] = {false, false, false, false, false, false};
+  st = gate == kGateScalar ? (add ? launch_grad(grad_kernel<kGateScalar, true>, lg[0])
+                                  : launch_grad(grad_kernel<kGateScalar, false>, lg[1]))
+     : gate == kGateNone   ? (add ? launch_grad(grad_kernel<kGateNone, true>, lg[2])
+                                  : launch_grad(grad_kernel<kGateNone, false>, lg[3]))
+                           : (add ? launch_grad(grad_kernel<kGateChannel, true>, lg[4])
+                                  : launch_grad(grad_kernel<kGateChannel, false>, lg[5]));
   if (st != KDA_OK) return st;
-  hipLaunchKernelGGL(grad_kernel, dim3((unsigned)items), dim3(kGradThreads), sizeof(GradSmem),
-                     stream, N, H, GradWs{w.tm, w.mkk, w.sc, w.uc, w.dsc, w.duc}, w.seq_start,
-                     w.seq_end, w.chunk_off,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), g, beta, static_cast<const uint16_t*>(d_o),
-                     static_cast<uint16_t*>(dq), static_cast<uint16_t*>(dk),
-                     static_cast<uint16_t*>(dv), dg, dbeta);
   return check_launch("chunk_bwd grad");
 }
 

@@ -234,18 +234,22 @@ size_t kda_chunk_bwd_workspace_bytes(const kda_shape_t* shape, int32_t chunk,
  * gradients in parallel.  Results equal the gradients of the token-by-token
  * recurrence up to rounding.
  *
- * Inputs are those of the forward call (same layouts; the per-channel gate,
- * the delta rule): q, k, v, g, beta, cu_seqlens, and with
- * KDA_READ_INITIAL_STATE the initial states[slot] (else zero).  g must be <= 0
- * (alpha <= 1), as for the forward.
+ * Inputs are those of the forward call (same layouts and variant flags): q, k,
+ * v, g, beta, cu_seqlens, and with KDA_READ_INITIAL_STATE the initial
+ * states[slot] (else zero).  g must be <= 0 (alpha <= 1), as for the forward.
  * d_o            device io dtype [total_tokens, H, dv]: dL/do.
  * d_final_state  device fp32 dense [num_seqs, H, dk, dv]: dL/dS_final, or NULL (0).
  * dq, dk         device io dtype [total_tokens, H, dk] (16-byte aligned);
  * dv             device io dtype [total_tokens, H, dv];
- * dg             device fp32 [total_tokens, H, dk];  dbeta: device fp32 [total_tokens, H].
- *                All fully overwritten.
+ * dg             device fp32 [total_tokens, H, dk]; [total_tokens, H] with
+ *                KDA_GATE_SCALAR (the gate is shared by the channels, so its gradient
+ *                is their sum); not written (may be NULL) with KDA_GATE_NONE.
+ * dbeta          device fp32 [total_tokens, H]; not written (may be NULL) with KDA_ADDITIVE.
+ *                All written outputs are fully overwritten.
  * d_initial_state  device fp32 dense [num_seqs, H, dk, dv]: dL/dS0, or NULL (not formed).
- * flags          0 or KDA_READ_INITIAL_STATE; other bits are KDA_ERR_INVALID_ARGUMENT.
+ * flags          KDA_READ_INITIAL_STATE | at most one of KDA_GATE_SCALAR, KDA_GATE_NONE |
+ *                KDA_ADDITIVE; KDA_WRITE_FINAL_STATE and unknown bits are
+ *                KDA_ERR_INVALID_ARGUMENT.
  * workspace      device scratch of kda_chunk_bwd_workspace_bytes() bytes, 256-byte
  *                aligned (about 345 KiB per chunk and head).
  * Supported: io_dtype KDA_BF16, dk = dv = 128, chunk 64 (else KDA_ERR_UNSUPPORTED).

@@ -81,6 +81,11 @@ def test_backward_many_chains():
     _case(44, [64, 100, 150, 33, 128, 90], 8, s0=True, d_final=True)
 
 
+def test_backward_zero_length_sequences_and_many_chains():
+    """Zero-length sequences between others (their dL/dS0 is dL/dS_final) and 12 x 16 chains."""
+    _case(46, [0, 90, 0, 200, 64, 0, 1, 130, 77, 0, 65, 300], 16, s0=True, d_final=True)
+
+
 def test_backward_full_prefill_shape():
     """The prefill workload's shape: one sequence of 4,096 tokens, 16 heads."""
     _case(45, [4096], 16, d_final=True)
@@ -94,3 +99,50 @@ def test_backward_empty_is_a_no_op():
                             torch.zeros(1, dtype=torch.int32, device="cuda"), z)
     torch.cuda.synchronize()
     assert out["dq"].numel() == 0
+
+
+VARIANTS = [(gate, additive) for gate in ("channel", "scalar", "none") for additive in (False, True)]
+
+
+@pytest.mark.parametrize("gate,additive", VARIANTS)
+def test_backward_variants(gate, additive):
+    """Scalar gate (Gated DeltaNet), no gate (DeltaNet), additive write (gated linear
+    attention): the oracle runs the per-channel recurrence with the gate broadcast (its dg
+    summed over channels is the scalar gate's gradient), g = 0, or its additive mode."""
+    rng = np.random.default_rng(47)
+    lengths, H, d = [70, 130, 1], 2, 128
+    T = sum(lengths)
+    p = workloads.random_problem(rng, T, H, d, d, io_dtype="bf16")
+    g_scalar = workloads.random_problem(rng, T, H, 1, 1)["g"][..., 0]
+    do = workloads.round_to_bf16(rng.standard_normal((T, H, d)).astype(np.float32))
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    S0 = (0.02 * rng.standard_normal((len(lengths), H, d, d))).astype(np.float32)
+    dST = (0.1 * rng.standard_normal((len(lengths), H, d, d))).astype(np.float32)
+    g_lib = {"channel": p["g"], "scalar": g_scalar, "none": None}[gate]
+    g_ref = {"channel": p["g"], "scalar": np.repeat(g_scalar[..., None], d, axis=2),
+             "none": np.zeros_like(p["g"])}[gate]
+    print(f"backward variant gate={gate} additive={additive}", flush=True)
+    dev = lambda a: to_dev(a, "bf16")
+    out = kda.kda_chunk_bwd(dev(p["q"]), dev(p["k"]), dev(p["v"]),
+                            None if g_lib is None else to_dev(g_lib, dtype=torch.float32),
+                            None if additive else to_dev(p["beta"], dtype=torch.float32),
+                            to_dev(cu, dtype=torch.int32), dev(do),
+                            states=to_dev(S0, dtype=torch.float32), read_initial=True,
+                            d_final=to_dev(dST, dtype=torch.float32), want_d_initial=True,
+                            gate=gate, additive=additive)
+    torch.cuda.synchronize()
+    ref = oracle.run_bwd(p["q"], p["k"], p["v"], g_ref, p["beta"], do, cu, s0=S0, ds_final=dST,
+                         mode=oracle.MODE_ADDITIVE if additive else oracle.MODE_DELTA)
+    for name in ("dq", "dk", "dv"):
+        assert_close(host(out[name]), ref[name], "bf16", name)
+    assert_close(host(out["d_initial"]), ref["ds0"], "bf16", "d_initial")
+    if gate == "channel":
+        assert_close(host(out["dg"]), ref["dg"], "bf16", "dg")
+    elif gate == "scalar":
+        assert_close(host(out["dg"]), ref["dg"].sum(axis=2), "bf16", "dg (scalar)")
+    else:
+        assert out["dg"] is None
+    if additive:
+        assert out["dbeta"] is None
+    else:
+        assert_close(host(out["dbeta"]), ref["dbeta"], "bf16", "dbeta")
