@@ -1338,17 +1338,17 @@ struct StateLds {
 };
 
 template <int CW, int NT, int LW>
-__global__ __launch_bounds__(64 * (CW + LW)) void scan_state_kernel(
-    int32_t N, int H, Workspace w, float* __restrict__ states, int32_t num_slots,
-    const int32_t* __restrict__ slots, uint32_t flags) {
-  extern __shared__ __align__(16) uint8_t smem_raw[];
+__device__ __forceinline__ void scan_state_role(int blk, uint8_t* smem_raw, int32_t N, int H,
+                                                const Workspace& w, float* __restrict__ states,
+                                                int32_t num_slots,
+                                                const int32_t* __restrict__ slots, uint32_t flags) {
   using L = StateLds<CW, NT>;
   using Buf = typename L::Buf;
   constexpr int kTiles = L::kTiles;
   L& sl = *reinterpret_cast<L*>(smem_raw);
   const int NH = N * H;
-  const int head_lin = blockIdx.x % NH;
-  const int group = blockIdx.x / NH;
+  const int head_lin = blk % NH;
+  const int group = blk / NH;
   const int n = head_lin / H, h = head_lin - n * H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
   const int nch = w.seq_nch[n];
@@ -1484,6 +1484,14 @@ __global__ __launch_bounds__(64 * (CW + LW)) void scan_state_kernel(
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) Sg[(size_t)(16 * t + 4 * lg + jj) * D + col[i]] = S[i][t][jj];
   }
+}
+
+template <int CW, int NT, int LW>
+__global__ __launch_bounds__(64 * (CW + LW)) void scan_state_kernel(
+    int32_t N, int H, Workspace w, float* __restrict__ states, int32_t num_slots,
+    const int32_t* __restrict__ slots, uint32_t flags) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  scan_state_role<CW, NT, LW>(blockIdx.x, smem_raw, N, H, w, states, num_slots, slots, flags);
 }
 
 // Outputs of every (chunk, head) in parallel from the operands stored by the
@@ -1642,15 +1650,15 @@ struct GradScanLds {
 };
 
 template <int LW>
-__global__ __launch_bounds__(64 * (1 + LW)) void scan_grad_kernel(
-    int32_t N, int H, Workspace w, const uint16_t* __restrict__ d_o,
-    const float* __restrict__ d_final, float* __restrict__ d_initial) {
-  extern __shared__ __align__(16) uint8_t smem_raw[];
+__device__ __forceinline__ void scan_grad_role(int blk, uint8_t* smem_raw, int32_t N, int H,
+                                               const Workspace& w, const uint16_t* __restrict__ d_o,
+                                               const float* __restrict__ d_final,
+                                               float* __restrict__ d_initial) {
   using Buf = GradScanLds::Buf;
   GradScanLds& sl = *reinterpret_cast<GradScanLds*>(smem_raw);
   const int NH = N * H;
-  const int head_lin = blockIdx.x % NH;
-  const int group = blockIdx.x / NH;
+  const int head_lin = blk % NH;
+  const int group = blk / NH;
   const int n = head_lin / H, h = head_lin - n * H;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
   const int nch = w.seq_nch[n];
@@ -1772,6 +1780,22 @@ __global__ __launch_bounds__(64 * (1 + LW)) void scan_grad_kernel(
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) d_initial[sb + (size_t)(16 * t + 4 * lg + jj) * D + col] = X[t][jj];
   }
+}
+
+// The forward state pass and the reverse pass need nothing from each other (the
+// reverse pass carries dL/dS without S), so one launch runs both side by side:
+// blocks [0, 8 N H) walk the chunks forward, the rest backward.
+constexpr int kScanPairThreads = 64 * 8;
+__global__ __launch_bounds__(kScanPairThreads) void scan_pair_kernel(
+    int32_t N, int H, Workspace w, float* __restrict__ states, int32_t num_slots,
+    const int32_t* __restrict__ slots, uint32_t flags, const uint16_t* __restrict__ d_o,
+    const float* __restrict__ d_final, float* __restrict__ d_initial) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  const int nf = N * H * (D / 16);
+  if ((int)blockIdx.x < nf)
+    scan_state_role<1, 1, 7>(blockIdx.x, smem_raw, N, H, w, states, num_slots, slots, flags);
+  else
+    scan_grad_role<7>(blockIdx.x - nf, smem_raw, N, H, w, d_o, d_final, d_initial);
 }
 
 // Gradient kernel: one workgroup of 8 waves per (chunk, head).  Phases:
@@ -2409,25 +2433,20 @@ kda_status_t launch_chunk_mfma_bwd(const kda_shape_t* sh, int32_t T, int32_t N, 
                            : (add ? KDA_BWD_PREP(kGateChannel, true) : KDA_BWD_PREP(kGateChannel, false));
 #undef KDA_BWD_PREP
   if (st != KDA_OK) return st;
-  // forward state pass: S at every chunk start and U
+  // forward state pass (S at every chunk start, U) and reverse pass (dL/dS at every chunk
+  // end, dL/dU) in one launch
   constexpr int kGroups = D / 16;
-  static bool lds_state = false, lds_scan = false;
-  st = allow_lds(reinterpret_cast<const void*>(scan_state_kernel<1, 1, 7>), sizeof(StateLds<1, 1>),
-                 lds_state, "hipFuncSetAttribute(scan)");
+  constexpr size_t kPairLds =
+      sizeof(StateLds<1, 1>) > sizeof(GradScanLds) ? sizeof(StateLds<1, 1>) : sizeof(GradScanLds);
+  static bool lds_pair = false;
+  st = allow_lds(reinterpret_cast<const void*>(scan_pair_kernel), kPairLds, lds_pair,
+                 "hipFuncSetAttribute(scan pair)");
   if (st != KDA_OK) return st;
-  hipLaunchKernelGGL((scan_state_kernel<1, 1, 7>), dim3((unsigned)(N * H * kGroups)), dim3(64 * 8),
-                     sizeof(StateLds<1, 1>), stream, N, H, w, const_cast<float*>(states), num_slots,
-                     slots, flags & KDA_READ_INITIAL_STATE);
-  st = check_launch("chunk_bwd state scan");
-  if (st != KDA_OK) return st;
-  // reverse pass: dL/dS at every chunk end and dL/dU
-  st = allow_lds(reinterpret_cast<const void*>(scan_grad_kernel<7>), sizeof(GradScanLds), lds_scan,
-                 "hipFuncSetAttribute(reverse scan)");
-  if (st != KDA_OK) return st;
-  hipLaunchKernelGGL((scan_grad_kernel<7>), dim3((unsigned)(N * H * kGroups)), dim3(64 * 8),
-                     sizeof(GradScanLds), stream, N, H, w, static_cast<const uint16_t*>(d_o),
-                     d_final, d_initial);
-  st = check_launch("chunk_bwd reverse scan");
+  hipLaunchKernelGGL(scan_pair_kernel, dim3((unsigned)(2 * N * H * kGroups)),
+                     dim3(kScanPairThreads), kPairLds, stream, N, H, w, const_cast<float*>(states),
+                     num_slots, slots, flags & KDA_READ_INITIAL_STATE,
+                     static_cast<const uint16_t*>(d_o), d_final, d_initial);
+  st = check_launch("chunk_bwd scans");
   if (st != KDA_OK) return st;
   // gradients of every (chunk, head)
   auto launch_grad = [&](auto kern, bool& done) -> kda_status_t {
