@@ -207,3 +207,50 @@ def prepare_inputs(q_raw, k_raw, gate_logits=None, beta_logits=None, gate_min=-n
     else:
         beta = 1.0 / (1.0 + np.exp(-_f64(beta_logits)))
     return q, k, g, beta
+
+
+def prepare_inputs_bwd(q_raw, k_raw, gate_logits, beta_logits, gate_min, gate, dq, dk, dg, dbeta):
+    """Gradients through prepare_inputs (float64): the chain rule of its four maps.
+
+    dq, dk: dL/dq, dL/dk [..., dk] of the prepared q, k; dg: dL/dg of the
+    per-channel log-decay [..., dk] (for gate="scalar" the gate is broadcast, so
+    its logit's gradient sums over the channels; unused for gate="none");
+    dbeta: dL/dbeta [...] (unused when beta_logits is None).
+    normalize(x) = x / max(|x|, 1e-12): d/dx = (I - y y^T) / |x| above the floor,
+    I / 1e-12 below it; silu'(z) = s (1 + z (1 - s)) with s = sigmoid(z);
+    d log sigmoid(a) / da = sigmoid(-a), zero where the floor gate_min is taken
+    (log sigmoid(a) < gate_min); d sigmoid(b) / db = s (1 - s).
+    Returns (dq_raw, dk_raw, dgate_logits or None, dbeta_logits or None).
+    """
+    def sig(x):
+        return 1.0 / (1.0 + np.exp(-x))
+
+    def silu_grad(z):
+        s_ = sig(z)
+        return s_ * (1.0 + z * (1.0 - s_))
+
+    def norm_silu_bwd(z, dy):
+        z, dy = _f64(z), _f64(dy)
+        x = z * sig(z)
+        n = np.sqrt((x * x).sum(axis=-1, keepdims=True))
+        above = n > 1e-12
+        nn = np.maximum(n, 1e-12)
+        y = x / nn
+        dx = np.where(above, (dy - y * (y * dy).sum(axis=-1, keepdims=True)) / nn, dy / nn)
+        return dx * silu_grad(z)
+
+    dq_raw = norm_silu_bwd(q_raw, dq)
+    dk_raw = norm_silu_bwd(k_raw, dk)
+    dgl = None
+    if gate != "none":
+        a = _f64(gate_logits)
+        ls = np.minimum(a, 0.0) - np.log1p(np.exp(-np.abs(a)))
+        pas = np.where(ls >= gate_min, sig(-a), 0.0)
+        dg = _f64(dg)
+        dgl = pas * (dg.sum(axis=-1) if gate == "scalar" else dg)
+    dbl = None
+    if beta_logits is not None:
+        s_ = sig(_f64(beta_logits))
+        dbl = _f64(dbeta) * s_ * (1.0 - s_)
+    return dq_raw, dk_raw, dgl, dbl
+

@@ -627,3 +627,50 @@ def test_gradient_linear_attention_closed_form():
     np.testing.assert_allclose(r["dq"][:, 0], dP @ K + dO @ S0.T, rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(r["dk"][:, 0], dP.T @ Q + V @ dST.T, rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(r["ds0"][0, 0], Q.T @ dO + dST, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("gate,additive,gate_min", [("channel", False, -np.inf),
+                                                    ("channel", False, -2.0),
+                                                    ("scalar", False, -1.5),
+                                                    ("none", True, -np.inf)])
+def test_preparation_gradients_match_central_differences(gate, additive, gate_min):
+    """prepare_inputs then the recurrence, as a function of the raw projections: the chain
+    rule of prepare_inputs_bwd applied to run_bwd equals central differences entry by entry
+    (with the gate floor active on some entries where set)."""
+    rng = np.random.default_rng(8)
+    T, H, dk, dv = 6, 1, 3, 2
+    raw = dict(q=rng.standard_normal((T, H, dk)), k=rng.standard_normal((T, H, dk)),
+               v=rng.standard_normal((T, H, dv)),
+               a=2.0 * rng.standard_normal((T, H, dk)) if gate == "channel"
+               else 2.0 * rng.standard_normal((T, H)) if gate == "scalar" else None,
+               b=None if additive else rng.standard_normal((T, H)))
+    mode = oracle.MODE_ADDITIVE if additive else oracle.MODE_DELTA
+    do, dsf = rng.standard_normal((T, H, dv)), rng.standard_normal((1, H, dk, dv))
+
+    def loss(r):
+        q, k, g, beta = oracle.prepare_inputs(r["q"], r["k"], r["a"], r["b"], gate_min, gate)
+        o, s = oracle.run(q, k, r["v"], g, beta, mode=mode)
+        return float((o * do).sum() + (s * dsf).sum())
+
+    q, k, g, beta = oracle.prepare_inputs(raw["q"], raw["k"], raw["a"], raw["b"], gate_min, gate)
+    if np.isfinite(gate_min):
+        ls = np.minimum(raw["a"], 0) - np.log1p(np.exp(-np.abs(raw["a"])))
+        assert (ls < gate_min).any() and (ls > gate_min).any()
+    gr = oracle.run_bwd(q, k, raw["v"], g, beta, do, ds_final=dsf, mode=mode)
+    dq_raw, dk_raw, dgl, dbl = oracle.prepare_inputs_bwd(raw["q"], raw["k"], raw["a"], raw["b"],
+                                                         gate_min, gate, gr["dq"], gr["dk"],
+                                                         gr["dg"], gr["dbeta"])
+    an = dict(q=dq_raw, k=dk_raw, v=gr["dv"], a=dgl, b=dbl)
+    h = 1e-6
+    for name in ("q", "k", "v", "a", "b"):
+        if raw[name] is None:
+            assert an[name] is None
+            continue
+        fd = np.zeros_like(raw[name])
+        for idx in np.ndindex(raw[name].shape):
+            rp = {kk: (vv.copy() if vv is not None else None) for kk, vv in raw.items()}
+            rm = {kk: (vv.copy() if vv is not None else None) for kk, vv in raw.items()}
+            rp[name][idx] += h
+            rm[name][idx] -= h
+            fd[idx] = (loss(rp) - loss(rm)) / (2 * h)
+        assert np.abs(fd - an[name]).max() <= 1e-6 * max(1.0, np.abs(fd).max()), name
