@@ -20,6 +20,7 @@ __all__ = [
     "kda_chunk_fwd_workspace_bytes", "kda_decode_step", "kda_state_init", "kda_state_load",
     "kda_state_store", "KDA_READ_INITIAL_STATE", "KDA_WRITE_FINAL_STATE", "kda_chunk_fwd_raw",
     "kda_decode_step_raw", "kda_state_affine", "kda_chunk_bwd",
+    "kda_chunk_bwd_raw",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -86,6 +87,11 @@ def load_library(path: str | None = None):
     lib.kda_chunk_bwd.argtypes = [SH, I32, I32, I32, P, P, P, P, P, P, P, I32, P, U32, P, P, P, P,
                                   P, P, P, P, P, SZ, P]
     lib.kda_chunk_bwd.restype = ctypes.c_int
+    lib.kda_chunk_bwd_raw_workspace_bytes.argtypes = [SH, I32, I32, I32]
+    lib.kda_chunk_bwd_raw_workspace_bytes.restype = SZ
+    lib.kda_chunk_bwd_raw.argtypes = [SH, I32, I32, I32, P, P, P, P, P, P, ctypes.c_float, P, I32,
+                                      P, U32, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.kda_chunk_bwd_raw.restype = ctypes.c_int
     lib.kda_state_affine.argtypes = [SH, I32, P, P, P, P, P]
     lib.kda_state_affine.restype = ctypes.c_int
     lib.kda_state_init.argtypes = [SH, P, I32, P]
@@ -287,6 +293,54 @@ def kda_chunk_bwd(q, k, v, g, beta, cu_seqlens, d_o, chunk: int = 64, states=Non
                              _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out.get("dg")),
                              _ptr(out.get("dbeta")), _ptr(out.get("d_initial")), _ptr(workspace),
                              ws_bytes, _stream(stream)))
+    return out
+
+
+def kda_chunk_bwd_raw(q_raw, k_raw, v, gate_logits, beta_logits, cu_seqlens, d_o, chunk: int = 64,
+                      gate_min: float = float("-inf"), states=None, state_slots=None,
+                      read_initial: bool = False, d_final=None, want_d_initial: bool = False,
+                      workspace=None, stream=None, gate: str = "channel", additive: bool = False):
+    """Gradients through kda_chunk_fwd_raw (see kda_chunk_bwd_raw in include/kda.h).
+
+    Returns a dict with dq_raw, dk_raw, dv, dgate_logits (None for gate="none"),
+    dbeta_logits (None when additive), all bf16, and d_initial (fp32) when
+    want_d_initial.
+    """
+    lib = load_library()
+    T, H, dk = q_raw.shape
+    dv = v.shape[2]
+    for t, name, d in ((q_raw, "q_raw", dk), (k_raw, "k_raw", dk), (v, "v", dv), (d_o, "d_o", dv)):
+        _need(t, name, (T, H, d), torch.bfloat16)
+    _need_raw_gate_beta(gate_logits, beta_logits, (T, H), dk, gate, additive)
+    N = cu_seqlens.numel() - 1
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32)
+    num_slots = 0
+    if states is not None:
+        _need(states, "states", (states.shape[0], H, dk, dv), torch.float32)
+        num_slots = states.shape[0]
+    if state_slots is not None:
+        _need(state_slots, "state_slots", (N,), torch.int32)
+    if d_final is not None:
+        _need(d_final, "d_final", (N, H, dk, dv), torch.float32)
+    out = dict(dq_raw=torch.empty_like(q_raw), dk_raw=torch.empty_like(k_raw),
+               dv=torch.empty_like(v),
+               dgate_logits=None if gate == "none" else torch.empty_like(gate_logits),
+               dbeta_logits=None if additive else torch.empty_like(beta_logits),
+               d_initial=(torch.empty((N, H, dk, dv), dtype=torch.float32, device=v.device)
+                          if want_d_initial else None))
+    sh = _Shape(H, dk, dv, KDA_BF16)
+    need = int(lib.kda_chunk_bwd_raw_workspace_bytes(ctypes.byref(sh), chunk, T, N))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=v.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    flags = (KDA_READ_INITIAL_STATE if read_initial else 0) | _variant_flags(gate, additive)
+    _check(lib.kda_chunk_bwd_raw(ctypes.byref(sh), chunk, T, N, _ptr(cu_seqlens), _ptr(q_raw),
+                                 _ptr(k_raw), _ptr(v), _ptr(gate_logits), _ptr(beta_logits),
+                                 float(gate_min), _ptr(states), num_slots, _ptr(state_slots), flags,
+                                 _ptr(d_o), _ptr(d_final), _ptr(out["dq_raw"]),
+                                 _ptr(out["dk_raw"]), _ptr(out["dv"]), _ptr(out["dgate_logits"]),
+                                 _ptr(out["dbeta_logits"]), _ptr(out["d_initial"]),
+                                 _ptr(workspace), ws_bytes, _stream(stream)))
     return out
 
 

@@ -47,6 +47,17 @@ kda_status_t launch_chunk_mfma_bwd(const kda_shape_t* sh, int32_t T, int32_t N, 
                                    float* dbeta, float* d_initial, void* workspace,
                                    hipStream_t stream);
 
+size_t chunk_mfma_bwd_raw_workspace_bytes(int H, int32_t T, int32_t N);
+kda_status_t launch_chunk_mfma_bwd_raw(const kda_shape_t* sh, int32_t T, int32_t N,
+                                       const int32_t* cu, const void* q_raw, const void* k_raw,
+                                       const void* v, const void* gate_logits,
+                                       const void* beta_logits, float gate_min,
+                                       const float* states, int32_t num_slots,
+                                       const int32_t* slots, uint32_t flags, const void* d_o,
+                                       const float* d_final, void* dq_raw, void* dk_raw, void* dv,
+                                       void* dgate_logits, void* dbeta_logits, float* d_initial,
+                                       void* workspace, hipStream_t stream);
+
 namespace {
 thread_local char g_last_error[512] = "";
 }
@@ -363,14 +374,20 @@ size_t kda_chunk_bwd_workspace_bytes(const kda_shape_t* sh, int32_t chunk, int32
   return chunk_mfma_bwd_workspace_bytes(sh->num_heads, total_tokens, num_seqs);
 }
 
-kda_status_t kda_chunk_bwd(const kda_shape_t* sh, int32_t chunk, int32_t total_tokens,
-                           int32_t num_seqs, const int32_t* cu_seqlens, const void* q,
-                           const void* k, const void* v, const float* g, const float* beta,
-                           const float* states, int32_t num_slots, const int32_t* state_slots,
-                           uint32_t flags, const void* d_o, const float* d_final_state, void* dq,
-                           void* dk, void* dv, float* dg, float* dbeta, float* d_initial_state,
-                           void* workspace, size_t workspace_bytes, void* stream) {
-  const char* W = "kda_chunk_bwd";
+}  // extern "C"
+
+namespace {
+
+// Validation shared by kda_chunk_bwd and kda_chunk_bwd_raw (raw: bf16 logits for
+// g and beta, bf16 gradients of them).
+kda_status_t chunk_bwd_impl(const char* W, const kda_shape_t* sh, int32_t chunk,
+                            int32_t total_tokens, int32_t num_seqs, const int32_t* cu_seqlens,
+                            const void* q, const void* k, const void* v, const void* g,
+                            const void* beta, bool raw, float gate_min, const float* states,
+                            int32_t num_slots, const int32_t* state_slots, uint32_t flags,
+                            const void* d_o, const float* d_final_state, void* dq, void* dk,
+                            void* dv, void* dg, void* dbeta, float* d_initial_state,
+                            void* workspace, size_t workspace_bytes, void* stream) {
   kda_status_t st = check_shape(sh, W);
   if (st != KDA_OK) return st;
   if (total_tokens < 0 || num_seqs < 0)
@@ -382,14 +399,15 @@ kda_status_t kda_chunk_bwd(const kda_shape_t* sh, int32_t chunk, int32_t total_t
   st = check_variant(flags, W);
   if (st != KDA_OK) return st;
   if (chunk <= 0) return invalid("%s: chunk must be >= 1 (got %d)", W, chunk);
+  if (raw && gate_min != gate_min) return invalid("%s: gate_min is NaN", W);
   if (!chunk_mfma_supported(sh->dk, sh->dv, chunk, sh->io_dtype)) return unsupported(W, sh, chunk);
   if (total_tokens == 0 || num_seqs == 0) return KDA_OK;
   if (!cu_seqlens) return invalid("%s: cu_seqlens is NULL", W);
   if (!q || !k || !v || !d_o || !dq || !dk || !dv) return invalid("%s: a tensor pointer is NULL", W);
-  st = check_gate_beta(flags, g, beta, false, W);
+  st = check_gate_beta(flags, g, beta, raw, W);
   if (st != KDA_OK) return st;
-  if (!(flags & KDA_GATE_NONE) && !dg) return invalid("%s: dg is NULL", W);
-  if (!(flags & KDA_ADDITIVE) && !dbeta) return invalid("%s: dbeta is NULL", W);
+  if (!(flags & KDA_GATE_NONE) && !dg) return invalid("%s: the gate gradient is NULL", W);
+  if (!(flags & KDA_ADDITIVE) && !dbeta) return invalid("%s: the beta gradient is NULL", W);
   if (flags & KDA_READ_INITIAL_STATE) {
     if (!states) return invalid("%s: states is NULL but KDA_READ_INITIAL_STATE is set", W);
     if (num_slots <= 0) return invalid("%s: num_slots must be >= 1 with initial states", W);
@@ -397,22 +415,71 @@ kda_status_t kda_chunk_bwd(const kda_shape_t* sh, int32_t chunk, int32_t total_t
       return invalid("%s: num_slots (%d) < num_seqs (%d) with implicit slots", W, num_slots,
                      num_seqs);
   }
+  const size_t ga = raw ? 2 : 4;  // element size of the gate and beta gradients
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 2) || !aligned(d_o, 16) ||
-      !aligned(dq, 16) || !aligned(dk, 16) ||
-      !aligned(dv, 2) || !aligned(dg, 4) || !aligned(dbeta, 4) ||
-      (states && !aligned(states, 16)) || (d_final_state && !aligned(d_final_state, 4)) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 2) || (dg && !aligned(dg, raw ? 8 : 4)) ||
+      (dbeta && !aligned(dbeta, ga)) || (states && !aligned(states, 16)) ||
+      (d_final_state && !aligned(d_final_state, 4)) ||
       (d_initial_state && !aligned(d_initial_state, 4)))
-    return invalid("%s: q, k, g, d_o, dq, dk, states must be 16-byte aligned, the rest "
+    return invalid("%s: q, k, d_o, dq, dk, states must be 16-byte aligned, the rest "
                    "element-aligned", W);
-  const size_t need = chunk_mfma_bwd_workspace_bytes(sh->num_heads, total_tokens, num_seqs);
+  const size_t need = raw ? chunk_mfma_bwd_raw_workspace_bytes(sh->num_heads, total_tokens, num_seqs)
+                          : chunk_mfma_bwd_workspace_bytes(sh->num_heads, total_tokens, num_seqs);
   if (!workspace || workspace_bytes < need) {
     set_error("%s: workspace of %zu bytes needed, %zu given", W, need, workspace_bytes);
     return KDA_ERR_WORKSPACE_TOO_SMALL;
   }
   if (!aligned(workspace, 256)) return invalid("%s: workspace must be 256-byte aligned", W);
-  return launch_chunk_mfma_bwd(sh, total_tokens, num_seqs, cu_seqlens, q, k, v, g, beta, states,
-                               num_slots, state_slots, flags, d_o, d_final_state, dq, dk, dv, dg,
-                               dbeta, d_initial_state, workspace, static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (raw)
+    return launch_chunk_mfma_bwd_raw(sh, total_tokens, num_seqs, cu_seqlens, q, k, v, g, beta,
+                                     gate_min, states, num_slots, state_slots, flags, d_o,
+                                     d_final_state, dq, dk, dv, dg, dbeta, d_initial_state,
+                                     workspace, s);
+  return launch_chunk_mfma_bwd(sh, total_tokens, num_seqs, cu_seqlens, q, k, v,
+                               static_cast<const float*>(g), static_cast<const float*>(beta),
+                               states, num_slots, state_slots, flags, d_o, d_final_state, dq, dk,
+                               dv, static_cast<float*>(dg), static_cast<float*>(dbeta),
+                               d_initial_state, workspace, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_chunk_bwd(const kda_shape_t* sh, int32_t chunk, int32_t total_tokens,
+                           int32_t num_seqs, const int32_t* cu_seqlens, const void* q,
+                           const void* k, const void* v, const float* g, const float* beta,
+                           const float* states, int32_t num_slots, const int32_t* state_slots,
+                           uint32_t flags, const void* d_o, const float* d_final_state, void* dq,
+                           void* dk, void* dv, float* dg, float* dbeta, float* d_initial_state,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_bwd_impl("kda_chunk_bwd", sh, chunk, total_tokens, num_seqs, cu_seqlens, q, k, v, g,
+                        beta, false, 0.f, states, num_slots, state_slots, flags, d_o,
+                        d_final_state, dq, dk, dv, dg, dbeta, d_initial_state, workspace,
+                        workspace_bytes, stream);
+}
+
+size_t kda_chunk_bwd_raw_workspace_bytes(const kda_shape_t* sh, int32_t chunk,
+                                         int32_t total_tokens, int32_t num_seqs) {
+  if (!sh || sh->num_heads <= 0 || total_tokens < 0 || num_seqs < 0) return 0;
+  if (!chunk_mfma_supported(sh->dk, sh->dv, chunk, sh->io_dtype)) return 0;
+  return chunk_mfma_bwd_raw_workspace_bytes(sh->num_heads, total_tokens, num_seqs);
+}
+
+kda_status_t kda_chunk_bwd_raw(const kda_shape_t* sh, int32_t chunk, int32_t total_tokens,
+                               int32_t num_seqs, const int32_t* cu_seqlens, const void* q_raw,
+                               const void* k_raw, const void* v, const void* gate_logits,
+                               const void* beta_logits, float gate_min, const float* states,
+                               int32_t num_slots, const int32_t* state_slots, uint32_t flags,
+                               const void* d_o, const float* d_final_state, void* dq_raw,
+                               void* dk_raw, void* dv, void* dgate_logits, void* dbeta_logits,
+                               float* d_initial_state, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return chunk_bwd_impl("kda_chunk_bwd_raw", sh, chunk, total_tokens, num_seqs, cu_seqlens, q_raw,
+                        k_raw, v, gate_logits, beta_logits, true, gate_min, states, num_slots,
+                        state_slots, flags, d_o, d_final_state, dq_raw, dk_raw, dv, dgate_logits,
+                        dbeta_logits, d_initial_state, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

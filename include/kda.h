@@ -262,6 +262,36 @@ kda_status_t kda_chunk_bwd(const kda_shape_t* shape, int32_t chunk, int32_t tota
                            void* dk, void* dv, float* dg, float* dbeta, float* d_initial_state,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Gradients through kda_chunk_fwd_raw: the backward from raw projections.
+ *
+ * The preparation of kda_chunk_fwd_raw (q, k = normalize(SiLU(.)), beta =
+ * sigmoid, g = max(log sigmoid, gate_min); heqinghuang section 09,
+ * engineermaxxing ch. 06b) is recomputed, kda_chunk_bwd runs on the prepared
+ * inputs, and the chain rule of the preparation maps the gradients back:
+ * normalize's projection (I - y y^T)/|x| (I/1e-12 below its floor), SiLU's
+ * derivative, sigmoid(-a) for the gate logit (0 where the floor is taken; a
+ * scalar gate's logit receives the sum over channels) and s(1 - s) for the
+ * write-strength logit.
+ *
+ * Inputs as kda_chunk_fwd_raw (bf16 raw q, k, gate and beta logits; v) plus d_o,
+ * d_final_state as for kda_chunk_bwd.  Outputs (device bf16, fully overwritten):
+ * dq_raw, dk_raw [tokens, H, dk] (16-byte aligned), dv [tokens, H, dv],
+ * dgate_logits shaped like gate_logits (not written with KDA_GATE_NONE),
+ * dbeta_logits [tokens, H] (not written with KDA_ADDITIVE); d_initial_state as
+ * for kda_chunk_bwd.  workspace: kda_chunk_bwd_raw_workspace_bytes() bytes.
+ * Supported: io_dtype KDA_BF16, dk = dv = 128, chunk 64. */
+size_t kda_chunk_bwd_raw_workspace_bytes(const kda_shape_t* shape, int32_t chunk,
+                                         int32_t total_tokens, int32_t num_seqs);
+kda_status_t kda_chunk_bwd_raw(const kda_shape_t* shape, int32_t chunk, int32_t total_tokens,
+                               int32_t num_seqs, const int32_t* cu_seqlens, const void* q_raw,
+                               const void* k_raw, const void* v, const void* gate_logits,
+                               const void* beta_logits, float gate_min, const float* states,
+                               int32_t num_slots, const int32_t* state_slots, uint32_t flags,
+                               const void* d_o, const float* d_final_state, void* dq_raw,
+                               void* dk_raw, void* dv, void* dgate_logits, void* dbeta_logits,
+                               float* d_initial_state, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 /* Composition of a segment's effect on its incoming state, for context-parallel
  * prefill of one long sequence split into segments (one per GPU):
  *

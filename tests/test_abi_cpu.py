@@ -160,3 +160,13 @@ def test_validation_errors_before_any_launch(lib):
     assert bwd(sh, 64, 0, fake) == 3                                 # workspace missing
     assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(sh), 64, 4096, 1) > 0
     assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(_shape(16, 64, 64, 1)), 64, 4096, 1) == 0
+    # backward from raw projections: bf16 only, gate_min not NaN
+    braw = lambda shape, gmin, flags=0: lib.kda_chunk_bwd_raw(
+        ctypes.byref(shape), 64, 128, 1, fake, fake, fake, fake, fake, fake, gmin, None, 0, None,
+        flags, fake, None, fake, fake, fake, fake, fake, None, None, 0, None)
+    assert braw(_shape(16, 128, 128, 0), 0.0) == 2                  # fp32 io
+    assert braw(sh, float("nan")) == 1
+    assert braw(sh, float("-inf")) == 3                              # valid up to the workspace
+    assert braw(sh, 0.0, 2) == 1                                     # WRITE_FINAL is forward-only
+    assert lib.kda_chunk_bwd_raw_workspace_bytes(ctypes.byref(sh), 64, 4096, 1) > \
+        lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(sh), 64, 4096, 1)

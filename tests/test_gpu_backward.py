@@ -146,3 +146,55 @@ def test_backward_variants(gate, additive):
         assert out["dbeta"] is None
     else:
         assert_close(host(out["dbeta"]), ref["dbeta"], "bf16", "dbeta")
+
+
+RAW_CASES = [("channel", False, -np.inf), ("channel", False, -0.2), ("scalar", False, -0.2),
+             ("none", False, -np.inf), ("channel", True, -np.inf), ("scalar", True, -np.inf)]
+
+
+@pytest.mark.parametrize("gate,additive,gmin", RAW_CASES)
+def test_backward_from_raw_projections(gate, additive, gmin):
+    """kda_chunk_bwd_raw against the oracle: prepare_inputs, run_bwd, then the chain rule of
+    prepare_inputs_bwd (the oracle's own, pinned by central differences)."""
+    rng = np.random.default_rng(48)
+    lengths, H, d = [70, 130, 1], 2, 128
+    T = sum(lengths)
+    bf = workloads.round_to_bf16
+    f32 = lambda a: np.asarray(a, dtype=np.float32)
+    q_raw = bf(f32(rng.standard_normal((T, H, d))))
+    k_raw = bf(f32(rng.standard_normal((T, H, d))))
+    v = bf(f32(rng.standard_normal((T, H, d))))
+    a_raw = bf(f32(rng.standard_normal((T, H, d) if gate == "channel" else (T, H)) + 3.0))
+    b_raw = bf(f32(rng.standard_normal((T, H))))
+    do = bf(f32(rng.standard_normal((T, H, d))))
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    S0 = (0.02 * rng.standard_normal((len(lengths), H, d, d))).astype(np.float32)
+    dST = (0.1 * rng.standard_normal((len(lengths), H, d, d))).astype(np.float32)
+    print(f"raw backward gate={gate} additive={additive} gate_min={gmin}", flush=True)
+    bdev = lambda a: to_dev(a, "bf16")
+    out = kda.kda_chunk_bwd_raw(bdev(q_raw), bdev(k_raw), bdev(v),
+                                None if gate == "none" else bdev(a_raw),
+                                None if additive else bdev(b_raw), to_dev(cu, dtype=torch.int32),
+                                bdev(do), gate_min=gmin, states=to_dev(S0, dtype=torch.float32),
+                                read_initial=True, d_final=to_dev(dST, dtype=torch.float32),
+                                want_d_initial=True, gate=gate, additive=additive)
+    torch.cuda.synchronize()
+    q, k, g, beta = oracle.prepare_inputs(q_raw, k_raw, None if gate == "none" else a_raw,
+                                          None if additive else b_raw, gmin, gate)
+    mode = oracle.MODE_ADDITIVE if additive else oracle.MODE_DELTA
+    ref = oracle.run_bwd(q, k, v, g, beta, do, cu, s0=S0, ds_final=dST, mode=mode)
+    dq_raw, dk_raw, dgl, dbl = oracle.prepare_inputs_bwd(
+        q_raw, k_raw, None if gate == "none" else a_raw, None if additive else b_raw, gmin, gate,
+        ref["dq"], ref["dk"], ref["dg"], ref["dbeta"])
+    assert_close(host(out["dq_raw"]), dq_raw, "bf16", "dq_raw")
+    assert_close(host(out["dk_raw"]), dk_raw, "bf16", "dk_raw")
+    assert_close(host(out["dv"]), ref["dv"], "bf16", "dv")
+    assert_close(host(out["d_initial"]), ref["ds0"], "bf16", "d_initial")
+    if gate == "none":
+        assert out["dgate_logits"] is None
+    else:
+        assert_close(host(out["dgate_logits"]), dgl, "bf16", "dgate_logits")
+    if additive:
+        assert out["dbeta_logits"] is None
+    else:
+        assert_close(host(out["dbeta_logits"]), dbl, "bf16", "dbeta_logits")
