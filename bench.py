@@ -189,8 +189,27 @@ def bench_variants(kda, torch, steps, warmup, flush):
 BACKWARD_BYTES_PER_TOKEN_HEAD = (3 * 2 * 128 + 4 * 128 + 4 + 2 * 128) + (3 * 2 * 128 + 4 * 128 + 4)
 
 
+def _time_calls(torch, step, steps, warmup, flush):
+    """Mean HIP-event time (ms) of step() on the current stream, cache evicted before each."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        flush()
+        step()
+    torch.cuda.synchronize()
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(steps)]
+    for s_, e_ in pairs:
+        flush()
+        s_.record(stream)
+        step()
+        e_.record(stream)
+    torch.cuda.synchronize()
+    return sum(_events_ms(pairs)) / steps
+
+
 def bench_backward(kda, torch, steps, warmup, flush):
-    """kda_chunk_bwd tokens/s on the c1 shape (same timing rules as the prefill)."""
+    """kda_chunk_bwd tokens/s on the c1 shape (same timing rules as the prefill), and the
+    scalar-gate and raw-projection variants of it."""
     from gated_delta_rule_08_amd import workloads
     p = workloads.make_inputs(1)
     cfg = p["config"]
@@ -226,7 +245,35 @@ def bench_backward(kda, torch, steps, warmup, flush):
     torch.cuda.synchronize()
     ms = sum(_events_ms(pairs)) / steps
     bytes_ = BACKWARD_BYTES_PER_TOKEN_HEAD * T * H
+    # variants: a [T, H] gate (Gated DeltaNet); raw bf16 projections (preparation and its
+    # chain rule included)
+    g1 = g[..., 0].contiguous()
+    ws_raw = torch.empty(kda.kda_chunk_bwd_raw_workspace_bytes(H, d, d, torch.bfloat16, cfg.chunk,
+                                                               T, N),
+                         dtype=torch.uint8, device="cuda")
+    q_raw = torch.randn(q.shape, device="cuda", generator=gen).to(torch.bfloat16)
+    k_raw = torch.randn(k.shape, device="cuda", generator=gen).to(torch.bfloat16)
+    a_raw = (torch.randn(g.shape, device="cuda", generator=gen) + 3.0).to(torch.bfloat16)
+    b_raw = torch.randn(beta.shape, device="cuda", generator=gen).to(torch.bfloat16)
+    ms_scalar = _time_calls(torch, lambda: kda.kda_chunk_bwd(
+        q, k, v, g1, beta, cu, do, chunk=cfg.chunk, workspace=ws, stream=stream, gate="scalar"),
+        steps, warmup, flush)
+    ms_raw = _time_calls(torch, lambda: kda.kda_chunk_bwd_raw(
+        q_raw, k_raw, v, a_raw, b_raw, cu, do, chunk=cfg.chunk, workspace=ws_raw, stream=stream),
+        steps, warmup, flush)
+    b_scalar = (BACKWARD_BYTES_PER_TOKEN_HEAD - 2 * 4 * 127) * T * H
+    # raw: reads bf16 q, k, v, dO, gate and beta logits; writes bf16 dq, dk, dv, gate, beta grads
+    b_raw_ = (4 * 256 + 256 + 2 + 3 * 256 + 256 + 2) * T * H
+    variants = {
+        "gated_deltanet_scalar_gate": {"tokens_per_s": T / (ms_scalar * 1e-3), "ms_per_call": ms_scalar,
+                                       "algorithmic_bytes": b_scalar,
+                                       "roofline_frac": b_scalar / (ms_scalar * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "from_raw_projections": {"tokens_per_s": T / (ms_raw * 1e-3), "ms_per_call": ms_raw,
+                                 "algorithmic_bytes": b_raw_,
+                                 "roofline_frac": b_raw_ / (ms_raw * 1e-3) / 1e9 / HBM_PEAK_GBS},
+    }
     return {"tokens_per_s": T / (ms * 1e-3), "ms_per_call": ms, "algorithmic_bytes": bytes_,
+            "variants": variants,
             "roofline_frac": bytes_ / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "traffic": _traffic("backward_bytes", TRAFFIC_BACKWARD_FILE),
             "workload": "backward_bf16_B1_H16_T4096_d128_C64 (dL/do given, zero initial state)"}

@@ -188,6 +188,13 @@ def kda_chunk_bwd_workspace_bytes(num_heads: int, dk: int, dv: int, io_dtype: to
                                                             total_tokens, num_seqs))
 
 
+def kda_chunk_bwd_raw_workspace_bytes(num_heads: int, dk: int, dv: int, io_dtype: torch.dtype,
+                                      chunk: int, total_tokens: int, num_seqs: int) -> int:
+    sh = _Shape(num_heads, dk, dv, KDA_BF16 if io_dtype == torch.bfloat16 else KDA_FP32)
+    return int(load_library().kda_chunk_bwd_raw_workspace_bytes(ctypes.byref(sh), chunk,
+                                                                total_tokens, num_seqs))
+
+
 def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens, chunk: int = 64, states=None, state_slots=None,
                   read_initial: bool = False, write_final: bool = False, o=None, workspace=None,
                   stream=None, gate: str = "channel", additive: bool = False):

@@ -91,6 +91,11 @@ def test_backward_full_prefill_shape():
     _case(45, [4096], 16, d_final=True)
 
 
+def test_backward_long_sequence():
+    """One sequence of 16,384 tokens (256 chunks through both passes), 2 heads, slow decay."""
+    _case(49, [16384], 2, s0=True, d_final=True)
+
+
 def test_backward_empty_is_a_no_op():
     d = 128
     z = torch.zeros((0, 2, d), dtype=torch.bfloat16, device="cuda")
