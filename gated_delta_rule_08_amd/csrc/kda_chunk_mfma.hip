@@ -1334,8 +1334,23 @@ struct StateLds {
     f32x4 ut[4][kTiles][64];   // [m][local column tile][lane]
     f32x4 gc[32];              // Gam_C
   };
-  Buf buf[2];
+  Buf buf[3];  // ring: the copies run two chunks ahead of the compute wave
 };
+
+// s_waitcnt vmcnt(n) for a wave-uniform n <= 8 (the count is an immediate)
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+  }
+}
 
 template <int CW, int NT, int LW>
 __device__ __forceinline__ void scan_state_role(int blk, uint8_t* smem_raw, int32_t N, int H,
@@ -1375,19 +1390,24 @@ __device__ __forceinline__ void scan_state_role(int blk, uint8_t* smem_raw, int3
       }
       if (lw == LW - 1 && lane < 32) dma16(w.gc + ci * kGcBytes + off, &dst->gc[0]);
     };
-    auto step_end = [&]() {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
-      lds_barrier();
-    };
+    // copies this wave issues per chunk: its pieces, plus Gam_C for the last wave
+    const int mine = (kPieces - lw + LW - 1) / LW + (lw == LW - 1 ? 1 : 0);
+    static_assert((kPieces + LW - 1) / LW + 1 <= 8, "graded wait covers at most 8 copies");
+    // Chunk c is in buf[c % 3].  Before the step on chunk lc, chunk lc + 1 is
+    // already in flight; the copies of chunk lc + 2 are issued last, so waiting
+    // for all but this wave's newest `mine` copies means chunk lc + 1 has landed.
     if (nch > 0) issue((size_t)cbase * H + h, &sl.buf[0]);
-    step_end();
-    for (int lc = 0; lc < nch; lc += 2) {
-      if (lc + 1 < nch) issue((size_t)(cbase + lc + 1) * H + h, &sl.buf[1]);
-      step_end();
-      if (lc + 1 < nch) {
-        if (lc + 2 < nch) issue((size_t)(cbase + lc + 2) * H + h, &sl.buf[0]);
-        step_end();
+    if (nch > 1) issue((size_t)(cbase + 1) * H + h, &sl.buf[1]);
+    wait_vm(nch > 1 ? mine : 0);  // chunk 0 has landed
+    lds_barrier();
+    for (int lc = 0; lc < nch; ++lc) {
+      if (lc + 2 < nch) {
+        issue((size_t)(cbase + lc + 2) * H + h, &sl.buf[(lc + 2) % 3]);
+        wait_vm(mine);
+      } else {
+        wait_vm(0);
       }
+      lds_barrier();
     }
     return;
   }
@@ -1471,10 +1491,7 @@ __device__ __forceinline__ void scan_state_role(int blk, uint8_t* smem_raw, int3
         for (int i = 0; i < NT; ++i) S[i][t] = mfma(a_kd[t * 2 + s2], ub[i][s2], S[i][t]);
     lds_barrier();
   };
-  for (int lc = 0; lc < nch; lc += 2) {
-    chunk_step(sl.buf[0], (size_t)(cbase + lc) * H + h);
-    if (lc + 1 < nch) chunk_step(sl.buf[1], (size_t)(cbase + lc + 1) * H + h);
-  }
+  for (int lc = 0; lc < nch; ++lc) chunk_step(sl.buf[lc % 3], (size_t)(cbase + lc) * H + h);
 
   if (slot_ok && (flags & KDA_WRITE_FINAL_STATE)) {
 #pragma unroll
