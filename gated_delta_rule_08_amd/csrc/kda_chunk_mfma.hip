@@ -1325,6 +1325,8 @@ __global__ __launch_bounds__(64 * (CW + LW)) void scan_ws_kernel(
 // S at the chunk start and U, for the output kernel, which then forms
 // O = (Q*Gam) S + A_qk U for all chunks in parallel.  The loaders copy -W,
 // Kd^T, the workgroup's Ut tiles and Gam_C.
+constexpr int kStateRing = 3;
+
 template <int CW, int NT>
 struct StateLds {
   static constexpr int kTiles = CW * NT;
@@ -1334,10 +1336,10 @@ struct StateLds {
     f32x4 ut[4][kTiles][64];   // [m][local column tile][lane]
     f32x4 gc[32];              // Gam_C
   };
-  Buf buf[3];  // ring: the copies run two chunks ahead of the compute wave
+  Buf buf[kStateRing];  // ring: the copies run kStateRing - 1 chunks ahead of the compute wave
 };
 
-// s_waitcnt vmcnt(n) for a wave-uniform n <= 8 (the count is an immediate)
+// s_waitcnt vmcnt(n) for a wave-uniform n <= 15 (the count is an immediate)
 __device__ __forceinline__ void wait_vm(int n) {
   switch (n) {
     case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
@@ -1348,7 +1350,14 @@ __device__ __forceinline__ void wait_vm(int n) {
     case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
     case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
     case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
+    case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
+    case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
+    case 13: __builtin_amdgcn_s_waitcnt(0x0F7D); break;
+    case 14: __builtin_amdgcn_s_waitcnt(0x0F7E); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F7F); break;
   }
 }
 
@@ -1392,21 +1401,21 @@ __device__ __forceinline__ void scan_state_role(int blk, uint8_t* smem_raw, int3
     };
     // copies this wave issues per chunk: its pieces, plus Gam_C for the last wave
     const int mine = (kPieces - lw + LW - 1) / LW + (lw == LW - 1 ? 1 : 0);
-    static_assert((kPieces + LW - 1) / LW + 1 <= 8, "graded wait covers at most 8 copies");
-    // Chunk c is in buf[c % 3].  Before the step on chunk lc, chunk lc + 1 is
-    // already in flight; the copies of chunk lc + 2 are issued last, so waiting
-    // for all but this wave's newest `mine` copies means chunk lc + 1 has landed.
-    if (nch > 0) issue((size_t)cbase * H + h, &sl.buf[0]);
-    if (nch > 1) issue((size_t)(cbase + 1) * H + h, &sl.buf[1]);
-    wait_vm(nch > 1 ? mine : 0);  // chunk 0 has landed
+    constexpr int kAhead = kStateRing - 1;  // chunks in flight beyond the current one
+    static_assert(((kPieces + LW - 1) / LW + 1) * (kAhead - 1) <= 15, "graded wait range");
+    // Chunk c is in buf[c % kStateRing].  At the end of the step before chunk lc,
+    // chunks up to lc + kAhead - 1 have been issued; waiting for all but this
+    // wave's newest (in-flight chunks - 1) x `mine` copies means chunk lc has
+    // landed while the later ones stay in flight.
+    for (int c = 0; c < kAhead && c < nch; ++c) issue((size_t)(cbase + c) * H + h, &sl.buf[c]);
+    wait_vm(mine * (min(nch, kAhead) - 1 > 0 ? min(nch, kAhead) - 1 : 0));  // chunk 0 landed
     lds_barrier();
     for (int lc = 0; lc < nch; ++lc) {
-      if (lc + 2 < nch) {
-        issue((size_t)(cbase + lc + 2) * H + h, &sl.buf[(lc + 2) % 3]);
-        wait_vm(mine);
-      } else {
-        wait_vm(0);
-      }
+      // chunk lc + 1 must land by the end of this step; lc + 2 .. lc + kAhead may fly
+      const int nxt = lc + kAhead;
+      if (nxt < nch) issue((size_t)(cbase + nxt) * H + h, &sl.buf[nxt % kStateRing]);
+      const int newest = min(nch - 1, nxt) - (lc + 1);  // chunks issued after lc + 1
+      wait_vm(newest > 0 ? mine * newest : 0);
       lds_barrier();
     }
     return;
@@ -1491,7 +1500,8 @@ __device__ __forceinline__ void scan_state_role(int blk, uint8_t* smem_raw, int3
         for (int i = 0; i < NT; ++i) S[i][t] = mfma(a_kd[t * 2 + s2], ub[i][s2], S[i][t]);
     lds_barrier();
   };
-  for (int lc = 0; lc < nch; ++lc) chunk_step(sl.buf[lc % 3], (size_t)(cbase + lc) * H + h);
+  for (int lc = 0; lc < nch; ++lc)
+    chunk_step(sl.buf[lc % kStateRing], (size_t)(cbase + lc) * H + h);
 
   if (slot_ok && (flags & KDA_WRITE_FINAL_STATE)) {
 #pragma unroll
