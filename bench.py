@@ -207,7 +207,7 @@ def _time_calls(torch, step, steps, warmup, flush):
     return sum(_events_ms(pairs)) / steps
 
 
-def bench_backward(kda, torch, steps, warmup, flush):
+def bench_backward(kda, torch, steps, warmup, flush, with_variants=True):
     """kda_chunk_bwd tokens/s on the c1 shape (same timing rules as the prefill), and the
     scalar-gate and raw-projection variants of it."""
     from gated_delta_rule_08_amd import workloads
@@ -245,6 +245,12 @@ def bench_backward(kda, torch, steps, warmup, flush):
     torch.cuda.synchronize()
     ms = sum(_events_ms(pairs)) / steps
     bytes_ = BACKWARD_BYTES_PER_TOKEN_HEAD * T * H
+    result = {"tokens_per_s": T / (ms * 1e-3), "ms_per_call": ms, "algorithmic_bytes": bytes_,
+              "roofline_frac": bytes_ / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+              "traffic": _traffic("backward_bytes", TRAFFIC_BACKWARD_FILE),
+              "workload": "backward_bf16_B1_H16_T4096_d128_C64 (dL/do given, zero initial state)"}
+    if not with_variants:
+        return result
     # variants: a [T, H] gate (Gated DeltaNet); raw bf16 projections (preparation and its
     # chain rule included)
     g1 = g[..., 0].contiguous()
@@ -272,11 +278,8 @@ def bench_backward(kda, torch, steps, warmup, flush):
                                  "algorithmic_bytes": b_raw_,
                                  "roofline_frac": b_raw_ / (ms_raw * 1e-3) / 1e9 / HBM_PEAK_GBS},
     }
-    return {"tokens_per_s": T / (ms * 1e-3), "ms_per_call": ms, "algorithmic_bytes": bytes_,
-            "variants": variants,
-            "roofline_frac": bytes_ / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "traffic": _traffic("backward_bytes", TRAFFIC_BACKWARD_FILE),
-            "workload": "backward_bf16_B1_H16_T4096_d128_C64 (dL/do given, zero initial state)"}
+    result["variants"] = variants
+    return result
 
 
 def bench_decode(kda, torch, steps, warmup, flush):
@@ -396,7 +399,8 @@ def main(argv=None):
             out["variants"] = bench_variants(kda, torch, max(5, args.steps // 2), 2, flush)
             out["backward"] = bench_backward(kda, torch, max(5, args.steps // 2), 2, flush)
     if args.only == "backward":
-        bw = bench_backward(kda, torch, args.steps, args.warmup, flush)
+        bw = bench_backward(kda, torch, args.steps, args.warmup, flush,
+                            with_variants=not args.no_variants)
         out.update({"value": bw["tokens_per_s"], "unit": "tokens/s", "ms_per_step": bw["ms_per_call"],
                     "config": {"workload": bw["workload"]}, "backward": bw})
     if args.only in (None, "decode"):

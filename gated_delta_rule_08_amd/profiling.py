@@ -30,7 +30,7 @@ def _short(name: str) -> str:
                 "zero_kernel", "gather_scatter_kernel", "scan_grad_kernel", "grad_kernel"):
         if key in name:
             return key
-    for key in ("scan_state_kernel", "scan_ws_kernel", "scan_kernel"):
+    for key in ("scan_state_kernel", "scan_ws_kernel", "scan_pair_kernel", "scan_kernel"):
         if key in name:
             return key + (name[name.index("<"):name.index(">") + 1] if "<" in name else "")
     if "MulFunctor" in name or "mul_kernel" in name:
