@@ -250,7 +250,15 @@ struct PrepSmem {
   float bs[C];
   bf16x8 rk[16][64];     // row-side Gram operands [R * 4 + s][lane]: k_r exp(G_r - G_sR)
   bf16x8 rq[16][64];     //                                         q_r exp(G_r - G_sR)
+  // sequence header built by the prep itself (up to kFuseMaxSeqs sequences)
+  int32_t hs[384];       // sanitised sequence starts
+  int32_t he[384];       // sanitised ends
+  int32_t ho[385];       // chunk offsets (prefix sums of chunk counts, capped)
 };
+// Up to this many sequences the prep builds the sequence header in LDS itself
+// (and workgroup 0 publishes it for the later launches), so no separate index
+// launch precedes it.
+constexpr int kFuseMaxSeqs = 384;
 
 // One item's inputs between the global loads and the LDS staging.
 struct PrepIn {
@@ -292,6 +300,67 @@ __device__ __forceinline__ ItemPos locate(const Header& hd, int N, int H, int it
   p.t0 = hd.seq_start[lo] + (p.gc - hd.chunk_off[lo]) * C;
   p.c = min(C, hd.seq_end[lo] - p.t0);
   return p;
+}
+
+// The same lookup in the header the prep built in LDS.
+__device__ __forceinline__ ItemPos locate_lds(const PrepSmem& sm, int N, int H, int item) {
+  ItemPos p;
+  p.gc = item / H;
+  p.h = item - p.gc * H;
+  int lo = 0, hi = N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (sm.ho[mid] <= p.gc) lo = mid; else hi = mid - 1;
+  }
+  p.t0 = sm.hs[lo] + (p.gc - sm.ho[lo]) * C;
+  p.c = min(C, sm.he[lo] - p.t0);
+  return p;
+}
+
+// The sequence header (as index_kernel builds it) for N <= kFuseMaxSeqs, by the
+// whole workgroup: chunk counts, their prefix sums by a scan over the waves,
+// capped at the workspace capacity.  Workgroup 0 also stores it to the workspace.
+__device__ __forceinline__ void build_header(PrepSmem& sm, const int32_t* __restrict__ cu, int32_t N,
+                                             int32_t T, int32_t cap, const Workspace& w,
+                                             bool publish, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  int32_t s = 0, e = 0, nch = 0;
+  if (tid < N) {
+    s = clamp_tok(cu[tid], T);
+    e = clamp_tok(cu[tid + 1], T);
+    if (e < s) e = s;
+    nch = (e - s + C - 1) / C;
+  }
+  // inclusive scan of nch inside the wave, then over the wave totals
+  int32_t incl = nch;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) sm.ho[kFuseMaxSeqs - kPrepWaves + wave] = incl;  // wave totals, scratch
+  __syncthreads();
+  int32_t base = 0;
+  for (int x = 0; x < wave; ++x) base += sm.ho[kFuseMaxSeqs - kPrepWaves + x];
+  __syncthreads();
+  const int32_t excl = base + incl - nch;
+  if (tid < N) {
+    const int32_t off = min(excl, cap), end = min(excl + nch, cap);
+    const int32_t n2 = end - off;
+    const int32_t e2 = s + n2 * C < e ? s + n2 * C : e;
+    sm.hs[tid] = s;
+    sm.he[tid] = e2;
+    sm.ho[tid] = off;
+    if (tid == N - 1) sm.ho[N] = end;
+    if (publish) {
+      w.seq_start[tid] = s;
+      w.seq_end[tid] = e2;
+      w.seq_nch[tid] = n2;
+      w.chunk_off[tid] = off;
+      if (tid == N - 1) w.chunk_off[N] = end;
+    }
+  }
+  __syncthreads();
 }
 
 // Rows past the end of the sequence read the last valid row (zeroed at staging).
@@ -452,18 +521,21 @@ template <int kGate, bool kAdd, bool kRaw, bool kBwd>
 __device__ __forceinline__ void prep_role(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const void* __restrict__ g, const void* __restrict__ beta, float gate_min, int32_t N, int H,
-    const Workspace& w, const Header& hd, uint8_t* smem_raw, int wg, int nwg) {
+    const Workspace& w, const Header& hd, const int32_t* __restrict__ cu, int32_t T, int32_t cap,
+    bool fused, uint8_t* smem_raw, int wg, int nwg) {
   // the additive write (u = v) has no correction: A_kk = 0, so T = I, W = 0, Ut = V
   constexpr bool additive = kAdd;
   PrepSmem& sm = *reinterpret_cast<PrepSmem*>(smem_raw);
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
-  const int total = hd.chunk_off[N] * H;
+  if (fused) build_header(sm, cu, N, T, cap, w, wg == 0, tid);
+  auto where = [&](int it) { return fused ? locate_lds(sm, N, H, it) : locate(hd, N, H, it); };
+  const int total = (fused ? sm.ho[N] : hd.chunk_off[N]) * H;
   int item = wg;
   if (item >= total) return;  // uniform
 
   PrepIn in;
-  ItemPos pos = locate(hd, N, H, item);
+  ItemPos pos = where(item);
   prep_load<kGate, kAdd, kRaw>(in, pos, q, k, v, g, beta, H, tid);
   // Wait for the first item here, so that inside the loop the wait for the
   // prefetched registers only has to cover the loads, not the stores issued
@@ -502,7 +574,7 @@ __device__ __forceinline__ void prep_role(
     // stores still occupy the memory pipeline.
     const int next = item + nwg;
     if (next < total) {
-      pos = locate(hd, N, H, next);
+      pos = where(next);
       prep_load<kGate, kAdd, kRaw>(in, pos, q, k, v, g, beta, H, tid);
     }
     lds_barrier();
@@ -758,17 +830,27 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const void* __restrict__ g, const void* __restrict__ beta, float gate_min, int32_t N, int H,
     Workspace w, const int32_t* __restrict__ seq_start, const int32_t* __restrict__ seq_end,
-    const int32_t* __restrict__ chunk_off) {
+    const int32_t* __restrict__ chunk_off, const int32_t* __restrict__ cu, int32_t T, int32_t cap,
+    int fused) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   const Header hd{seq_start, seq_end, chunk_off};
-  prep_role<kGate, kAdd, kRaw, kBwd>(q, k, v, g, beta, gate_min, N, H, w, hd, smem_raw, blockIdx.x,
-                               gridDim.x);
+  prep_role<kGate, kAdd, kRaw, kBwd>(q, k, v, g, beta, gate_min, N, H, w, hd, cu, T, cap,
+                                     fused != 0, smem_raw, blockIdx.x, gridDim.x);
 }
+
+// What the prep needs to build the sequence header itself (fused = 1) instead of
+// reading the one index_kernel wrote.
+struct PrepIndex {
+  const int32_t* cu;
+  int32_t T;
+  int32_t cap;
+  int fused;
+};
 
 template <int kGate, bool kAdd, bool kRaw, bool kBwd = false>
 kda_status_t launch_prep(unsigned grid, const void* q, const void* k, const void* v, const void* g,
                          const void* beta, float gate_min, int32_t N, int H, const Workspace& w,
-                         hipStream_t stream) {
+                         const PrepIndex& ix, hipStream_t stream) {
   static bool attr_set = false;  // idempotent; set before the first launch
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep_kernel<kGate, kAdd, kRaw, kBwd>),
@@ -780,23 +862,22 @@ kda_status_t launch_prep(unsigned grid, const void* q, const void* k, const void
   hipLaunchKernelGGL((prep_kernel<kGate, kAdd, kRaw, kBwd>), dim3(grid), dim3(kPrepThreads),
                      sizeof(PrepSmem), stream, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), g, beta,
-                     gate_min, N, H, w, w.seq_start, w.seq_end, w.chunk_off);
+                     gate_min, N, H, w, w.seq_start, w.seq_end, w.chunk_off, ix.cu, ix.T, ix.cap,
+                     ix.fused);
   return check_launch("chunk_fwd prep");
 }
 
 template <bool kRaw>
 kda_status_t launch_prep_variant(uint32_t flags, unsigned grid, const void* q, const void* k,
                                  const void* v, const void* g, const void* beta, float gate_min,
-                                 int32_t N, int H, const Workspace& w, hipStream_t s) {
+                                 int32_t N, int H, const Workspace& w, const PrepIndex& ix,
+                                 hipStream_t s) {
   const bool add = flags & KDA_ADDITIVE;
-  if (flags & KDA_GATE_SCALAR)
-    return add ? launch_prep<kGateScalar, true, kRaw>(grid, q, k, v, g, beta, gate_min, N, H, w, s)
-               : launch_prep<kGateScalar, false, kRaw>(grid, q, k, v, g, beta, gate_min, N, H, w, s);
-  if (flags & KDA_GATE_NONE)
-    return add ? launch_prep<kGateNone, true, kRaw>(grid, q, k, v, g, beta, gate_min, N, H, w, s)
-               : launch_prep<kGateNone, false, kRaw>(grid, q, k, v, g, beta, gate_min, N, H, w, s);
-  return add ? launch_prep<kGateChannel, true, kRaw>(grid, q, k, v, g, beta, gate_min, N, H, w, s)
-             : launch_prep<kGateChannel, false, kRaw>(grid, q, k, v, g, beta, gate_min, N, H, w, s);
+#define KDA_PREP(G, A) launch_prep<G, A, kRaw>(grid, q, k, v, g, beta, gate_min, N, H, w, ix, s)
+  if (flags & KDA_GATE_SCALAR) return add ? KDA_PREP(kGateScalar, true) : KDA_PREP(kGateScalar, false);
+  if (flags & KDA_GATE_NONE) return add ? KDA_PREP(kGateNone, true) : KDA_PREP(kGateNone, false);
+  return add ? KDA_PREP(kGateChannel, true) : KDA_PREP(kGateChannel, false);
+#undef KDA_PREP
 }
 
 // ------------------------------------------------------------------ 3. scan
@@ -2400,13 +2481,18 @@ kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, cons
     int x = 0;
     if (hipDeviceGetAttribute(&x, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && x > 0) ncu = x;
   }
-  hipLaunchKernelGGL(index_kernel, dim3(1), dim3(64), 0, stream, cu, N, T, (int32_t)cap, w);
-  kda_status_t st = check_launch("chunk_fwd index");
-  if (st != KDA_OK) return st;
+  // few sequences: the prep builds the sequence header itself (no index launch)
+  const PrepIndex ix{cu, T, (int32_t)cap, N <= kFuseMaxSeqs ? 1 : 0};
+  kda_status_t st = KDA_OK;
+  if (!ix.fused) {
+    hipLaunchKernelGGL(index_kernel, dim3(1), dim3(64), 0, stream, cu, N, T, (int32_t)cap, w);
+    st = check_launch("chunk_fwd index");
+    if (st != KDA_OK) return st;
+  }
   // persistent prep: one workgroup per CU, each walks items with a grid stride
   const unsigned grid = (unsigned)(items < (size_t)ncu ? items : (size_t)ncu);
-  st = raw ? launch_prep_variant<true>(flags, grid, q, k, v, g, beta, gate_min, N, H, w, stream)
-           : launch_prep_variant<false>(flags, grid, q, k, v, g, beta, gate_min, N, H, w, stream);
+  st = raw ? launch_prep_variant<true>(flags, grid, q, k, v, g, beta, gate_min, N, H, w, ix, stream)
+           : launch_prep_variant<false>(flags, grid, q, k, v, g, beta, gate_min, N, H, w, ix, stream);
   if (st != KDA_OK) return st;
   // Few chains: the serial chain of chunk steps is the critical path; each
   // head's state is split over 8 warp-specialised workgroups of 16 columns that
@@ -2446,15 +2532,19 @@ kda_status_t launch_chunk_mfma_bwd(const kda_shape_t* sh, int32_t T, int32_t N, 
     int x = 0;
     if (hipDeviceGetAttribute(&x, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && x > 0) ncu = x;
   }
-  hipLaunchKernelGGL(index_kernel, dim3(1), dim3(64), 0, stream, cu, N, T, (int32_t)cap, w);
-  kda_status_t st = check_launch("chunk_bwd index");
-  if (st != KDA_OK) return st;
+  const PrepIndex ix{cu, T, (int32_t)cap, N <= kFuseMaxSeqs ? 1 : 0};
+  kda_status_t st = KDA_OK;
+  if (!ix.fused) {
+    hipLaunchKernelGGL(index_kernel, dim3(1), dim3(64), 0, stream, cu, N, T, (int32_t)cap, w);
+    st = check_launch("chunk_bwd index");
+    if (st != KDA_OK) return st;
+  }
   // chunk operands of the forward pass plus the transposed ones of the reverse pass
   const unsigned grid = (unsigned)(items < (size_t)ncu ? items : (size_t)ncu);
   const bool add = flags & KDA_ADDITIVE;
   const int gate = (flags & KDA_GATE_SCALAR) ? kGateScalar : (flags & KDA_GATE_NONE) ? kGateNone
                                                                                     : kGateChannel;
-#define KDA_BWD_PREP(G, A) launch_prep<G, A, false, true>(grid, q, k, v, g, beta, 0.f, N, H, w, stream)
+#define KDA_BWD_PREP(G, A) launch_prep<G, A, false, true>(grid, q, k, v, g, beta, 0.f, N, H, w, ix, stream)
   st = gate == kGateScalar ? (add ? KDA_BWD_PREP(kGateScalar, true) : KDA_BWD_PREP(kGateScalar, false))
      : gate == kGateNone   ? (add ? KDA_BWD_PREP(kGateNone, true) : KDA_BWD_PREP(kGateNone, false))
                            : (add ? KDA_BWD_PREP(kGateChannel, true) : KDA_BWD_PREP(kGateChannel, false));
