@@ -20,7 +20,7 @@ __all__ = [
     "kda_chunk_fwd_workspace_bytes", "kda_decode_step", "kda_state_init", "kda_state_load",
     "kda_state_store", "KDA_READ_INITIAL_STATE", "KDA_WRITE_FINAL_STATE", "kda_chunk_fwd_raw",
     "kda_decode_step_raw", "kda_state_affine", "kda_chunk_bwd",
-    "kda_chunk_bwd_raw",
+    "kda_chunk_bwd_raw", "launch_timer", "KDA_LAUNCH_TIMER_MAX",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,6 +33,7 @@ KDA_WRITE_FINAL_STATE = 2
 KDA_GATE_SCALAR = 4
 KDA_GATE_NONE = 8
 KDA_ADDITIVE = 16
+KDA_LAUNCH_TIMER_MAX = 16
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
            3: "KDA_ERR_WORKSPACE_TOO_SMALL", 4: "KDA_ERR_HIP"}
 
@@ -100,6 +101,12 @@ def load_library(path: str | None = None):
     lib.kda_state_load.restype = ctypes.c_int
     lib.kda_state_store.argtypes = [SH, P, I32, P, I32, P, P]
     lib.kda_state_store.restype = ctypes.c_int
+    lib.kda_launch_timer_begin.argtypes = [P]
+    lib.kda_launch_timer_begin.restype = ctypes.c_int
+    lib.kda_launch_timer_end.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                         ctypes.POINTER(ctypes.c_char_p), I32,
+                                         ctypes.POINTER(ctypes.c_int32)]
+    lib.kda_launch_timer_end.restype = ctypes.c_int
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -525,3 +532,33 @@ def kda_state_store(states, slots=None, n=None, dst=None, stream=None):
     _check(load_library().kda_state_store(ctypes.byref(sh), _ptr(states), S, _ptr(slots), n,
                                           _ptr(dst), _stream(stream)))
     return dst
+
+
+class launch_timer:
+    """Per-launch timing of the library's kernels (kda_launch_timer_begin/end):
+
+        with launch_timer(stream) as lt:
+            kda_chunk_fwd(..., stream=stream)
+        lt.launches  # [(kernel name, milliseconds), ...] in launch order
+
+    Every library call inside the block must use `stream`; leaving the block
+    waits for the last launch."""
+
+    def __init__(self, stream=None):
+        self.stream = stream
+        self.launches = []
+
+    def __enter__(self):
+        _check(load_library().kda_launch_timer_begin(_stream(self.stream)))
+        return self
+
+    def __exit__(self, exc_type, exc, tb):
+        cap = KDA_LAUNCH_TIMER_MAX
+        ms = (ctypes.c_float * cap)()
+        names = (ctypes.c_char_p * cap)()
+        n = ctypes.c_int32(0)
+        st = load_library().kda_launch_timer_end(ms, names, cap, ctypes.byref(n))
+        if exc_type is None:
+            _check(st)
+            self.launches = [(names[i].decode(), float(ms[i])) for i in range(min(n.value, cap))]
+        return False

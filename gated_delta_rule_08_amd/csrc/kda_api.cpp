@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <new>
+
 #include "kda_common.h"
 
 namespace kda {
@@ -75,7 +77,35 @@ kda_status_t hip_status(hipError_t e, const char* what) {
   return KDA_ERR_HIP;
 }
 
-kda_status_t check_launch(const char* what) { return hip_status(hipGetLastError(), what); }
+namespace {
+// Per-launch timing between kda_launch_timer_begin and kda_launch_timer_end:
+// event 0 is recorded by begin, event i + 1 after the i-th launch.
+struct LaunchTimer {
+  hipStream_t stream = nullptr;
+  hipEvent_t ev[KDA_LAUNCH_TIMER_MAX + 1] = {};
+  const char* name[KDA_LAUNCH_TIMER_MAX] = {};
+  int created = 0;
+  int n = 0;
+  hipError_t err = hipSuccess;
+};
+thread_local LaunchTimer* t_timer = nullptr;
+
+void timer_free(LaunchTimer* t) {
+  for (int i = 0; i < t->created; ++i) (void)hipEventDestroy(t->ev[i]);
+  delete t;
+}
+}  // namespace
+
+kda_status_t check_launch(const char* what) {
+  const kda_status_t st = hip_status(hipGetLastError(), what);
+  LaunchTimer* t = t_timer;
+  if (st == KDA_OK && t && t->n < KDA_LAUNCH_TIMER_MAX) {
+    const hipError_t e = hipEventRecord(t->ev[t->n + 1], t->stream);
+    if (e != hipSuccess && t->err == hipSuccess) t->err = e;
+    t->name[t->n++] = what;
+  }
+  return st;
+}
 
 namespace {
 
@@ -480,6 +510,60 @@ kda_status_t kda_chunk_bwd_raw(const kda_shape_t* sh, int32_t chunk, int32_t tot
                         k_raw, v, gate_logits, beta_logits, true, gate_min, states, num_slots,
                         state_slots, flags, d_o, d_final_state, dq_raw, dk_raw, dv, dgate_logits,
                         dbeta_logits, d_initial_state, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+kda_status_t kda_launch_timer_begin(void* stream) {
+  using namespace kda;
+  if (t_timer) return invalid("kda_launch_timer_begin: a timer is already active on this thread");
+  LaunchTimer* t = new (std::nothrow) LaunchTimer;
+  if (!t) return invalid("kda_launch_timer_begin: out of host memory");
+  t->stream = static_cast<hipStream_t>(stream);
+  for (int i = 0; i <= KDA_LAUNCH_TIMER_MAX; ++i) {
+    const hipError_t e = hipEventCreate(&t->ev[i]);
+    if (e != hipSuccess) {
+      timer_free(t);
+      return hip_status(e, "kda_launch_timer_begin: hipEventCreate");
+    }
+    t->created = i + 1;
+  }
+  const hipError_t e = hipEventRecord(t->ev[0], t->stream);
+  if (e != hipSuccess) {
+    timer_free(t);
+    return hip_status(e, "kda_launch_timer_begin: hipEventRecord");
+  }
+  t_timer = t;
+  return KDA_OK;
+}
+
+kda_status_t kda_launch_timer_end(float* ms, const char** names, int32_t capacity,
+                                  int32_t* launches) {
+  using namespace kda;
+  LaunchTimer* t = t_timer;
+  if (!t) return invalid("kda_launch_timer_end: no timer is active on this thread");
+  t_timer = nullptr;
+  kda_status_t st = KDA_OK;
+  if (capacity < 0 || (capacity > 0 && (!ms || !names)))
+    st = invalid("kda_launch_timer_end: capacity < 0, or ms / names NULL with capacity > 0");
+  else if (t->err != hipSuccess)
+    st = hip_status(t->err, "kda_launch_timer_end: hipEventRecord");
+  if (st == KDA_OK) {
+    hipError_t e = hipEventSynchronize(t->ev[t->n]);
+    if (e != hipSuccess) st = hip_status(e, "kda_launch_timer_end: hipEventSynchronize");
+    for (int i = 0; st == KDA_OK && i < t->n && i < capacity; ++i) {
+      float x = 0.f;
+      e = hipEventElapsedTime(&x, t->ev[i], t->ev[i + 1]);
+      if (e != hipSuccess) st = hip_status(e, "kda_launch_timer_end: hipEventElapsedTime");
+      ms[i] = x;
+      names[i] = t->name[i];
+    }
+  }
+  if (launches) *launches = t->n;
+  timer_free(t);
+  return st;
 }
 
 }  // extern "C"

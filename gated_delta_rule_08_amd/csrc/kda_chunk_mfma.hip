@@ -864,7 +864,7 @@ kda_status_t launch_prep(unsigned grid, const void* q, const void* k, const void
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), g, beta,
                      gate_min, N, H, w, w.seq_start, w.seq_end, w.chunk_off, ix.cu, ix.T, ix.cap,
                      ix.fused);
-  return check_launch("chunk_fwd prep");
+  return check_launch("prep_kernel");
 }
 
 template <bool kRaw>
@@ -1694,11 +1694,11 @@ kda_status_t launch_split(int32_t N, int H, const Workspace& w, float* states, i
   hipLaunchKernelGGL((scan_state_kernel<CW, NT, LW>), dim3((unsigned)(N * H * kGroups)),
                      dim3(64 * (CW + LW)), sizeof(StateLds<CW, NT>), stream, N, H, w, states,
                      num_slots, slots, flags);
-  kda_status_t st = check_launch("chunk_fwd scan");
+  kda_status_t st = check_launch("scan_state_kernel");
   if (st != KDA_OK) return st;
   hipLaunchKernelGGL(out_kernel, dim3((unsigned)items), dim3(kOutThreads), 0, stream, N, H, w,
                      w.seq_start, w.seq_end, w.chunk_off, static_cast<uint16_t*>(o));
-  return check_launch("chunk_fwd out");
+  return check_launch("out_kernel");
 }
 
 template <int CW, int NT, int LW>
@@ -1716,7 +1716,7 @@ kda_status_t launch_scan_ws(int32_t N, int H, const Workspace& w, float* states,
   hipLaunchKernelGGL((scan_ws_kernel<CW, NT, LW>), dim3((unsigned)(N * H * kGroups)),
                      dim3(64 * (CW + LW)), sizeof(ScanLds<CW, NT>), stream, N, H, w, states,
                      num_slots, slots, flags, static_cast<uint16_t*>(o));
-  return check_launch("chunk_fwd scan");
+  return check_launch("scan_ws_kernel");
 }
 
 template <int WAVES, int NT>
@@ -1725,7 +1725,7 @@ kda_status_t launch_scan(int32_t N, int H, const Workspace& w, float* states, in
   constexpr int kGroups = D / (16 * WAVES * NT);
   hipLaunchKernelGGL((scan_kernel<WAVES, NT>), dim3((unsigned)(N * H * kGroups)), dim3(64 * WAVES),
                      0, stream, N, H, w, states, num_slots, slots, flags, static_cast<uint16_t*>(o));
-  return check_launch("chunk_fwd scan");
+  return check_launch("scan_kernel");
 }
 
 // ------------------------------------------------------------------ 4. backward
@@ -2486,7 +2486,7 @@ kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, cons
   kda_status_t st = KDA_OK;
   if (!ix.fused) {
     hipLaunchKernelGGL(index_kernel, dim3(1), dim3(64), 0, stream, cu, N, T, (int32_t)cap, w);
-    st = check_launch("chunk_fwd index");
+    st = check_launch("index_kernel");
     if (st != KDA_OK) return st;
   }
   // persistent prep: one workgroup per CU, each walks items with a grid stride
@@ -2536,7 +2536,7 @@ kda_status_t launch_chunk_mfma_bwd(const kda_shape_t* sh, int32_t T, int32_t N, 
   kda_status_t st = KDA_OK;
   if (!ix.fused) {
     hipLaunchKernelGGL(index_kernel, dim3(1), dim3(64), 0, stream, cu, N, T, (int32_t)cap, w);
-    st = check_launch("chunk_bwd index");
+    st = check_launch("index_kernel");
     if (st != KDA_OK) return st;
   }
   // chunk operands of the forward pass plus the transposed ones of the reverse pass
@@ -2563,7 +2563,7 @@ kda_status_t launch_chunk_mfma_bwd(const kda_shape_t* sh, int32_t T, int32_t N, 
                      dim3(kScanPairThreads), kPairLds, stream, N, H, w, const_cast<float*>(states),
                      num_slots, slots, flags & KDA_READ_INITIAL_STATE,
                      static_cast<const uint16_t*>(d_o), d_final, d_initial);
-  st = check_launch("chunk_bwd scans");
+  st = check_launch("scan_pair_kernel");
   if (st != KDA_OK) return st;
   // gradients of every (chunk, head)
   auto launch_grad = [&](auto kern, bool& done) -> kda_status_t {
@@ -2586,7 +2586,7 @@ kda_status_t launch_chunk_mfma_bwd(const kda_shape_t* sh, int32_t T, int32_t N, 
                            : (add ? launch_grad(grad_kernel<kGateChannel, true>, lg[4])
                                   : launch_grad(grad_kernel<kGateChannel, false>, lg[5]));
   if (st != KDA_OK) return st;
-  return check_launch("chunk_bwd grad");
+  return check_launch("grad_kernel");
 }
 
 }  // namespace kda

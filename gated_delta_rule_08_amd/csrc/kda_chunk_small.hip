@@ -179,7 +179,7 @@ kda_status_t launch_dc(int32_t T, int32_t N, const int32_t* cu, const void* q, c
                      0, stream, cu, T, static_cast<const IO*>(q), static_cast<const IO*>(k),
                      static_cast<const IO*>(v), g, beta, states, num_slots, slots, flags,
                      static_cast<IO*>(o), H);
-  return check_launch("chunk_fwd (fp32 path)");
+  return check_launch("chunk_small_kernel");
 }
 
 template <typename IO>

@@ -179,7 +179,7 @@ kda_status_t launch_typed(int32_t batch, int H, const void* q, const void* k, co
                        static_cast<const IO*>(q), static_cast<const IO*>(k),
                        static_cast<const IO*>(v), g, beta, gate_min, states, num_slots, slots,
                        flags, static_cast<IO*>(o), H);
-  return check_launch("decode_step");
+  return check_launch("decode_kernel");
 }
 
 template <typename IO>

@@ -173,7 +173,7 @@ kda_status_t launch_raw_pair(bool forward, int64_t rows, const void* q_raw, cons
                        stream, rows, qr, kr, ar, br, gate_min, r.dq, r.dk, r.dg, r.dbeta,
                        static_cast<uint16_t*>(dq_raw), static_cast<uint16_t*>(dk_raw),
                        static_cast<uint16_t*>(da_raw), static_cast<uint16_t*>(db_raw));
-  return check_launch(forward ? "chunk_bwd_raw prepare" : "chunk_bwd_raw chain rule");
+  return check_launch(forward ? "prepare_kernel" : "prepare_bwd_kernel");
 }
 
 kda_status_t launch_raw(uint32_t flags, bool forward, int64_t rows, const void* q_raw,

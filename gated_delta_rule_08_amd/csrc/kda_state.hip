@@ -88,7 +88,7 @@ kda_status_t launch_state_init(float* states, size_t n_floats, hipStream_t strea
   const size_t n4 = n_floats / 4;
   hipLaunchKernelGGL(zero_kernel, dim3(grid_for(n4)), dim3(kThreads), 0, stream,
                      reinterpret_cast<float4*>(states), n4);
-  return check_launch("state_init");
+  return check_launch("zero_kernel");
 }
 
 kda_status_t launch_state_affine(int32_t n, int H, int dk, int dv, const float* M,
@@ -98,7 +98,7 @@ kda_status_t launch_state_affine(int32_t n, int H, int dk, int dv, const float* 
   hipLaunchKernelGGL(affine_kernel, dim3((unsigned)((size_t)n * H * col_blocks)), dim3(kThreads),
                      (size_t)dk * kAffCols * sizeof(float), stream, M, S_in, B, S_out, dk, dv,
                      col_blocks);
-  return check_launch("state_affine");
+  return check_launch("affine_kernel");
 }
 
 kda_status_t launch_state_copy(bool to_pool, float* states, int32_t num_slots,
@@ -114,7 +114,7 @@ kda_status_t launch_state_copy(bool to_pool, float* states, int32_t num_slots,
     hipLaunchKernelGGL(gather_scatter_kernel<false>, dim3(grid), dim3(kThreads), 0, stream,
                        reinterpret_cast<float4*>(states), num_slots, slots, n,
                        reinterpret_cast<float4*>(dense), per4);
-  return check_launch(to_pool ? "state_load" : "state_store");
+  return check_launch("gather_scatter_kernel");
 }
 
 }  // namespace kda

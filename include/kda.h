@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum {
   KDA_OK = 0,
@@ -326,6 +326,29 @@ kda_status_t kda_state_load(const kda_shape_t* shape, float* states, int32_t num
  * an out-of-range slot leave their dst rows unwritten. */
 kda_status_t kda_state_store(const kda_shape_t* shape, const float* states, int32_t num_slots,
                              const int32_t* slots, int32_t n, float* dst, void* stream);
+
+/* ---------------------------------------------------------------- measurement
+ * Per-launch timing of the library's own kernels, for benchmarks and profiles
+ * (not part of the computation).  After kda_launch_timer_begin(stream), every
+ * kernel launch that the library makes on the calling host thread records a
+ * HIP event on `stream` right after itself; begin records the first.  All
+ * library calls made before kda_launch_timer_end must use that same stream
+ * (events on another stream would not bracket the launches).
+ * kda_launch_timer_end waits for the last event and, for the i-th launch
+ * (i < min(capacity, launches)), writes its elapsed time in milliseconds (the
+ * previous event to its own) to ms[i] and its kernel name, a static string
+ * owned by the library, to names[i]; *launches (if not NULL) receives the
+ * number of launches recorded, at most KDA_LAUNCH_TIMER_MAX (later launches
+ * are not timed).  ms and names are host arrays of `capacity` entries.
+ * The timer creates HIP events (host-side runtime objects, no device memory)
+ * and synchronises in end, so it must not be used under graph capture.
+ * Errors: begin while a timer is active on the thread, end without one, or
+ * capacity < 0 / NULL arrays with capacity > 0 -> KDA_ERR_INVALID_ARGUMENT
+ * (end always stops the timer); event failures -> KDA_ERR_HIP. */
+#define KDA_LAUNCH_TIMER_MAX 16
+kda_status_t kda_launch_timer_begin(void* stream);
+kda_status_t kda_launch_timer_end(float* ms, const char** names, int32_t capacity,
+                                  int32_t* launches);
 
 #ifdef __cplusplus
 }

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 2
+    assert lib.kda_abi_version() == 3
     assert lib.kda_status_string(0) == b"KDA_OK"
     assert lib.kda_status_string(3) == b"KDA_ERR_WORKSPACE_TOO_SMALL"
 
@@ -170,3 +170,13 @@ def test_validation_errors_before_any_launch(lib):
     assert braw(sh, 0.0, 2) == 1                                     # WRITE_FINAL is forward-only
     assert lib.kda_chunk_bwd_raw_workspace_bytes(ctypes.byref(sh), 64, 4096, 1) > \
         lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(sh), 64, 4096, 1)
+
+
+def test_launch_timer_end_without_begin(lib):
+    """kda_launch_timer_end with no timer active is an argument error (no HIP call)."""
+    ms = (ctypes.c_float * 4)()
+    names = (ctypes.c_char_p * 4)()
+    n = ctypes.c_int32(-1)
+    assert lib.kda_launch_timer_end(ms, names, 4, ctypes.byref(n)) == 1
+    assert b"no timer" in lib.kda_last_error()
+    assert n.value == -1                                             # nothing written
