@@ -80,8 +80,10 @@ def _kernel_traffic(name: str, path: str = TRAFFIC_FILE):
         return None
     if rec.get("source_digest") != _source_digest():
         return None
-    k = rec.get("per_kernel", {}).get(name)
-    return None if k is None else k["fetch_bytes"] + k["write_bytes"]
+    for kname, k in rec.get("per_kernel", {}).items():
+        if kname == name or kname.startswith(name + "<"):   # template arguments in the trace
+            return k["fetch_bytes"] + k["write_bytes"]
+    return None
 
 
 def _events_ms(pairs):

@@ -1,14 +1,18 @@
 """Turn rocprofv3 CSV output into the short summaries kept under profiles/.
 
     python -m gated_delta_rule_08_amd.profiling stats  <kernel_stats.csv>  [--command "..."]
+    python -m gated_delta_rule_08_amd.profiling evicted <kernel_trace.csv>
     python -m gated_delta_rule_08_amd.profiling traffic <fetch_counter_collection.csv>
             <write_counter_collection.csv> [--copy-mib 256] [--out profiles/traffic.json]
 
-`stats` prints a table of per-kernel call counts and durations.  `traffic`
+`stats` prints a table of per-kernel call counts and durations; `evicted` the
+same from the kernel trace over the calls that follow a cache-evicting fill only
+(the calls bench.py times, without its warm-cache pass).  `traffic`
 averages FETCH_SIZE and WRITE_SIZE (KiB per dispatch) per kernel, scales both
 by the factor that makes a plain device copy of a known size (an elementwise
 multiply by 1 of a 256 MiB tensor) read and write exactly that size, and writes the HBM bytes
-per launch of the prefill path (index, prep, scan and output kernels) and of the decode kernel
+per launch of the prefill path (prep, scan and output kernels, and the index kernel where
+there is one) and of the decode kernel
 (or, for a backward-only run, of the backward's launches), tagged with a digest
 of the kernel sources (bench.py reports the figures only while the sources are
 unchanged).
@@ -52,6 +56,32 @@ def stats(path: str, cmd: str | None = None) -> str:
         lines.append(f"{_short(r['Name']):40s} {int(r['Calls']):6d} {float(r['AverageNs'])/1e3:10.2f} "
                      f"{float(r['MinNs'])/1e3:10.2f} {float(r['MaxNs'])/1e3:10.2f} "
                      f"{float(r['Percentage']):6.2f}%")
+    return "\n".join(lines)
+
+
+def evicted(path: str, fill_us: float = 50.0) -> str:
+    """Per-kernel durations over the library calls that follow an eviction fill
+    (a torch fill of at least fill_us): a kernel seen twice since the last fill
+    starts a call without one, and that call is left out."""
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
+    cold, seen = False, set()
+    per = defaultdict(list)
+    for r in rows:
+        k = _short(r["Kernel_Name"])
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if k == "torch:fill" and us >= fill_us:
+            cold, seen = True, set()
+            continue
+        if k.startswith(("torch:", "runtime:")):
+            continue
+        if k in seen:
+            cold = False
+        seen.add(k)
+        if cold:
+            per[k].append(us)
+    lines = [f"{'kernel (after an eviction)':40s} {'calls':>6s} {'avg us':>10s} {'min us':>10s} {'max us':>10s}"]
+    for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1]) / len(kv[1])):
+        lines.append(f"{k:40s} {len(v):6d} {sum(v) / len(v):10.2f} {min(v):10.2f} {max(v):10.2f}")
     return "\n".join(lines)
 
 
@@ -107,6 +137,8 @@ def main(argv=None):
     a = sub.add_parser("stats")
     a.add_argument("csv")
     a.add_argument("--command", default=None, help="the command that produced the CSV")
+    e = sub.add_parser("evicted")
+    e.add_argument("trace_csv")
     b = sub.add_parser("traffic")
     b.add_argument("fetch_csv")
     b.add_argument("write_csv")
@@ -115,6 +147,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.cmd == "stats":
         print(stats(args.csv, args.command))
+    elif args.cmd == "evicted":
+        print(evicted(args.trace_csv))
     else:
         print(json.dumps(traffic(args.fetch_csv, args.write_csv, args.copy_mib, args.out), indent=1))
 
