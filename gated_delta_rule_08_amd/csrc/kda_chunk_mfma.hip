@@ -368,41 +368,61 @@ __device__ __forceinline__ void build_header(PrepSmem& sm, const int32_t* __rest
 // gate reads nothing (G = 0); the additive write reads no beta (beta = 1, and
 // the correction is dropped later).  kRaw: q, k are raw projections and the
 // gate and write strength are bf16 logits (prepared at staging).
-template <int kGate, bool kAdd, bool kRaw>
-__device__ __forceinline__ void prep_load(PrepIn& in, const ItemPos& p, const uint16_t* q,
-                                          const uint16_t* k, const uint16_t* v, const void* gp,
-                                          const void* bp, int H, int tid) {
+// The next item's loads, in four parts that the item loop issues at four
+// points of the current item: all of them at once would hold the wave at the
+// issue until the CU's memory pipeline takes them.  Part 0: k, q; part 1: v,
+// beta; parts 2 and 3: the gate rows of the first and second half.
+template <int kGate, bool kAdd, bool kRaw, int kPart>
+__device__ __forceinline__ void prep_load_part(PrepIn& in, const ItemPos& p, const uint16_t* q,
+                                               const uint16_t* k, const uint16_t* v,
+                                               const void* gp, const void* bp, int H, int tid) {
   const float* g = static_cast<const float*>(gp);
   const float* beta = static_cast<const float*>(bp);
   const uint16_t* g16 = static_cast<const uint16_t*>(gp);
   const uint16_t* b16 = static_cast<const uint16_t*>(bp);
   const size_t rowstride = (size_t)H * D;
   const size_t base = ((size_t)p.t0 * H + p.h) * D;
+  if constexpr (kPart <= 1) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int u = tid + kPrepThreads * i, r = u >> 4, cc = (u & 15) * 8;
-    const size_t gi = base + (size_t)min(r, p.c - 1) * rowstride + cc;
-    in.k[i] = *reinterpret_cast<const uint4*>(k + gi);
-    in.q[i] = *reinterpret_cast<const uint4*>(q + gi);
-    in.v[i] = *reinterpret_cast<const uint4*>(v + gi);
-  }
+    for (int i = 0; i < 2; ++i) {
+      const int u = tid + kPrepThreads * i, r = u >> 4, cc = (u & 15) * 8;
+      const size_t gi = base + (size_t)min(r, p.c - 1) * rowstride + cc;
+      if constexpr (kPart == 0) {
+        in.k[i] = *reinterpret_cast<const uint4*>(k + gi);
+        in.q[i] = *reinterpret_cast<const uint4*>(q + gi);
+      } else {
+        in.v[i] = *reinterpret_cast<const uint4*>(v + gi);
+      }
+    }
+    if constexpr (kPart == 1 && !kAdd) {
+      const size_t bi = (size_t)(p.t0 + min(tid & 63, p.c - 1)) * H + p.h;
+      if (kRaw) in.b16 = b16[bi];
+      else in.beta = beta[bi];
+    }
+  } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int u = tid + kPrepThreads * i, r = u >> 5, cc = (u & 31) * 4;
-    const size_t row = (size_t)min(r, p.c - 1);
-    if (kGate == kGateScalar) {
-      if (kRaw) in.gs16[i] = g16[(p.t0 + row) * H + p.h];
-      else in.g[i].x = g[(p.t0 + row) * H + p.h];
-    } else if (kGate == kGateChannel) {
-      if (kRaw) in.gl[i] = *reinterpret_cast<const uint2*>(g16 + base + row * rowstride + cc);
-      else in.g[i] = *reinterpret_cast<const float4*>(g + base + row * rowstride + cc);
+    for (int i = 2 * (kPart - 2); i < 2 * (kPart - 2) + 2; ++i) {
+      const int u = tid + kPrepThreads * i, r = u >> 5, cc = (u & 31) * 4;
+      const size_t row = (size_t)min(r, p.c - 1);
+      if (kGate == kGateScalar) {
+        if (kRaw) in.gs16[i] = g16[(p.t0 + row) * H + p.h];
+        else in.g[i].x = g[(p.t0 + row) * H + p.h];
+      } else if (kGate == kGateChannel) {
+        if (kRaw) in.gl[i] = *reinterpret_cast<const uint2*>(g16 + base + row * rowstride + cc);
+        else in.g[i] = *reinterpret_cast<const float4*>(g + base + row * rowstride + cc);
+      }
     }
   }
-  if (!kAdd) {
-    const size_t bi = (size_t)(p.t0 + min(tid & 63, p.c - 1)) * H + p.h;
-    if (kRaw) in.b16 = b16[bi];
-    else in.beta = beta[bi];
-  }
+}
+
+template <int kGate, bool kAdd, bool kRaw>
+__device__ __forceinline__ void prep_load(PrepIn& in, const ItemPos& p, const uint16_t* q,
+                                          const uint16_t* k, const uint16_t* v, const void* gp,
+                                          const void* bp, int H, int tid) {
+  prep_load_part<kGate, kAdd, kRaw, 0>(in, p, q, k, v, gp, bp, H, tid);
+  prep_load_part<kGate, kAdd, kRaw, 1>(in, p, q, k, v, gp, bp, H, tid);
+  prep_load_part<kGate, kAdd, kRaw, 2>(in, p, q, k, v, gp, bp, H, tid);
+  prep_load_part<kGate, kAdd, kRaw, 3>(in, p, q, k, v, gp, bp, H, tid);
 }
 
 // normalize(silu(x)) of one row held by the 16 lanes of a lane group, 8 channels
@@ -569,13 +589,15 @@ __device__ __forceinline__ void prep_role(
       for (int off = 32; off >= 1; off >>= 1) sp = fmaxf(sp, __shfl_xor(sp, off, 64));
       if (lane == 0) sm.spr[wave] = sp;  // waves 2qt and 2qt + 1 cover block qt
     }
-    // The next item's loads overlap this item's compute.  They are issued here
-    // rather than at the top of the item, where the previous item's output
-    // stores still occupy the memory pipeline.
+    // The next item's loads overlap this item's compute, issued in four parts
+    // (here, before the Gram blocks, before the diagonal inverse, before the
+    // off-diagonal blocks), not at the top of the item where the previous
+    // item's output stores still occupy the memory pipeline.
     const int next = item + nwg;
-    if (next < total) {
+    const bool prefetch = next < total;
+    if (prefetch) {
       pos = where(next);
-      prep_load<kGate, kAdd, kRaw>(in, pos, q, k, v, g, beta, H, tid);
+      prep_load_part<kGate, kAdd, kRaw, 0>(in, pos, q, k, v, g, beta, H, tid);
     }
     lds_barrier();
 
@@ -604,6 +626,8 @@ __device__ __forceinline__ void prep_role(
       }
     }
     lds_barrier();
+
+    if (prefetch) prep_load_part<kGate, kAdd, kRaw, 1>(in, pos, q, k, v, g, beta, H, tid);
 
     // ---- gated Gram blocks (10 block pairs over 8 waves)
     {
@@ -671,6 +695,8 @@ __device__ __forceinline__ void prep_role(
       }
     }
 
+    if (prefetch) prep_load_part<kGate, kAdd, kRaw, 2>(in, pos, q, k, v, g, beta, H, tid);
+
     // ---- T = (I + A_kk)^-1 in 16x16 blocks.  Diagonal blocks: T_JJ = (I + A_JJ)^-1
     // by right-looking forward substitution (wave J, lane = column): once x[m]
     // is final it is eliminated from every later row at once, so the dependency
@@ -688,6 +714,7 @@ __device__ __forceinline__ void prep_role(
       for (int i = 0; i < 16; ++i) sm.Tm[sJ + i][sJ + lane] = x[i];
     }
     lds_barrier();
+    if (prefetch) prep_load_part<kGate, kAdd, kRaw, 3>(in, pos, q, k, v, g, beta, H, tid);
     // Off-diagonal blocks by distance L = R - J, the blocks of one distance in
     // parallel (one wave each): T_RJ = -T_RR X with X = sum_{J<=K<R} A_RK T_KJ,
     // both products on fp32 MFMA.  The second product takes X straight from the
