@@ -54,6 +54,7 @@ constexpr float kMaxSpread = 80.f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Per chunk-head operand blocks in the workspace (bytes).
@@ -1447,7 +1448,8 @@ struct StateLds {
   Buf buf[kStateRing];  // ring: the copies run kStateRing - 1 chunks ahead of the compute wave
 };
 
-// s_waitcnt vmcnt(n) for a wave-uniform n <= 15 (the count is an immediate)
+// s_waitcnt vmcnt(n) for a wave-uniform n <= 23 (the count is an immediate; its
+// bits 5:4 sit in bits 15:14 of the encoding)
 __device__ __forceinline__ void wait_vm(int n) {
   switch (n) {
     case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
@@ -1465,7 +1467,15 @@ __device__ __forceinline__ void wait_vm(int n) {
     case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
     case 13: __builtin_amdgcn_s_waitcnt(0x0F7D); break;
     case 14: __builtin_amdgcn_s_waitcnt(0x0F7E); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F7F); break;
+    case 15: __builtin_amdgcn_s_waitcnt(0x0F7F); break;
+    case 16: __builtin_amdgcn_s_waitcnt(0x4F70); break;
+    case 17: __builtin_amdgcn_s_waitcnt(0x4F71); break;
+    case 18: __builtin_amdgcn_s_waitcnt(0x4F72); break;
+    case 19: __builtin_amdgcn_s_waitcnt(0x4F73); break;
+    case 20: __builtin_amdgcn_s_waitcnt(0x4F74); break;
+    case 21: __builtin_amdgcn_s_waitcnt(0x4F75); break;
+    case 22: __builtin_amdgcn_s_waitcnt(0x4F76); break;
+    default: __builtin_amdgcn_s_waitcnt(0x4F77); break;
   }
 }
 
@@ -1768,23 +1778,38 @@ kda_status_t launch_scan(int32_t N, int H, const Workspace& w, float* states, in
 // stores S at every chunk start and U); the reverse pass stores X and dU; the
 // gradient kernel then handles every (chunk, head) independently.
 
-// Reverse pass: 8 workgroups of 16 value columns per (sequence, head), one
-// compute wave and LW loader waves copying the chunk's operands (Kd, -W^T,
-// (Q*Gam)^T, A_qk^T, dO rows, Gam_C) into LDS, double buffered, chunks walked
-// from the last to the first.
+// Reverse pass: 8 workgroups of 16 value columns per (sequence, head), chunks
+// walked from the last to the first.  Wave 0 carries X = dL/dS; the other seven
+// keep a ring of kGradRing chunk buffers filled, two chunks ahead of it:
+//  * waves 3..6 copy Kd, -W^T and Gam_C into LDS with direct global->LDS
+//    loads, two chunks ahead; wave 7 copies the chunk's dO rows (this
+//    workgroup's columns, 64 rows 32 bytes each) kDoAhead chunks ahead into a
+//    ring of their own.  A wave's loads complete in issue order, so rows
+//    copied far ahead need a wave that waits for nothing issued after them;
+//  * waves 1 and 2 form the chunk's products that do not depend on X, for this
+//    workgroup's columns: A_qk^T dO (the start of dU) and (Q*Gam)^T dO (X's
+//    increment), from operand tiles they load into registers a step ahead and
+//    the dO rows in LDS, and write them to LDS in the accumulator layout.
+// Wave 0 then does the two products on the chain per chunk, as the forward pass.
+// The role and piece of a wave are taken from a scalar copy of its index, so
+// each choice is a branch, never a lane mask (a matrix instruction in a
+// masked-off block still writes its accumulator, and the copies' waits count
+// every issued load).
+constexpr int kGradRing = 3;
+constexpr int kDoAhead = 5;        // dO rows are copied this many chunks ahead of wave 0
+constexpr int kDoRing = kDoAhead;  // chunk c's dO rows in slot c % kDoRing
 struct GradScanLds {
   struct Buf {
     bf16x8 kdr[16][64];   // Kd      [m*4 + s][lane]   (M = rows, K = dk)
     bf16x8 wt[16][64];    // -W^T    [t*2 + s2][lane]  (M = dk, K = rows)
-    bf16x8 qgt[16][64];   // (Q*Gam)^T
-    bf16x8 aqt[8][64];    // A_qk^T  [m*2 + s2][lane]  (M = rows j, K = rows r)
-    uint16_t dob[C][16];  // dO rows, this workgroup's 16 columns
+    f32x4 p[4][64];       // A_qk^T dO      [m][lane]  (rows 16m + 4lg + jj, column li)
+    f32x4 r[8][64];       // (Q*Gam)^T dO   [t][lane]  (channels 16t + 4lg + jj)
     f32x4 gc[32];         // Gam_C
   };
-  Buf buf[2];
+  Buf buf[kGradRing];
+  uint16_t dob[kDoRing][C][16];  // dO rows, this workgroup's 16 columns
 };
 
-template <int LW>
 __device__ __forceinline__ void scan_grad_role(int blk, uint8_t* smem_raw, int32_t N, int H,
                                                const Workspace& w, const uint16_t* __restrict__ d_o,
                                                const float* __restrict__ d_final,
@@ -1795,53 +1820,156 @@ __device__ __forceinline__ void scan_grad_role(int blk, uint8_t* smem_raw, int32
   const int head_lin = blk % NH;
   const int group = blk / NH;
   const int n = head_lin / H, h = head_lin - n * H;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nch = w.seq_nch[n];
   const int cbase = w.chunk_off[n];
   const int s_start = w.seq_start[n], s_end = w.seq_end[n];
+  // the k-th chunk processed is chunk nch - 1 - k, in buffer k % kGradRing
+  auto chunk_ci = [&](int k) { return (size_t)(cbase + nch - 1 - k) * H + h; };
 
-  if (wave >= 1) {
-    // ------------------------------------------------------------ loaders
-    const int lw = wave - 1;
-    const int off = lane * 16;
-    constexpr int kPieces = 58;  // 1 KiB pieces: Kd 16, -W^T 16, (Q*Gam)^T 16, A_qk^T 8, dO 2
-    auto issue = [&](int lc, Buf* dst) {
-      const size_t ci = (size_t)(cbase + lc) * H + h;
-      const uint8_t* kdr = w.kdr + ci * kKdBytes;
-      const uint8_t* wt = w.wt + ci * kKdBytes;
-      const uint8_t* qgt = w.qgt + ci * kKdBytes;
-      const uint8_t* aqt = w.aqt + ci * kAqBytes;
-      const int t0 = s_start + lc * C;
+  if (wave == 1 || wave == 2) {
+    // ------------------------------------------------------ product waves
+    // wave mw: (Q*Gam)^T dO for channel tiles 4mw .. 4mw + 3 and A_qk^T dO for
+    // row tiles 2mw, 2mw + 1 (both K halves; those of row tiles 2, 3 with K
+    // rows 0..31 are stored zeros)
+    const int mw = wave - 1;
+    struct Ops {
+      bf16x8 qa[8];   // (Q*Gam)^T tiles [t*2 + s2], t = 4mw + x / 2
+      bf16x8 aq[4];   // A_qk^T tiles [m*2 + s2], m = 2mw + x / 2
+    };
+    auto load = [&](int k, Ops& o) {
+      const size_t ci = chunk_ci(k);
+      const bf16x8* qgt = reinterpret_cast<const bf16x8*>(w.qgt + ci * kKdBytes);
+      const bf16x8* aqt = reinterpret_cast<const bf16x8*>(w.aqt + ci * kAqBytes);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) o.qa[x] = qgt[(8 * mw + x) * 64 + lane];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) o.aq[x] = aqt[(4 * mw + x) * 64 + lane];
+    };
+    auto emit = [&](const Ops& o, int k, Buf& dst) {
+      // dO as a B operand: K = row (kpos order), N = column li
+      const uint16_t(&rows)[C][16] = sl.dob[k % kDoRing];
+      bf16x8 dob[2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        u16x8 t;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[e] = rows[32 * s2 + kpos(lg, e)][li];
+        dob[s2] = __builtin_bit_cast(bf16x8, t);
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mfma(o.qa[2 * x], dob[0], acc);
+        acc = mfma(o.qa[2 * x + 1], dob[1], acc);
+        dst.r[4 * mw + x][lane] = acc;
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mfma(o.aq[2 * x], dob[0], acc);
+        acc = mfma(o.aq[2 * x + 1], dob[1], acc);
+        dst.p[2 * mw + x][lane] = acc;
+      }
+    };
+    if (nch == 0) {
+      lds_barrier();
+      lds_barrier();
+      return;
+    }
+    // Chunk k + 1's products are written during step k while chunk k + 2's
+    // operand tiles load; the two register sets alternate.  The loads are
+    // issued on every step (the last steps re-load the last chunk), so the
+    // wait before a product always leaves exactly one set in flight.
+    Ops o0, o1;
+    load(0, o0);
+    load(min(1, nch - 1), o1);
+    lds_barrier();  // dO rows of chunks 0 and 1 landed
+    emit(o0, 0, sl.buf[0]);
+    lds_barrier();
+    for (int k = 0; k < nch; k += 2) {
+      load(min(k + 2, nch - 1), o0);
+      if (k + 1 < nch) emit(o1, k + 1, sl.buf[(k + 1) % kGradRing]);
+      lds_barrier();
+      if (k + 1 < nch) {
+        load(min(k + 3, nch - 1), o1);
+        if (k + 2 < nch) emit(o0, k + 2, sl.buf[(k + 2) % kGradRing]);
+        lds_barrier();
+      }
+    }
+    return;
+  }
+  if (wave == 7) {
+    // ----------------------------------------------------------- dO rows
+    // two pieces per chunk: rows 0..31 and 32..63, lane -> row lane / 2, 8 columns
+    auto issue_do = [&](int k) {
+      const int t0 = s_start + (nch - 1 - k) * C;
       const int last = min(C, s_end - t0) - 1;  // rows past the end re-read the last row
 #pragma unroll
-      for (int i = 0; i < (kPieces + LW - 1) / LW; ++i) {
-        const int p = lw + LW * i;  // wave-uniform
-        if (p < 16) dma16(kdr + p * 1024 + off, &dst->kdr[p][0]);
-        else if (p < 32) dma16(wt + (p - 16) * 1024 + off, &dst->wt[p - 16][0]);
-        else if (p < 48) dma16(qgt + (p - 32) * 1024 + off, &dst->qgt[p - 32][0]);
-        else if (p < 56) dma16(aqt + (p - 48) * 1024 + off, &dst->aqt[p - 48][0]);
-        else if (p < kPieces) {
-          const int row = min(32 * (p - 56) + (lane >> 1), last);
-          const uint16_t* src = d_o + ((size_t)(t0 + row) * H + h) * D + 16 * group + 8 * (lane & 1);
-          dma16(reinterpret_cast<const uint8_t*>(src), &dst->dob[32 * (p - 56)][0]);
-        }
+      for (int half = 0; half < 2; ++half) {
+        const int row = min(32 * half + (lane >> 1), last);
+        const uint16_t* src = d_o + ((size_t)(t0 + row) * H + h) * D + 16 * group + 8 * (lane & 1);
+        dma16(reinterpret_cast<const uint8_t*>(src), &sl.dob[k % kDoRing][32 * half][0]);
       }
-      if (lw == LW - 1 && lane < 32) dma16(w.gc + ci * kGcBytes + off, &dst->gc[0]);
     };
-    auto step_end = [&]() {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+    static_assert(2 * (kDoAhead - 2) <= 23, "graded wait range");
+    if (nch == 0) {
       lds_barrier();
-    };
-    // the k-th chunk processed is chunk nch - 1 - k, in buffer k & 1
-    if (nch > 0) issue(nch - 1, &sl.buf[0]);
-    step_end();
-    for (int kx = 0; kx < nch; kx += 2) {
-      if (kx + 1 < nch) issue(nch - 2 - kx, &sl.buf[1]);
-      step_end();
-      if (kx + 1 < nch) {
-        if (kx + 2 < nch) issue(nch - 3 - kx, &sl.buf[0]);
-        step_end();
+      lds_barrier();
+      return;
+    }
+    const int first = min(nch, kDoAhead);
+    for (int k = 0; k < first; ++k) issue_do(k);
+    wait_vm(2 * max(first - 2, 0));  // chunks 0 and 1 landed
+    lds_barrier();
+    lds_barrier();
+    for (int k = 0; k < nch; ++k) {
+      // by the end of this step chunk k + 2 has landed; later ones may fly
+      if (k + kDoAhead < nch) issue_do(k + kDoAhead);
+      wait_vm(2 * max(min(nch - 1, k + kDoAhead) - (k + 2), 0));
+      lds_barrier();
+    }
+    return;
+  }
+  if (wave >= 3) {
+    // --------------------------------------------------------- copy waves
+    // the 32 pieces of Kd and -W^T are dealt round-robin to the four waves,
+    // Gam_C (half a piece) goes with the last
+    const int cw = wave - 3;
+    const int off = lane * 16;
+    const int nrest = cw == 3 ? 9 : 8;
+    auto issue = [&](int k, Buf* dst) {
+      const size_t ci = chunk_ci(k);
+      const uint8_t* kdr = w.kdr + ci * kKdBytes;
+      const uint8_t* wt = w.wt + ci * kKdBytes;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int p = cw + 4 * i;  // scalar
+        if (p < 16) dma16(kdr + p * 1024 + off, &dst->kdr[p][0]);
+        else dma16(wt + (p - 16) * 1024 + off, &dst->wt[p - 16][0]);
       }
+      if (cw == 3 && lane < 32) dma16(w.gc + ci * kGcBytes + off, &dst->gc[0]);
+    };
+    if (nch == 0) {
+      lds_barrier();
+      lds_barrier();
+      return;
+    }
+    issue(0, &sl.buf[0]);
+    if (nch > 1) issue(1, &sl.buf[1]);
+    lds_barrier();
+    wait_vm(nch > 1 ? nrest : 0);  // chunk 0 landed
+    lds_barrier();
+    for (int k = 0; k < nch; ++k) {
+      // chunk k + 1 must land by the end of this step; k + 2 may fly
+      if (k + 2 < nch) {
+        issue(k + 2, &sl.buf[(k + 2) % kGradRing]);
+        wait_vm(nrest);
+      } else {
+        wait_vm(0);
+      }
+      lds_barrier();
     }
     return;
   }
@@ -1856,35 +1984,25 @@ __device__ __forceinline__ void scan_grad_role(int blk, uint8_t* smem_raw, int32
     for (int jj = 0; jj < 4; ++jj)
       X[t][jj] = d_final ? d_final[sb + (size_t)(16 * t + 4 * lg + jj) * D + col] : 0.f;
   lds_barrier();
+  lds_barrier();
 
-  auto chunk_step = [&](const Buf& B, size_t ci) {
+  for (int k = 0; k < nch; ++k) {
+    const Buf& B = sl.buf[k % kGradRing];
+    const size_t ci = chunk_ci(k);
     bf16x8 xb[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) xb[s] = pack_acc(X[2 * s], X[2 * s + 1]);
     bf16x8* dsc = reinterpret_cast<bf16x8*>(w.dsc + ci * kScBytes);
 #pragma unroll
     for (int s = 0; s < 4; ++s) dsc[(group * 4 + s) * 64 + lane] = xb[s];
-    // dO as a B operand: K = row (kpos order), N = column li
-    bf16x8 dob[2];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      u16x8 t;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) t[e] = B.dob[32 * s2 + kpos(lg, e)][li];
-      dob[s2] = __builtin_bit_cast(bf16x8, t);
-    }
-    // dU = A_qk^T dO + Kd X   (A_qk^T is zero for K rows 0..31 of row tiles 2, 3)
+    // dU = A_qk^T dO + Kd X
     f32x4 dU[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) dU[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < 4; ++m) dU[m] = B.p[m][lane];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int m = 0; m < 4; ++m) dU[m] = mfma(B.kdr[m * 4 + s][lane], xb[s], dU[m]);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) dU[m] = mfma(B.aqt[m * 2 + 1][lane], dob[1], dU[m]);
-#pragma unroll
-    for (int m = 0; m < 2; ++m) dU[m] = mfma(B.aqt[m * 2][lane], dob[0], dU[m]);
     bf16x8 ub[2];
     bf16x8* duc = reinterpret_cast<bf16x8*>(w.duc + ci * kUcBytes);
 #pragma unroll
@@ -1894,20 +2012,12 @@ __device__ __forceinline__ void scan_grad_role(int blk, uint8_t* smem_raw, int32
     }
     // X <- Diag(Gam_C) X + (Q*Gam)^T dO - W^T dU
 #pragma unroll
-    for (int t = 0; t < 8; ++t) X[t] = X[t] * B.gc[4 * t + lg];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int t = 0; t < 8; ++t) X[t] = mfma(B.qgt[t * 2 + s2][lane], dob[s2], X[t]);
+    for (int t = 0; t < 8; ++t) X[t] = X[t] * B.gc[4 * t + lg] + B.r[t][lane];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int t = 0; t < 8; ++t) X[t] = mfma(B.wt[t * 2 + s2][lane], ub[s2], X[t]);
     lds_barrier();
-  };
-  for (int kx = 0; kx < nch; kx += 2) {
-    chunk_step(sl.buf[0], (size_t)(cbase + nch - 1 - kx) * H + h);
-    if (kx + 1 < nch) chunk_step(sl.buf[1], (size_t)(cbase + nch - 2 - kx) * H + h);
   }
   if (d_initial) {
 #pragma unroll
@@ -1930,7 +2040,7 @@ __global__ __launch_bounds__(kScanPairThreads) void scan_pair_kernel(
   if ((int)blockIdx.x < nf)
     scan_state_role<1, 1, 7>(blockIdx.x, smem_raw, N, H, w, states, num_slots, slots, flags);
   else
-    scan_grad_role<7>(blockIdx.x - nf, smem_raw, N, H, w, d_o, d_final, d_initial);
+    scan_grad_role(blockIdx.x - nf, smem_raw, N, H, w, d_o, d_final, d_initial);
 }
 
 // Gradient kernel: one workgroup of 8 waves per (chunk, head).  Phases:
