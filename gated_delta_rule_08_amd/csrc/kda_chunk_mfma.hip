@@ -1808,6 +1808,7 @@ struct GradScanLds {
   };
   Buf buf[kGradRing];
   uint16_t dob[kDoRing][C][16];  // dO rows, this workgroup's 16 columns
+  uint8_t sink[1024];            // target of the L2 prefetch loads (never read)
 };
 
 __device__ __forceinline__ void scan_grad_role(int blk, uint8_t* smem_raw, int32_t N, int H,
@@ -1901,8 +1902,15 @@ __device__ __forceinline__ void scan_grad_role(int blk, uint8_t* smem_raw, int32
     return;
   }
   if (wave == 7) {
-    // ----------------------------------------------------------- dO rows
-    // two pieces per chunk: rows 0..31 and 32..63, lane -> row lane / 2, 8 columns
+    // ------------------------------------------------- dO rows, L2 prefetch
+    // dO: two pieces per chunk, rows 0..31 and 32..63, lane -> row lane / 2, 8 columns.
+    // With them, the chunk's operand blocks are pulled into L2 for the copies
+    // that follow kDoAhead - 2 steps later: every 128-byte line of the head's
+    // Kd, -W^T, (Q*Gam)^T (two 64-line units each), A_qk^T, dO rows (two units:
+    // the lines holding columns 0..63 and 64..127) and Gam_C (4 lines), ten
+    // units of one load each (lane -> line), units 2g and 2g + 1 by column
+    // group g < 5 of the head (the eight groups share the L2 of one XCD).
+    const int npf = group < 5 ? 2 : 0;
     auto issue_do = [&](int k) {
       const int t0 = s_start + (nch - 1 - k) * C;
       const int last = min(C, s_end - t0) - 1;  // rows past the end re-read the last row
@@ -1912,22 +1920,44 @@ __device__ __forceinline__ void scan_grad_role(int blk, uint8_t* smem_raw, int32
         const uint16_t* src = d_o + ((size_t)(t0 + row) * H + h) * D + 16 * group + 8 * (lane & 1);
         dma16(reinterpret_cast<const uint8_t*>(src), &sl.dob[k % kDoRing][32 * half][0]);
       }
+      if (npf) {
+        const size_t ci = chunk_ci(k);
+        const size_t line = (size_t)lane * 128;
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int unit = 2 * group + x;  // scalar
+          const uint8_t* src;
+          if (unit < 2) src = w.kdr + ci * kKdBytes + unit * 8192 + line;
+          else if (unit < 4) src = w.wt + ci * kKdBytes + (unit - 2) * 8192 + line;
+          else if (unit < 6) src = w.qgt + ci * kKdBytes + (unit - 4) * 8192 + line;
+          else if (unit == 6) src = w.aqt + ci * kAqBytes + line;
+          else if (unit < 9) {
+            const int row = min(lane, last);
+            src = reinterpret_cast<const uint8_t*>(d_o + ((size_t)(t0 + row) * H + h) * D + 64 * (unit - 7));
+          } else {
+            src = w.gc + ci * kGcBytes + (size_t)min(lane, 3) * 128;
+          }
+          dma16(src, &sl.sink[0]);
+        }
+      }
     };
-    static_assert(2 * (kDoAhead - 2) <= 23, "graded wait range");
+    static_assert(2 + 4 * (kDoAhead - 2) <= 23, "graded wait range");
     if (nch == 0) {
       lds_barrier();
       lds_barrier();
       return;
     }
+    // loads issued after chunk j's dO rows, up to chunk `newest`
+    auto after = [&](int j, int newest) { return npf + (2 + npf) * max(newest - j, 0); };
     const int first = min(nch, kDoAhead);
     for (int k = 0; k < first; ++k) issue_do(k);
-    wait_vm(2 * max(first - 2, 0));  // chunks 0 and 1 landed
+    wait_vm(after(min(1, nch - 1), first - 1));  // dO rows of chunks 0 and 1 landed
     lds_barrier();
     lds_barrier();
     for (int k = 0; k < nch; ++k) {
-      // by the end of this step chunk k + 2 has landed; later ones may fly
+      // by the end of this step chunk k + 2's dO rows have landed; later ones may fly
       if (k + kDoAhead < nch) issue_do(k + kDoAhead);
-      wait_vm(2 * max(min(nch - 1, k + kDoAhead) - (k + 2), 0));
+      wait_vm(k + 2 < nch ? after(k + 2, min(nch - 1, k + kDoAhead)) : 0);
       lds_barrier();
     }
     return;
