@@ -86,6 +86,12 @@ def test_backward_zero_length_sequences_and_many_chains():
     _case(46, [0, 90, 0, 200, 64, 0, 1, 130, 77, 0, 65, 300], 16, s0=True, d_final=True)
 
 
+def test_backward_chain_lengths_around_the_copy_lookahead():
+    """Chains of 6-9 chunks: the reverse pass's copies, dO rows and products start
+    several chunks ahead of its carried state, so these lengths end inside each lookahead."""
+    _case(47, [330, 420, 449, 520], 2, s0=True, d_final=True)
+
+
 def test_backward_full_prefill_shape():
     """The prefill workload's shape: one sequence of 4,096 tokens, 16 heads."""
     _case(45, [4096], 16, d_final=True)
