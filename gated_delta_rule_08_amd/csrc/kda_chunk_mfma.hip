@@ -243,7 +243,7 @@ struct PrepSmem {
   uint16_t Q[C][KP];
   uint16_t V[C][KP];
   float G[C][GP];
-  float A[C][AP];        // beta-scaled strictly lower A_kk
+  float A[C][AP];        // beta-scaled strictly lower A_kk (backward: A_qk^T above it)
   float Tm[C][AP];       // (I + A_kk)^-1
   float tot[4][D];       // per-quarter column totals of the running gate sums
   float es[4][D];        // exp(G) at the first row of each 16-row block
@@ -659,14 +659,14 @@ __device__ __forceinline__ void prep_role(
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) (&mrow.x)[jj] = 16 * J + 4 * lg + jj < r ? acck[jj] : 0.f;
           *reinterpret_cast<float4*>(w.mkk + ci * kMkBytes + (size_t)(r * C + 16 * J + 4 * lg) * 4) = mrow;
-          // A_qk^T as the reverse scan's A operand (M = column j, K = row r, kpos
-          // order): every value lands in another lane's slot, so 2-byte stores
-          const int ro = 16 * (R & 1) + li;  // row inside the 32-row K block R / 2
-          const int slot = (ro & 3) + 4 * (ro >> 4), lgd = (ro & 15) >> 2;
-          uint16_t* at = reinterpret_cast<uint16_t*>(w.aqt + ci * kAqBytes) +
-                         ((size_t)(J * 2 + (R >> 1)) * 64 + lgd * 16) * 8 + slot;
+          // A_qk^T into the upper triangle of A (row j, column r >= j), which the
+          // triangular solve never reads; for the diagonal block this follows the
+          // A_kk row's zeros in the same wave, so these values stay
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) at[(4 * lg + jj) * 8] = f32_to_bf16(qv[jj]);
+          for (int jj = 0; jj < 4; ++jj) {
+            const int j = 16 * J + 4 * lg + jj;
+            if (j <= r) sm.A[j][r] = qv[jj];
+          }
         }
         // A_qk as the scan's A operand: [m = R][s' = J / 2][lane][slots (J & 1) * 4 ..]
         uint16_t* dst = aq_out + ((size_t)(R * 2 + (J >> 1)) * 64 + lane) * 8 + (J & 1) * 4;
@@ -682,19 +682,6 @@ __device__ __forceinline__ void prep_role(
       }
     }
     lds_barrier();
-    if constexpr (kBwd) {
-      // zeros of A_qk^T where A_qk is above the diagonal: pairs (R, J), J > R
-      if (wave < 6) {
-        const int R = wave < 3 ? 0 : wave < 5 ? 1 : 2;
-        const int J = wave < 3 ? wave + 1 : wave < 5 ? wave - 1 : 3;
-        const int ro = 16 * (R & 1) + li;
-        const int slot = (ro & 3) + 4 * (ro >> 4), lgd = (ro & 15) >> 2;
-        uint16_t* at = reinterpret_cast<uint16_t*>(w.aqt + ci * kAqBytes) +
-                       ((size_t)(J * 2 + (R >> 1)) * 64 + lgd * 16) * 8 + slot;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) at[(4 * lg + jj) * 8] = 0;
-      }
-    }
 
     if (prefetch) prep_load_part<kGate, kAdd, kRaw, 2>(in, pos, q, k, v, g, beta, H, tid);
 
@@ -821,6 +808,19 @@ __device__ __forceinline__ void prep_role(
     }
     if constexpr (kBwd) {
       // the reverse pass's other operands, from LDS only
+      {
+        // A_qk^T as the reverse scan's A operand (M = row j, K = row r, kpos
+        // order) from the upper triangle of A, one tile per wave; columns r < j
+        // hold A_kk there and are zero in A_qk^T
+        const int m = wave >> 1, s2 = wave & 1, j = 16 * m + li;
+        const float4 a = *reinterpret_cast<const float4*>(&sm.A[j][32 * s2 + 4 * lg]);
+        const float4 b = *reinterpret_cast<const float4*>(&sm.A[j][32 * s2 + 16 + 4 * lg]);
+        float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (32 * s2 + kpos(lg, e) < j) f[e] = 0.f;
+        *reinterpret_cast<bf16x8*>(w.aqt + ci * kAqBytes + ((size_t)wave * 64 + lane) * 16) = pack8(f);
+      }
       {
         // (Q*Gam)^T as the reverse scan's A operand (M = channel, K = row)
         const int ch = 16 * wave + li;
@@ -1784,8 +1784,9 @@ kda_status_t launch_scan(int32_t N, int H, const Workspace& w, float* states, in
 //  * waves 3..6 copy Kd, -W^T and Gam_C into LDS with direct global->LDS
 //    loads, two chunks ahead; wave 7 copies the chunk's dO rows (this
 //    workgroup's columns, 64 rows 32 bytes each) kDoAhead chunks ahead into a
-//    ring of their own.  A wave's loads complete in issue order, so rows
-//    copied far ahead need a wave that waits for nothing issued after them;
+//    ring of their own, and with them pulls the lines of that chunk's blocks
+//    into L2.  A wave's loads complete in issue order, so rows copied far ahead
+//    need a wave that waits for nothing issued after them;
 //  * waves 1 and 2 form the chunk's products that do not depend on X, for this
 //    workgroup's columns: A_qk^T dO (the start of dU) and (Q*Gam)^T dO (X's
 //    increment), from operand tiles they load into registers a step ahead and
