@@ -1446,6 +1446,7 @@ struct StateLds {
     f32x4 gc[32];              // Gam_C
   };
   Buf buf[kStateRing];  // ring: the copies run kStateRing - 1 chunks ahead of the compute wave
+  uint8_t sink[1024];   // target of the L2 warming loads (never read)
 };
 
 // s_waitcnt vmcnt(n) for a wave-uniform n <= 23 (the count is an immediate; its
@@ -1479,11 +1480,16 @@ __device__ __forceinline__ void wait_vm(int n) {
   }
 }
 
-template <int CW, int NT, int LW>
+// kWarm (the backward's paired launch): one loader wave also pulls the dO rows
+// of the reverse pass's next chunks into L2, two of its chunks per step of this
+// pass (which runs about twice as fast), so that the reverse pass, which reads
+// them as scattered 32-byte pieces, finds them there rather than in HBM.
+template <int CW, int NT, int LW, bool kWarm = false>
 __device__ __forceinline__ void scan_state_role(int blk, uint8_t* smem_raw, int32_t N, int H,
                                                 const Workspace& w, float* __restrict__ states,
                                                 int32_t num_slots,
-                                                const int32_t* __restrict__ slots, uint32_t flags) {
+                                                const int32_t* __restrict__ slots, uint32_t flags,
+                                                const uint16_t* __restrict__ d_o = nullptr) {
   using L = StateLds<CW, NT>;
   using Buf = typename L::Buf;
   constexpr int kTiles = L::kTiles;
@@ -1525,6 +1531,21 @@ __device__ __forceinline__ void scan_state_role(int blk, uint8_t* smem_raw, int3
     // chunks up to lc + kAhead - 1 have been issued; waiting for all but this
     // wave's newest (in-flight chunks - 1) x `mine` copies means chunk lc has
     // landed while the later ones stay in flight.
+    // Warming (kWarm, wave LW - 2 of the loaders): exactly one load per step,
+    // issued after the step's wait, so each wait also leaves the previous step's
+    // warming load in flight.  Lanes 0..15 take chunk 2 lc of the reverse order
+    // (chunk nch - 1 - 2 lc), lanes 16..31 the next one, rows 8 group .. + 7 of
+    // the head, both 128-byte lines of each row; lanes 32..63 repeat them.
+    const bool warmer = kWarm && __builtin_amdgcn_readfirstlane(lw) == LW - 2;
+    auto warm = [&](int lc) {
+      const int l = lane & 31;
+      const int chunk = max(nch - 1 - 2 * lc - (l >> 4), 0);
+      const int t0 = w.seq_start[n] + chunk * C;
+      const int last = min(C, w.seq_end[n] - t0) - 1;
+      const int row = min(8 * group + ((l & 15) >> 1), last);
+      dma16(reinterpret_cast<const uint8_t*>(d_o + ((size_t)(t0 + row) * H + h) * D + 64 * (l & 1)),
+            &sl.sink[0]);
+    };
     for (int c = 0; c < kAhead && c < nch; ++c) issue((size_t)(cbase + c) * H + h, &sl.buf[c]);
     wait_vm(mine * (min(nch, kAhead) - 1 > 0 ? min(nch, kAhead) - 1 : 0));  // chunk 0 landed
     lds_barrier();
@@ -1533,9 +1554,11 @@ __device__ __forceinline__ void scan_state_role(int blk, uint8_t* smem_raw, int3
       const int nxt = lc + kAhead;
       if (nxt < nch) issue((size_t)(cbase + nxt) * H + h, &sl.buf[nxt % kStateRing]);
       const int newest = min(nch - 1, nxt) - (lc + 1);  // chunks issued after lc + 1
-      wait_vm(newest > 0 ? mine * newest : 0);
+      wait_vm((newest > 0 ? mine * newest : 0) + (warmer && lc > 0 ? 1 : 0));
+      if (warmer) warm(lc);
       lds_barrier();
     }
+    if (warmer) wait_vm(0);  // no load into LDS outlives the wave
     return;
   }
 
@@ -2069,7 +2092,7 @@ __global__ __launch_bounds__(kScanPairThreads) void scan_pair_kernel(
   extern __shared__ __align__(16) uint8_t smem_raw[];
   const int nf = N * H * (D / 16);
   if ((int)blockIdx.x < nf)
-    scan_state_role<1, 1, 7>(blockIdx.x, smem_raw, N, H, w, states, num_slots, slots, flags);
+    scan_state_role<1, 1, 7, true>(blockIdx.x, smem_raw, N, H, w, states, num_slots, slots, flags, d_o);
   else
     scan_grad_role(blockIdx.x - nf, smem_raw, N, H, w, d_o, d_final, d_initial);
 }
