@@ -1808,8 +1808,9 @@ kda_status_t launch_scan(int32_t N, int H, const Workspace& w, float* states, in
 //    loads, two chunks ahead; wave 7 copies the chunk's dO rows (this
 //    workgroup's columns, 64 rows 32 bytes each) kDoAhead chunks ahead into a
 //    ring of their own, and with them pulls the lines of that chunk's blocks
-//    into L2.  A wave's loads complete in issue order, so rows copied far ahead
-//    need a wave that waits for nothing issued after them;
+//    into L2 (the forward pass beside it pulls the dO rows earlier still).  A
+//    wave's loads complete in issue order, so rows copied far ahead need a wave
+//    that waits for nothing issued after them;
 //  * waves 1 and 2 form the chunk's products that do not depend on X, for this
 //    workgroup's columns: A_qk^T dO (the start of dU) and (Q*Gam)^T dO (X's
 //    increment), from operand tiles they load into registers a step ahead and
