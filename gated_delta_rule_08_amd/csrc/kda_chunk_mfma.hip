@@ -1480,10 +1480,11 @@ __device__ __forceinline__ void wait_vm(int n) {
   }
 }
 
-// kWarm (the backward's paired launch): one loader wave also pulls the dO rows
-// of the reverse pass's next chunks into L2, two of its chunks per step of this
-// pass (which runs about twice as fast), so that the reverse pass, which reads
-// them as scattered 32-byte pieces, finds them there rather than in HBM.
+// kWarm (the backward's paired launch): wave CW + LW, beside the LW loaders,
+// pulls the dO rows of the reverse pass's chunks into the caches, four of its
+// chunks per step of this pass (which runs about twice as fast), waiting for
+// none of them until its end, so that the reverse pass, which reads them as
+// scattered 32-byte pieces, does not find them in HBM.
 template <int CW, int NT, int LW, bool kWarm = false>
 __device__ __forceinline__ void scan_state_role(int blk, uint8_t* smem_raw, int32_t N, int H,
                                                 const Workspace& w, float* __restrict__ states,
@@ -1502,6 +1503,27 @@ __device__ __forceinline__ void scan_state_role(int blk, uint8_t* smem_raw, int3
   const int nch = w.seq_nch[n];
   const int cbase = w.chunk_off[n];
 
+  if (kWarm && __builtin_amdgcn_readfirstlane(wave) == CW + LW) {
+    // --------------------------------------------------------- dO warming
+    // Lanes: chunk 4 lc + l / 16 of the reverse order (chunk nch - 1 - that),
+    // row 8 group + (l % 16) / 2 of the head, its 128-byte line l % 2.
+    auto warm = [&](int lc) {
+      const int chunk = max(nch - 1 - (4 * lc + (lane >> 4)), 0);
+      const int t0 = w.seq_start[n] + chunk * C;
+      const int last = min(C, w.seq_end[n] - t0) - 1;
+      const int row = min(8 * group + ((lane & 15) >> 1), last);
+      dma16(reinterpret_cast<const uint8_t*>(d_o + ((size_t)(t0 + row) * H + h) * D + 64 * (lane & 1)),
+            &sl.sink[0]);
+    };
+    if (nch > 0) warm(0);
+    lds_barrier();
+    for (int lc = 0; lc < nch; ++lc) {
+      if (4 * (lc + 1) < nch) warm(lc + 1);
+      lds_barrier();
+    }
+    wait_vm(0);  // no load into LDS outlives the wave
+    return;
+  }
   if (wave >= CW) {
     // ------------------------------------------------------------ loaders
     const int lw = wave - CW;
@@ -1531,21 +1553,6 @@ __device__ __forceinline__ void scan_state_role(int blk, uint8_t* smem_raw, int3
     // chunks up to lc + kAhead - 1 have been issued; waiting for all but this
     // wave's newest (in-flight chunks - 1) x `mine` copies means chunk lc has
     // landed while the later ones stay in flight.
-    // Warming (kWarm, wave LW - 2 of the loaders): exactly one load per step,
-    // issued after the step's wait, so each wait also leaves the previous step's
-    // warming load in flight.  Lanes 0..15 take chunk 2 lc of the reverse order
-    // (chunk nch - 1 - 2 lc), lanes 16..31 the next one, rows 8 group .. + 7 of
-    // the head, both 128-byte lines of each row; lanes 32..63 repeat them.
-    const bool warmer = kWarm && __builtin_amdgcn_readfirstlane(lw) == LW - 2;
-    auto warm = [&](int lc) {
-      const int l = lane & 31;
-      const int chunk = max(nch - 1 - 2 * lc - (l >> 4), 0);
-      const int t0 = w.seq_start[n] + chunk * C;
-      const int last = min(C, w.seq_end[n] - t0) - 1;
-      const int row = min(8 * group + ((l & 15) >> 1), last);
-      dma16(reinterpret_cast<const uint8_t*>(d_o + ((size_t)(t0 + row) * H + h) * D + 64 * (l & 1)),
-            &sl.sink[0]);
-    };
     for (int c = 0; c < kAhead && c < nch; ++c) issue((size_t)(cbase + c) * H + h, &sl.buf[c]);
     wait_vm(mine * (min(nch, kAhead) - 1 > 0 ? min(nch, kAhead) - 1 : 0));  // chunk 0 landed
     lds_barrier();
@@ -1554,11 +1561,9 @@ __device__ __forceinline__ void scan_state_role(int blk, uint8_t* smem_raw, int3
       const int nxt = lc + kAhead;
       if (nxt < nch) issue((size_t)(cbase + nxt) * H + h, &sl.buf[nxt % kStateRing]);
       const int newest = min(nch - 1, nxt) - (lc + 1);  // chunks issued after lc + 1
-      wait_vm((newest > 0 ? mine * newest : 0) + (warmer && lc > 0 ? 1 : 0));
-      if (warmer) warm(lc);
+      wait_vm(newest > 0 ? mine * newest : 0);
       lds_barrier();
     }
-    if (warmer) wait_vm(0);  // no load into LDS outlives the wave
     return;
   }
 
@@ -2093,7 +2098,7 @@ __global__ __launch_bounds__(kScanPairThreads) void scan_pair_kernel(
   extern __shared__ __align__(16) uint8_t smem_raw[];
   const int nf = N * H * (D / 16);
   if ((int)blockIdx.x < nf)
-    scan_state_role<1, 1, 7, true>(blockIdx.x, smem_raw, N, H, w, states, num_slots, slots, flags, d_o);
+    scan_state_role<1, 1, 6, true>(blockIdx.x, smem_raw, N, H, w, states, num_slots, slots, flags, d_o);
   else
     scan_grad_role(blockIdx.x - nf, smem_raw, N, H, w, d_o, d_final, d_initial);
 }
