@@ -68,11 +68,11 @@ constexpr size_t kGcBytes = D * 4;             // Gam_C   fp32
 constexpr size_t kScBytes = 8 * 4 * 64 * 16;   // S at chunk start, B operand (K=dk, N=dv), bf16
 constexpr size_t kUcBytes = 8 * 2 * 64 * 16;   // U, B operand (K=rows, N=dv), bf16
 // Backward only (the reverse scan's A operands use the Kd^T / A_qk block sizes;
-// the gradient kernel reads M_kk and T as plain fp32 [64][64]):
+// the gradient kernel reads T as plain fp32 [64][64] and M_kk in 16 x 16 tiles):
 //   kdr  Kd        A operand, M=rows, K=dk      wt   -W^T    A operand, M=dk, K=rows
 //   qgt  (Q*Gam)^T A operand, M=dk,   K=rows    aqt  A_qk^T  A operand, M=rows j, K=rows r
 //   dsc  dL/dS at chunk end and duc dL/dU, laid out as S and U above.
-constexpr size_t kMkBytes = C * C * 4;
+constexpr size_t kMkBytes = C * C * 4;        // M_kk fp32, 16x16 tiles [R*4 + J][row][column]
 constexpr size_t kTmBytes = C * C * 4;
 
 // Chains (sequence-heads) up to which the scan only carries the state and a
@@ -654,11 +654,12 @@ __device__ __forceinline__ void prep_role(
         }
         *reinterpret_cast<float4*>(&sm.A[r][16 * J + 4 * lg]) = arow;
         if constexpr (kBwd) {
-          // M_kk (unscaled, strictly lower) for the gradient of beta
+          // M_kk (unscaled, strictly lower) for the gradient of beta, 16 x 16 tiles
+          // [R * 4 + J][row][column], each written as one contiguous 1 KiB block
           float4 mrow;
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) (&mrow.x)[jj] = 16 * J + 4 * lg + jj < r ? acck[jj] : 0.f;
-          *reinterpret_cast<float4*>(w.mkk + ci * kMkBytes + (size_t)(r * C + 16 * J + 4 * lg) * 4) = mrow;
+          *reinterpret_cast<float4*>(w.mkk + ci * kMkBytes + (size_t)(((R * 4 + J) * 16 + li) * 16 + 4 * lg) * 4) = mrow;
           // A_qk^T into the upper triangle of A (row j, column r >= j), which the
           // triangular solve never reads; for the diagonal block this follows the
           // A_kk row's zeros in the same wave, so these values stay
@@ -2450,7 +2451,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
         const bool low = J <= R;
         const float aq = low && j <= r ? aAq[x][jj] : 0.f;
         const float ak = !kAdd && low && j < r ? -aAk[x][jj] : 0.f;   // dA_kk = -(dR U^T)
-        const float mv = !kAdd && low && j < r ? mk[r * C + j] : 0.f;
+        const float mv = !kAdd && low && j < r ? mk[((R * 4 + J) * 16 + 4 * lg + jj) * 16 + li] : 0.f;
         // dbeta_r += sum_j dA_kk[r,j] M_kk[r,j]; R is 0 or 1 (x = 0), 2 or 3 (x = 1)
         const float add = ak * mv;
         pb[8 * x + jj] += (R & 1) ? 0.f : add;
