@@ -68,12 +68,12 @@ constexpr size_t kGcBytes = D * 4;             // Gam_C   fp32
 constexpr size_t kScBytes = 8 * 4 * 64 * 16;   // S at chunk start, B operand (K=dk, N=dv), bf16
 constexpr size_t kUcBytes = 8 * 2 * 64 * 16;   // U, B operand (K=rows, N=dv), bf16
 // Backward only (the reverse scan's A operands use the Kd^T / A_qk block sizes;
-// the gradient kernel reads T as plain fp32 [64][64] and M_kk in 16 x 16 tiles):
+// the gradient kernel reads T^T as bf16 operand tiles and M_kk as fp32 16 x 16 tiles):
 //   kdr  Kd        A operand, M=rows, K=dk      wt   -W^T    A operand, M=dk, K=rows
 //   qgt  (Q*Gam)^T A operand, M=dk,   K=rows    aqt  A_qk^T  A operand, M=rows j, K=rows r
 //   dsc  dL/dS at chunk end and duc dL/dU, laid out as S and U above.
 constexpr size_t kMkBytes = C * C * 4;        // M_kk fp32, 16x16 tiles [R*4 + J][row][column]
-constexpr size_t kTmBytes = C * C * 4;
+constexpr size_t kTmBytes = 8 * 64 * 16;       // T^T bf16 A-operand tiles [m*2 + s2][lane]
 
 // Chains (sequence-heads) up to which the scan only carries the state and a
 // separate, fully parallel kernel forms the outputs: with few chains the
@@ -728,12 +728,15 @@ __device__ __forceinline__ void prep_role(
     }
 
     if constexpr (kBwd) {
-      // T for the gradient kernel, plain [j][r] fp32 (upper blocks are zero)
-      float* tm_out = reinterpret_cast<float*>(w.tm + ci * kTmBytes);
+      // T^T for the gradient kernel, as the A operand of dR = T^T dU there (M = row
+      // r, K = row j, kpos order): bf16 tiles [m * 2 + s2][lane], wave = m * 2 + s2.
+      // Tiles m >= 2, s2 = 0 are zero (T is lower triangular) and not stored.
+      const int m = wave >> 1, s2 = wave & 1;
+      if (m < 2 || s2 == 1) {
+        float f[8];
 #pragma unroll
-      for (int x = 0; x < C * C / 4 / kPrepThreads; ++x) {
-        const int u = tid + kPrepThreads * x, r = u >> 4, c4 = (u & 15) * 4;
-        *reinterpret_cast<float4*>(tm_out + r * C + c4) = *reinterpret_cast<const float4*>(&sm.Tm[r][c4]);
+        for (int e = 0; e < 8; ++e) f[e] = sm.Tm[32 * s2 + kpos(lg, e)][16 * m + li];
+        *reinterpret_cast<bf16x8*>(w.tm + ci * kTmBytes + ((size_t)wave * 64 + lane) * 16) = pack8(f);
       }
     }
 
@@ -2105,7 +2108,7 @@ __global__ __launch_bounds__(kScanPairThreads) void scan_pair_kernel(
 }
 
 // Gradient kernel: one workgroup of 8 waves per (chunk, head).  Phases:
-//  0  stage K, Q, the gates (running sums), beta and T; T^T operands to registers
+//  0  stage K, Q, the gates (running sums) and beta; the T^T operand tiles to registers
 //  1  two halves of 64 value columns: dR = T^T dU (-> dV, dbeta), then
 //     Z = dR S^T, d(Q*Gam) = dO S^T, dKd = U X^T, dA_qk = dO U^T, dR U^T, dGam_C
 //  2  elementwise terms of dq, dk, dG; dbeta terms; dA_qk and dM = beta dA_kk to LDS
@@ -2128,7 +2131,6 @@ struct GradSmem {
   float dgl[D];        // dG of the chunk's last row from Gam_C
   float spr[kGradThreads / 64];
   union {
-    float T[C][AP];       // phase 0
     uint16_t dR[C][KB];   // phase 1: all 128 value columns
   } x;
   union {
@@ -2272,13 +2274,16 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
     sm.db[tid] = 0.f;
   }
   if (tid < D) sm.dgl[tid] = 0.f;
+  // T^T as the A operand of dR = T^T dU (M = row r, K = row j, kpos order), tiles
+  // stored by the prep; T^T is zero for K rows 0..31 of row tiles 2 and 3.
+  bf16x8 tT[4][2];
   {
-    const float* tm = reinterpret_cast<const float*>(w.tm + ci * kTmBytes);
+    const bf16x8* tmt = reinterpret_cast<const bf16x8*>(w.tm + ci * kTmBytes);
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int u = tid + kGradThreads * x, r = u >> 4, c4 = (u & 15) * 4;
-      *reinterpret_cast<float4*>(&sm.x.T[r][c4]) = *reinterpret_cast<const float4*>(tm + r * C + c4);
-    }
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+        if (m < 2 || s2 == 1) tT[m][s2] = tmt[(m * 2 + s2) * 64 + lane];
   }
   block_sync();
   {
@@ -2299,20 +2304,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
     for (int off = 32; off >= 1; off >>= 1) sp = fmaxf(sp, __shfl_xor(sp, off, 64));
     if (lane == 0) sm.spr[wave] = sp;  // waves 2qt and 2qt + 1 cover block qt
   }
-  // T^T as the A operand of dR = T^T dU (M = row r, K = row j, kpos order); T^T is
-  // zero for K rows 0..31 of row tiles 2 and 3.
-  bf16x8 tT[4][2];
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      if (m >= 2 && s2 == 0) continue;
-      float f[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = sm.x.T[32 * s2 + kpos(lg, e)][16 * m + li];
-      tT[m][s2] = pack8(f);
-    }
-  block_sync();  // T is read; its space holds dR from here
+  block_sync();  // the running sums are read before the tile area is reused
 
   // ---- 1. dR = T^T dU for value column tile `wave` (dU straight from the reverse
   // pass), then dV = Diag(beta) dR and the dbeta term rowsum(dR * V)
