@@ -413,8 +413,8 @@ def main(argv=None):
         return 2
     kda.load_library()
     # No cyclic garbage collection while anything is timed: a full collection that falls
-    # inside an event-timed region stalls the launching thread for tens of milliseconds
-    # while the GPU idles (seen once as a 3.8 ms mean over ten 0.3 ms calls).
+    # inside an event-timed region can stall the launching thread for tens of milliseconds
+    # while the GPU idles (the likely cause of a 3.8 ms mean over ten 0.3 ms calls).
     gc.collect()
     gc.disable()
     flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
