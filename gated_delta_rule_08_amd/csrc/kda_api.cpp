@@ -18,6 +18,8 @@ kda_status_t launch_state_init(float* states, size_t n_floats, hipStream_t strea
 kda_status_t launch_state_copy(bool to_pool, float* states, int32_t num_slots,
                                const int32_t* slots, int32_t n, float* dense,
                                size_t per_state_floats, hipStream_t stream);
+kda_status_t launch_state_fill(float* dst, int32_t num_slots, const int32_t* slots, int32_t n,
+                               const float* src, size_t per_state_floats, hipStream_t stream);
 kda_status_t launch_state_affine(int32_t n, int H, int dk, int dv, const float* M,
                                  const float* S_in, const float* B, float* S_out,
                                  hipStream_t stream);
@@ -222,7 +224,20 @@ kda_status_t chunk_fwd_impl(const char* W, const kda_shape_t* sh, int32_t chunk,
   if (raw && gate_min != gate_min) return invalid("%s: gate_min is NaN", W);
   if (raw ? !chunk_mfma_supported(sh->dk, sh->dv, chunk, sh->io_dtype) : !chunk_supported(sh, chunk))
     return unsupported(W, sh, chunk);
-  if (total_tokens == 0 || num_seqs == 0) return KDA_OK;
+  if (num_seqs == 0) return KDA_OK;
+  if (total_tokens == 0) {
+    // Every sequence is empty and ends in the state it starts from (zero without
+    // an initial state), so only a final-state write alone changes the pool.
+    if ((flags & kStateFlags) != KDA_WRITE_FINAL_STATE) return KDA_OK;
+    if (!states) return invalid("%s: states is NULL but flags request state I/O", W);
+    if (num_slots <= 0) return invalid("%s: num_slots must be >= 1 with state I/O", W);
+    if (!state_slots && num_slots < num_seqs)
+      return invalid("%s: num_slots (%d) < num_seqs (%d) with implicit slots", W, num_slots,
+                     num_seqs);
+    return launch_state_fill(states, num_slots, state_slots, num_seqs, nullptr,
+                             (size_t)sh->num_heads * sh->dk * sh->dv,
+                             static_cast<hipStream_t>(stream));
+  }
   if (!cu_seqlens) return invalid("%s: cu_seqlens is NULL", W);
   if (!q || !k || !v || !o) return invalid("%s: a tensor pointer is NULL", W);
   st = check_gate_beta(flags, g, beta, raw, W);
@@ -431,7 +446,17 @@ kda_status_t chunk_bwd_impl(const char* W, const kda_shape_t* sh, int32_t chunk,
   if (chunk <= 0) return invalid("%s: chunk must be >= 1 (got %d)", W, chunk);
   if (raw && gate_min != gate_min) return invalid("%s: gate_min is NaN", W);
   if (!chunk_mfma_supported(sh->dk, sh->dv, chunk, sh->io_dtype)) return unsupported(W, sh, chunk);
-  if (total_tokens == 0 || num_seqs == 0) return KDA_OK;
+  if (num_seqs == 0) return KDA_OK;
+  if (total_tokens == 0) {
+    // Every sequence is empty and passes its state through unchanged, so
+    // dL/dS0 = dL/dS_final (zero when no final-state gradient is given).
+    if (!d_initial_state) return KDA_OK;
+    if (!aligned(d_initial_state, 4) || (d_final_state && !aligned(d_final_state, 4)))
+      return invalid("%s: the state gradients must be 4-byte aligned", W);
+    return launch_state_fill(d_initial_state, num_seqs, nullptr, num_seqs, d_final_state,
+                             (size_t)sh->num_heads * sh->dk * sh->dv,
+                             static_cast<hipStream_t>(stream));
+  }
   if (!cu_seqlens) return invalid("%s: cu_seqlens is NULL", W);
   if (!q || !k || !v || !d_o || !dq || !dk || !dv) return invalid("%s: a tensor pointer is NULL", W);
   st = check_gate_beta(flags, g, beta, raw, W);

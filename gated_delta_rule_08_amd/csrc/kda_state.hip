@@ -39,6 +39,25 @@ __global__ __launch_bounds__(kThreads) void gather_scatter_kernel(
   }
 }
 
+// dst[slot(i)] = src[i], or zero when src is NULL, for i < n; one state is per
+// floats (slot i when slots is NULL; slots outside [0, num_slots) are skipped).
+// Plain float accesses: the callers' buffers are only element-aligned.
+__global__ __launch_bounds__(kThreads) void state_fill_kernel(float* __restrict__ dst,
+                                                              int32_t num_slots,
+                                                              const int32_t* __restrict__ slots,
+                                                              int32_t n,
+                                                              const float* __restrict__ src,
+                                                              size_t per) {
+  const size_t total = (size_t)n * per;
+  for (size_t e = blockIdx.x * (size_t)kThreads + threadIdx.x; e < total;
+       e += (size_t)gridDim.x * kThreads) {
+    const size_t i = e / per, off = e - i * per;
+    const int32_t slot = slots ? slots[i] : (int32_t)i;
+    if (slot < 0 || slot >= num_slots) continue;
+    dst[(size_t)slot * per + off] = src ? src[e] : 0.f;
+  }
+}
+
 // S_out = M S_in + B for one (entry, head) and a block of kAffCols columns:
 // the effect of a segment on its incoming state is affine, and composing it is
 // the exchange step of context-parallel prefill (heqinghuang "From GPT2 to
@@ -89,6 +108,13 @@ kda_status_t launch_state_init(float* states, size_t n_floats, hipStream_t strea
   hipLaunchKernelGGL(zero_kernel, dim3(grid_for(n4)), dim3(kThreads), 0, stream,
                      reinterpret_cast<float4*>(states), n4);
   return check_launch("zero_kernel");
+}
+
+kda_status_t launch_state_fill(float* dst, int32_t num_slots, const int32_t* slots, int32_t n,
+                               const float* src, size_t per_state_floats, hipStream_t stream) {
+  hipLaunchKernelGGL(state_fill_kernel, dim3(grid_for((size_t)n * per_state_floats)),
+                     dim3(kThreads), 0, stream, dst, num_slots, slots, n, src, per_state_floats);
+  return check_launch("state_fill_kernel");
 }
 
 kda_status_t launch_state_affine(int32_t n, int H, int dk, int dv, const float* M,

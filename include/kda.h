@@ -143,7 +143,11 @@ size_t kda_chunk_fwd_workspace_bytes(const kda_shape_t* shape, int32_t chunk,
  * flags       KDA_READ_INITIAL_STATE | KDA_WRITE_FINAL_STATE | at most one of
  *             KDA_GATE_SCALAR, KDA_GATE_NONE | KDA_ADDITIVE; other bits, or
  *             both gate bits, are KDA_ERR_INVALID_ARGUMENT.
- * total_tokens == 0 or num_seqs == 0 is a no-op returning KDA_OK. */
+ * num_seqs == 0 is a no-op returning KDA_OK.  total_tokens == 0 makes every
+ * sequence empty: each ends in the state it starts from (zero without an
+ * initial state), so KDA_WRITE_FINAL_STATE without KDA_READ_INITIAL_STATE
+ * zeroes each sequence's slot, every other flag setting leaves the pool as it
+ * is, and nothing else is read or written. */
 kda_status_t kda_chunk_fwd(const kda_shape_t* shape, int32_t chunk, int32_t total_tokens,
                            int32_t num_seqs, const int32_t* cu_seqlens, const void* q,
                            const void* k, const void* v, const float* g, const float* beta,
@@ -253,7 +257,10 @@ size_t kda_chunk_bwd_workspace_bytes(const kda_shape_t* shape, int32_t chunk,
  * workspace      device scratch of kda_chunk_bwd_workspace_bytes() bytes, 256-byte
  *                aligned (about 345 KiB per chunk and head).
  * Supported: io_dtype KDA_BF16, dk = dv = 128, chunk 64 (else KDA_ERR_UNSUPPORTED).
- * total_tokens == 0 or num_seqs == 0 is a no-op returning KDA_OK. */
+ * num_seqs == 0 is a no-op returning KDA_OK.  total_tokens == 0 makes every
+ * sequence empty, passing its state through unchanged: d_initial_state (when
+ * given) is set to d_final_state, or to zero when that is NULL, and nothing
+ * else is read or written. */
 kda_status_t kda_chunk_bwd(const kda_shape_t* shape, int32_t chunk, int32_t total_tokens,
                            int32_t num_seqs, const int32_t* cu_seqlens, const void* q,
                            const void* k, const void* v, const float* g, const float* beta,

@@ -209,3 +209,22 @@ def test_backward_from_raw_projections(gate, additive, gmin):
         assert out["dbeta_logits"] is None
     else:
         assert_close(host(out["dbeta_logits"]), dbl, "bf16", "dbeta_logits")
+
+
+def test_backward_every_sequence_empty_passes_the_state_gradient():
+    """total_tokens 0 with sequences given: an empty sequence's final state is its initial
+    state, so dL/dS0 = dL/dS_final, and zero when no final-state gradient is given."""
+    d, H, N = 128, 2, 3
+    z = torch.zeros((0, H, d), dtype=torch.bfloat16, device="cuda")
+    g = torch.zeros((0, H, d), device="cuda")
+    beta = torch.zeros((0, H), device="cuda")
+    cu = torch.zeros(N + 1, dtype=torch.int32, device="cuda")
+    s0 = torch.randn((N, H, d, d), device="cuda")
+    d_final = torch.randn((N, H, d, d), device="cuda")
+    out = kda.kda_chunk_bwd(z, z, z, g, beta, cu, z, states=s0, read_initial=True,
+                            d_final=d_final, want_d_initial=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out["d_initial"], d_final)
+    out = kda.kda_chunk_bwd(z, z, z, g, beta, cu, z, want_d_initial=True)
+    torch.cuda.synchronize()
+    assert not out["d_initial"].any()

@@ -331,3 +331,44 @@ def test_prefill_c3_long_context_sampled():
 def test_prefill_c4_varlen_sampled():
     """64 packed sequences, heads 0-7 per-channel gates, 8-15 scalar gates, S0 != 0."""
     _sampled_check(4, [(0, 0), (17, 9), (63, 15), (40, 3)])
+
+
+@pytest.mark.parametrize("d,chunk,io", [(128, 64, torch.bfloat16), (32, 16, torch.float32)])
+def test_prefill_every_sequence_empty(d, chunk, io):
+    """total_tokens 0 with sequences given: each ends in the state it starts from (zero
+    without one), so a final-state write alone zeroes the sequences' slots and every other
+    flag setting leaves the pool as it was."""
+    H, N = 2, 3
+    z = torch.zeros((0, H, d), dtype=io, device="cuda")
+    g = torch.zeros((0, H, d), device="cuda")
+    beta = torch.zeros((0, H), device="cuda")
+    cu = torch.zeros(N + 1, dtype=torch.int32, device="cuda")
+    pool0 = torch.randn((5, H, d, d), device="cuda")
+    for slots, used in [(torch.tensor([4, 0, 2], dtype=torch.int32, device="cuda"), [4, 0, 2]),
+                        (None, [0, 1, 2])]:
+        for read, write in [(False, True), (True, True), (True, False), (False, False)]:
+            pool = pool0.clone()
+            kda.kda_chunk_fwd(z, z, z, g, beta, cu, chunk=chunk, states=pool, state_slots=slots,
+                              read_initial=read, write_final=write)
+            torch.cuda.synchronize()
+            want = pool0.clone()
+            if write and not read:
+                want[used] = 0
+            assert torch.equal(pool, want), (slots is None, read, write)
+
+
+@pytest.mark.parametrize("d,chunk,io", [(128, 64, "bf16"), (32, 16, "fp32")])
+def test_prefill_empty_sequences_without_initial_state(d, chunk, io):
+    """A final-state write without an initial state: the empty sequences' slots become zero
+    (over a pool that held other values), the others hold the recurrence's final state."""
+    rng = np.random.default_rng(d + chunk)
+    lens, H = [0, chunk + 6, 0], 2
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    p = workloads.random_problem(rng, int(cu[-1]), H, d, d, io_dtype=io)
+    p["cu_seqlens"] = cu
+    pool = rng.standard_normal((len(lens), H, d, d)).astype(np.float32)
+    o, s = _prefill(p, io, chunk, s0=pool, write=True)
+    o_ref, s_ref = oracle.run(p["q"], p["k"], p["v"], p["g"], p["beta"], cu)
+    assert not s[0].any() and not s[2].any()
+    assert_close(o, o_ref, io, "o")
+    assert_close(s, s_ref, io, "state")
