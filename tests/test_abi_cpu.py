@@ -106,6 +106,12 @@ def test_validation_errors_before_any_launch(lib):
     assert b"workspace" in lib.kda_last_error()
     assert call(sh, args(T=0)) == 0                                  # empty: no-op
     assert call(sh, args(N=0)) == 0
+    # every sequence empty: a final-state write alone zeroes the slots, so it needs the pool;
+    # with the initial state read as well the pool is left as it is (nothing launched)
+    assert call(sh, args(T=0, flags=2)) == 1
+    assert call(sh, args(T=0, flags=2, states=fake, ns=0)) == 1
+    assert call(sh, args(T=0, N=2, flags=2, states=fake, ns=1)) == 1  # implicit slots: too few
+    assert call(sh, args(T=0, flags=3, cu=None, q=None)) == 0
     # decode
     assert lib.kda_decode_step(ctypes.byref(_shape(32, 96, 96, 1)), 4, fake, fake, fake, fake,
                                fake, fake, 4, None, fake, None) == 2
@@ -158,6 +164,13 @@ def test_validation_errors_before_any_launch(lib):
     assert bwd(sh, 64, 0, None) == 1                                 # q NULL
     assert bwd(sh, 64, 1, fake) == 1                                 # initial state without states
     assert bwd(sh, 64, 0, fake) == 3                                 # workspace missing
+    # every sequence empty: dL/dS0 = dL/dS_final, so only the state gradients are checked
+    bempty = lambda d_final, d_init: lib.kda_chunk_bwd(
+        ctypes.byref(sh), 64, 0, 2, None, None, None, None, None, None, None, 0, None, 0, None,
+        d_final, None, None, None, None, None, d_init, None, 0, None)
+    assert bempty(None, None) == 0                                   # dL/dS0 not asked for
+    assert bempty(None, P(0x1002)) == 1                              # misaligned dL/dS0
+    assert bempty(P(0x1001), fake) == 1                              # misaligned dL/dS_final
     assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(sh), 64, 4096, 1) > 0
     assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(_shape(16, 64, 64, 1)), 64, 4096, 1) == 0
     # backward from raw projections: bf16 only, gate_min not NaN
