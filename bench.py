@@ -387,6 +387,68 @@ def cpu_baseline(p, budget_s=10.0):
                       f"in {el:.1f} s, fp64 sequential recurrence, one thread per head"}
 
 
+def bench_context(kda, torch, flush, calls=5, warmup=2):
+    """Prefill on the long-context shape (2 x 65,536 tokens, 32 heads) and the packed-varlen
+    shape (64 sequences of 128-8,192 tokens, 16 heads, half of them with a scalar gate,
+    initial states given).  Inputs follow the generators' distributions but are drawn on the
+    GPU (host generation of 8.6e8 values per tensor would dominate the run): unit-norm q and k
+    rows, normal v, beta = sigmoid(normal), log alpha = log sigmoid(normal + mu).  Each call
+    follows a cache eviction; per-launch times come from the library's launch timer."""
+    from gated_delta_rule_08_amd import workloads
+    import numpy as np
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    nz = lambda *shape: torch.randn(*shape, device="cuda", generator=gen)
+    norm = torch.nn.functional.normalize
+    res = []
+    for index in (3, 4):
+        cfg = workloads.CONFIGS[index]
+        lens = workloads.seq_lengths(cfg)
+        T, N, H, d = int(lens.sum()), len(lens), cfg.num_heads, cfg.dk
+        q = norm(nz(T, H, d), dim=-1).to(torch.bfloat16)
+        k = norm(nz(T, H, d), dim=-1).to(torch.bfloat16)
+        v = nz(T, H, d).to(torch.bfloat16)
+        beta = torch.sigmoid(nz(T, H))
+        g = torch.nn.functional.logsigmoid(nz(T, H, d) + cfg.alpha_mu)
+        for h in cfg.scalar_gate_heads:
+            g[:, h, :] = g[:, h, :1]
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), device="cuda")
+        states = (0.02 * nz(N, H, d, d)) if cfg.with_s0 else torch.zeros(N, H, d, d, device="cuda")
+        ws = torch.empty(kda.kda_chunk_fwd_workspace_bytes(H, d, d, torch.bfloat16, cfg.chunk, T, N),
+                         dtype=torch.uint8, device="cuda")
+        o = torch.empty_like(v)
+        call = lambda: kda.kda_chunk_fwd(q, k, v, g, beta, cu, chunk=cfg.chunk, states=states,
+                                         read_initial=cfg.with_s0, write_final=True, o=o,
+                                         workspace=ws)
+        for _ in range(warmup):
+            flush()
+            call()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        ms, per = [], {}
+        for _ in range(calls):
+            flush()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record(stream)
+            with kda.launch_timer(stream) as lt:
+                call()
+            t1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(t0.elapsed_time(t1))
+            for name, x in lt.launches:
+                per.setdefault(name, []).append(x)
+        m = sum(ms) / len(ms)
+        res.append({"workload": cfg.name, "tokens": T, "sequences": N, "heads": H,
+                    "ms_per_call": m, "tokens_per_s": T / (m * 1e-3), "calls": calls,
+                    "launches_us": {n: 1e3 * sum(x) / len(x) for n, x in per.items()}})
+        print(f"{cfg.name}: {m:.3f} ms per call", file=sys.stderr, flush=True)
+        del q, k, v, g, beta, states, ws, o
+        torch.cuda.empty_cache()
+    return {"metric": "KDA prefill tokens/s on the long-context and packed-varlen shapes",
+            "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True, "dtype": "bf16",
+            "data": "synthetic (drawn on the GPU)", "context": res}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -395,8 +457,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the prefill timings of the variant flags")
-    ap.add_argument("--only", choices=["prefill", "decode", "backward"], default=None,
-                    help="run one leg only (for profiling)")
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "context"], default=None,
+                    help="run one leg only (for profiling); 'context' times the prefill on the "
+                         "long-context and packed-varlen shapes instead (its own JSON line)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one plain device copy of MIB MiB (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -433,6 +496,9 @@ def main(argv=None):
         torch.cuda.synchronize()
         del src, dst
 
+    if args.only == "context":
+        print(json.dumps(bench_context(kda, torch, flush)), flush=True)
+        return 0
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic"}
