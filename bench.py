@@ -1,6 +1,7 @@
 """Benchmark of the KDA hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-variants]
+                    [--no-context] [--only prefill|decode|backward|context]
 
 Prefill: kda_chunk_fwd on the packed-sequence workload B=1, H=16, T=4096,
 dk=dv=128, chunk=64, bf16 I/O, fp32 state, zero initial state, final state
@@ -18,7 +19,11 @@ decode steps/s is reported next to it with its own roofline.  The oracle
 
 The variant flags (scalar gate, no gate, additive write) and the prefill from raw
 bf16 projections (input preparation fused in) are timed on the same prefill
-shape and reported under "variants", each with its own algorithmic bytes.
+shape and reported under "variants", each with its own algorithmic bytes.  The
+backward is timed on the same shape ("backward").  The long-context shape
+(B=2, H=32, T=65,536) and the packed-varlen shape (64 sequences of 128-8,192
+tokens, H=16) are timed last ("context"), each with its path roofline and the
+roofline of its dominant launch.
 
 Prints one JSON line.
 """
@@ -392,15 +397,19 @@ def bench_context(kda, torch, flush, calls=5, warmup=2):
     shape (64 sequences of 128-8,192 tokens, 16 heads, half of them with a scalar gate,
     initial states given).  Inputs follow the generators' distributions but are drawn on the
     GPU (host generation of 8.6e8 values per tensor would dominate the run): unit-norm q and k
-    rows, normal v, beta = sigmoid(normal), log alpha = log sigmoid(normal + mu).  Each call
-    follows a cache eviction; per-launch times come from the library's launch timer."""
+    rows, normal v, beta = sigmoid(normal), log alpha = log sigmoid(normal + mu); the sequence
+    lengths are the generator's own.  Each call follows a cache eviction; per-launch times come
+    from the library's launch timer.  Algorithmic bytes per call: 1,540 per token-head (q, k,
+    v, o bf16; g fp32 per channel, the scalar-gate heads included, as the call reads it; beta)
+    plus the final states written and, where given, the initial states read (64 KiB per
+    sequence-head each)."""
     from gated_delta_rule_08_amd import workloads
     import numpy as np
     gen = torch.Generator(device="cuda")
     gen.manual_seed(7)
     nz = lambda *shape: torch.randn(*shape, device="cuda", generator=gen)
     norm = torch.nn.functional.normalize
-    res = []
+    res = {}
     for index in (3, 4):
         cfg = workloads.CONFIGS[index]
         lens = workloads.seq_lengths(cfg)
@@ -438,15 +447,39 @@ def bench_context(kda, torch, flush, calls=5, warmup=2):
             for name, x in lt.launches:
                 per.setdefault(name, []).append(x)
         m = sum(ms) / len(ms)
-        res.append({"workload": cfg.name, "tokens": T, "sequences": N, "heads": H,
-                    "ms_per_call": m, "tokens_per_s": T / (m * 1e-3), "calls": calls,
-                    "launches_us": {n: 1e3 * sum(x) / len(x) for n, x in per.items()}})
+        state_bytes = N * H * d * d * 4 * (2 if cfg.with_s0 else 1)
+        bytes_ = PREFILL_BYTES_PER_TOKEN_HEAD * T * H + state_bytes
+        achieved = bytes_ / (m * 1e-3) / 1e9
+        # per launch: the prep reads the inputs, the scan writes o and the states
+        launch_bytes = {"prep_kernel": PREFILL_LAUNCH_BYTES_PER_TOKEN_HEAD["prep_kernel"] * T * H}
+        for name in per:
+            if name.startswith("scan"):
+                launch_bytes[name] = 2 * 128 * T * H + state_bytes
+        launches = {n: {"mean_us": 1e3 * sum(x) / len(x), "calls": len(x),
+                        "algorithmic_bytes": launch_bytes.get(n),
+                        "achieved_gbs": (None if launch_bytes.get(n) is None else
+                                         launch_bytes[n] / (1e-3 * sum(x) / len(x)) / 1e9)}
+                    for n, x in per.items()}
+        dom = max(launches, key=lambda n: launches[n]["mean_us"])
+        dl = launches[dom]
+        res[cfg.name] = {
+            "tokens": T, "sequences": N, "heads": H, "ms_per_call": m,
+            "tokens_per_s": T / (m * 1e-3), "calls": calls, "algorithmic_bytes": bytes_,
+            "path_roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                              "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS},
+            "roofline": {"bound": "hbm", "kernel": dom, "achieved": dl["achieved_gbs"],
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": (None if dl["achieved_gbs"] is None
+                                  else dl["achieved_gbs"] / HBM_PEAK_GBS),
+                         "algorithmic_bytes": dl["algorithmic_bytes"],
+                         "duration_us": dl["mean_us"]},
+            "launches": launches,
+            "data": "synthetic, drawn on the GPU with the generators' distributions",
+        }
         print(f"{cfg.name}: {m:.3f} ms per call", file=sys.stderr, flush=True)
         del q, k, v, g, beta, states, ws, o
         torch.cuda.empty_cache()
-    return {"metric": "KDA prefill tokens/s on the long-context and packed-varlen shapes",
-            "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True, "dtype": "bf16",
-            "data": "synthetic (drawn on the GPU)", "context": res}
+    return res
 
 
 def main(argv=None):
@@ -457,6 +490,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the prefill timings of the variant flags")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the prefill on the long-context and packed-varlen shapes")
     ap.add_argument("--only", choices=["prefill", "decode", "backward", "context"], default=None,
                     help="run one leg only (for profiling); 'context' times the prefill on the "
                          "long-context and packed-varlen shapes instead (its own JSON line)")
@@ -497,7 +532,11 @@ def main(argv=None):
         del src, dst
 
     if args.only == "context":
-        print(json.dumps(bench_context(kda, torch, flush)), flush=True)
+        print(json.dumps({"metric": "KDA prefill tokens/s on the long-context and packed-varlen "
+                                    "shapes", "unit": "tokens/s", "n_gpus": 1,
+                          "higher_is_better": True, "dtype": "bf16",
+                          "data": "synthetic (drawn on the GPU)",
+                          "context": bench_context(kda, torch, flush)}), flush=True)
         return 0
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
@@ -565,6 +604,9 @@ def main(argv=None):
         if args.only == "decode":
             out.update({"value": 1e3 / ms, "unit": "steps/s", "ms_per_step": ms,
                         "config": {"workload": "decode_bf16_B256_H32_d128"}})
+    if args.only is None and not args.no_context:
+        # the long-context and packed-varlen shapes: parity cases that also carry throughput
+        out["context"] = bench_context(kda, torch, flush)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -98,6 +98,19 @@ void timer_free(LaunchTimer* t) {
 }
 }  // namespace
 
+kda_status_t allow_dynamic_lds(const void* fn, size_t bytes, std::atomic<uint64_t>& done,
+                               const char* what) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, what);
+  const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return KDA_OK;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess) return hip_status(e, what);
+  if (bit) done.fetch_or(bit, std::memory_order_release);
+  return KDA_OK;
+}
+
 kda_status_t check_launch(const char* what) {
   const kda_status_t st = hip_status(hipGetLastError(), what);
   LaunchTimer* t = t_timer;
@@ -249,10 +262,10 @@ kda_status_t chunk_fwd_impl(const char* W, const kda_shape_t* sh, int32_t chunk,
       return invalid("%s: num_slots (%d) < num_seqs (%d) with implicit slots", W, num_slots,
                      num_seqs);
   }
-  const size_t esz = sh->io_dtype == KDA_BF16 ? 2 : 4;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, esz) ||
+  // the MFMA path reads q, k, v and writes o in 16-byte row pieces
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       (states && !aligned(states, 16)))
-    return invalid("%s: q, k, v, states must be 16-byte aligned", W);
+    return invalid("%s: q, k, v, o and states must be 16-byte aligned", W);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (chunk_mfma_supported(sh->dk, sh->dv, chunk, sh->io_dtype)) {
     const size_t need = chunk_mfma_workspace_bytes(sh->num_heads, total_tokens, num_seqs);
@@ -471,12 +484,13 @@ kda_status_t chunk_bwd_impl(const char* W, const kda_shape_t* sh, int32_t chunk,
                      num_seqs);
   }
   const size_t ga = raw ? 2 : 4;  // element size of the gate and beta gradients
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 2) || !aligned(d_o, 16) ||
+  // q, k, v and d_o are read, dq and dk written, in 16-byte row pieces
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(d_o, 16) ||
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 2) || (dg && !aligned(dg, raw ? 8 : 4)) ||
       (dbeta && !aligned(dbeta, ga)) || (states && !aligned(states, 16)) ||
       (d_final_state && !aligned(d_final_state, 4)) ||
       (d_initial_state && !aligned(d_initial_state, 4)))
-    return invalid("%s: q, k, d_o, dq, dk, states must be 16-byte aligned, the rest "
+    return invalid("%s: q, k, v, d_o, dq, dk, states must be 16-byte aligned, the rest "
                    "element-aligned", W);
   const size_t need = raw ? chunk_mfma_bwd_raw_workspace_bytes(sh->num_heads, total_tokens, num_seqs)
                           : chunk_mfma_bwd_workspace_bytes(sh->num_heads, total_tokens, num_seqs);

@@ -883,14 +883,10 @@ template <int kGate, bool kAdd, bool kRaw, bool kBwd = false>
 kda_status_t launch_prep(unsigned grid, const void* q, const void* k, const void* v, const void* g,
                          const void* beta, float gate_min, int32_t N, int H, const Workspace& w,
                          const PrepIndex& ix, hipStream_t stream) {
-  static bool attr_set = false;  // idempotent; set before the first launch
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep_kernel<kGate, kAdd, kRaw, kBwd>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)sizeof(PrepSmem));
-    if (e != hipSuccess) return hip_status(e, "hipFuncSetAttribute(prep)");
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};  // devices on which the limit is raised
+  kda_status_t st = allow_dynamic_lds(reinterpret_cast<const void*>(prep_kernel<kGate, kAdd, kRaw, kBwd>),
+                                      sizeof(PrepSmem), lds_set, "hipFuncSetAttribute(prep)");
+  if (st != KDA_OK) return st;
   hipLaunchKernelGGL((prep_kernel<kGate, kAdd, kRaw, kBwd>), dim3(grid), dim3(kPrepThreads),
                      sizeof(PrepSmem), stream, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), g, beta,
@@ -1752,18 +1748,14 @@ kda_status_t launch_split(int32_t N, int H, const Workspace& w, float* states, i
                           const int32_t* slots, uint32_t flags, void* o, size_t items,
                           hipStream_t stream) {
   constexpr int kGroups = D / (16 * CW * NT);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(scan_state_kernel<CW, NT, LW>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)sizeof(StateLds<CW, NT>));
-    if (e != hipSuccess) return hip_status(e, "hipFuncSetAttribute(scan)");
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  kda_status_t st = allow_dynamic_lds(reinterpret_cast<const void*>(scan_state_kernel<CW, NT, LW>),
+                                      sizeof(StateLds<CW, NT>), lds_set, "hipFuncSetAttribute(scan)");
+  if (st != KDA_OK) return st;
   hipLaunchKernelGGL((scan_state_kernel<CW, NT, LW>), dim3((unsigned)(N * H * kGroups)),
                      dim3(64 * (CW + LW)), sizeof(StateLds<CW, NT>), stream, N, H, w, states,
                      num_slots, slots, flags);
-  kda_status_t st = check_launch("scan_state_kernel");
+  st = check_launch("scan_state_kernel");
   if (st != KDA_OK) return st;
   hipLaunchKernelGGL(out_kernel, dim3((unsigned)items), dim3(kOutThreads), 0, stream, N, H, w,
                      w.seq_start, w.seq_end, w.chunk_off, static_cast<uint16_t*>(o));
@@ -1774,14 +1766,10 @@ template <int CW, int NT, int LW>
 kda_status_t launch_scan_ws(int32_t N, int H, const Workspace& w, float* states, int32_t num_slots,
                             const int32_t* slots, uint32_t flags, void* o, hipStream_t stream) {
   constexpr int kGroups = D / (16 * CW * NT);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(scan_ws_kernel<CW, NT, LW>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)sizeof(ScanLds<CW, NT>));
-    if (e != hipSuccess) return hip_status(e, "hipFuncSetAttribute(scan)");
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  kda_status_t st = allow_dynamic_lds(reinterpret_cast<const void*>(scan_ws_kernel<CW, NT, LW>),
+                                      sizeof(ScanLds<CW, NT>), lds_set, "hipFuncSetAttribute(scan)");
+  if (st != KDA_OK) return st;
   hipLaunchKernelGGL((scan_ws_kernel<CW, NT, LW>), dim3((unsigned)(N * H * kGroups)),
                      dim3(64 * (CW + LW)), sizeof(ScanLds<CW, NT>), stream, N, H, w, states,
                      num_slots, slots, flags, static_cast<uint16_t*>(o));
@@ -2634,15 +2622,6 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
   if (!kAdd && tid < c) dbeta[row0 + tid * rs] = sm.db[tid];
 }
 
-// Sets the dynamic LDS limit of a kernel once (before its first launch).
-kda_status_t allow_lds(const void* fn, size_t bytes, bool& done, const char* what) {
-  if (done) return KDA_OK;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (e != hipSuccess) return hip_status(e, what);
-  done = true;
-  return KDA_OK;
-}
-
 }  // namespace
 
 bool chunk_mfma_supported(int dk, int dv, int chunk, int io_dtype) {
@@ -2745,9 +2724,9 @@ kda_status_t launch_chunk_mfma_bwd(const kda_shape_t* sh, int32_t T, int32_t N, 
   constexpr int kGroups = D / 16;
   constexpr size_t kPairLds =
       sizeof(StateLds<1, 1>) > sizeof(GradScanLds) ? sizeof(StateLds<1, 1>) : sizeof(GradScanLds);
-  static bool lds_pair = false;
-  st = allow_lds(reinterpret_cast<const void*>(scan_pair_kernel), kPairLds, lds_pair,
-                 "hipFuncSetAttribute(scan pair)");
+  static std::atomic<uint64_t> lds_pair{0};
+  st = allow_dynamic_lds(reinterpret_cast<const void*>(scan_pair_kernel), kPairLds, lds_pair,
+                         "hipFuncSetAttribute(scan pair)");
   if (st != KDA_OK) return st;
   hipLaunchKernelGGL(scan_pair_kernel, dim3((unsigned)(2 * N * H * kGroups)),
                      dim3(kScanPairThreads), kPairLds, stream, N, H, w, const_cast<float*>(states),
@@ -2756,9 +2735,9 @@ kda_status_t launch_chunk_mfma_bwd(const kda_shape_t* sh, int32_t T, int32_t N, 
   st = check_launch("scan_pair_kernel");
   if (st != KDA_OK) return st;
   // gradients of every (chunk, head)
-  auto launch_grad = [&](auto kern, bool& done) -> kda_status_t {
-    kda_status_t e = allow_lds(reinterpret_cast<const void*>(kern), sizeof(GradSmem), done,
-                               "hipFuncSetAttribute(grad)");
+  auto launch_grad = [&](auto kern, std::atomic<uint64_t>& done) -> kda_status_t {
+    kda_status_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), sizeof(GradSmem), done,
+                                       "hipFuncSetAttribute(grad)");
     if (e != KDA_OK) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)items), dim3(kGradThreads), sizeof(GradSmem), stream, N,
                        H, GradWs{w.tm, w.mkk, w.sc, w.uc, w.dsc, w.duc}, w.seq_start, w.seq_end,
@@ -2768,7 +2747,7 @@ kda_status_t launch_chunk_mfma_bwd(const kda_shape_t* sh, int32_t T, int32_t N, 
                        static_cast<uint16_t*>(dv), dg, dbeta);
     return KDA_OK;
   };
-  static bool lg[6] = {false, false, false, false, false, false};
+  static std::atomic<uint64_t> lg[6] = {{0}, {0}, {0}, {0}, {0}, {0}};
   st = gate == kGateScalar ? (add ? launch_grad(grad_kernel<kGateScalar, true>, lg[0])
                                   : launch_grad(grad_kernel<kGateScalar, false>, lg[1]))
      : gate == kGateNone   ? (add ? launch_grad(grad_kernel<kGateNone, true>, lg[2])

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "kda.h"
 
 namespace kda {
@@ -58,5 +60,13 @@ __device__ __forceinline__ int clamp_tok(int x, int T) { return x < 0 ? 0 : (x >
 void set_error(const char* fmt, ...);
 kda_status_t hip_status(hipError_t e, const char* what);
 kda_status_t check_launch(const char* what);
+
+// Raises a kernel's dynamic LDS limit to `bytes` before its first launch on the
+// current device.  `done` holds one bit per device (devices 64 and up set the
+// attribute on every call); the attribute call is idempotent, so two threads
+// racing on a first launch both set it, which is harmless, and the bit is
+// published with release order.  Safe to call from several host threads.
+kda_status_t allow_dynamic_lds(const void* fn, size_t bytes, std::atomic<uint64_t>& done,
+                               const char* what);
 
 }  // namespace kda

@@ -123,21 +123,22 @@ size_t kda_chunk_fwd_workspace_bytes(const kda_shape_t* shape, int32_t chunk,
  *             [cu_seqlens[n], cu_seqlens[n+1]); expected cu[0] = 0,
  *             nondecreasing, cu[num_seqs] = total_tokens.  Lengths need not
  *             be multiples of `chunk`; a zero-length sequence is allowed.
- * q, k        device [total_tokens, H, dk], io dtype.
- * v           device [total_tokens, H, dv], io dtype.
+ * q, k        device [total_tokens, H, dk], io dtype, 16-byte aligned.
+ * v           device [total_tokens, H, dv], io dtype, 16-byte aligned.
  * g           device fp32 [total_tokens, H, dk], log of the per-channel gate
  *             (16-byte aligned); [total_tokens, H] with KDA_GATE_SCALAR;
  *             unused (may be NULL) with KDA_GATE_NONE.
  * beta        device fp32 [total_tokens, H], write strengths; unused (may be
  *             NULL) with KDA_ADDITIVE.
- * states      device fp32 pool [num_slots, H, dk, dv] (may be NULL when
- *             neither state flag is set).  Read at the start of sequence n when
+ * states      device fp32 pool [num_slots, H, dk, dv], 16-byte aligned (may be
+ *             NULL when neither state flag is set).  Read at the start of sequence n when
  *             KDA_READ_INITIAL_STATE is set, overwritten with its final state
  *             when KDA_WRITE_FINAL_STATE is set.
  * state_slots device int32 [num_seqs] (slot of sequence n), or NULL for slot n
  *             (then num_slots >= num_seqs is required).  Slots must be
  *             distinct within a call.
- * o           device [total_tokens, H, dv], io dtype, fully overwritten.
+ * o           device [total_tokens, H, dv], io dtype, fully overwritten;
+ *             16-byte aligned (rows are written in 16-byte pieces).
  * workspace   device scratch of at least kda_chunk_fwd_workspace_bytes()
  *             bytes, 256-byte aligned; contents on entry are ignored.
  * flags       KDA_READ_INITIAL_STATE | KDA_WRITE_FINAL_STATE | at most one of
@@ -201,7 +202,8 @@ kda_status_t kda_decode_step_ex(const kda_shape_t* shape, int32_t batch, const v
  * Reading bf16 logits instead of fp32 log-decays moves 1,282 instead of 1,540
  * bytes per token and head.
  *
- * q_raw, k_raw  device bf16 [tokens, H, dk];  v: device bf16 [tokens, H, dv].
+ * q_raw, k_raw  device bf16 [tokens, H, dk];  v: device bf16 [tokens, H, dv]; all
+ *               three 16-byte aligned in the prefill (as q, k, v of kda_chunk_fwd).
  * gate_logits   device bf16 [tokens, H, dk] (8-byte aligned); [tokens, H] with
  *               KDA_GATE_SCALAR; unused (may be NULL) with KDA_GATE_NONE.
  * beta_logits   device bf16 [tokens, H]; unused (may be NULL) with KDA_ADDITIVE.
@@ -241,10 +243,11 @@ size_t kda_chunk_bwd_workspace_bytes(const kda_shape_t* shape, int32_t chunk,
  * Inputs are those of the forward call (same layouts and variant flags): q, k,
  * v, g, beta, cu_seqlens, and with KDA_READ_INITIAL_STATE the initial
  * states[slot] (else zero).  g must be <= 0 (alpha <= 1), as for the forward.
- * d_o            device io dtype [total_tokens, H, dv]: dL/do.
+ * q, k, v, states  16-byte aligned (read in 16-byte pieces).
+ * d_o            device io dtype [total_tokens, H, dv]: dL/do (16-byte aligned).
  * d_final_state  device fp32 dense [num_seqs, H, dk, dv]: dL/dS_final, or NULL (0).
  * dq, dk         device io dtype [total_tokens, H, dk] (16-byte aligned);
- * dv             device io dtype [total_tokens, H, dv];
+ * dv             device io dtype [total_tokens, H, dv] (element-aligned);
  * dg             device fp32 [total_tokens, H, dk]; [total_tokens, H] with
  *                KDA_GATE_SCALAR (the gate is shared by the channels, so its gradient
  *                is their sum); not written (may be NULL) with KDA_GATE_NONE.
@@ -255,7 +258,8 @@ size_t kda_chunk_bwd_workspace_bytes(const kda_shape_t* shape, int32_t chunk,
  *                KDA_ADDITIVE; KDA_WRITE_FINAL_STATE and unknown bits are
  *                KDA_ERR_INVALID_ARGUMENT.
  * workspace      device scratch of kda_chunk_bwd_workspace_bytes() bytes, 256-byte
- *                aligned (about 345 KiB per chunk and head).
+ *                aligned (264.5 KiB per chunk and head of chunk capacity, the capacity
+ *                being total_tokens / chunk + num_seqs chunks, plus a small header).
  * Supported: io_dtype KDA_BF16, dk = dv = 128, chunk 64 (else KDA_ERR_UNSUPPORTED).
  * num_seqs == 0 is a no-op returning KDA_OK.  total_tokens == 0 makes every
  * sequence empty, passing its state through unchanged: d_initial_state (when
@@ -320,17 +324,31 @@ kda_status_t kda_chunk_bwd_raw(const kda_shape_t* shape, int32_t chunk, int32_t 
 kda_status_t kda_state_affine(const kda_shape_t* shape, int32_t n, const float* M,
                               const float* S_in, const float* B, float* S_out, void* stream);
 
-/* Zero every state of a pool [num_slots, H, dk, dv] (fp32). */
+/* The state pool.  Each (slot, head) holds one fp32 dk x dv state: the layer's
+ * whole memory of its sequence, which is what the recurrent form carries from
+ * one token to the next instead of a growing cache (heqinghuang "From GPT2 to
+ * Kimi3, Explained", section 09: the forward pass takes an optional cache and
+ * returns the updated state, and no cache means a zero state; engineermaxxing
+ * ch. 02g: the decode step returns the state it was given, updated).  These
+ * calls start sequences from zero and move states between the pool and dense
+ * [n, H, dk, dv] buffers (for example to checkpoint, resume or migrate a
+ * sequence).  Every buffer is device fp32, 16-byte aligned; H * dk * dv must be a
+ * multiple of 4; bandwidth only, no arithmetic.
+ *
+ * kda_state_init: zero every state of a pool [num_slots, H, dk, dv]. */
 kda_status_t kda_state_init(const kda_shape_t* shape, float* states, int32_t num_slots,
                             void* stream);
 
-/* Copy n dense states src [n, H, dk, dv] into pool slots slots[i] (or i when
- * slots is NULL).  src and the pool must not overlap. */
+/* kda_state_load: copy n dense states src [n, H, dk, dv] into pool slots
+ * slots[i] (device int32 [n], or i when slots is NULL, then num_slots >= n).
+ * Entries with an out-of-range slot are skipped.  src and the pool must not
+ * overlap.  n == 0 is a no-op. */
 kda_status_t kda_state_load(const kda_shape_t* shape, float* states, int32_t num_slots,
                             const int32_t* slots, int32_t n, const float* src, void* stream);
 
-/* Copy pool slots slots[i] (or i) into dense dst [n, H, dk, dv].  Entries with
- * an out-of-range slot leave their dst rows unwritten. */
+/* kda_state_store: copy pool slots slots[i] (or i) into dense dst [n, H, dk, dv].
+ * Entries with an out-of-range slot leave their dst rows unwritten.  n == 0 is
+ * a no-op. */
 kda_status_t kda_state_store(const kda_shape_t* shape, const float* states, int32_t num_slots,
                              const int32_t* slots, int32_t n, float* dst, void* stream);
 

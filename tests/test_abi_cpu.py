@@ -101,6 +101,11 @@ def test_validation_errors_before_any_launch(lib):
     assert call(sh, args(flags=4, g=P(0x1004))) == 3                 # scalar gate: 4-byte aligned
     assert call(sh, args(flags=16, beta=None)) == 3                  # KDA_ADDITIVE
     assert call(sh, args(q=None)) == 1                               # NULL tensor
+    # q, k, v are read and o written in 16-byte row pieces: element-aligned is not enough
+    for name in ("q", "k", "v", "o"):
+        assert call(sh, args(**{name: P(0x1002)})) == 1, name
+        assert b"16-byte aligned" in lib.kda_last_error()
+        assert call(_shape(2, 32, 32, 0), args(chunk=16, **{name: P(0x1004)})) == 1, name
     assert call(sh, args(flags=1)) == 1                              # state I/O without states
     assert call(sh, args()) == 3                                     # workspace missing
     assert b"workspace" in lib.kda_last_error()
@@ -164,6 +169,13 @@ def test_validation_errors_before_any_launch(lib):
     assert bwd(sh, 64, 0, None) == 1                                 # q NULL
     assert bwd(sh, 64, 1, fake) == 1                                 # initial state without states
     assert bwd(sh, 64, 0, fake) == 3                                 # workspace missing
+    # v is read in 16-byte row pieces by the backward as well
+    bwd_v = lambda v: lib.kda_chunk_bwd(
+        ctypes.byref(sh), 64, 128, 1, fake, fake, fake, v, fake, fake, None, 1, None, 0, fake,
+        None, fake, fake, fake, fake, fake, None, None, 0, None)
+    assert bwd_v(P(0x1002)) == 1
+    assert b"16-byte aligned" in lib.kda_last_error()
+    assert bwd_v(fake) == 3
     # every sequence empty: dL/dS0 = dL/dS_final, so only the state gradients are checked
     bempty = lambda d_final, d_init: lib.kda_chunk_bwd(
         ctypes.byref(sh), 64, 0, 2, None, None, None, None, None, None, None, 0, None, 0, None,
@@ -183,6 +195,25 @@ def test_validation_errors_before_any_launch(lib):
     assert braw(sh, 0.0, 2) == 1                                     # WRITE_FINAL is forward-only
     assert lib.kda_chunk_bwd_raw_workspace_bytes(ctypes.byref(sh), 64, 4096, 1) > \
         lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(sh), 64, 4096, 1)
+
+
+def test_header_alignment_contract_matches_validation():
+    """The header states the 16-byte alignment the validation enforces for o (forward) and
+    v (backward), and the backward workspace size the library computes."""
+    text = open(HEADER).read()
+    assert "o           device [total_tokens, H, dv], io dtype, fully overwritten;\n" \
+           " *             16-byte aligned" in text
+    assert "q, k, v, states  16-byte aligned" in text
+    assert "264.5 KiB per chunk and head" in text
+
+
+def test_backward_workspace_per_chunk_head(lib):
+    """264.5 KiB of operands per (chunk, head) of capacity, plus a header under 4 KiB."""
+    sh = _shape(16, 128, 128, 1)
+    a = lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(sh), 64, 4096, 1)
+    b = lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(sh), 64, 8192, 1)
+    assert b - a == 64 * 16 * int(264.5 * 1024)
+    assert 0 <= a - 65 * 16 * int(264.5 * 1024) < 8192
 
 
 def test_launch_timer_end_without_begin(lib):

@@ -42,7 +42,8 @@ def _case(seed, lengths, H, s0=False, d_final=False, wipe=False):
     N = len(lengths)
     S0 = (0.02 * rng.standard_normal((N, H, d, d))).astype(np.float32) if s0 else None
     dST = (0.1 * rng.standard_normal((N, H, d, d))).astype(np.float32) if d_final else None
-    print(f"backward seed={seed} lengths={lengths} H={H} s0={s0} d_final={d_final} wipe={wipe}",
+    shown = lengths if len(lengths) <= 16 else f"{len(lengths)} sequences, {T} tokens"
+    print(f"backward seed={seed} lengths={shown} H={H} s0={s0} d_final={d_final} wipe={wipe}",
           flush=True)
     dev = lambda a: to_dev(a, "bf16")
     out = kda.kda_chunk_bwd(dev(p["q"]), dev(p["k"]), dev(p["v"]),
@@ -100,6 +101,15 @@ def test_backward_full_prefill_shape():
 def test_backward_long_sequence():
     """One sequence of 16,384 tokens (256 chunks through both passes), 2 heads, slow decay."""
     _case(49, [16384], 2, s0=True, d_final=True)
+
+
+def test_backward_more_sequences_than_the_fused_header():
+    """450 packed sequences of 0-100 tokens (a tenth empty), 2 heads: the sequence header
+    comes from its own launch instead of the prep's LDS copy."""
+    rng = np.random.default_rng(48)
+    lens = rng.integers(1, 101, size=450)
+    lens[rng.random(450) < 0.1] = 0
+    _case(48, [int(x) for x in lens], 2, s0=True, d_final=True)
 
 
 def test_backward_empty_is_a_no_op():
