@@ -20,7 +20,8 @@ __all__ = [
     "kda_chunk_fwd_workspace_bytes", "kda_decode_step", "kda_state_init", "kda_state_load",
     "kda_state_store", "KDA_READ_INITIAL_STATE", "KDA_WRITE_FINAL_STATE", "kda_chunk_fwd_raw",
     "kda_decode_step_raw", "kda_state_affine", "kda_chunk_bwd",
-    "kda_chunk_bwd_raw", "launch_timer", "KDA_LAUNCH_TIMER_MAX",
+    "kda_chunk_bwd_raw", "launch_timer", "KDA_LAUNCH_TIMER_MAX", "kda_chunk_fwd_noalloc",
+    "KDA_NOALLOC_SCRATCH_BYTES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -34,6 +35,7 @@ KDA_GATE_SCALAR = 4
 KDA_GATE_NONE = 8
 KDA_ADDITIVE = 16
 KDA_LAUNCH_TIMER_MAX = 16
+KDA_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
            3: "KDA_ERR_WORKSPACE_TOO_SMALL", 4: "KDA_ERR_HIP"}
 
@@ -73,6 +75,9 @@ def load_library(path: str | None = None):
     lib.kda_chunk_fwd_workspace_bytes.restype = SZ
     lib.kda_chunk_fwd.argtypes = [SH, I32, I32, I32, P, P, P, P, P, P, P, I32, P, U32, P, P, SZ, P]
     lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd_noalloc.argtypes = [SH, I32, I32, I32, P, P, P, P, P, P, P, I32, P, U32, P,
+                                          P]
+    lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [SH, I32, P, P, P, P, P, P, I32, P, P, P]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step_ex.argtypes = [SH, I32, P, P, P, P, P, P, I32, P, U32, P, P]
@@ -245,6 +250,40 @@ def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens, chunk: int = 64, states=None, st
                              _ptr(v), _ptr(g), _ptr(beta), _ptr(states), num_slots,
                              _ptr(state_slots), flags, _ptr(o), _ptr(workspace), ws_bytes,
                              _stream(stream)))
+    return o
+
+
+def kda_chunk_fwd_noalloc(q, k, v, g, beta, cu_seqlens, o, chunk: int = 64, states=None,
+                          state_slots=None, read_initial: bool = False, write_final: bool = False,
+                          stream=None, gate: str = "channel", additive: bool = False):
+    """kda_chunk_fwd with the library's own scratch (see kda_chunk_fwd_noalloc in
+    include/kda.h): the call allocates no device memory, so the output ``o`` [T, H, dv]
+    must be given.  Calls needing more than KDA_NOALLOC_SCRATCH_BYTES of scratch raise
+    KDA_ERR_WORKSPACE_TOO_SMALL; calls that overlap on one GPU race on the scratch."""
+    lib = load_library()
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    io = _io_dtype(q)
+    _need(q, "q", (T, H, dk), q.dtype)
+    _need(k, "k", (T, H, dk), q.dtype)
+    _need(v, "v", (T, H, dv), q.dtype)
+    _need_gate_beta(g, beta, (T, H), dk, gate, additive)
+    N = cu_seqlens.numel() - 1
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32)
+    _need(o, "o", (T, H, dv), q.dtype)
+    flags = ((KDA_READ_INITIAL_STATE if read_initial else 0)
+             | (KDA_WRITE_FINAL_STATE if write_final else 0) | _variant_flags(gate, additive))
+    num_slots = 0
+    if states is not None:
+        _need(states, "states", (states.shape[0], H, dk, dv), torch.float32)
+        num_slots = states.shape[0]
+    if state_slots is not None:
+        _need(state_slots, "state_slots", (N,), torch.int32)
+    sh = _Shape(H, dk, dv, io)
+    _check(lib.kda_chunk_fwd_noalloc(ctypes.byref(sh), chunk, T, N, _ptr(cu_seqlens), _ptr(q),
+                                     _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(states),
+                                     num_slots, _ptr(state_slots), flags, _ptr(o),
+                                     _stream(stream)))
     return o
 
 

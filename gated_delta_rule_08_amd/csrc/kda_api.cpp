@@ -42,6 +42,8 @@ kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, cons
                                int32_t num_slots, const int32_t* slots, uint32_t flags, void* o,
                                void* workspace, hipStream_t stream);
 
+kda_status_t noalloc_scratch(void** out);
+
 size_t chunk_mfma_bwd_workspace_bytes(int H, int32_t T, int32_t N);
 kda_status_t launch_chunk_mfma_bwd(const kda_shape_t* sh, int32_t T, int32_t N, const int32_t* cu,
                                    const void* q, const void* k, const void* v, const float* g,
@@ -219,12 +221,15 @@ size_t kda_chunk_fwd_workspace_bytes(const kda_shape_t* sh, int32_t chunk, int32
 
 namespace {
 
+// noalloc: the scratch is the library's own device array (kda_chunk_fwd_noalloc),
+// looked up only once every argument has been validated.
 kda_status_t chunk_fwd_impl(const char* W, const kda_shape_t* sh, int32_t chunk,
                             int32_t total_tokens, int32_t num_seqs, const int32_t* cu_seqlens,
                             const void* q, const void* k, const void* v, const void* g,
                             const void* beta, bool raw, float gate_min, float* states,
                             int32_t num_slots, const int32_t* state_slots, uint32_t flags,
-                            void* o, void* workspace, size_t workspace_bytes, void* stream) {
+                            void* o, void* workspace, size_t workspace_bytes, void* stream,
+                            bool noalloc = false) {
   kda_status_t st = check_shape(sh, W);
   if (st != KDA_OK) return st;
   if (total_tokens < 0 || num_seqs < 0)
@@ -269,6 +274,17 @@ kda_status_t chunk_fwd_impl(const char* W, const kda_shape_t* sh, int32_t chunk,
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (chunk_mfma_supported(sh->dk, sh->dv, chunk, sh->io_dtype)) {
     const size_t need = chunk_mfma_workspace_bytes(sh->num_heads, total_tokens, num_seqs);
+    if (noalloc) {
+      if (need > (size_t)KDA_NOALLOC_SCRATCH_BYTES) {
+        set_error("%s: the call needs %zu bytes of scratch, the library's array holds %zu "
+                  "(KDA_NOALLOC_SCRATCH_BYTES): split it into smaller calls, or pass a "
+                  "workspace to kda_chunk_fwd", W, need, (size_t)KDA_NOALLOC_SCRATCH_BYTES);
+        return KDA_ERR_WORKSPACE_TOO_SMALL;
+      }
+      st = noalloc_scratch(&workspace);
+      if (st != KDA_OK) return st;
+      workspace_bytes = KDA_NOALLOC_SCRATCH_BYTES;
+    }
     if (!workspace || workspace_bytes < need) {
       set_error("%s: workspace of %zu bytes needed, %zu given", W, need, workspace_bytes);
       return KDA_ERR_WORKSPACE_TOO_SMALL;
@@ -320,6 +336,17 @@ kda_status_t kda_chunk_fwd(const kda_shape_t* sh, int32_t chunk, int32_t total_t
   return chunk_fwd_impl("kda_chunk_fwd", sh, chunk, total_tokens, num_seqs, cu_seqlens, q, k, v,
                         g, beta, false, 0.f, states, num_slots, state_slots, flags, o, workspace,
                         workspace_bytes, stream);
+}
+
+kda_status_t kda_chunk_fwd_noalloc(const kda_shape_t* sh, int32_t chunk, int32_t total_tokens,
+                                   int32_t num_seqs, const int32_t* cu_seqlens, const void* q,
+                                   const void* k, const void* v, const float* g,
+                                   const float* beta, float* states, int32_t num_slots,
+                                   const int32_t* state_slots, uint32_t flags, void* o,
+                                   void* stream) {
+  return chunk_fwd_impl("kda_chunk_fwd_noalloc", sh, chunk, total_tokens, num_seqs, cu_seqlens,
+                        q, k, v, g, beta, false, 0.f, states, num_slots, state_slots, flags, o,
+                        nullptr, 0, stream, true);
 }
 
 kda_status_t kda_chunk_fwd_raw(const kda_shape_t* sh, int32_t chunk, int32_t total_tokens,

@@ -187,6 +187,31 @@ kda_status_t kda_decode_step_ex(const kda_shape_t* shape, int32_t batch, const v
                                 const int32_t* state_slots, uint32_t flags, void* o,
                                 void* stream);
 
+/* Prefill that allocates nothing, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): kda_chunk_fwd with its scratch taken from a device array inside
+ * the library instead of a caller workspace.  Every GPU the library runs on
+ * holds that array, KDA_NOALLOC_SCRATCH_BYTES bytes, until the process ends; its
+ * address is looked up on the first call on each device.
+ *
+ * Arguments, layouts, flags, results and errors are those of kda_chunk_fwd
+ * without workspace / workspace_bytes.  A call that needs more scratch than the
+ * array holds (kda_chunk_fwd_workspace_bytes() > KDA_NOALLOC_SCRATCH_BYTES: with
+ * d = 128 and chunk 64, a chunk capacity (total_tokens / 64 + num_seqs) times H
+ * above about 480 when num_seqs * H <= 32, above about 740 otherwise) returns
+ * KDA_ERR_WORKSPACE_TOO_SMALL before anything is enqueued.  The scratch's contents on entry are ignored, so nothing needs
+ * clearing between calls.  All calls on one GPU share its array and it keeps the
+ * last call's contents: calls that overlap in time on one GPU (different streams
+ * or host threads) race on it, and the caller must order them.  No hipMalloc,
+ * hipFree or allocating library routine is called. */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+kda_status_t kda_chunk_fwd_noalloc(const kda_shape_t* shape, int32_t chunk, int32_t total_tokens,
+                                   int32_t num_seqs, const int32_t* cu_seqlens, const void* q,
+                                   const void* k, const void* v, const float* g,
+                                   const float* beta, float* states, int32_t num_slots,
+                                   const int32_t* state_slots, uint32_t flags, void* o,
+                                   void* stream);
+
 /* Prefill and decode from the raw projection outputs, with the input
  * preparation fused into the path (heqinghuang section 09: q and k pass through
  * SiLU and are scaled to unit length, beta is a sigmoid; engineermaxxing

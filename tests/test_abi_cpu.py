@@ -216,6 +216,31 @@ def test_backward_workspace_per_chunk_head(lib):
     assert 0 <= a - 65 * 16 * int(264.5 * 1024) < 8192
 
 
+def test_noalloc_prefill_validation(lib):
+    """kda_chunk_fwd_noalloc validates like kda_chunk_fwd and rejects a call larger than its
+    static scratch before it touches the GPU."""
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    sh = _shape(16, 128, 128, 1)
+    call = lambda shape, T, N, q=fake, o=fake, flags=0: lib.kda_chunk_fwd_noalloc(
+        ctypes.byref(shape), 64, T, N, fake, q, fake, fake, fake, fake, None, 0, None, flags, o,
+        None)
+    assert call(sh, 128, 1, q=None) == 1                              # NULL tensor
+    assert call(sh, 128, 1, o=P(0x1002)) == 1                         # misaligned output
+    assert call(sh, 128, 0) == 0                                      # no sequences: no-op
+    # 16 heads x (4096 / 64 + 1) chunks x 136.5 KiB is more than 64 MiB
+    assert call(sh, 4096, 1) == 3
+    assert b"KDA_NOALLOC_SCRATCH_BYTES" in lib.kda_last_error()
+    # the byte limit the header states is the one the library applies: the largest call
+    # that fits needs at most that much
+    lim = 64 * 1024 * 1024
+    H = 16
+    T = 64 * 28
+    need = lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(_shape(H, 128, 128, 1)), 64, T, 1)
+    assert need <= lim < lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(_shape(H, 128, 128, 1)),
+                                                           64, T + 64 * 2, 1)
+
+
 def test_launch_timer_end_without_begin(lib):
     """kda_launch_timer_end with no timer active is an argument error (no HIP call)."""
     ms = (ctypes.c_float * 4)()
