@@ -62,7 +62,7 @@ constexpr size_t kWnBytes = 4 * 4 * 64 * 16;   // -W      A operand, M=rows,  K=
 constexpr size_t kQgBytes = 4 * 4 * 64 * 16;   // Q*Gam   A operand, M=rows,  K=dk
 constexpr size_t kKdBytes = 8 * 2 * 64 * 16;   // Kd^T    A operand, M=dk,    K=rows
 constexpr size_t kAqBytes = 4 * 2 * 64 * 16;   // A_qk    A operand, M=rows,  K=rows
-constexpr size_t kUtBytes = 4 * 8 * 64 * 16;   // Ut      accumulator layout, fp32
+constexpr size_t kUtBytes = 2 * 8 * 64 * 16;   // Ut      accumulator layout, bf16, row tiles in pairs
 constexpr size_t kGcBytes = D * 4;             // Gam_C   fp32
 // Written by the state-only scan for the output kernel (few chains):
 constexpr size_t kScBytes = 8 * 4 * 64 * 16;   // S at chunk start, B operand (K=dk, N=dv), bf16
@@ -107,6 +107,15 @@ __device__ __forceinline__ bf16x8 pack8(const float* f) {
 __device__ __forceinline__ bf16x8 pack_acc(f32x4 lo, f32x4 hi) {
   const f32x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_convertvector(v, bf16x8);
+}
+
+// The two accumulator tiles that pack_acc packed, back in fp32 (exact: bf16 -> fp32).
+__device__ __forceinline__ void unpack_acc(bf16x8 p, f32x4& lo, f32x4& hi) {
+  const u32x4 w = __builtin_bit_cast(u32x4, p);
+  lo = f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+             __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
+  hi = f32x4{__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xffff0000u),
+             __uint_as_float(w[3] << 16), __uint_as_float(w[3] & 0xffff0000u)};
 }
 
 // The 8 values a lane holds for K-block s: elements 32s+4g .. +3 and 32s+16+4g .. +3
@@ -261,14 +270,15 @@ struct PrepSmem {
 // launch precedes it.
 constexpr int kFuseMaxSeqs = 384;
 
-// One item's inputs between the global loads and the LDS staging.
+// One item's inputs between the global loads and the LDS staging.  The gate is
+// held by thread (channel tid % 128, quarter tid / 128) down its 16 rows, so the
+// running sums over the rows are formed in registers.
 struct PrepIn {
   uint4 k[2], q[2], v[2];
-  float4 g[4];        // per-channel gate; a scalar gate is read into .x and broadcast at staging
+  float g[16];        // the gate of this thread's channel at rows 16 quarter + i (scalar gate: the row's)
   float beta;
   // raw projections (kRaw): bf16 logits kept as loaded, converted at staging
-  uint2 gl[4];        // 4 per-channel gate logits
-  uint16_t gs16[4];   // scalar gate logit
+  uint16_t gl[16];    // gate logits, per channel or scalar, of the same entries
   uint16_t b16;       // write-strength logit
 };
 
@@ -372,7 +382,8 @@ __device__ __forceinline__ void build_header(PrepSmem& sm, const int32_t* __rest
 // The next item's loads, in four parts that the item loop issues at four
 // points of the current item: all of them at once would hold the wave at the
 // issue until the CU's memory pipeline takes them.  Part 0: k, q; part 1: v,
-// beta; parts 2 and 3: the gate rows of the first and second half.
+// beta; parts 2 and 3: the first and last eight of the thread's 16 gate rows
+// (one channel each; a wave reads 64 consecutive channels of a row).
 template <int kGate, bool kAdd, bool kRaw, int kPart>
 __device__ __forceinline__ void prep_load_part(PrepIn& in, const ItemPos& p, const uint16_t* q,
                                                const uint16_t* k, const uint16_t* v,
@@ -401,16 +412,16 @@ __device__ __forceinline__ void prep_load_part(PrepIn& in, const ItemPos& p, con
       else in.beta = beta[bi];
     }
   } else {
+    const int col = tid & (D - 1), qt = tid >> 7;
 #pragma unroll
-    for (int i = 2 * (kPart - 2); i < 2 * (kPart - 2) + 2; ++i) {
-      const int u = tid + kPrepThreads * i, r = u >> 5, cc = (u & 31) * 4;
-      const size_t row = (size_t)min(r, p.c - 1);
+    for (int i = 8 * (kPart - 2); i < 8 * (kPart - 2) + 8; ++i) {
+      const size_t row = (size_t)min(16 * qt + i, p.c - 1);
       if (kGate == kGateScalar) {
-        if (kRaw) in.gs16[i] = g16[(p.t0 + row) * H + p.h];
-        else in.g[i].x = g[(p.t0 + row) * H + p.h];
+        if (kRaw) in.gl[i] = g16[(p.t0 + row) * H + p.h];
+        else in.g[i] = g[(p.t0 + row) * H + p.h];
       } else if (kGate == kGateChannel) {
-        if (kRaw) in.gl[i] = *reinterpret_cast<const uint2*>(g16 + base + row * rowstride + cc);
-        else in.g[i] = *reinterpret_cast<const float4*>(g + base + row * rowstride + cc);
+        if (kRaw) in.gl[i] = g16[base + row * rowstride + col];
+        else in.g[i] = g[base + row * rowstride + col];
       }
     }
   }
@@ -468,29 +479,22 @@ __device__ __forceinline__ void prep_stage(PrepSmem& sm, const PrepIn& in, int c
     pq[0] = make_uint2(b.x, b.y); pq[1] = make_uint2(b.z, b.w);
     pv[0] = make_uint2(d.x, d.y); pv[1] = make_uint2(d.z, d.w);
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int u = tid + kPrepThreads * i, r = u >> 5, cc = (u & 31) * 4;
-    float4 gv;
-    if (kGate == kGateNone) {
-      gv = make_float4(0.f, 0.f, 0.f, 0.f);
-    } else if (kGate == kGateScalar) {
-      const float x = kRaw ? fmaxf(log_sigmoid(bf16_to_f32(in.gs16[i])), gate_min) : in.g[i].x;
-      gv = make_float4(x, x, x, x);
-    } else if (kRaw) {
-      const uint2 l = in.gl[i];
-      gv = make_float4(fmaxf(log_sigmoid(__uint_as_float(l.x << 16)), gate_min),
-                       fmaxf(log_sigmoid(__uint_as_float(l.x & 0xffff0000u)), gate_min),
-                       fmaxf(log_sigmoid(__uint_as_float(l.y << 16)), gate_min),
-                       fmaxf(log_sigmoid(__uint_as_float(l.y & 0xffff0000u)), gate_min));
-    } else {
-      gv = in.g[i];
-    }
-    *reinterpret_cast<float4*>(&sm.G[r][cc]) = r < c ? gv : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
   const float bt = kAdd ? 1.f : kRaw ? sigmoid(bf16_to_f32(in.b16)) : in.beta;
   if (tid < C) sm.bs[tid] = tid < c ? bt : 0.f;
-  for (int u = tid; u < C * AP; u += kPrepThreads) (&sm.Tm[0][0])[u] = 0.f;
+  // the two blocks above the diagonal that the W / Ut products read, (0,1) and (2,3);
+  // the inverse writes every block on and below the diagonal
+  {
+    const int blk = tid >> 8, e = tid & 255;
+    sm.Tm[32 * blk + (e >> 4)][32 * blk + 16 + (e & 15)] = 0.f;
+  }
+}
+
+// The log-gate of this thread's entry i (channel tid % 128, row 16 (tid / 128) + i),
+// zero past the end of the sequence (neutral padding).
+template <int kGate, bool kRaw>
+__device__ __forceinline__ float prep_gate(const PrepIn& in, int i, int row, int c, float gate_min) {
+  if (kGate == kGateNone || row >= c) return 0.f;
+  return kRaw ? fmaxf(log_sigmoid(bf16_to_f32(in.gl[i])), gate_min) : in.g[i];
 }
 
 __device__ __forceinline__ float ld_bf(const uint16_t* row, int c) { return bf16_to_f32(row[c]); }
@@ -568,14 +572,14 @@ __device__ __forceinline__ void prep_role(
     const int c = pos.c;
     lds_barrier();  // the previous item is done with LDS
     prep_stage<kGate, kAdd, kRaw>(sm, in, c, tid, gate_min);
-    lds_barrier();
 
-    // ---- running sum of the log-gates down each channel (four quarters of 16 rows)
+    // ---- running sum of the log-gates down each channel: each thread sums its
+    // channel's 16 rows of one quarter in registers, then adds the quarters before it
     {
       const int col = tid & 127, qt = tid >> 7;
       float x[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = sm.G[16 * qt + i][col];
+      for (int i = 0; i < 16; ++i) x[i] = prep_gate<kGate, kRaw>(in, i, 16 * qt + i, c, gate_min);
 #pragma unroll
       for (int i = 1; i < 16; ++i) x[i] += x[i - 1];
       sm.tot[qt][col] = x[15];
@@ -776,7 +780,8 @@ __device__ __forceinline__ void prep_role(
       }
       // -W: [m = nt][s = tile / 2][lane][slots (tile & 1) * 4 ..]
       uint16_t* wn_out = reinterpret_cast<uint16_t*>(w.wn + ci * kWnBytes);
-      float* ut_out = reinterpret_cast<float*>(w.ut + ci * kUtBytes);
+      bf16x8* ut_out = reinterpret_cast<bf16x8*>(w.ut + ci * kUtBytes);
+      f32x4 ut_even = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -787,11 +792,14 @@ __device__ __forceinline__ void prep_role(
         *reinterpret_cast<uint2*>(dst) =
             make_uint2((uint32_t)f32_to_bf16(-acc[0]) | ((uint32_t)f32_to_bf16(-acc[1]) << 16),
                        (uint32_t)f32_to_bf16(-acc[2]) | ((uint32_t)f32_to_bf16(-acc[3]) << 16));
-        // Ut = T Diag(beta) V, value tile `tile`, accumulator layout
+        // Ut = T Diag(beta) V, value tile `tile`, accumulator layout; row tiles 2mp and
+        // 2mp + 1 share one bf16 piece [mp][tile][lane] (the scans round U to bf16 for
+        // their products as well)
         f32x4 u = {0.f, 0.f, 0.f, 0.f};
         u = mfma(tt[nt][0], bv[0], u);
         if (nt >= 2) u = mfma(tt[nt][1], bv[1], u);
-        *reinterpret_cast<f32x4*>(ut_out + ((size_t)(nt * 8 + tile) * 64 + lane) * 4) = u;
+        if (nt & 1) ut_out[((size_t)(nt >> 1) * 8 + tile) * 64 + lane] = pack_acc(ut_even, u);
+        else ut_even = u;
       }
       if (tid < D) reinterpret_cast<float*>(w.gc + ci * kGcBytes)[tid] = fast_exp(sm.G[C - 1][tid]);
       if constexpr (kBwd) {
@@ -931,7 +939,7 @@ struct ScanBuf {
   bf16x8 qg[16][64];                        // [m*4 + s][lane]
   bf16x8 kd[16][64];                        // [t*2 + s'][lane]
   bf16x8 aq[8][64];                         // [m*2 + s'][lane]
-  f32x4 ut[4][kUtInLds ? kTiles : 1][64];   // [m][local column tile][lane]
+  bf16x8 ut[2][kUtInLds ? kTiles : 1][64];  // [row tile pair][local column tile][lane]
   f32x4 gc[32];                             // Gam_C
 };
 
@@ -958,7 +966,7 @@ __device__ __forceinline__ void issue_chunk(const Workspace& w, size_t ci, int g
       else if (p < 32) dma16(qg + (p - 16) * 1024 + off, &dst->qg[p - 16][0]);
     }
   } else {
-    constexpr int kPieces = 24 + (ScanBuf<WAVES, NT>::kUtInLds ? 4 * kTiles : 0);
+    constexpr int kPieces = 24 + (ScanBuf<WAVES, NT>::kUtInLds ? 2 * kTiles : 0);
     const uint8_t* kd = w.kd + ci * kKdBytes;
     const uint8_t* aq = w.aq + ci * kAqBytes;
     const uint8_t* ut = w.ut + ci * kUtBytes;
@@ -968,8 +976,8 @@ __device__ __forceinline__ void issue_chunk(const Workspace& w, size_t ci, int g
       if (p < 16) dma16(kd + p * 1024 + off, &dst->kd[p][0]);
       else if (p < 24) dma16(aq + (p - 16) * 1024 + off, &dst->aq[p - 16][0]);
       else if (p < kPieces) {
-        const int q = p - 24, m = q / kTiles, tl = q % kTiles;
-        dma16(ut + (size_t)((m * 8 + group * kTiles + tl) * 64) * 16 + off, &dst->ut[m][tl][0]);
+        const int q = p - 24, mp = q / kTiles, tl = q % kTiles;
+        dma16(ut + (size_t)((mp * 8 + group * kTiles + tl) * 64) * 16 + off, &dst->ut[mp][tl][0]);
       }
     }
     if (wave == WAVES - 1 && lane < 32) dma16(w.gc + ci * kGcBytes + off, &dst->gc[0]);
@@ -1038,13 +1046,13 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(1, 1
   };
 
   constexpr bool kUtInLds = Buf::kUtInLds;
-  f32x4 Unext[NT][4];
+  bf16x8 Unext[NT][2];
   auto load_ut = [&](size_t ci) {  // this wave's Ut tiles, straight into registers
-    const f32x4* ut = reinterpret_cast<const f32x4*>(w.ut + ci * kUtBytes);
+    const bf16x8* ut = reinterpret_cast<const bf16x8*>(w.ut + ci * kUtBytes);
 #pragma unroll
     for (int i = 0; i < NT; ++i)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) Unext[i][m] = ut[(m * 8 + (col[i] >> 4)) * 64 + lane];
+      for (int mp = 0; mp < 2; ++mp) Unext[i][mp] = ut[(mp * 8 + (col[i] >> 4)) * 64 + lane];
   };
 
   // One chunk: compute from B (copied during the previous chunk), copy the next
@@ -1063,7 +1071,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(1, 1
 #pragma unroll
       for (int i = 0; i < NT; ++i)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) U[i][m] = Unext[i][m];
+        for (int mp = 0; mp < 2; ++mp) unpack_acc(Unext[i][mp], U[i][2 * mp], U[i][2 * mp + 1]);
       if (more) load_ut(ci_next);
     }
 
@@ -1078,7 +1086,8 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(1, 1
 #pragma unroll
       for (int i = 0; i < NT; ++i)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) U[i][m] = B.ut[m][kUtInLds ? wave * NT + i : 0][lane];
+        for (int mp = 0; mp < 2; ++mp)
+          unpack_acc(B.ut[mp][kUtInLds ? wave * NT + i : 0][lane], U[i][2 * mp], U[i][2 * mp + 1]);
     }
     bf16x8 sb[NT][4];
 #pragma unroll
@@ -1206,7 +1215,7 @@ struct ScanLds {
     bf16x8 qg[16][64];         // [m*4 + s][lane]
     bf16x8 kd[16][64];         // [t*2 + s'][lane]
     bf16x8 aq[8][64];          // [m*2 + s'][lane]
-    f32x4 ut[4][kTiles][64];   // [m][local column tile][lane]
+    bf16x8 ut[2][kTiles][64];  // [row tile pair][local column tile][lane]
     f32x4 gc[32];              // Gam_C
   };
   Buf buf[2];
@@ -1234,7 +1243,7 @@ __device__ __forceinline__ void scan_role(int b, uint8_t* smem, int32_t N, int H
     // ------------------------------------------------------------ loaders
     const int lw = wave - CW, ltid = tid - 64 * CW;
     const int off = lane * 16;
-    constexpr int kPieces = 56 + 4 * kTiles;  // 1 KiB pieces of a chunk's operands
+    constexpr int kPieces = 56 + 2 * kTiles;  // 1 KiB pieces of a chunk's operands
     auto issue = [&](size_t ci, Buf* dst) {
       const uint8_t* wn = w.wn + ci * kWnBytes;
       const uint8_t* qg = w.qg + ci * kQgBytes;
@@ -1249,9 +1258,9 @@ __device__ __forceinline__ void scan_role(int b, uint8_t* smem, int32_t N, int H
         else if (p < 48) dma16(kd + (p - 32) * 1024 + off, &dst->kd[p - 32][0]);
         else if (p < 56) dma16(aq + (p - 48) * 1024 + off, &dst->aq[p - 48][0]);
         else if (p < kPieces) {
-          const int x = p - 56, m = x / kTiles, tl = x % kTiles;
-          dma16(ut + (size_t)((m * 8 + group * kTiles + tl) * 64) * 16 + off,
-                      &dst->ut[m][tl][0]);
+          const int x = p - 56, mp = x / kTiles, tl = x % kTiles;
+          dma16(ut + (size_t)((mp * 8 + group * kTiles + tl) * 64) * 16 + off,
+                      &dst->ut[mp][tl][0]);
         }
       }
       if (lw == LW - 1 && lane < 32) dma16(w.gc + ci * kGcBytes + off, &dst->gc[0]);
@@ -1325,7 +1334,8 @@ __device__ __forceinline__ void scan_role(int b, uint8_t* smem, int32_t N, int H
 #pragma unroll
     for (int i = 0; i < NT; ++i)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) U[i][m] = B.ut[m][wave * NT + i][lane];
+      for (int mp = 0; mp < 2; ++mp)
+        unpack_acc(B.ut[mp][wave * NT + i][lane], U[i][2 * mp], U[i][2 * mp + 1]);
     bf16x8 a_wn[16];
 #pragma unroll
     for (int x = 0; x < 16; ++x) a_wn[x] = B.wn[x][lane];
@@ -1442,7 +1452,7 @@ struct StateLds {
   struct Buf {
     bf16x8 wn[16][64];         // [m*4 + s][lane]
     bf16x8 kd[16][64];         // [t*2 + s'][lane]
-    f32x4 ut[4][kTiles][64];   // [m][local column tile][lane]
+    bf16x8 ut[2][kTiles][64];  // [row tile pair][local column tile][lane]
     f32x4 gc[32];              // Gam_C
   };
   Buf buf[kStateRing];  // ring: the copies run kStateRing - 1 chunks ahead of the compute wave
@@ -1528,7 +1538,7 @@ __device__ __forceinline__ void scan_state_role(int blk, uint8_t* smem_raw, int3
     // ------------------------------------------------------------ loaders
     const int lw = wave - CW;
     const int off = lane * 16;
-    constexpr int kPieces = 32 + 4 * kTiles;  // 1 KiB pieces of a chunk's operands
+    constexpr int kPieces = 32 + 2 * kTiles;  // 1 KiB pieces of a chunk's operands
     auto issue = [&](size_t ci, Buf* dst) {
       const uint8_t* wn = w.wn + ci * kWnBytes;
       const uint8_t* kd = w.kd + ci * kKdBytes;
@@ -1539,8 +1549,8 @@ __device__ __forceinline__ void scan_state_role(int blk, uint8_t* smem_raw, int3
         if (p < 16) dma16(wn + p * 1024 + off, &dst->wn[p][0]);
         else if (p < 32) dma16(kd + (p - 16) * 1024 + off, &dst->kd[p - 16][0]);
         else if (p < kPieces) {
-          const int x = p - 32, m = x / kTiles, tl = x % kTiles;
-          dma16(ut + (size_t)((m * 8 + group * kTiles + tl) * 64) * 16 + off, &dst->ut[m][tl][0]);
+          const int x = p - 32, mp = x / kTiles, tl = x % kTiles;
+          dma16(ut + (size_t)((mp * 8 + group * kTiles + tl) * 64) * 16 + off, &dst->ut[mp][tl][0]);
         }
       }
       if (lw == LW - 1 && lane < 32) dma16(w.gc + ci * kGcBytes + off, &dst->gc[0]);
@@ -1598,7 +1608,8 @@ __device__ __forceinline__ void scan_state_role(int blk, uint8_t* smem_raw, int3
 #pragma unroll
     for (int i = 0; i < NT; ++i)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) U[i][m] = B.ut[m][wave * NT + i][lane];
+      for (int mp = 0; mp < 2; ++mp)
+        unpack_acc(B.ut[mp][wave * NT + i][lane], U[i][2 * mp], U[i][2 * mp + 1]);
     bf16x8 a_wn[16];
 #pragma unroll
     for (int x = 0; x < 16; ++x) a_wn[x] = B.wn[x][lane];

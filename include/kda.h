@@ -198,7 +198,7 @@ kda_status_t kda_decode_step_ex(const kda_shape_t* shape, int32_t batch, const v
  * without workspace / workspace_bytes.  A call that needs more scratch than the
  * array holds (kda_chunk_fwd_workspace_bytes() > KDA_NOALLOC_SCRATCH_BYTES: with
  * d = 128 and chunk 64, a chunk capacity (total_tokens / 64 + num_seqs) times H
- * above about 480 when num_seqs * H <= 32, above about 740 otherwise) returns
+ * above about 540 when num_seqs * H <= 32, above about 900 otherwise) returns
  * KDA_ERR_WORKSPACE_TOO_SMALL before anything is enqueued.  The scratch's contents on entry are ignored, so nothing needs
  * clearing between calls.  All calls on one GPU share its array and it keeps the
  * last call's contents: calls that overlap in time on one GPU (different streams
@@ -283,7 +283,7 @@ size_t kda_chunk_bwd_workspace_bytes(const kda_shape_t* shape, int32_t chunk,
  *                KDA_ADDITIVE; KDA_WRITE_FINAL_STATE and unknown bits are
  *                KDA_ERR_INVALID_ARGUMENT.
  * workspace      device scratch of kda_chunk_bwd_workspace_bytes() bytes, 256-byte
- *                aligned (264.5 KiB per chunk and head of chunk capacity, the capacity
+ *                aligned (248.5 KiB per chunk and head of chunk capacity, the capacity
  *                being total_tokens / chunk + num_seqs chunks, plus a small header).
  * Supported: io_dtype KDA_BF16, dk = dv = 128, chunk 64 (else KDA_ERR_UNSUPPORTED).
  * num_seqs == 0 is a no-op returning KDA_OK.  total_tokens == 0 makes every
