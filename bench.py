@@ -46,10 +46,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 PREFILL_BYTES_PER_TOKEN_HEAD = 3 * 2 * 128 + 4 * 128 + 4 + 2 * 128   # q,k,v bf16 + g fp32 + beta + o bf16
 DECODE_BYTES_PER_HEAD = 2 * 128 * 128 * 4 + PREFILL_BYTES_PER_TOKEN_HEAD  # state read+write + token
 # Algorithmic bytes of each launch of the prefill call, per token-head: the prep reads the
-# inputs (q, k, v bf16, g fp32, beta), the output kernel writes o; the state-only scan
-# writes the final state (per sequence-head, added where it is used).
+# inputs (q, k, v bf16, g fp32, beta), the scan writes o and the final state (per
+# sequence-head, added where it is used).
 PREFILL_LAUNCH_BYTES_PER_TOKEN_HEAD = {"prep_kernel": 3 * 2 * 128 + 4 * 128 + 4,
-                                       "scan_state_kernel": 0, "out_kernel": 2 * 128}
+                                       "scan_out_kernel": 2 * 128}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 TRAFFIC_BACKWARD_FILE = os.path.join(ROOT, "profiles", "traffic_backward.json")
 
@@ -548,7 +548,7 @@ def main(argv=None):
         bytes_ = PREFILL_BYTES_PER_TOKEN_HEAD * T * H + N * H * 128 * 128 * 4
         achieved = bytes_ / (ms * 1e-3) / 1e9
         launch_bytes = {k: b * T * H for k, b in PREFILL_LAUNCH_BYTES_PER_TOKEN_HEAD.items()}
-        launch_bytes["scan_state_kernel"] += N * H * 128 * 128 * 4   # final state
+        launch_bytes["scan_out_kernel"] += N * H * 128 * 128 * 4   # final state
         launches = _launch_table(pr["launches"], launch_bytes, TRAFFIC_FILE)
         dom = max(launches, key=lambda n: launches[n]["mean_us"])
         dl = launches[dom]

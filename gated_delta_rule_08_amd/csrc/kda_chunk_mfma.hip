@@ -16,9 +16,11 @@
 // folded through it (heqinghuang section 11; engineermaxxing ch. 05d keeps
 // them as sums of logs).  It equals the sequential recurrence up to rounding.
 //
-// Work split (three launches on the caller's stream):
-//  1. index: per-sequence chunk counts and offsets (sanitised, one thread).
-//  2. prep:  one workgroup per (chunk, head), fully parallel over chunks.  It
+// Work split (launches on the caller's stream):
+//  1. index: per-sequence chunk counts and offsets (sanitised, one thread); up
+//     to 384 sequences the prep builds them itself and this launch is skipped.
+//  2. prep:  persistent workgroups over the (chunk, head) items, fully parallel
+//     over chunks.  It
 //     computes everything that does not depend on the incoming state: the
 //     gated Gram blocks, the triangular inverse (fp32), W, Ut, Q*Gam,
 //     (K*exp(G_C-G))^T, A_qk and Gam_C, and stores the MFMA operands in the
@@ -30,8 +32,9 @@
 //     only loop-carried dependency of the method (heqinghuang section 10: the
 //     only sequential loop is over chunks).  The waves of a workgroup share
 //     each chunk's operands through LDS.  With few chains, dedicated loader
-//     waves copy the operands so the compute waves never wait on the copies;
-//     with many chains, one workgroup per head fetches them once per chunk.
+//     waves copy the operands so the compute waves never wait on the copies
+//     (and with very few, a wave of its own forms the outputs beside the state
+//     wave); with many chains, one workgroup per head fetches them once per chunk.
 //
 // Numerics of the gated Gram products: exp(G_r - G_j) is split at the first
 // row s of the 16-row block of r as exp(G_r - G_s) * exp(G_s - G_j).  For j in
@@ -64,7 +67,7 @@ constexpr size_t kKdBytes = 8 * 2 * 64 * 16;   // Kd^T    A operand, M=dk,    K=
 constexpr size_t kAqBytes = 4 * 2 * 64 * 16;   // A_qk    A operand, M=rows,  K=rows
 constexpr size_t kUtBytes = 2 * 8 * 64 * 16;   // Ut      accumulator layout, bf16, row tiles in pairs
 constexpr size_t kGcBytes = D * 4;             // Gam_C   fp32
-// Written by the state-only scan for the output kernel (few chains):
+// Written by the backward's forward state pass for the gradient kernel:
 constexpr size_t kScBytes = 8 * 4 * 64 * 16;   // S at chunk start, B operand (K=dk, N=dv), bf16
 constexpr size_t kUcBytes = 8 * 2 * 64 * 16;   // U, B operand (K=rows, N=dv), bf16
 // Backward only (the reverse scan's A operands use the Kd^T / A_qk block sizes;
@@ -75,9 +78,10 @@ constexpr size_t kUcBytes = 8 * 2 * 64 * 16;   // U, B operand (K=rows, N=dv), b
 constexpr size_t kMkBytes = C * C * 4;        // M_kk fp32, 16x16 tiles [R*4 + J][row][column]
 constexpr size_t kTmBytes = 8 * 64 * 16;       // T^T bf16 A-operand tiles [m*2 + s2][lane]
 
-// Chains (sequence-heads) up to which the scan only carries the state and a
-// separate, fully parallel kernel forms the outputs: with few chains the
-// serial chain of chunk steps is the critical path, so work is moved off it.
+// Chains (sequence-heads) up to which each head's state is split over eight
+// workgroups of 16 columns whose state wave does only the state recurrence and
+// a wave beside it forms the outputs: with few chains the serial chain of chunk
+// steps is the critical path, so work is moved off it.
 constexpr int kSplitMaxChains = 32;
 bool split_outputs(int32_t N, int H) { return (int64_t)N * H <= kSplitMaxChains; }
 
@@ -186,7 +190,7 @@ Workspace carve(void* base, int32_t T, int32_t N, int H, bool bwd = false) {
   w.gc = p; p += align256(ci * kGcBytes);
   w.sc = w.uc = nullptr;
   w.kdr = w.wt = w.qgt = w.aqt = w.mkk = w.tm = w.dsc = w.duc = nullptr;
-  if (bwd || split_outputs(N, H)) {
+  if (bwd) {
     w.sc = p; p += align256(ci * kScBytes);
     w.uc = p; p += align256(ci * kUcBytes);
   }
@@ -1438,12 +1442,12 @@ __global__ __launch_bounds__(64 * (CW + LW)) void scan_ws_kernel(
   scan_role<CW, NT, LW>(blockIdx.x, smem_raw, N, H, w, states, num_slots, slots, flags, o);
 }
 
-// State-only warp-specialised scan (few chains).  Per chunk only the state
-// recurrence is on the serial path: U = Ut - W S and S' = Diag(Gam_C) S +
-// Kd^T U.  The compute waves store the bf16 MFMA operands they form anyway,
-// S at the chunk start and U, for the output kernel, which then forms
-// O = (Q*Gam) S + A_qk U for all chunks in parallel.  The loaders copy -W,
-// Kd^T, the workgroup's Ut tiles and Gam_C.
+// State-only warp-specialised scan: the backward's forward state pass.  Per
+// chunk only the state recurrence is on the serial path: U = Ut - W S and S' =
+// Diag(Gam_C) S + Kd^T U.  The compute waves store the bf16 MFMA operands they
+// form anyway, S at the chunk start and U, for the gradient kernel.  The loaders
+// copy -W, Kd^T, the workgroup's Ut tiles and Gam_C.  (The forward's few-chains
+// scan, scan_out_kernel, keeps the same ring and forms the outputs instead.)
 constexpr int kStateRing = 3;
 
 template <int CW, int NT>
@@ -1670,107 +1674,222 @@ __device__ __forceinline__ void scan_state_role(int blk, uint8_t* smem_raw, int3
   }
 }
 
-template <int CW, int NT, int LW>
-__global__ __launch_bounds__(64 * (CW + LW)) void scan_state_kernel(
+// State scan with the outputs formed beside it (few chains).  A workgroup owns
+// 16 state columns of one (sequence, head).  Wave 0 carries the state as in
+// scan_state_role and, per chunk c, leaves S_c (at the chunk start) and U_c in
+// LDS as the bf16 B operands it forms anyway; wave 1 forms O_c = (Q*Gam)_c S_c +
+// A_qk,c U_c one step later, with the MFMA order of the single-pass scan, from
+// Q*Gam and A_qk that it loads from the workspace into registers two chunks
+// ahead, and stores the chunk's 64 x 16 outputs as 16-byte row pieces staged in
+// LDS; waves 2..7 keep the three-buffer ring of the chain's operands filled.
+// Nothing of S or U goes through memory, and no separate output launch re-reads
+// the chunk operands.
+constexpr int kOutLoaders = 6;
+constexpr int kScanOutThreads = 64 * (2 + kOutLoaders);
+
+struct ScanOutLds {
+  StateLds<1, 1>::Buf buf[kStateRing];
+  bf16x8 xs[2][6][64];  // per chunk parity: S_c as 4 B operands (K = dk), then U_c as 2 (K = rows)
+  uint16_t ob[C][16];   // the output wave's bf16 outputs of one chunk
+};
+
+__global__ __launch_bounds__(kScanOutThreads) void scan_out_kernel(
     int32_t N, int H, Workspace w, float* __restrict__ states, int32_t num_slots,
-    const int32_t* __restrict__ slots, uint32_t flags) {
+    const int32_t* __restrict__ slots, uint32_t flags, uint16_t* __restrict__ o) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
-  scan_state_role<CW, NT, LW>(blockIdx.x, smem_raw, N, H, w, states, num_slots, slots, flags);
-}
+  using Buf = StateLds<1, 1>::Buf;
+  constexpr int LW = kOutLoaders;
+  ScanOutLds& sl = *reinterpret_cast<ScanOutLds*>(smem_raw);
+  const int NH = N * H;
+  const int head_lin = blockIdx.x % NH;
+  const int group = blockIdx.x / NH;  // 16-column tile of the state
+  const int n = head_lin / H, h = head_lin - n * H;
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nch = w.seq_nch[n];
+  const int cbase = w.chunk_off[n];
 
-// Outputs of every (chunk, head) in parallel from the operands stored by the
-// prep (Q*Gam, A_qk) and by the state-only scan (S at the chunk start, U):
-// O = (Q*Gam) S + A_qk U, with the MFMA sequence of the single-pass scan.
-// Four waves, each owning two 16-column tiles; the bf16 outputs are staged in
-// LDS and stored as whole 16-byte row pieces of the valid rows.
-constexpr int kOutThreads = 256;
-__global__ __launch_bounds__(kOutThreads) void out_kernel(
-    int32_t N, int H, Workspace w, const int32_t* __restrict__ seq_start,
-    const int32_t* __restrict__ seq_end, const int32_t* __restrict__ chunk_off,
-    uint16_t* __restrict__ o) {
-  __shared__ uint16_t ob[C][D + 8];
-  const Header hd{seq_start, seq_end, chunk_off};
-  const int item = blockIdx.x;
-  if (item >= hd.chunk_off[N] * H) return;  // uniform
-  const ItemPos pos = locate(hd, N, H, item);
-  const size_t ci = (size_t)item;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
-  constexpr int NT = 2;
-  const bf16x8* qg = reinterpret_cast<const bf16x8*>(w.qg + ci * kQgBytes);
-  const bf16x8* aq = reinterpret_cast<const bf16x8*>(w.aq + ci * kAqBytes);
-  const bf16x8* sc = reinterpret_cast<const bf16x8*>(w.sc + ci * kScBytes);
-  const bf16x8* uc = reinterpret_cast<const bf16x8*>(w.uc + ci * kUcBytes);
-  bf16x8 sb[NT][4], ub[NT][2], a_qg[16], a_aq[6];
+  if (wave >= 2) {
+    // ------------------------------------------------------------ loaders
+    const int lw = wave - 2;
+    const int off = lane * 16;
+    constexpr int kPieces = 32 + 2;  // 1 KiB pieces: -W, Kd^T, this group's two Ut pieces
+    auto issue = [&](size_t ci, Buf* dst) {
+      const uint8_t* wn = w.wn + ci * kWnBytes;
+      const uint8_t* kd = w.kd + ci * kKdBytes;
+      const uint8_t* ut = w.ut + ci * kUtBytes;
 #pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    const int t = wave * NT + i;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) sb[i][s] = sc[(t * 4 + s) * 64 + lane];
-    ub[i][0] = uc[(t * 2 + 0) * 64 + lane];
-    ub[i][1] = uc[(t * 2 + 1) * 64 + lane];
+      for (int i = 0; i < (kPieces + LW - 1) / LW; ++i) {
+        const int p = lw + LW * i;  // wave-uniform
+        if (p < 16) dma16(wn + p * 1024 + off, &dst->wn[p][0]);
+        else if (p < 32) dma16(kd + (p - 16) * 1024 + off, &dst->kd[p - 16][0]);
+        else if (p < kPieces) {
+          const int mp = p - 32;
+          dma16(ut + (size_t)((mp * 8 + group) * 64) * 16 + off, &dst->ut[mp][0][0]);
+        }
+      }
+      if (lw == LW - 1 && lane < 32) dma16(w.gc + ci * kGcBytes + off, &dst->gc[0]);
+    };
+    const int mine = (kPieces - lw + LW - 1) / LW + (lw == LW - 1 ? 1 : 0);
+    constexpr int kAhead = kStateRing - 1;
+    static_assert(((kPieces + LW - 1) / LW + 1) * (kAhead - 1) <= 15, "graded wait range");
+    for (int c = 0; c < kAhead && c < nch; ++c) issue((size_t)(cbase + c) * H + h, &sl.buf[c]);
+    wait_vm(mine * (min(nch, kAhead) - 1 > 0 ? min(nch, kAhead) - 1 : 0));  // chunk 0 landed
+    lds_barrier();
+    for (int lc = 0; lc < nch; ++lc) {
+      const int nxt = lc + kAhead;
+      if (nxt < nch) issue((size_t)(cbase + nxt) * H + h, &sl.buf[nxt % kStateRing]);
+      const int newest = min(nch - 1, nxt) - (lc + 1);
+      wait_vm(newest > 0 ? mine * newest : 0);
+      lds_barrier();
+    }
+    return;
   }
+
+  if (wave == 1) {
+    // ------------------------------------------------------------ outputs
+    // chunk c's Q*Gam and A_qk tiles sit in register set c % 2, loaded at step c - 1
+    bf16x8 qg0[16], aq0[6], qg1[16], aq1[6];
+    auto load_ops = [&](bf16x8* qgr, bf16x8* aqr, int c) {
+      const size_t ci = (size_t)(cbase + c) * H + h;
+      const bf16x8* qg = reinterpret_cast<const bf16x8*>(w.qg + ci * kQgBytes);
+      const bf16x8* aq = reinterpret_cast<const bf16x8*>(w.aq + ci * kAqBytes);
 #pragma unroll
-  for (int x = 0; x < 16; ++x) a_qg[x] = qg[x * 64 + lane];
+      for (int x = 0; x < 16; ++x) qgr[x] = qg[x * 64 + lane];
 #pragma unroll
-  for (int x = 0; x < 6; ++x) a_aq[x] = aq[(x < 2 ? 2 * x : x + 2) * 64 + lane];  // [0],[2],[4..7]
-  f32x4 O[NT][4];
+      for (int x = 0; x < 6; ++x) aqr[x] = aq[(x < 2 ? 2 * x : x + 2) * 64 + lane];  // [0],[2],[4..7]
+    };
+    const int start = w.seq_start[n], end = w.seq_end[n];
+    // O_c from slot c % 2 of the exchange and the operand tiles qgr, aqr
+    auto out_chunk = [&](const bf16x8* qgr, const bf16x8* aqr, int c) {
+      const bf16x8(*x)[64] = sl.xs[c & 1];
+      bf16x8 sb[4], ub[2];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+      for (int s2 = 0; s2 < 4; ++s2) sb[s2] = x[s2][lane];
+      ub[0] = x[4][lane];
+      ub[1] = x[5][lane];
+      f32x4 O[4];
 #pragma unroll
-    for (int i = 0; i < NT; ++i) O[i][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int m = 0; m < 4; ++m) O[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
+      for (int s2 = 0; s2 < 4; ++s2)
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+        for (int m = 0; m < 4; ++m) O[m] = mfma(qgr[m * 4 + s2], sb[s2], O[m]);
+      // A_qk rows 0-31 have no entries in columns 32-63
+      O[0] = mfma(aqr[0], ub[0], O[0]);
+      O[1] = mfma(aqr[1], ub[0], O[1]);
+      O[2] = mfma(aqr[2], ub[0], O[2]);
+      O[3] = mfma(aqr[4], ub[0], O[3]);
+      O[2] = mfma(aqr[3], ub[1], O[2]);
+      O[3] = mfma(aqr[5], ub[1], O[3]);
+      // stage as bf16 rows of 16 columns, then store whole 16-byte row pieces (this
+      // wave alone writes and reads the staging tile, in program order)
 #pragma unroll
-      for (int i = 0; i < NT; ++i) O[i][m] = mfma(a_qg[m * 4 + s], sb[i][s], O[i][m]);
+      for (int m = 0; m < 4; ++m)
 #pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    O[i][0] = mfma(a_aq[0], ub[i][0], O[i][0]);
-    O[i][1] = mfma(a_aq[1], ub[i][0], O[i][1]);
-    O[i][2] = mfma(a_aq[2], ub[i][0], O[i][2]);
-    O[i][3] = mfma(a_aq[4], ub[i][0], O[i][3]);
+        for (int jj = 0; jj < 4; ++jj) sl.ob[16 * m + 4 * lg + jj][li] = f32_to_bf16(O[m][jj]);
+      const int t0 = start + c * C, rows = min(C, end - t0);
+#pragma unroll
+      for (int xx = 0; xx < 2; ++xx) {
+        const int pc = lane + 64 * xx, r = pc >> 1, half = pc & 1;
+        const uint4 v4 = *reinterpret_cast<const uint4*>(&sl.ob[r][8 * half]);
+        if (r < rows)
+          *reinterpret_cast<uint4*>(o + ((size_t)(t0 + r) * H + h) * D + 16 * group + 8 * half) = v4;
+      }
+    };
+    if (nch > 0) load_ops(qg0, aq0, 0);
+    if (nch > 1) load_ops(qg1, aq1, 1);
+    lds_barrier();
+    // after the barrier that ends chunk c: O_c, then chunk c + 2's tiles into the set
+    // just used; unrolled by two so that every register set is named
+    for (int c = 0; c < nch; c += 2) {
+      lds_barrier();  // end of chunk c
+      out_chunk(qg0, aq0, c);
+      if (c + 2 < nch) load_ops(qg0, aq0, c + 2);
+      if (c + 1 < nch) {
+        lds_barrier();  // end of chunk c + 1
+        out_chunk(qg1, aq1, c + 1);
+        if (c + 3 < nch) load_ops(qg1, aq1, c + 3);
+      }
+    }
+    return;
   }
+
+  // -------------------------------------------------------------- state (wave 0)
+  const int col = 16 * group + li;
+  const int slot = slots ? slots[n] : n;
+  const bool slot_ok = states != nullptr && slot >= 0 && slot < num_slots;
+  float* Sg = slot_ok ? states + ((size_t)slot * H + h) * (size_t)(D * D) : nullptr;
+  f32x4 S[8];
+  if (slot_ok && (flags & KDA_READ_INITIAL_STATE)) {
 #pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    O[i][2] = mfma(a_aq[3], ub[i][1], O[i][2]);
-    O[i][3] = mfma(a_aq[5], ub[i][1], O[i][3]);
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) S[t][jj] = Sg[(size_t)(16 * t + 4 * lg + jj) * D + col];
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-#pragma unroll
-  for (int i = 0; i < NT; ++i)
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        ob[16 * m + 4 * lg + jj][16 * (wave * NT + i) + li] = f32_to_bf16(O[i][m][jj]);
   lds_barrier();
-  // 64 rows x 16 pieces of 16 bytes
+  for (int lc = 0; lc < nch; ++lc) {
+    const Buf& B = sl.buf[lc % kStateRing];
+    bf16x8(*x)[64] = sl.xs[lc & 1];
+    f32x4 U[4];
+    unpack_acc(B.ut[0][0][lane], U[0], U[1]);
+    unpack_acc(B.ut[1][0][lane], U[2], U[3]);
+    bf16x8 a_wn[16];
 #pragma unroll
-  for (int x = 0; x < C * (D / 8) / kOutThreads; ++x) {
-    const int u = tid + kOutThreads * x, r = u >> 4, pc = u & 15;
-    if (r < pos.c)
-      *reinterpret_cast<uint4*>(o + ((size_t)(pos.t0 + r) * H + pos.h) * D + 8 * pc) =
-          *reinterpret_cast<const uint4*>(&ob[r][8 * pc]);
+    for (int xx = 0; xx < 16; ++xx) a_wn[xx] = B.wn[xx][lane];
+    bf16x8 sb[4];
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) sb[s2] = pack_acc(S[2 * s2], S[2 * s2 + 1]);
+    bf16x8 a_kd[16];
+    f32x4 gcv[8];
+#pragma unroll
+    for (int xx = 0; xx < 16; ++xx) a_kd[xx] = B.kd[xx][lane];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) gcv[t] = B.gc[4 * t + lg];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) x[s2][lane] = sb[s2];
+    // U = Ut - W S   (consecutive MFMAs go to different accumulators)
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) U[m] = mfma(a_wn[m * 4 + s2], sb[s2], U[m]);
+    bf16x8 ub[2];
+    ub[0] = pack_acc(U[0], U[1]);
+    ub[1] = pack_acc(U[2], U[3]);
+    x[4][lane] = ub[0];
+    x[5][lane] = ub[1];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) S[t] = S[t] * gcv[t];
+    // S' = Diag(Gam_C) S + Kd^T U
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) S[t] = mfma(a_kd[t * 2 + s2], ub[s2], S[t]);
+    lds_barrier();
+  }
+  if (slot_ok && (flags & KDA_WRITE_FINAL_STATE)) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) Sg[(size_t)(16 * t + 4 * lg + jj) * D + col] = S[t][jj];
   }
 }
 
-template <int CW, int NT, int LW>
-kda_status_t launch_split(int32_t N, int H, const Workspace& w, float* states, int32_t num_slots,
-                          const int32_t* slots, uint32_t flags, void* o, size_t items,
-                          hipStream_t stream) {
-  constexpr int kGroups = D / (16 * CW * NT);
+kda_status_t launch_scan_out(int32_t N, int H, const Workspace& w, float* states,
+                             int32_t num_slots, const int32_t* slots, uint32_t flags, void* o,
+                             hipStream_t stream) {
   static std::atomic<uint64_t> lds_set{0};
-  kda_status_t st = allow_dynamic_lds(reinterpret_cast<const void*>(scan_state_kernel<CW, NT, LW>),
-                                      sizeof(StateLds<CW, NT>), lds_set, "hipFuncSetAttribute(scan)");
+  kda_status_t st = allow_dynamic_lds(reinterpret_cast<const void*>(scan_out_kernel),
+                                      sizeof(ScanOutLds), lds_set, "hipFuncSetAttribute(scan)");
   if (st != KDA_OK) return st;
-  hipLaunchKernelGGL((scan_state_kernel<CW, NT, LW>), dim3((unsigned)(N * H * kGroups)),
-                     dim3(64 * (CW + LW)), sizeof(StateLds<CW, NT>), stream, N, H, w, states,
-                     num_slots, slots, flags);
-  st = check_launch("scan_state_kernel");
-  if (st != KDA_OK) return st;
-  hipLaunchKernelGGL(out_kernel, dim3((unsigned)items), dim3(kOutThreads), 0, stream, N, H, w,
-                     w.seq_start, w.seq_end, w.chunk_off, static_cast<uint16_t*>(o));
-  return check_launch("out_kernel");
+  hipLaunchKernelGGL(scan_out_kernel, dim3((unsigned)(N * H * (D / 16))), dim3(kScanOutThreads),
+                     sizeof(ScanOutLds), stream, N, H, w, states, num_slots, slots, flags,
+                     static_cast<uint16_t*>(o));
+  return check_launch("scan_out_kernel");
 }
 
 template <int CW, int NT, int LW>
@@ -2643,8 +2762,7 @@ size_t chunk_mfma_workspace_bytes(int H, int32_t T, int32_t N) {
   const size_t ci = nchunks_max(T, N) * (size_t)H;
   return header_bytes(N) + align256(ci * kWnBytes) + align256(ci * kQgBytes) +
          align256(ci * kKdBytes) + align256(ci * kAqBytes) + align256(ci * kUtBytes) +
-         align256(ci * kGcBytes) + 256 +
-         (split_outputs(N, H) ? align256(ci * kScBytes) + align256(ci * kUcBytes) : 0);
+         align256(ci * kGcBytes) + 256;
 }
 
 kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, const int32_t* cu,
@@ -2675,13 +2793,13 @@ kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, cons
            : launch_prep_variant<false>(flags, grid, q, k, v, g, beta, gate_min, N, H, w, ix, stream);
   if (st != KDA_OK) return st;
   // Few chains: the serial chain of chunk steps is the critical path; each
-  // head's state is split over 8 warp-specialised workgroups of 16 columns that
-  // carry only the state, and the outputs are formed afterwards in parallel.
+  // head's state is split over 8 warp-specialised workgroups of 16 columns whose
+  // state wave carries only the state while a wave beside it forms the outputs.
   // Up to one workgroup per CU at 4 per head: the single-pass warp-specialised
   // scan.  Many chains: one workgroup of 4 waves x 32 columns per head, which
   // fetches each chunk's shared operands once.
   if (split_outputs(N, H))
-    return launch_split<1, 1, 7>(N, H, w, states, num_slots, slots, flags, o, items, stream);
+    return launch_scan_out(N, H, w, states, num_slots, slots, flags, o, stream);
   if ((size_t)N * H * 4 <= (size_t)ncu)
     return launch_scan_ws<2, 1, 6>(N, H, w, states, num_slots, slots, flags, o, stream);
   return launch_scan<4, 2>(N, H, w, states, num_slots, slots, flags, o, stream);

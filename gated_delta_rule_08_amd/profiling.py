@@ -30,13 +30,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _short(name: str) -> str:
-    for key in ("prep_kernel", "index_kernel", "out_kernel", "decode_kernel", "chunk_small_kernel",
-                "zero_kernel", "gather_scatter_kernel", "scan_grad_kernel", "grad_kernel"):
-        if key in name:
-            return key
-    for key in ("scan_state_kernel", "scan_ws_kernel", "scan_pair_kernel", "scan_kernel"):
+    for key in ("scan_out_kernel", "scan_ws_kernel", "scan_pair_kernel", "scan_kernel"):
         if key in name:
             return key + (name[name.index("<"):name.index(">") + 1] if "<" in name else "")
+    for key in ("prep_kernel", "index_kernel", "decode_kernel", "chunk_small_kernel",
+                "zero_kernel", "gather_scatter_kernel", "grad_kernel"):
+        if key in name:
+            return key
     if "MulFunctor" in name or "mul_kernel" in name:
         return "torch:mul"
     if "FillFunctor" in name:
@@ -117,7 +117,7 @@ def traffic(fetch_csv: str, write_csv: str, copy_mib: float, out: str) -> dict:
         per[k] = {"fetch_bytes": fk, "write_bytes": wk}
     both = lambda k: per[k]["fetch_bytes"] + per[k]["write_bytes"]
     prefill = sum(both(k) for k in per
-                  if k in ("index_kernel", "prep_kernel", "out_kernel") or k.startswith("scan_"))
+                  if k in ("index_kernel", "prep_kernel") or k.startswith("scan_"))
     decode = sum(both(k) for k in per if k == "decode_kernel")
     # a backward-only run (bench.py --only backward): its index, prep and scans are the backward's
     backward = sum(both(k) for k in per if k in ("index_kernel", "prep_kernel", "grad_kernel")

@@ -198,8 +198,8 @@ kda_status_t kda_decode_step_ex(const kda_shape_t* shape, int32_t batch, const v
  * without workspace / workspace_bytes.  A call that needs more scratch than the
  * array holds (kda_chunk_fwd_workspace_bytes() > KDA_NOALLOC_SCRATCH_BYTES: with
  * d = 128 and chunk 64, a chunk capacity (total_tokens / 64 + num_seqs) times H
- * above about 540 when num_seqs * H <= 32, above about 900 otherwise) returns
- * KDA_ERR_WORKSPACE_TOO_SMALL before anything is enqueued.  The scratch's contents on entry are ignored, so nothing needs
+ * above about 900) returns KDA_ERR_WORKSPACE_TOO_SMALL before anything is
+ * enqueued.  The scratch's contents on entry are ignored, so nothing needs
  * clearing between calls.  All calls on one GPU share its array and it keeps the
  * last call's contents: calls that overlap in time on one GPU (different streams
  * or host threads) race on it, and the caller must order them.  No hipMalloc,
