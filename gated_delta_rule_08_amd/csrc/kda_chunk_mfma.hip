@@ -317,6 +317,21 @@ __device__ __forceinline__ ItemPos locate(const Header& hd, int N, int H, int it
   return p;
 }
 
+// Heads up to which the prep's 32-bit row offsets (row < 64 times H * D elements)
+// are exact; the host refuses more before any launch.
+constexpr int kMaxHeads = 65536;
+
+// The position of a workgroup-uniform item in scalar registers (values read from
+// LDS are vector registers to the compiler), so that the row addresses built on it
+// are a scalar base plus a 32-bit lane offset.
+__device__ __forceinline__ ItemPos uniform_pos(ItemPos p) {
+  p.gc = __builtin_amdgcn_readfirstlane(p.gc);
+  p.h = __builtin_amdgcn_readfirstlane(p.h);
+  p.t0 = __builtin_amdgcn_readfirstlane(p.t0);
+  p.c = __builtin_amdgcn_readfirstlane(p.c);
+  return p;
+}
+
 // The same lookup in the header the prep built in LDS.
 __device__ __forceinline__ ItemPos locate_lds(const PrepSmem& sm, int N, int H, int item) {
   ItemPos p;
@@ -329,7 +344,7 @@ __device__ __forceinline__ ItemPos locate_lds(const PrepSmem& sm, int N, int H, 
   }
   p.t0 = sm.hs[lo] + (p.gc - sm.ho[lo]) * C;
   p.c = min(C, sm.he[lo] - p.t0);
-  return p;
+  return uniform_pos(p);
 }
 
 // The sequence header (as index_kernel builds it) for N <= kFuseMaxSeqs, by the
@@ -396,36 +411,41 @@ __device__ __forceinline__ void prep_load_part(PrepIn& in, const ItemPos& p, con
   const float* beta = static_cast<const float*>(bp);
   const uint16_t* g16 = static_cast<const uint16_t*>(gp);
   const uint16_t* b16 = static_cast<const uint16_t*>(bp);
-  const size_t rowstride = (size_t)H * D;
+  // a scalar base at the chunk's first row, plus 32-bit lane offsets (rows < 64,
+  // H * D < 2^24 elements, so the 24-bit multiply is exact and offsets fit)
+  const uint32_t rowstride = (uint32_t)H * D;
   const size_t base = ((size_t)p.t0 * H + p.h) * D;
+  const size_t bbase = (size_t)p.t0 * H + p.h;
   if constexpr (kPart <= 1) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int u = tid + kPrepThreads * i, r = u >> 4, cc = (u & 15) * 8;
-      const size_t gi = base + (size_t)min(r, p.c - 1) * rowstride + cc;
+      const uint32_t gi = __umul24((uint32_t)min(r, p.c - 1), rowstride) + cc;
       if constexpr (kPart == 0) {
-        in.k[i] = *reinterpret_cast<const uint4*>(k + gi);
-        in.q[i] = *reinterpret_cast<const uint4*>(q + gi);
+        in.k[i] = *reinterpret_cast<const uint4*>(k + base + gi);
+        in.q[i] = *reinterpret_cast<const uint4*>(q + base + gi);
       } else {
-        in.v[i] = *reinterpret_cast<const uint4*>(v + gi);
+        in.v[i] = *reinterpret_cast<const uint4*>(v + base + gi);
       }
     }
     if constexpr (kPart == 1 && !kAdd) {
-      const size_t bi = (size_t)(p.t0 + min(tid & 63, p.c - 1)) * H + p.h;
-      if (kRaw) in.b16 = b16[bi];
-      else in.beta = beta[bi];
+      const uint32_t bi = __umul24((uint32_t)min(tid & 63, p.c - 1), (uint32_t)H);
+      if (kRaw) in.b16 = (b16 + bbase)[bi];
+      else in.beta = (beta + bbase)[bi];
     }
   } else {
     const int col = tid & (D - 1), qt = tid >> 7;
 #pragma unroll
     for (int i = 8 * (kPart - 2); i < 8 * (kPart - 2) + 8; ++i) {
-      const size_t row = (size_t)min(16 * qt + i, p.c - 1);
+      const uint32_t row = (uint32_t)min(16 * qt + i, p.c - 1);
       if (kGate == kGateScalar) {
-        if (kRaw) in.gl[i] = g16[(p.t0 + row) * H + p.h];
-        else in.g[i] = g[(p.t0 + row) * H + p.h];
+        const uint32_t gi = __umul24(row, (uint32_t)H);
+        if (kRaw) in.gl[i] = (g16 + bbase)[gi];
+        else in.g[i] = (g + bbase)[gi];
       } else if (kGate == kGateChannel) {
-        if (kRaw) in.gl[i] = g16[base + row * rowstride + col];
-        else in.g[i] = g[base + row * rowstride + col];
+        const uint32_t gi = __umul24(row, rowstride) + col;
+        if (kRaw) in.gl[i] = (g16 + base)[gi];
+        else in.g[i] = (g + base)[gi];
       }
     }
   }
@@ -2771,6 +2791,10 @@ kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, cons
                                int32_t num_slots, const int32_t* slots, uint32_t flags, void* o,
                                void* workspace, hipStream_t stream) {
   const int H = sh->num_heads;
+  if (H > kMaxHeads) {
+    set_error("kda_chunk_fwd: at most %d heads are supported (got %d)", kMaxHeads, H);
+    return KDA_ERR_UNSUPPORTED;
+  }
   Workspace w = carve(workspace, T, N, H);
   const size_t cap = nchunks_max(T, N);
   const size_t items = cap * (size_t)H;
@@ -2822,6 +2846,10 @@ kda_status_t launch_chunk_mfma_bwd(const kda_shape_t* sh, int32_t T, int32_t N, 
                                    float* dbeta, float* d_initial, void* workspace,
                                    hipStream_t stream) {
   const int H = sh->num_heads;
+  if (H > kMaxHeads) {
+    set_error("kda_chunk_bwd: at most %d heads are supported (got %d)", kMaxHeads, H);
+    return KDA_ERR_UNSUPPORTED;
+  }
   Workspace w = carve(workspace, T, N, H, true);
   const size_t cap = nchunks_max(T, N);
   const size_t items = cap * (size_t)H;
