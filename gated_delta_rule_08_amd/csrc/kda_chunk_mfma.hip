@@ -249,13 +249,18 @@ __device__ __forceinline__ void lds_barrier() {
 // stride of the grid size.  The global loads of the next item are issued into
 // registers before the current item is computed, so they overlap its compute.
 constexpr int kPrepWaves = 8;
+
+// The prep keeps the running gate sums in base-2 units, G * log2(e), so that every
+// decay factor exp(G_a - G_b) is one hardware exp2 of a difference.
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr int kPrepThreads = 64 * kPrepWaves;
 
 struct PrepSmem {
   uint16_t K[C][KP];
   uint16_t Q[C][KP];
   uint16_t V[C][KP];
-  float G[C][GP];
+  float G[C][GP];        // running gate sums, in base-2 units (G * log2 e)
   float A[C][AP];        // beta-scaled strictly lower A_kk (backward: A_qk^T above it)
   float Tm[C][AP];       // (I + A_kk)^-1
   float tot[4][D];       // per-quarter column totals of the running gate sums
@@ -541,7 +546,7 @@ __device__ __forceinline__ void gram_pair(const PrepSmem& sm, int R, int J, bool
       runs_bf(sm.K[j], s, lg, kj);
       runs_f32(sm.G[j], s, lg, gj);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) fa[i] = kj[i] * fast_exp(gs[i] - gj[i]);  // rows j: exp(G_s - G_j)
+      for (int i = 0; i < 8; ++i) fa[i] = kj[i] * exp2_fast(gs[i] - gj[i]);  // rows j: exp(G_s - G_j)
       const bf16x8 ak = pack8(fa);
       acck = mfma(ak, sm.rk[R * 4 + s][lane], acck);
       accq = mfma(ak, sm.rq[R * 4 + s][lane], accq);
@@ -553,7 +558,7 @@ __device__ __forceinline__ void gram_pair(const PrepSmem& sm, int R, int J, bool
       float kk = 0.f, qk = 0.f;
       if (jd <= r) {
         for (int cc = 0; cc < D; ++cc) {
-          const float e = fast_exp(sm.G[r][cc] - sm.G[jd][cc]);
+          const float e = exp2_fast(sm.G[r][cc] - sm.G[jd][cc]);
           const float kv = ld_bf(sm.K[jd], cc) * e;
           kk += ld_bf(sm.K[r], cc) * kv;
           qk += ld_bf(sm.Q[r], cc) * kv;
@@ -603,7 +608,7 @@ __device__ __forceinline__ void prep_role(
       const int col = tid & 127, qt = tid >> 7;
       float x[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = prep_gate<kGate, kRaw>(in, i, 16 * qt + i, c, gate_min);
+      for (int i = 0; i < 16; ++i) x[i] = prep_gate<kGate, kRaw>(in, i, 16 * qt + i, c, gate_min) * kLog2e;
 #pragma unroll
       for (int i = 1; i < 16; ++i) x[i] += x[i - 1];
       sm.tot[qt][col] = x[15];
@@ -612,7 +617,7 @@ __device__ __forceinline__ void prep_role(
       for (int j = 0; j < qt; ++j) base += sm.tot[j][col];
 #pragma unroll
       for (int i = 0; i < 16; ++i) sm.G[16 * qt + i][col] = x[i] + base;
-      sm.es[qt][col] = fast_exp(x[0] + base);
+      sm.es[qt][col] = exp2_fast(x[0] + base);
       float sp = x[0] - x[15];  // spread of this channel inside block qt
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) sp = fmaxf(sp, __shfl_xor(sp, off, 64));
@@ -644,7 +649,7 @@ __device__ __forceinline__ void prep_role(
         runs_f32(sm.es[R], s, lg, e0);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float f = fast_exp(gr[i] - gs[i]);  // exp(G_r - G_sR) <= 1
+          const float f = exp2_fast(gr[i] - gs[i]);  // exp(G_r - G_sR) <= 1
           fk[i] = kr[i] * f;
           fq[i] = qr[i] * f;
           fg[i] = fq[i] * e0[i];                    // q_r exp(G_r)
@@ -668,7 +673,7 @@ __device__ __forceinline__ void prep_role(
         const int R = pi < 4 ? 3 : pi < 7 ? 2 : pi < 9 ? 1 : 0;
         const int J = pi < 4 ? 3 - pi : pi < 7 ? 6 - pi : pi < 9 ? 8 - pi : 0;
         f32x4 acck, accq;
-        const bool wide = fmaxf(sm.spr[2 * R], sm.spr[2 * R + 1]) > kMaxSpread;
+        const bool wide = fmaxf(sm.spr[2 * R], sm.spr[2 * R + 1]) > kMaxSpread * kLog2e;
         gram_pair(sm, R, J, wide, li, lg, lane, acck, accq);
         const int r = 16 * R + li;
         const float br = sm.bs[r];
@@ -794,8 +799,8 @@ __device__ __forceinline__ void prep_role(
         for (int qq = 0; qq < 8; ++qq) {
           const int j = 32 * s2 + kpos(lg, qq);
           const float kv = ld_bf(sm.K[j], ch), gv = sm.G[j][ch], bj = sm.bs[j];
-          fb[qq] = bj * kv * fast_exp(gv);
-          fd[qq] = kv * fast_exp(gl - gv);
+          fb[qq] = bj * kv * exp2_fast(gv);
+          fd[qq] = kv * exp2_fast(gl - gv);
           fv[qq] = bj * ld_bf(sm.V[j], ch);  // B operand of Ut for value tile `tile`
         }
         *reinterpret_cast<bf16x8*>(kd_out + ((size_t)(tile * 2 + s2) * 64 + lane) * 8) = pack8(fd);
@@ -825,7 +830,7 @@ __device__ __forceinline__ void prep_role(
         if (nt & 1) ut_out[((size_t)(nt >> 1) * 8 + tile) * 64 + lane] = pack_acc(ut_even, u);
         else ut_even = u;
       }
-      if (tid < D) reinterpret_cast<float*>(w.gc + ci * kGcBytes)[tid] = fast_exp(sm.G[C - 1][tid]);
+      if (tid < D) reinterpret_cast<float*>(w.gc + ci * kGcBytes)[tid] = exp2_fast(sm.G[C - 1][tid]);
       if constexpr (kBwd) {
         // -W^T (M = channel, K = row): W tiles with rows in the accumulator, packed in pairs
         f32x4 wr[4];
@@ -866,7 +871,7 @@ __device__ __forceinline__ void prep_role(
 #pragma unroll
           for (int qq = 0; qq < 8; ++qq) {
             const int j = 32 * s2 + kpos(lg, qq);
-            fq[qq] = ld_bf(sm.Q[j], ch) * fast_exp(sm.G[j][ch]);
+            fq[qq] = ld_bf(sm.Q[j], ch) * exp2_fast(sm.G[j][ch]);
           }
           *reinterpret_cast<bf16x8*>(w.qgt + ci * kKdBytes +
                                      ((size_t)(wave * 2 + s2) * 64 + lane) * 16) = pack8(fq);
@@ -880,7 +885,7 @@ __device__ __forceinline__ void prep_role(
 #pragma unroll
         for (int qq = 0; qq < 8; ++qq) {
           const int cc = 32 * sk + kpos(lg, qq);
-          fk[qq] = ld_bf(sm.K[r], cc) * fast_exp(sm.G[C - 1][cc] - sm.G[r][cc]);
+          fk[qq] = ld_bf(sm.K[r], cc) * exp2_fast(sm.G[C - 1][cc] - sm.G[r][cc]);
         }
         *reinterpret_cast<bf16x8*>(w.kdr + ci * kKdBytes + ((size_t)opi * 64 + lane) * 16) = pack8(fk);
       }
