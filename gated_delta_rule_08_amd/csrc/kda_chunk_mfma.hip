@@ -663,15 +663,14 @@ __device__ __forceinline__ void prep_role(
 
     if (prefetch) prep_load_part<kGate, kAdd, kRaw, 1>(in, pos, q, k, v, g, beta, H, tid);
 
-    // ---- gated Gram blocks (10 block pairs over 8 waves)
+    // ---- gated Gram blocks, then the diagonal blocks of T = (I + A_kk)^-1.
+    // T_JJ = (I + A_JJ)^-1 by right-looking forward substitution (wave J, lane =
+    // column): once x[m] is final it is eliminated from every later row at once,
+    // so the dependency chain is 15 steps deep.
     {
+      const int wv = __builtin_amdgcn_readfirstlane(wave);  // scalar role choices
       uint16_t* aq_out = reinterpret_cast<uint16_t*>(w.aq + ci * kAqBytes);
-      for (int pi = wave; pi < 10; pi += kPrepWaves) {
-        // pairs in the order (3,3) (3,2) (3,1) (3,0) (2,2) (2,1) (2,0) (1,1) (1,0) (0,0),
-        // computed rather than read from a table (a memory read would wait for
-        // the next item's prefetched loads)
-        const int R = pi < 4 ? 3 : pi < 7 ? 2 : pi < 9 ? 1 : 0;
-        const int J = pi < 4 ? 3 - pi : pi < 7 ? 6 - pi : pi < 9 ? 8 - pi : 0;
+      auto gram = [&](int R, int J) {
         f32x4 acck, accq;
         const bool wide = fmaxf(sm.spr[2 * R], sm.spr[2 * R + 1]) > kMaxSpread * kLog2e;
         gram_pair(sm, R, J, wide, li, lg, lane, acck, accq);
@@ -707,33 +706,58 @@ __device__ __forceinline__ void prep_role(
         *reinterpret_cast<uint2*>(dst) =
             make_uint2((uint32_t)f32_to_bf16(qv[0]) | ((uint32_t)f32_to_bf16(qv[1]) << 16),
                        (uint32_t)f32_to_bf16(qv[2]) | ((uint32_t)f32_to_bf16(qv[3]) << 16));
-      }
-      // blocks above the diagonal stored by the scan: (R, J) = (0,1), (2,3)
-      if (wave == 7) {
+      };
+      auto invert_diag = [&](int J) {
+        if (lane < 16) {
+          const int sJ = 16 * J;
+          float x[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) x[i] = i == lane ? 1.f : 0.f;
+#pragma unroll
+          for (int m = 0; m < 15; ++m)
+#pragma unroll
+            for (int i = m + 1; i < 16; ++i) x[i] -= sm.A[sJ + i][sJ + m] * x[m];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sm.Tm[sJ + i][sJ + lane] = x[i];
+        }
+      };
+      auto zero_aq_upper = [&]() {
+        // blocks above the diagonal stored by the scan: (R, J) = (0,1), (2,3)
         const uint2 z = make_uint2(0, 0);
         *reinterpret_cast<uint2*>(aq_out + ((size_t)(0 * 2 + 0) * 64 + lane) * 8 + 4) = z;
         *reinterpret_cast<uint2*>(aq_out + ((size_t)(2 * 2 + 1) * 64 + lane) * 8 + 4) = z;
+      };
+      if constexpr (!kAdd && !kBwd) {
+        // Round 1: wave w < 4 forms the diagonal pair (w, w), waves 4..7 the
+        // pairs (1,0) (2,1) (3,2) (2,0).  Round 2: waves 0..3 invert their own
+        // diagonal block (no barrier: the wave wrote it itself, and a wave's LDS
+        // accesses are done in order) while waves 4 and 5 form (3,1) and (3,0),
+        // which only the second and third off-diagonal distances need.
+        if (wv < 4) {
+          gram(wv, wv);
+        } else {
+          const int x = wv - 4;
+          gram(x == 3 ? 2 : x + 1, x == 3 ? 0 : x);
+        }
+        if (wv == 7) zero_aq_upper();
+        if (wv < 4) invert_diag(wv);
+        else if (wv < 6) gram(3, 5 - wv);  // wave 4: (3,1), wave 5: (3,0)
+        if (prefetch) prep_load_part<kGate, kAdd, kRaw, 2>(in, pos, q, k, v, g, beta, H, tid);
+      } else {
+        // The variants that hold more registers take the 10 pairs in the order
+        // (3,3) (3,2) (3,1) (3,0) (2,2) (2,1) (2,0) (1,1) (1,0) (0,0), computed
+        // rather than read from a table (a memory read would wait for the next
+        // item's prefetched loads), and invert after a barrier.
+        for (int pi = wv; pi < 10; pi += kPrepWaves) {
+          const int R = pi < 4 ? 3 : pi < 7 ? 2 : pi < 9 ? 1 : 0;
+          const int J = pi < 4 ? 3 - pi : pi < 7 ? 6 - pi : pi < 9 ? 8 - pi : 0;
+          gram(R, J);
+        }
+        if (wv == 7) zero_aq_upper();
+        lds_barrier();
+        if (prefetch) prep_load_part<kGate, kAdd, kRaw, 2>(in, pos, q, k, v, g, beta, H, tid);
+        if (wv < 4) invert_diag(wv);
       }
-    }
-    lds_barrier();
-
-    if (prefetch) prep_load_part<kGate, kAdd, kRaw, 2>(in, pos, q, k, v, g, beta, H, tid);
-
-    // ---- T = (I + A_kk)^-1 in 16x16 blocks.  Diagonal blocks: T_JJ = (I + A_JJ)^-1
-    // by right-looking forward substitution (wave J, lane = column): once x[m]
-    // is final it is eliminated from every later row at once, so the dependency
-    // chain is 15 steps deep.
-    if (wave < 4 && lane < 16) {
-      const int sJ = 16 * wave;
-      float x[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = i == lane ? 1.f : 0.f;
-#pragma unroll
-      for (int m = 0; m < 15; ++m)
-#pragma unroll
-        for (int i = m + 1; i < 16; ++i) x[i] -= sm.A[sJ + i][sJ + m] * x[m];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sm.Tm[sJ + i][sJ + lane] = x[i];
     }
     lds_barrier();
     if (prefetch) prep_load_part<kGate, kAdd, kRaw, 3>(in, pos, q, k, v, g, beta, H, tid);
@@ -1702,90 +1726,124 @@ __device__ __forceinline__ void scan_state_role(int blk, uint8_t* smem_raw, int3
 // State scan with the outputs formed beside it (few chains).  A workgroup owns
 // 16 state columns of one (sequence, head).  Wave 0 carries the state as in
 // scan_state_role and, per chunk c, leaves S_c (at the chunk start) and U_c in
-// LDS as the bf16 B operands it forms anyway; wave 1 forms O_c = (Q*Gam)_c S_c +
-// A_qk,c U_c one step later, with the MFMA order of the single-pass scan, from
-// Q*Gam and A_qk that it loads from the workspace into registers two chunks
-// ahead, and stores the chunk's 64 x 16 outputs as 16-byte row pieces staged in
-// LDS; waves 2..7 keep the three-buffer ring of the chain's operands filled.
-// Nothing of S or U goes through memory, and no separate output launch re-reads
-// the chunk operands.
-constexpr int kOutLoaders = 6;
-constexpr int kScanOutThreads = 64 * (2 + kOutLoaders);
+// LDS as the bf16 B operands it forms anyway; waves 1 and 2 form the rows 0-31
+// and 32-63 of O_c = (Q*Gam)_c S_c + A_qk,c U_c one step later, with the MFMA
+// order of the single-pass scan, from Q*Gam and A_qk tiles that they load from
+// the workspace into registers two chunks ahead, and store their 32 x 16 outputs
+// as 16-byte row pieces staged in LDS; waves 3..7 keep a four-buffer ring of the
+// chain's operands filled.  Nothing of S or U goes through memory, and no
+// separate output launch re-reads the chunk operands.
+constexpr int kScanOutThreads = 512;
+constexpr int kOutRing = 4;
 
 struct ScanOutLds {
-  StateLds<1, 1>::Buf buf[kStateRing];
+  // one chunk's operands; 1 KiB pieces in the loaders' order (Gam_C is padded to
+  // a whole piece so that every lane of its loader stores)
+  struct Buf {
+    bf16x8 wn[16][64];    // [m*4 + s][lane]
+    bf16x8 kd[16][64];    // [t*2 + s'][lane]
+    bf16x8 ut[2][1][64];  // [row tile pair][this group's column tile][lane]
+    f32x4 gc[32];         // Gam_C
+    f32x4 gc_pad[32];
+  };
+  Buf buf[kOutRing];
   bf16x8 xs[2][6][64];  // per chunk parity: S_c as 4 B operands (K = dk), then U_c as 2 (K = rows)
-  uint16_t ob[C][16];   // the output wave's bf16 outputs of one chunk
+  uint16_t ob[C][16];   // the output waves' bf16 outputs of one chunk
 };
 
-__global__ __launch_bounds__(kScanOutThreads) void scan_out_kernel(
-    int32_t N, int H, Workspace w, float* __restrict__ states, int32_t num_slots,
-    const int32_t* __restrict__ slots, uint32_t flags, uint16_t* __restrict__ o) {
-  extern __shared__ __align__(16) uint8_t smem_raw[];
-  using Buf = StateLds<1, 1>::Buf;
-  constexpr int LW = kOutLoaders;
+__device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_t N, int H,
+                                              const Workspace& w, float* __restrict__ states,
+                                              int32_t num_slots, const int32_t* __restrict__ slots,
+                                              uint32_t flags, uint16_t* __restrict__ o) {
+  using Buf = ScanOutLds::Buf;
+  constexpr int kOutWaves = 2;
+  constexpr int LW = kScanOutThreads / 64 - 1 - kOutWaves;
   ScanOutLds& sl = *reinterpret_cast<ScanOutLds*>(smem_raw);
   const int NH = N * H;
-  const int head_lin = blockIdx.x % NH;
-  const int group = blockIdx.x / NH;  // 16-column tile of the state
+  const int head_lin = blk % NH;
+  const int group = blk / NH;  // 16-column tile of the state
   const int n = head_lin / H, h = head_lin - n * H;
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nch = w.seq_nch[n];
   const int cbase = w.chunk_off[n];
 
-  if (wave >= 2) {
+  if (wave > kOutWaves) {
     // ------------------------------------------------------------ loaders
-    const int lw = wave - 2;
-    const int off = lane * 16;
-    constexpr int kPieces = 32 + 2;  // 1 KiB pieces: -W, Kd^T, this group's two Ut pieces
-    auto issue = [&](size_t ci, Buf* dst) {
-      const uint8_t* wn = w.wn + ci * kWnBytes;
-      const uint8_t* kd = w.kd + ci * kKdBytes;
-      const uint8_t* ut = w.ut + ci * kUtBytes;
+    // Pieces of 1 KiB, dealt to the loaders in turn: 0-15 -W, 16-31 Kd^T, 32-33
+    // this group's two Ut pieces, 34 Gam_C (512 B, copied twice so that every lane
+    // has a part).  A buffer holds them in this order, piece p at byte 1024 p.
+    // The copies go straight to LDS, three chunks ahead: a chunk's copies take
+    // longer than one chunk step to land.
+    const int lw = wave - kOutWaves - 1;
+    constexpr int kPieces = 35;
+    constexpr int kPer = (kPieces + LW - 1) / LW;
+    static_assert(kPer * LW == kPieces, "every loader takes the same number of pieces");
+    static_assert(sizeof(Buf) == kPieces * 1024, "piece p at byte 1024 p");
+    // per piece: its array's address at chunk-head 0, that array's stride per
+    // chunk-head, and the lane's byte offset (fixed for the wave)
+    const uint8_t* pbase[kPer];
+    uint32_t pstride[kPer], ploff[kPer];
 #pragma unroll
-      for (int i = 0; i < (kPieces + LW - 1) / LW; ++i) {
-        const int p = lw + LW * i;  // wave-uniform
-        if (p < 16) dma16(wn + p * 1024 + off, &dst->wn[p][0]);
-        else if (p < 32) dma16(kd + (p - 16) * 1024 + off, &dst->kd[p - 16][0]);
-        else if (p < kPieces) {
-          const int mp = p - 32;
-          dma16(ut + (size_t)((mp * 8 + group) * 64) * 16 + off, &dst->ut[mp][0][0]);
-        }
+    for (int i = 0; i < kPer; ++i) {
+      const int p = lw + LW * i;  // wave-uniform
+      if (p < 16) {
+        pbase[i] = w.wn + p * 1024;
+        pstride[i] = (uint32_t)kWnBytes;
+      } else if (p < 32) {
+        pbase[i] = w.kd + (p - 16) * 1024;
+        pstride[i] = (uint32_t)kKdBytes;
+      } else if (p < 34) {
+        pbase[i] = w.ut + (size_t)((p - 32) * 8 + group) * 1024;
+        pstride[i] = (uint32_t)kUtBytes;
+      } else {
+        pbase[i] = w.gc;
+        pstride[i] = (uint32_t)kGcBytes;
       }
-      if (lw == LW - 1 && lane < 32) dma16(w.gc + ci * kGcBytes + off, &dst->gc[0]);
+      ploff[i] = (uint32_t)(p < 34 ? lane : (lane & 31)) * 16;
+    }
+    auto issue = [&](int c) {
+      const size_t ci = (size_t)(cbase + c) * H + h;
+      uint8_t* dst = reinterpret_cast<uint8_t*>(&sl.buf[c % kOutRing]);
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) dma16(pbase[i] + ci * pstride[i] + ploff[i], dst + (lw + LW * i) * 1024);
     };
-    const int mine = (kPieces - lw + LW - 1) / LW + (lw == LW - 1 ? 1 : 0);
-    constexpr int kAhead = kStateRing - 1;
-    static_assert(((kPieces + LW - 1) / LW + 1) * (kAhead - 1) <= 15, "graded wait range");
-    for (int c = 0; c < kAhead && c < nch; ++c) issue((size_t)(cbase + c) * H + h, &sl.buf[c]);
-    wait_vm(mine * (min(nch, kAhead) - 1 > 0 ? min(nch, kAhead) - 1 : 0));  // chunk 0 landed
+    constexpr int kAhead = kOutRing - 1;
+    static_assert(kPer * (kAhead - 1) <= 23, "graded wait range");
+    for (int c = 0; c < kAhead && c < nch; ++c) issue(c);
+    wait_vm(kPer * (min(nch, kAhead) - 1 > 0 ? min(nch, kAhead) - 1 : 0));  // chunk 0 landed
     lds_barrier();
     for (int lc = 0; lc < nch; ++lc) {
       const int nxt = lc + kAhead;
-      if (nxt < nch) issue((size_t)(cbase + nxt) * H + h, &sl.buf[nxt % kStateRing]);
+      if (nxt < nch) issue(nxt);
       const int newest = min(nch - 1, nxt) - (lc + 1);
-      wait_vm(newest > 0 ? mine * newest : 0);
+      wait_vm(newest > 0 ? kPer * newest : 0);
       lds_barrier();
     }
     return;
   }
 
-  if (wave == 1) {
+  if (wave >= 1) {
     // ------------------------------------------------------------ outputs
-    // chunk c's Q*Gam and A_qk tiles sit in register set c % 2, loaded at step c - 1
-    bf16x8 qg0[16], aq0[6], qg1[16], aq1[6];
+    // rows 32 hf .. 32 hf + 31; chunk c's Q*Gam and A_qk tiles sit in register set
+    // c % 2, loaded at step c - 1.  A_qk tiles (block row R, column half s'): half
+    // 0 needs (0,0) (1,0); half 1 needs (2,0) (2,1) (3,0) (3,1) (rows 0-31 have no
+    // entries in columns 32-63).
+    const int hf = wave - 1;
+    bf16x8 qg0[8], aq0[4], qg1[8], aq1[4];
     auto load_ops = [&](bf16x8* qgr, bf16x8* aqr, int c) {
       const size_t ci = (size_t)(cbase + c) * H + h;
-      const bf16x8* qg = reinterpret_cast<const bf16x8*>(w.qg + ci * kQgBytes);
+      const bf16x8* qg = reinterpret_cast<const bf16x8*>(w.qg + ci * kQgBytes) + 8 * hf * 64;
       const bf16x8* aq = reinterpret_cast<const bf16x8*>(w.aq + ci * kAqBytes);
 #pragma unroll
-      for (int x = 0; x < 16; ++x) qgr[x] = qg[x * 64 + lane];
+      for (int x = 0; x < 8; ++x) qgr[x] = qg[x * 64 + lane];
+      // four tiles on both halves (half 0 uses the first two), so that the waits
+      // for a register set count the same loads on both
 #pragma unroll
-      for (int x = 0; x < 6; ++x) aqr[x] = aq[(x < 2 ? 2 * x : x + 2) * 64 + lane];  // [0],[2],[4..7]
+      for (int x = 0; x < 4; ++x) aqr[x] = aq[(hf ? 4 + x : 2 * x) * 64 + lane];
     };
     const int start = w.seq_start[n], end = w.seq_end[n];
-    // O_c from slot c % 2 of the exchange and the operand tiles qgr, aqr
+    // rows of O_c from slot c % 2 of the exchange and the operand tiles qgr, aqr
     auto out_chunk = [&](const bf16x8* qgr, const bf16x8* aqr, int c) {
       const bf16x8(*x)[64] = sl.xs[c & 1];
       bf16x8 sb[4], ub[2];
@@ -1793,48 +1851,53 @@ __global__ __launch_bounds__(kScanOutThreads) void scan_out_kernel(
       for (int s2 = 0; s2 < 4; ++s2) sb[s2] = x[s2][lane];
       ub[0] = x[4][lane];
       ub[1] = x[5][lane];
-      f32x4 O[4];
+      f32x4 O[2];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) O[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int mm = 0; mm < 2; ++mm) O[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s2 = 0; s2 < 4; ++s2)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) O[m] = mfma(qgr[m * 4 + s2], sb[s2], O[m]);
-      // A_qk rows 0-31 have no entries in columns 32-63
-      O[0] = mfma(aqr[0], ub[0], O[0]);
-      O[1] = mfma(aqr[1], ub[0], O[1]);
-      O[2] = mfma(aqr[2], ub[0], O[2]);
-      O[3] = mfma(aqr[4], ub[0], O[3]);
-      O[2] = mfma(aqr[3], ub[1], O[2]);
-      O[3] = mfma(aqr[5], ub[1], O[3]);
-      // stage as bf16 rows of 16 columns, then store whole 16-byte row pieces (this
-      // wave alone writes and reads the staging tile, in program order)
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) sl.ob[16 * m + 4 * lg + jj][li] = f32_to_bf16(O[m][jj]);
-      const int t0 = start + c * C, rows = min(C, end - t0);
-#pragma unroll
-      for (int xx = 0; xx < 2; ++xx) {
-        const int pc = lane + 64 * xx, r = pc >> 1, half = pc & 1;
-        const uint4 v4 = *reinterpret_cast<const uint4*>(&sl.ob[r][8 * half]);
-        if (r < rows)
-          *reinterpret_cast<uint4*>(o + ((size_t)(t0 + r) * H + h) * D + 16 * group + 8 * half) = v4;
+        for (int mm = 0; mm < 2; ++mm) O[mm] = mfma(qgr[mm * 4 + s2], sb[s2], O[mm]);
+      if (hf == 0) {
+        O[0] = mfma(aqr[0], ub[0], O[0]);
+        O[1] = mfma(aqr[1], ub[0], O[1]);
+      } else {
+        O[0] = mfma(aqr[0], ub[0], O[0]);
+        O[1] = mfma(aqr[2], ub[0], O[1]);
+        O[0] = mfma(aqr[1], ub[1], O[0]);
+        O[1] = mfma(aqr[3], ub[1], O[1]);
       }
+      // stage as bf16 rows of 16 columns, then store whole 16-byte row pieces (each
+      // wave writes and reads only its own rows of the staging tile, in program order)
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          sl.ob[32 * hf + 16 * mm + 4 * lg + jj][li] = f32_to_bf16(O[mm][jj]);
+      const int t0 = start + c * C, rows = min(C, end - t0);
+      const int r = 32 * hf + (lane >> 1), half = lane & 1;
+      const uint4 v4 = *reinterpret_cast<const uint4*>(&sl.ob[r][8 * half]);
+      if (r < rows)
+        *reinterpret_cast<uint4*>(o + ((size_t)(t0 + r) * H + h) * D + 16 * group + 8 * half) = v4;
     };
-    if (nch > 0) load_ops(qg0, aq0, 0);
-    if (nch > 1) load_ops(qg1, aq1, 1);
+    // loads on every path (past the last chunk: the last again), so that the wait
+    // for one register set counts the other set's loads
+    const int last = nch - 1;
+    if (nch > 0) {
+      load_ops(qg0, aq0, 0);
+      load_ops(qg1, aq1, min(1, last));
+    }
     lds_barrier();
     // after the barrier that ends chunk c: O_c, then chunk c + 2's tiles into the set
     // just used; unrolled by two so that every register set is named
     for (int c = 0; c < nch; c += 2) {
       lds_barrier();  // end of chunk c
       out_chunk(qg0, aq0, c);
-      if (c + 2 < nch) load_ops(qg0, aq0, c + 2);
+      load_ops(qg0, aq0, min(c + 2, last));
       if (c + 1 < nch) {
         lds_barrier();  // end of chunk c + 1
         out_chunk(qg1, aq1, c + 1);
-        if (c + 3 < nch) load_ops(qg1, aq1, c + 3);
+        load_ops(qg1, aq1, min(c + 3, last));
       }
     }
     return;
@@ -1857,7 +1920,7 @@ __global__ __launch_bounds__(kScanOutThreads) void scan_out_kernel(
   }
   lds_barrier();
   for (int lc = 0; lc < nch; ++lc) {
-    const Buf& B = sl.buf[lc % kStateRing];
+    const Buf& B = sl.buf[lc % kOutRing];
     bf16x8(*x)[64] = sl.xs[lc & 1];
     f32x4 U[4];
     unpack_acc(B.ut[0][0][lane], U[0], U[1]);
@@ -1902,6 +1965,13 @@ __global__ __launch_bounds__(kScanOutThreads) void scan_out_kernel(
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) Sg[(size_t)(16 * t + 4 * lg + jj) * D + col] = S[t][jj];
   }
+}
+
+__global__ __launch_bounds__(kScanOutThreads) void scan_out_kernel(
+    int32_t N, int H, Workspace w, float* __restrict__ states, int32_t num_slots,
+    const int32_t* __restrict__ slots, uint32_t flags, uint16_t* __restrict__ o) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  scan_out_role(blockIdx.x, smem_raw, N, H, w, states, num_slots, slots, flags, o);
 }
 
 kda_status_t launch_scan_out(int32_t N, int H, const Workspace& w, float* states,
