@@ -1808,16 +1808,18 @@ __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_
 #pragma unroll
       for (int i = 0; i < kPer; ++i) dma16(pbase[i] + ci * pstride[i] + ploff[i], dst + (lw + LW * i) * 1024);
     };
+    // Chunk c + 1 must have landed by the barrier that ends step c - 1 (the state
+    // wave reads it at the end of step c), so each wait leaves only the newest
+    // chunk's copies in flight.
     constexpr int kAhead = kOutRing - 1;
-    static_assert(kPer * (kAhead - 1) <= 23, "graded wait range");
+    static_assert(kPer * (kAhead - 2) <= 23, "graded wait range");
     for (int c = 0; c < kAhead && c < nch; ++c) issue(c);
-    wait_vm(kPer * (min(nch, kAhead) - 1 > 0 ? min(nch, kAhead) - 1 : 0));  // chunk 0 landed
+    wait_vm(kPer * (min(nch, kAhead) - min(nch, kAhead - 1)));  // chunks 0 and 1 landed
     lds_barrier();
     for (int lc = 0; lc < nch; ++lc) {
       const int nxt = lc + kAhead;
       if (nxt < nch) issue(nxt);
-      const int newest = min(nch - 1, nxt) - (lc + 1);
-      wait_vm(newest > 0 ? kPer * newest : 0);
+      wait_vm(kPer * (min(nch, nxt + 1) - min(nch, nxt)));  // chunk lc + 2 landed
       lds_barrier();
     }
     return;
@@ -1919,25 +1921,29 @@ __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_
     for (int t = 0; t < 8; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   lds_barrier();
-  for (int lc = 0; lc < nch; ++lc) {
-    const Buf& B = sl.buf[lc % kOutRing];
-    bf16x8(*x)[64] = sl.xs[lc & 1];
-    f32x4 U[4];
+  // The operands of chunk c are read at the end of step c - 1, after its products
+  // are issued: they land while the wave waits at the step's barrier (which
+  // waits for its LDS writes, not for these reads).
+  f32x4 U[4];
+  bf16x8 a_wn[16], a_kd[16];
+  f32x4 gcv[8];
+  auto read_ops = [&](int c) {
+    const Buf& B = sl.buf[c % kOutRing];
     unpack_acc(B.ut[0][0][lane], U[0], U[1]);
     unpack_acc(B.ut[1][0][lane], U[2], U[3]);
-    bf16x8 a_wn[16];
 #pragma unroll
     for (int xx = 0; xx < 16; ++xx) a_wn[xx] = B.wn[xx][lane];
-    bf16x8 sb[4];
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) sb[s2] = pack_acc(S[2 * s2], S[2 * s2 + 1]);
-    bf16x8 a_kd[16];
-    f32x4 gcv[8];
 #pragma unroll
     for (int xx = 0; xx < 16; ++xx) a_kd[xx] = B.kd[xx][lane];
 #pragma unroll
     for (int t = 0; t < 8; ++t) gcv[t] = B.gc[4 * t + lg];
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  if (nch > 0) read_ops(0);
+  for (int lc = 0; lc < nch; ++lc) {
+    bf16x8(*x)[64] = sl.xs[lc & 1];
+    bf16x8 sb[4];
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) sb[s2] = pack_acc(S[2 * s2], S[2 * s2 + 1]);
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) x[s2][lane] = sb[s2];
     // U = Ut - W S   (consecutive MFMAs go to different accumulators)
@@ -1957,7 +1963,10 @@ __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int t = 0; t < 8; ++t) S[t] = mfma(a_kd[t * 2 + s2], ub[s2], S[t]);
-    lds_barrier();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the exchange tiles are written
+    if (lc + 1 < nch) read_ops(lc + 1);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   }
   if (slot_ok && (flags & KDA_WRITE_FINAL_STATE)) {
 #pragma unroll
