@@ -1729,10 +1729,11 @@ __device__ __forceinline__ void scan_state_role(int blk, uint8_t* smem_raw, int3
 // LDS as the bf16 B operands it forms anyway; waves 1 and 2 form the rows 0-31
 // and 32-63 of O_c = (Q*Gam)_c S_c + A_qk,c U_c one step later, with the MFMA
 // order of the single-pass scan, from Q*Gam and A_qk tiles that they load from
-// the workspace into registers two chunks ahead, and store their 32 x 16 outputs
-// as 16-byte row pieces staged in LDS; waves 3..7 keep a four-buffer ring of the
-// chain's operands filled.  Nothing of S or U goes through memory, and no
-// separate output launch re-reads the chunk operands.
+// the workspace into registers two chunks ahead, and leave their 32 x 16 outputs
+// in LDS as bf16 rows, which wave 3 stores as 16-byte row pieces one step later;
+// waves 4..7 keep a four-buffer ring of the chain's operands filled.  Nothing of S
+// or U goes through memory, and no separate output launch re-reads the chunk
+// operands.
 constexpr int kScanOutThreads = 512;
 constexpr int kOutRing = 4;
 
@@ -1748,7 +1749,7 @@ struct ScanOutLds {
   };
   Buf buf[kOutRing];
   bf16x8 xs[2][6][64];  // per chunk parity: S_c as 4 B operands (K = dk), then U_c as 2 (K = rows)
-  uint16_t ob[C][16];   // the output waves' bf16 outputs of one chunk
+  uint16_t ob[2][C][16];  // per chunk parity: the output waves' bf16 outputs of the chunk
 };
 
 __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_t N, int H,
@@ -1757,7 +1758,8 @@ __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_
                                               uint32_t flags, uint16_t* __restrict__ o) {
   using Buf = ScanOutLds::Buf;
   constexpr int kOutWaves = 2;
-  constexpr int LW = kScanOutThreads / 64 - 1 - kOutWaves;
+  constexpr int kStoreWave = 1 + kOutWaves;
+  constexpr int LW = kScanOutThreads / 64 - 2 - kOutWaves;
   ScanOutLds& sl = *reinterpret_cast<ScanOutLds*>(smem_raw);
   const int NH = N * H;
   const int head_lin = blk % NH;
@@ -1768,17 +1770,17 @@ __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_
   const int nch = w.seq_nch[n];
   const int cbase = w.chunk_off[n];
 
-  if (wave > kOutWaves) {
+  if (wave > kStoreWave) {
     // ------------------------------------------------------------ loaders
     // Pieces of 1 KiB, dealt to the loaders in turn: 0-15 -W, 16-31 Kd^T, 32-33
     // this group's two Ut pieces, 34 Gam_C (512 B, copied twice so that every lane
     // has a part).  A buffer holds them in this order, piece p at byte 1024 p.
     // The copies go straight to LDS, three chunks ahead: a chunk's copies take
     // longer than one chunk step to land.
-    const int lw = wave - kOutWaves - 1;
+    const int lw = wave - kStoreWave - 1;
     constexpr int kPieces = 35;
     constexpr int kPer = (kPieces + LW - 1) / LW;
-    static_assert(kPer * LW == kPieces, "every loader takes the same number of pieces");
+    const int mine = (kPieces - lw + LW - 1) / LW;  // this loader's pieces
     static_assert(sizeof(Buf) == kPieces * 1024, "piece p at byte 1024 p");
     // per piece: its array's address at chunk-head 0, that array's stride per
     // chunk-head, and the lane's byte offset (fixed for the wave)
@@ -1806,7 +1808,8 @@ __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_
       const size_t ci = (size_t)(cbase + c) * H + h;
       uint8_t* dst = reinterpret_cast<uint8_t*>(&sl.buf[c % kOutRing]);
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) dma16(pbase[i] + ci * pstride[i] + ploff[i], dst + (lw + LW * i) * 1024);
+      for (int i = 0; i < kPer; ++i)
+        if (lw + LW * i < kPieces) dma16(pbase[i] + ci * pstride[i] + ploff[i], dst + (lw + LW * i) * 1024);
     };
     // Chunk c + 1 must have landed by the barrier that ends step c - 1 (the state
     // wave reads it at the end of step c), so each wait leaves only the newest
@@ -1814,14 +1817,42 @@ __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_
     constexpr int kAhead = kOutRing - 1;
     static_assert(kPer * (kAhead - 2) <= 23, "graded wait range");
     for (int c = 0; c < kAhead && c < nch; ++c) issue(c);
-    wait_vm(kPer * (min(nch, kAhead) - min(nch, kAhead - 1)));  // chunks 0 and 1 landed
+    wait_vm(mine * (min(nch, kAhead) - min(nch, kAhead - 1)));  // chunks 0 and 1 landed
     lds_barrier();
     for (int lc = 0; lc < nch; ++lc) {
       const int nxt = lc + kAhead;
       if (nxt < nch) issue(nxt);
-      wait_vm(kPer * (min(nch, nxt + 1) - min(nch, nxt)));  // chunk lc + 2 landed
+      wait_vm(mine * (min(nch, nxt + 1) - min(nch, nxt)));  // chunk lc + 2 landed
       lds_barrier();
     }
+    lds_barrier();  // the closing barrier of the output and store waves
+    return;
+  }
+
+  const int start = w.seq_start[n], end = w.seq_end[n];
+  if (wave == kStoreWave) {
+    // ------------------------------------------------------------ stores
+    // Chunk c's outputs, staged by the output waves during step c + 1, go out as
+    // 16-byte row pieces during step c + 2 (the staging tile has a slot per chunk
+    // parity), so the output waves never wait on a store.
+    auto store_chunk = [&](int c) {
+      const int t0 = start + c * C, rows = min(C, end - t0);
+#pragma unroll
+      for (int xx = 0; xx < 2; ++xx) {
+        const int pc = lane + 64 * xx, r = pc >> 1, half = pc & 1;
+        const uint4 v4 = *reinterpret_cast<const uint4*>(&sl.ob[c & 1][r][8 * half]);
+        if (r < rows)
+          *reinterpret_cast<uint4*>(o + ((size_t)(t0 + r) * H + h) * D + 16 * group + 8 * half) = v4;
+      }
+    };
+    lds_barrier();
+    for (int lc = 0; lc < nch; ++lc) {
+      if (lc >= 2) store_chunk(lc - 2);
+      lds_barrier();
+    }
+    if (nch >= 2) store_chunk(nch - 2);
+    lds_barrier();  // the last chunk's outputs are staged
+    if (nch >= 1) store_chunk(nch - 1);
     return;
   }
 
@@ -1844,7 +1875,6 @@ __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_
 #pragma unroll
       for (int x = 0; x < 4; ++x) aqr[x] = aq[(hf ? 4 + x : 2 * x) * 64 + lane];
     };
-    const int start = w.seq_start[n], end = w.seq_end[n];
     // rows of O_c from slot c % 2 of the exchange and the operand tiles qgr, aqr
     auto out_chunk = [&](const bf16x8* qgr, const bf16x8* aqr, int c) {
       const bf16x8(*x)[64] = sl.xs[c & 1];
@@ -1869,18 +1899,12 @@ __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_
         O[0] = mfma(aqr[1], ub[1], O[0]);
         O[1] = mfma(aqr[3], ub[1], O[1]);
       }
-      // stage as bf16 rows of 16 columns, then store whole 16-byte row pieces (each
-      // wave writes and reads only its own rows of the staging tile, in program order)
+      // stage as bf16 rows of 16 columns for the store wave
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
-          sl.ob[32 * hf + 16 * mm + 4 * lg + jj][li] = f32_to_bf16(O[mm][jj]);
-      const int t0 = start + c * C, rows = min(C, end - t0);
-      const int r = 32 * hf + (lane >> 1), half = lane & 1;
-      const uint4 v4 = *reinterpret_cast<const uint4*>(&sl.ob[r][8 * half]);
-      if (r < rows)
-        *reinterpret_cast<uint4*>(o + ((size_t)(t0 + r) * H + h) * D + 16 * group + 8 * half) = v4;
+          sl.ob[c & 1][32 * hf + 16 * mm + 4 * lg + jj][li] = f32_to_bf16(O[mm][jj]);
     };
     // loads on every path (past the last chunk: the last again), so that the wait
     // for one register set counts the other set's loads
@@ -1902,6 +1926,7 @@ __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_
         load_ops(qg1, aq1, min(c + 3, last));
       }
     }
+    lds_barrier();  // the last chunk's outputs are staged for the store wave
     return;
   }
 
@@ -1968,6 +1993,7 @@ __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   }
+  lds_barrier();  // the closing barrier of the output and store waves
   if (slot_ok && (flags & KDA_WRITE_FINAL_STATE)) {
 #pragma unroll
     for (int t = 0; t < 8; ++t)
