@@ -1250,247 +1250,6 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(1, 1
   }
 }
 
-// Warp-specialised scan: CW compute waves own the state columns (NT tiles of
-// 16 each) and touch only LDS and registers; LW loader waves copy the next
-// chunk's operands (-W, Q*Gam, Kd^T, A_qk, the group's Ut tiles, Gam_C) into
-// LDS with direct global->LDS loads and store the previous chunk's staged
-// outputs.  The copy rate of a CU grows with the number of waves issuing
-// copies, and the compute waves never stall on issuing them.  One LDS barrier
-// per chunk separates the steps: in step c the compute waves read buffer c % 2
-// and write staging tile c % 2, while the loaders store staging tile (c-1) % 2
-// and fill buffer (c + 1) % 2.
-template <int CW, int NT>
-struct ScanLds {
-  static constexpr int kTiles = CW * NT;
-  static constexpr int kCols = 16 * kTiles;
-  struct Buf {
-    bf16x8 wn[16][64];         // [m*4 + s][lane]
-    bf16x8 qg[16][64];         // [m*4 + s][lane]
-    bf16x8 kd[16][64];         // [t*2 + s'][lane]
-    bf16x8 aq[8][64];          // [m*2 + s'][lane]
-    bf16x8 ut[2][kTiles][64];  // [row tile pair][local column tile][lane]
-    f32x4 gc[32];              // Gam_C
-  };
-  Buf buf[2];
-  uint16_t out[2][C][kCols];   // staged bf16 outputs of a chunk
-};
-
-template <int CW, int NT, int LW>
-__device__ __forceinline__ void scan_role(int b, uint8_t* smem, int32_t N, int H, const Workspace& w,
-                                          float* __restrict__ states, int32_t num_slots,
-                                          const int32_t* __restrict__ slots, uint32_t flags,
-                                          uint16_t* __restrict__ o) {
-  using L = ScanLds<CW, NT>;
-  using Buf = typename L::Buf;
-  constexpr int kTiles = L::kTiles, kCols = L::kCols;
-  L& sl = *reinterpret_cast<L*>(smem);
-  const int NH = N * H;
-  const int head_lin = b % NH;
-  const int group = b / NH;
-  const int n = head_lin / H, h = head_lin - n * H;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
-  const int start = w.seq_start[n], end = w.seq_end[n], nch = w.seq_nch[n];
-  const int cbase = w.chunk_off[n];
-
-  if (wave >= CW) {
-    // ------------------------------------------------------------ loaders
-    const int lw = wave - CW, ltid = tid - 64 * CW;
-    const int off = lane * 16;
-    constexpr int kPieces = 56 + 2 * kTiles;  // 1 KiB pieces of a chunk's operands
-    auto issue = [&](size_t ci, Buf* dst) {
-      const uint8_t* wn = w.wn + ci * kWnBytes;
-      const uint8_t* qg = w.qg + ci * kQgBytes;
-      const uint8_t* kd = w.kd + ci * kKdBytes;
-      const uint8_t* aq = w.aq + ci * kAqBytes;
-      const uint8_t* ut = w.ut + ci * kUtBytes;
-#pragma unroll
-      for (int i = 0; i < (kPieces + LW - 1) / LW; ++i) {
-        const int p = lw + LW * i;  // wave-uniform
-        if (p < 16) dma16(wn + p * 1024 + off, &dst->wn[p][0]);
-        else if (p < 32) dma16(qg + (p - 16) * 1024 + off, &dst->qg[p - 16][0]);
-        else if (p < 48) dma16(kd + (p - 32) * 1024 + off, &dst->kd[p - 32][0]);
-        else if (p < 56) dma16(aq + (p - 48) * 1024 + off, &dst->aq[p - 48][0]);
-        else if (p < kPieces) {
-          const int x = p - 56, mp = x / kTiles, tl = x % kTiles;
-          dma16(ut + (size_t)((mp * 8 + group * kTiles + tl) * 64) * 16 + off,
-                      &dst->ut[mp][tl][0]);
-        }
-      }
-      if (lw == LW - 1 && lane < 32) dma16(w.gc + ci * kGcBytes + off, &dst->gc[0]);
-    };
-    // Staged outputs, as whole 16-byte row pieces; pieces of rows past the
-    // sequence end go to the workspace sink, which keeps the stores free of
-    // branches on the data path.  They are read before the next copies are
-    // issued, so no copy into LDS is outstanding when they are.
-    constexpr int kRowPieces = kCols / 8;
-    constexpr int kOutPieces = C * kRowPieces;
-    auto store_rows = [&](const uint16_t (*ob)[kCols], int base) {
-#pragma unroll
-      for (int x = 0; x < (kOutPieces + 64 * LW - 1) / (64 * LW); ++x) {
-        const int u = ltid + 64 * LW * x;
-        if (kOutPieces % (64 * LW) == 0 || u < kOutPieces) {
-          const int r = u / kRowPieces, pc = u % kRowPieces, tok = base + r;
-          uint4* dst = tok < end
-              ? reinterpret_cast<uint4*>(o + ((size_t)tok * H + h) * D + kCols * group + 8 * pc)
-              : reinterpret_cast<uint4*>(w.sink) + (lane & 15);
-          *dst = *reinterpret_cast<const uint4*>(&ob[r][8 * pc]);
-        }
-      }
-    };
-    auto step_end = [&]() {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
-      lds_barrier();
-    };
-    if (nch > 0) issue((size_t)cbase * H + h, &sl.buf[0]);
-    step_end();
-    for (int lc = 0; lc < nch; lc += 2) {
-      if (lc > 0) store_rows(sl.out[1], start + (lc - 1) * C);
-      if (lc + 1 < nch) issue((size_t)(cbase + lc + 1) * H + h, &sl.buf[1]);
-      step_end();
-      if (lc + 1 < nch) {
-        store_rows(sl.out[0], start + lc * C);
-        if (lc + 2 < nch) issue((size_t)(cbase + lc + 2) * H + h, &sl.buf[0]);
-        step_end();
-      }
-    }
-    if (nch > 0) store_rows(sl.out[(nch - 1) & 1], start + (nch - 1) * C);
-    return;
-  }
-
-  // -------------------------------------------------------------- compute
-  int col[NT];
-#pragma unroll
-  for (int i = 0; i < NT; ++i) col[i] = 16 * (group * kTiles + wave * NT + i) + li;
-  const int slot = slots ? slots[n] : n;
-  const bool slot_ok = states != nullptr && slot >= 0 && slot < num_slots;
-  float* Sg = slot_ok ? states + ((size_t)slot * H + h) * (size_t)(D * D) : nullptr;
-
-  // state slices: S[i][t] lane holds rows 16t + 4lg + jj of column col[i]
-  f32x4 S[NT][8];
-  if (slot_ok && (flags & KDA_READ_INITIAL_STATE)) {
-#pragma unroll
-    for (int i = 0; i < NT; ++i)
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) S[i][t][jj] = Sg[(size_t)(16 * t + 4 * lg + jj) * D + col[i]];
-  } else {
-#pragma unroll
-    for (int i = 0; i < NT; ++i)
-#pragma unroll
-      for (int t = 0; t < 8; ++t) S[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  lds_barrier();
-
-  auto chunk_step = [&](const Buf& B, uint16_t (*ob)[kCols]) {
-    f32x4 U[NT][4];
-#pragma unroll
-    for (int i = 0; i < NT; ++i)
-#pragma unroll
-      for (int mp = 0; mp < 2; ++mp)
-        unpack_acc(B.ut[mp][wave * NT + i][lane], U[i][2 * mp], U[i][2 * mp + 1]);
-    bf16x8 a_wn[16];
-#pragma unroll
-    for (int x = 0; x < 16; ++x) a_wn[x] = B.wn[x][lane];
-    bf16x8 sb[NT][4];
-#pragma unroll
-    for (int i = 0; i < NT; ++i)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) sb[i][s] = pack_acc(S[i][2 * s], S[i][2 * s + 1]);
-    bf16x8 a_qg[16], a_aq[6];
-#pragma unroll
-    for (int x = 0; x < 16; ++x) a_qg[x] = B.qg[x][lane];
-#pragma unroll
-    for (int x = 0; x < 6; ++x) a_aq[x] = B.aq[x < 2 ? 2 * x : x + 2][lane];  // [0],[2],[4..7]
-    __builtin_amdgcn_sched_barrier(0);
-
-    // U = Ut - W S   (consecutive MFMAs go to different accumulators)
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int i = 0; i < NT; ++i) U[i][m] = mfma(a_wn[m * 4 + s], sb[i][s], U[i][m]);
-    // O, first part: (Q*Gam) S
-    f32x4 O[NT][4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int i = 0; i < NT; ++i) O[i][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int i = 0; i < NT; ++i) O[i][m] = mfma(a_qg[m * 4 + s], sb[i][s], O[i][m]);
-    bf16x8 a_kd[16];
-    f32x4 gcv[8];
-#pragma unroll
-    for (int x = 0; x < 16; ++x) a_kd[x] = B.kd[x][lane];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) gcv[t] = B.gc[4 * t + lg];
-    __builtin_amdgcn_sched_barrier(0);
-
-    bf16x8 ub[NT][2];
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      ub[i][0] = pack_acc(U[i][0], U[i][1]);
-      ub[i][1] = pack_acc(U[i][2], U[i][3]);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) S[i][t] = S[i][t] * gcv[t];
-    }
-    // S' = Diag(Gam_C) S + Kd^T U  (the chain's critical path: issued first)
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int i = 0; i < NT; ++i) S[i][t] = mfma(a_kd[t * 2 + s2], ub[i][s2], S[i][t]);
-    // O += A_qk U   (A_qk rows 0-31 have no entries in columns 32-63)
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      O[i][0] = mfma(a_aq[0], ub[i][0], O[i][0]);
-      O[i][1] = mfma(a_aq[1], ub[i][0], O[i][1]);
-      O[i][2] = mfma(a_aq[2], ub[i][0], O[i][2]);
-      O[i][3] = mfma(a_aq[4], ub[i][0], O[i][3]);
-    }
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      O[i][2] = mfma(a_aq[3], ub[i][1], O[i][2]);
-      O[i][3] = mfma(a_aq[5], ub[i][1], O[i][3]);
-    }
-#pragma unroll
-    for (int i = 0; i < NT; ++i)
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          ob[16 * m + 4 * lg + jj][16 * (wave * NT + i) + li] = f32_to_bf16(O[i][m][jj]);
-    lds_barrier();
-  };
-  for (int lc = 0; lc < nch; lc += 2) {
-    chunk_step(sl.buf[0], sl.out[0]);
-    if (lc + 1 < nch) chunk_step(sl.buf[1], sl.out[1]);
-  }
-
-  if (slot_ok && (flags & KDA_WRITE_FINAL_STATE)) {
-#pragma unroll
-    for (int i = 0; i < NT; ++i)
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) Sg[(size_t)(16 * t + 4 * lg + jj) * D + col[i]] = S[i][t][jj];
-  }
-}
-
-template <int CW, int NT, int LW>
-__global__ __launch_bounds__(64 * (CW + LW)) void scan_ws_kernel(
-    int32_t N, int H, Workspace w, float* __restrict__ states, int32_t num_slots,
-    const int32_t* __restrict__ slots, uint32_t flags, uint16_t* __restrict__ o) {
-  extern __shared__ __align__(16) uint8_t smem_raw[];
-  scan_role<CW, NT, LW>(blockIdx.x, smem_raw, N, H, w, states, num_slots, slots, flags, o);
-}
-
 // State-only warp-specialised scan: the backward's forward state pass.  Per
 // chunk only the state recurrence is on the serial path: U = Ut - W S and S' =
 // Diag(Gam_C) S + Kd^T U.  The compute waves store the bf16 MFMA operands they
@@ -1723,47 +1482,57 @@ __device__ __forceinline__ void scan_state_role(int blk, uint8_t* smem_raw, int3
   }
 }
 
-// State scan with the outputs formed beside it (few chains).  A workgroup owns
-// 16 state columns of one (sequence, head).  Wave 0 carries the state as in
-// scan_state_role and, per chunk c, leaves S_c (at the chunk start) and U_c in
-// LDS as the bf16 B operands it forms anyway; waves 1 and 2 form the rows 0-31
-// and 32-63 of O_c = (Q*Gam)_c S_c + A_qk,c U_c one step later, with the MFMA
-// order of the single-pass scan, from Q*Gam and A_qk tiles that they load from
-// the workspace into registers two chunks ahead, and leave their 32 x 16 outputs
-// in LDS as bf16 rows, which wave 3 stores as 16-byte row pieces one step later;
-// waves 4..7 keep a four-buffer ring of the chain's operands filled.  Nothing of S
-// or U goes through memory, and no separate output launch re-reads the chunk
-// operands.
+// State scan with the outputs formed beside it.  A workgroup owns NCT tiles of 16
+// state columns of one (sequence, head) (the columns evolve independently, so
+// the workgroups of a head need no exchange).  Waves 0..NCT-1 carry one column
+// tile of the state each, as in scan_state_role, and per chunk c leave S_c (at
+// the chunk start) and U_c in LDS as the bf16 B operands they form anyway; the
+// next two waves form the rows 0-31 and 32-63 of O_c = (Q*Gam)_c S_c +
+// A_qk,c U_c one step later, with the MFMA order of the single-pass scan, from
+// Q*Gam and A_qk tiles that they load from the workspace into registers two
+// chunks ahead, and leave their outputs in LDS as bf16 rows, which the next wave
+// stores as 16-byte row pieces one step later; the other waves keep a ring of the
+// chain's operands filled.  Nothing of S or U goes through memory, and no
+// separate output launch re-reads the chunk operands.
 constexpr int kScanOutThreads = 512;
-constexpr int kOutRing = 4;
 
+template <int NCT>
 struct ScanOutLds {
+  // NCT = 1: four buffers, and the state wave reads chunk c's operands at the end
+  // of step c - 1 (they land while it waits at the barrier); NCT = 2: three
+  // buffers (the LDS holds no more), read at the top of the step.
+  static constexpr int kRing = NCT == 1 ? 4 : 3;
+  static constexpr bool kPipe = NCT == 1;
   // one chunk's operands; 1 KiB pieces in the loaders' order (Gam_C is padded to
   // a whole piece so that every lane of its loader stores)
   struct Buf {
-    bf16x8 wn[16][64];    // [m*4 + s][lane]
-    bf16x8 kd[16][64];    // [t*2 + s'][lane]
-    bf16x8 ut[2][1][64];  // [row tile pair][this group's column tile][lane]
-    f32x4 gc[32];         // Gam_C
+    bf16x8 wn[16][64];      // [m*4 + s][lane]
+    bf16x8 kd[16][64];      // [t*2 + s'][lane]
+    bf16x8 ut[2][NCT][64];  // [row tile pair][this group's column tile][lane]
+    f32x4 gc[32];           // Gam_C
     f32x4 gc_pad[32];
   };
-  Buf buf[kOutRing];
-  bf16x8 xs[2][6][64];  // per chunk parity: S_c as 4 B operands (K = dk), then U_c as 2 (K = rows)
-  uint16_t ob[2][C][16];  // per chunk parity: the output waves' bf16 outputs of the chunk
+  Buf buf[kRing];
+  bf16x8 xs[2][6 * NCT][64];  // per chunk parity: S_c as 4 B operands per tile (K = dk), then U_c as 2
+  uint16_t ob[2][C][16 * NCT];  // per chunk parity: the output waves' bf16 outputs of the chunk
 };
 
+template <int NCT>
 __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_t N, int H,
                                               const Workspace& w, float* __restrict__ states,
                                               int32_t num_slots, const int32_t* __restrict__ slots,
                                               uint32_t flags, uint16_t* __restrict__ o) {
-  using Buf = ScanOutLds::Buf;
-  constexpr int kOutWaves = 2;
-  constexpr int kStoreWave = 1 + kOutWaves;
-  constexpr int LW = kScanOutThreads / 64 - 2 - kOutWaves;
-  ScanOutLds& sl = *reinterpret_cast<ScanOutLds*>(smem_raw);
+  using L = ScanOutLds<NCT>;
+  using Buf = typename L::Buf;
+  constexpr int kOutRing = L::kRing;
+  constexpr bool kPipe = L::kPipe;
+  constexpr int kOutWave0 = NCT, kOutWaves = 2;
+  constexpr int kStoreWave = kOutWave0 + kOutWaves;
+  constexpr int LW = kScanOutThreads / 64 - kStoreWave - 1;
+  L& sl = *reinterpret_cast<L*>(smem_raw);
   const int NH = N * H;
   const int head_lin = blk % NH;
-  const int group = blk / NH;  // 16-column tile of the state
+  const int group = blk / NH;  // NCT consecutive 16-column tiles of the state
   const int n = head_lin / H, h = head_lin - n * H;
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1772,13 +1541,13 @@ __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_
 
   if (wave > kStoreWave) {
     // ------------------------------------------------------------ loaders
-    // Pieces of 1 KiB, dealt to the loaders in turn: 0-15 -W, 16-31 Kd^T, 32-33
-    // this group's two Ut pieces, 34 Gam_C (512 B, copied twice so that every lane
-    // has a part).  A buffer holds them in this order, piece p at byte 1024 p.
-    // The copies go straight to LDS, three chunks ahead: a chunk's copies take
-    // longer than one chunk step to land.
+    // Pieces of 1 KiB, dealt to the loaders in turn: 0-15 -W, 16-31 Kd^T, then
+    // this group's 2 NCT Ut pieces, then Gam_C (512 B, copied twice so that every
+    // lane has a part).  A buffer holds them in this order, piece p at byte
+    // 1024 p.  The copies go straight to LDS, kRing - 1 chunks ahead: a chunk's
+    // copies take longer than one chunk step to land.
     const int lw = wave - kStoreWave - 1;
-    constexpr int kPieces = 35;
+    constexpr int kUt0 = 32, kGc = kUt0 + 2 * NCT, kPieces = kGc + 1;
     constexpr int kPer = (kPieces + LW - 1) / LW;
     const int mine = (kPieces - lw + LW - 1) / LW;  // this loader's pieces
     static_assert(sizeof(Buf) == kPieces * 1024, "piece p at byte 1024 p");
@@ -1795,14 +1564,15 @@ __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_
       } else if (p < 32) {
         pbase[i] = w.kd + (p - 16) * 1024;
         pstride[i] = (uint32_t)kKdBytes;
-      } else if (p < 34) {
-        pbase[i] = w.ut + (size_t)((p - 32) * 8 + group) * 1024;
+      } else if (p < kGc) {
+        const int mp = (p - kUt0) / NCT, ct = (p - kUt0) % NCT;
+        pbase[i] = w.ut + (size_t)(mp * 8 + group * NCT + ct) * 1024;
         pstride[i] = (uint32_t)kUtBytes;
       } else {
         pbase[i] = w.gc;
         pstride[i] = (uint32_t)kGcBytes;
       }
-      ploff[i] = (uint32_t)(p < 34 ? lane : (lane & 31)) * 16;
+      ploff[i] = (uint32_t)(p < kGc ? lane : (lane & 31)) * 16;
     }
     auto issue = [&](int c) {
       const size_t ci = (size_t)(cbase + c) * H + h;
@@ -1811,18 +1581,19 @@ __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_
       for (int i = 0; i < kPer; ++i)
         if (lw + LW * i < kPieces) dma16(pbase[i] + ci * pstride[i] + ploff[i], dst + (lw + LW * i) * 1024);
     };
-    // Chunk c + 1 must have landed by the barrier that ends step c - 1 (the state
-    // wave reads it at the end of step c), so each wait leaves only the newest
-    // chunk's copies in flight.
+    // Chunk c + kLead must have landed by the barrier that ends step c (kPipe: the
+    // state wave reads chunk c + 2 at the end of step c + 1), so each wait leaves
+    // only the newest chunk's copies in flight.
     constexpr int kAhead = kOutRing - 1;
-    static_assert(kPer * (kAhead - 2) <= 23, "graded wait range");
+    constexpr int kLead = kPipe ? 2 : 1;
+    static_assert(kPer * (kAhead - kLead) <= 23, "graded wait range");
     for (int c = 0; c < kAhead && c < nch; ++c) issue(c);
-    wait_vm(mine * (min(nch, kAhead) - min(nch, kAhead - 1)));  // chunks 0 and 1 landed
+    wait_vm(mine * (min(nch, kAhead) - min(nch, kLead)));  // chunks before kLead landed
     lds_barrier();
     for (int lc = 0; lc < nch; ++lc) {
       const int nxt = lc + kAhead;
       if (nxt < nch) issue(nxt);
-      wait_vm(mine * (min(nch, nxt + 1) - min(nch, nxt)));  // chunk lc + 2 landed
+      wait_vm(mine * (min(nch, nxt + 1) - min(nch, lc + kLead + 1)));  // chunk lc + kLead landed
       lds_barrier();
     }
     lds_barrier();  // the closing barrier of the output and store waves
@@ -1835,14 +1606,15 @@ __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_
     // Chunk c's outputs, staged by the output waves during step c + 1, go out as
     // 16-byte row pieces during step c + 2 (the staging tile has a slot per chunk
     // parity), so the output waves never wait on a store.
+    constexpr int kRowPieces = 2 * NCT;  // 16-byte pieces per output row
     auto store_chunk = [&](int c) {
       const int t0 = start + c * C, rows = min(C, end - t0);
 #pragma unroll
-      for (int xx = 0; xx < 2; ++xx) {
-        const int pc = lane + 64 * xx, r = pc >> 1, half = pc & 1;
-        const uint4 v4 = *reinterpret_cast<const uint4*>(&sl.ob[c & 1][r][8 * half]);
+      for (int xx = 0; xx < kRowPieces; ++xx) {
+        const int pc = lane + 64 * xx, r = pc / kRowPieces, piece = pc % kRowPieces;
+        const uint4 v4 = *reinterpret_cast<const uint4*>(&sl.ob[c & 1][r][8 * piece]);
         if (r < rows)
-          *reinterpret_cast<uint4*>(o + ((size_t)(t0 + r) * H + h) * D + 16 * group + 8 * half) = v4;
+          *reinterpret_cast<uint4*>(o + ((size_t)(t0 + r) * H + h) * D + 16 * NCT * group + 8 * piece) = v4;
       }
     };
     lds_barrier();
@@ -1856,13 +1628,13 @@ __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_
     return;
   }
 
-  if (wave >= 1) {
+  if (wave >= kOutWave0) {
     // ------------------------------------------------------------ outputs
-    // rows 32 hf .. 32 hf + 31; chunk c's Q*Gam and A_qk tiles sit in register set
-    // c % 2, loaded at step c - 1.  A_qk tiles (block row R, column half s'): half
-    // 0 needs (0,0) (1,0); half 1 needs (2,0) (2,1) (3,0) (3,1) (rows 0-31 have no
-    // entries in columns 32-63).
-    const int hf = wave - 1;
+    // rows 32 hf .. 32 hf + 31 of every column tile; chunk c's Q*Gam and A_qk tiles
+    // sit in register set c % 2, loaded at step c - 1.  A_qk tiles (block row R,
+    // column half s'): half 0 needs (0,0) (1,0); half 1 needs (2,0) (2,1) (3,0)
+    // (3,1) (rows 0-31 have no entries in columns 32-63).
+    const int hf = wave - kOutWave0;
     bf16x8 qg0[8], aq0[4], qg1[8], aq1[4];
     auto load_ops = [&](bf16x8* qgr, bf16x8* aqr, int c) {
       const size_t ci = (size_t)(cbase + c) * H + h;
@@ -1878,33 +1650,36 @@ __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_
     // rows of O_c from slot c % 2 of the exchange and the operand tiles qgr, aqr
     auto out_chunk = [&](const bf16x8* qgr, const bf16x8* aqr, int c) {
       const bf16x8(*x)[64] = sl.xs[c & 1];
-      bf16x8 sb[4], ub[2];
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) sb[s2] = x[s2][lane];
-      ub[0] = x[4][lane];
-      ub[1] = x[5][lane];
-      f32x4 O[2];
+      for (int ct = 0; ct < NCT; ++ct) {
+        bf16x8 sb[4], ub[2];
 #pragma unroll
-      for (int mm = 0; mm < 2; ++mm) O[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s2 = 0; s2 < 4; ++s2) sb[s2] = x[4 * ct + s2][lane];
+        ub[0] = x[4 * NCT + 2 * ct][lane];
+        ub[1] = x[4 * NCT + 2 * ct + 1][lane];
+        f32x4 O[2];
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2)
+        for (int mm = 0; mm < 2; ++mm) O[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int mm = 0; mm < 2; ++mm) O[mm] = mfma(qgr[mm * 4 + s2], sb[s2], O[mm]);
-      if (hf == 0) {
-        O[0] = mfma(aqr[0], ub[0], O[0]);
-        O[1] = mfma(aqr[1], ub[0], O[1]);
-      } else {
-        O[0] = mfma(aqr[0], ub[0], O[0]);
-        O[1] = mfma(aqr[2], ub[0], O[1]);
-        O[0] = mfma(aqr[1], ub[1], O[0]);
-        O[1] = mfma(aqr[3], ub[1], O[1]);
+        for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm) O[mm] = mfma(qgr[mm * 4 + s2], sb[s2], O[mm]);
+        if (hf == 0) {
+          O[0] = mfma(aqr[0], ub[0], O[0]);
+          O[1] = mfma(aqr[1], ub[0], O[1]);
+        } else {
+          O[0] = mfma(aqr[0], ub[0], O[0]);
+          O[1] = mfma(aqr[2], ub[0], O[1]);
+          O[0] = mfma(aqr[1], ub[1], O[0]);
+          O[1] = mfma(aqr[3], ub[1], O[1]);
+        }
+        // stage as bf16 rows for the store wave
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            sl.ob[c & 1][32 * hf + 16 * mm + 4 * lg + jj][16 * ct + li] = f32_to_bf16(O[mm][jj]);
       }
-      // stage as bf16 rows of 16 columns for the store wave
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          sl.ob[c & 1][32 * hf + 16 * mm + 4 * lg + jj][li] = f32_to_bf16(O[mm][jj]);
     };
     // loads on every path (past the last chunk: the last again), so that the wait
     // for one register set counts the other set's loads
@@ -1930,8 +1705,9 @@ __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_
     return;
   }
 
-  // -------------------------------------------------------------- state (wave 0)
-  const int col = 16 * group + li;
+  // ------------------------------------------------------ state (wave ct < NCT)
+  const int ct = wave;
+  const int col = 16 * (NCT * group + ct) + li;
   const int slot = slots ? slots[n] : n;
   const bool slot_ok = states != nullptr && slot >= 0 && slot < num_slots;
   float* Sg = slot_ok ? states + ((size_t)slot * H + h) * (size_t)(D * D) : nullptr;
@@ -1946,16 +1722,13 @@ __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_
     for (int t = 0; t < 8; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   lds_barrier();
-  // The operands of chunk c are read at the end of step c - 1, after its products
-  // are issued: they land while the wave waits at the step's barrier (which
-  // waits for its LDS writes, not for these reads).
   f32x4 U[4];
   bf16x8 a_wn[16], a_kd[16];
   f32x4 gcv[8];
   auto read_ops = [&](int c) {
     const Buf& B = sl.buf[c % kOutRing];
-    unpack_acc(B.ut[0][0][lane], U[0], U[1]);
-    unpack_acc(B.ut[1][0][lane], U[2], U[3]);
+    unpack_acc(B.ut[0][ct][lane], U[0], U[1]);
+    unpack_acc(B.ut[1][ct][lane], U[2], U[3]);
 #pragma unroll
     for (int xx = 0; xx < 16; ++xx) a_wn[xx] = B.wn[xx][lane];
 #pragma unroll
@@ -1963,14 +1736,15 @@ __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_
 #pragma unroll
     for (int t = 0; t < 8; ++t) gcv[t] = B.gc[4 * t + lg];
   };
-  if (nch > 0) read_ops(0);
+  if (kPipe && nch > 0) read_ops(0);
   for (int lc = 0; lc < nch; ++lc) {
+    if (!kPipe) read_ops(lc);
     bf16x8(*x)[64] = sl.xs[lc & 1];
     bf16x8 sb[4];
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) sb[s2] = pack_acc(S[2 * s2], S[2 * s2 + 1]);
 #pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) x[s2][lane] = sb[s2];
+    for (int s2 = 0; s2 < 4; ++s2) x[4 * ct + s2][lane] = sb[s2];
     // U = Ut - W S   (consecutive MFMAs go to different accumulators)
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2)
@@ -1979,8 +1753,8 @@ __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_
     bf16x8 ub[2];
     ub[0] = pack_acc(U[0], U[1]);
     ub[1] = pack_acc(U[2], U[3]);
-    x[4][lane] = ub[0];
-    x[5][lane] = ub[1];
+    x[4 * NCT + 2 * ct][lane] = ub[0];
+    x[4 * NCT + 2 * ct + 1][lane] = ub[1];
 #pragma unroll
     for (int t = 0; t < 8; ++t) S[t] = S[t] * gcv[t];
     // S' = Diag(Gam_C) S + Kd^T U
@@ -1988,10 +1762,16 @@ __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int t = 0; t < 8; ++t) S[t] = mfma(a_kd[t * 2 + s2], ub[s2], S[t]);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the exchange tiles are written
-    if (lc + 1 < nch) read_ops(lc + 1);
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    if constexpr (kPipe) {
+      // the next chunk's operands, issued after this chunk's products: they land
+      // while the wave waits at the barrier (which waits for its LDS writes only)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the exchange tiles are written
+      if (lc + 1 < nch) read_ops(lc + 1);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    } else {
+      lds_barrier();
+    }
   }
   lds_barrier();  // the closing barrier of the output and store waves
   if (slot_ok && (flags & KDA_WRITE_FINAL_STATE)) {
@@ -2002,38 +1782,27 @@ __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_
   }
 }
 
+template <int NCT>
 __global__ __launch_bounds__(kScanOutThreads) void scan_out_kernel(
     int32_t N, int H, Workspace w, float* __restrict__ states, int32_t num_slots,
     const int32_t* __restrict__ slots, uint32_t flags, uint16_t* __restrict__ o) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
-  scan_out_role(blockIdx.x, smem_raw, N, H, w, states, num_slots, slots, flags, o);
+  scan_out_role<NCT>(blockIdx.x, smem_raw, N, H, w, states, num_slots, slots, flags, o);
 }
 
+// NCT tiles of 16 columns per workgroup: N * H * 8 / NCT workgroups.
+template <int NCT>
 kda_status_t launch_scan_out(int32_t N, int H, const Workspace& w, float* states,
                              int32_t num_slots, const int32_t* slots, uint32_t flags, void* o,
                              hipStream_t stream) {
   static std::atomic<uint64_t> lds_set{0};
-  kda_status_t st = allow_dynamic_lds(reinterpret_cast<const void*>(scan_out_kernel),
-                                      sizeof(ScanOutLds), lds_set, "hipFuncSetAttribute(scan)");
+  kda_status_t st = allow_dynamic_lds(reinterpret_cast<const void*>(scan_out_kernel<NCT>),
+                                      sizeof(ScanOutLds<NCT>), lds_set, "hipFuncSetAttribute(scan)");
   if (st != KDA_OK) return st;
-  hipLaunchKernelGGL(scan_out_kernel, dim3((unsigned)(N * H * (D / 16))), dim3(kScanOutThreads),
-                     sizeof(ScanOutLds), stream, N, H, w, states, num_slots, slots, flags,
-                     static_cast<uint16_t*>(o));
-  return check_launch("scan_out_kernel");
-}
-
-template <int CW, int NT, int LW>
-kda_status_t launch_scan_ws(int32_t N, int H, const Workspace& w, float* states, int32_t num_slots,
-                            const int32_t* slots, uint32_t flags, void* o, hipStream_t stream) {
-  constexpr int kGroups = D / (16 * CW * NT);
-  static std::atomic<uint64_t> lds_set{0};
-  kda_status_t st = allow_dynamic_lds(reinterpret_cast<const void*>(scan_ws_kernel<CW, NT, LW>),
-                                      sizeof(ScanLds<CW, NT>), lds_set, "hipFuncSetAttribute(scan)");
-  if (st != KDA_OK) return st;
-  hipLaunchKernelGGL((scan_ws_kernel<CW, NT, LW>), dim3((unsigned)(N * H * kGroups)),
-                     dim3(64 * (CW + LW)), sizeof(ScanLds<CW, NT>), stream, N, H, w, states,
+  hipLaunchKernelGGL(scan_out_kernel<NCT>, dim3((unsigned)(N * H * (D / (16 * NCT)))),
+                     dim3(kScanOutThreads), sizeof(ScanOutLds<NCT>), stream, N, H, w, states,
                      num_slots, slots, flags, static_cast<uint16_t*>(o));
-  return check_launch("scan_ws_kernel");
+  return check_launch("scan_out_kernel");
 }
 
 template <int WAVES, int NT>
@@ -2928,14 +2697,14 @@ kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, cons
   if (st != KDA_OK) return st;
   // Few chains: the serial chain of chunk steps is the critical path; each
   // head's state is split over 8 warp-specialised workgroups of 16 columns whose
-  // state wave carries only the state while a wave beside it forms the outputs.
-  // Up to one workgroup per CU at 4 per head: the single-pass warp-specialised
-  // scan.  Many chains: one workgroup of 4 waves x 32 columns per head, which
-  // fetches each chunk's shared operands once.
+  // state wave carries only the state while waves beside it form the outputs.
+  // Up to one workgroup per CU at 4 per head: the same scan with 32 columns (two
+  // state waves) per workgroup.  Many chains: one workgroup of 4 waves x 32
+  // columns per head, which fetches each chunk's shared operands once.
   if (split_outputs(N, H))
-    return launch_scan_out(N, H, w, states, num_slots, slots, flags, o, stream);
+    return launch_scan_out<1>(N, H, w, states, num_slots, slots, flags, o, stream);
   if ((size_t)N * H * 4 <= (size_t)ncu)
-    return launch_scan_ws<2, 1, 6>(N, H, w, states, num_slots, slots, flags, o, stream);
+    return launch_scan_out<2>(N, H, w, states, num_slots, slots, flags, o, stream);
   return launch_scan<4, 2>(N, H, w, states, num_slots, slots, flags, o, stream);
 }
 

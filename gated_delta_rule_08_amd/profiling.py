@@ -30,7 +30,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _short(name: str) -> str:
-    for key in ("scan_out_kernel", "scan_ws_kernel", "scan_pair_kernel", "scan_kernel"):
+    for key in ("scan_out_kernel", "scan_pair_kernel", "scan_kernel"):
         if key in name:
             return key + (name[name.index("<"):name.index(">") + 1] if "<" in name else "")
     for key in ("prep_kernel", "index_kernel", "decode_kernel", "chunk_small_kernel",
