@@ -1539,17 +1539,20 @@ __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_
   const int nch = w.seq_nch[n];
   const int cbase = w.chunk_off[n];
 
-  if (wave > kStoreWave) {
-    // ------------------------------------------------------------ loaders
-    // Pieces of 1 KiB, dealt to the loaders in turn: 0-15 -W, 16-31 Kd^T, then
+  const int start = w.seq_start[n], end = w.seq_end[n];
+  if (wave >= kStoreWave) {
+    // -------------------------------------------------- copies (and stores)
+    // Pieces of 1 KiB, dealt to the copy waves in turn: 0-15 -W, 16-31 Kd^T, then
     // this group's 2 NCT Ut pieces, then Gam_C (512 B, copied twice so that every
     // lane has a part).  A buffer holds them in this order, piece p at byte
     // 1024 p.  The copies go straight to LDS, kRing - 1 chunks ahead: a chunk's
-    // copies take longer than one chunk step to land.
-    const int lw = wave - kStoreWave - 1;
+    // copies take longer than one chunk step to land, and a CU takes them in
+    // faster the more waves issue them.
+    const int lw = wave - kStoreWave;
+    constexpr int kCopyWaves = LW + 1;
     constexpr int kUt0 = 32, kGc = kUt0 + 2 * NCT, kPieces = kGc + 1;
-    constexpr int kPer = (kPieces + LW - 1) / LW;
-    const int mine = (kPieces - lw + LW - 1) / LW;  // this loader's pieces
+    constexpr int kPer = (kPieces + kCopyWaves - 1) / kCopyWaves;
+    const int mine = (kPieces - lw + kCopyWaves - 1) / kCopyWaves;  // this wave's pieces
     static_assert(sizeof(Buf) == kPieces * 1024, "piece p at byte 1024 p");
     // per piece: its array's address at chunk-head 0, that array's stride per
     // chunk-head, and the lane's byte offset (fixed for the wave)
@@ -1557,7 +1560,7 @@ __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_
     uint32_t pstride[kPer], ploff[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int p = lw + LW * i;  // wave-uniform
+      const int p = lw + kCopyWaves * i;  // wave-uniform
       if (p < 16) {
         pbase[i] = w.wn + p * 1024;
         pstride[i] = (uint32_t)kWnBytes;
@@ -1579,52 +1582,49 @@ __device__ __forceinline__ void scan_out_role(int blk, uint8_t* smem_raw, int32_
       uint8_t* dst = reinterpret_cast<uint8_t*>(&sl.buf[c % kOutRing]);
 #pragma unroll
       for (int i = 0; i < kPer; ++i)
-        if (lw + LW * i < kPieces) dma16(pbase[i] + ci * pstride[i] + ploff[i], dst + (lw + LW * i) * 1024);
+        if (lw + kCopyWaves * i < kPieces)
+          dma16(pbase[i] + ci * pstride[i] + ploff[i], dst + (lw + kCopyWaves * i) * 1024);
     };
-    // Chunk c + kLead must have landed by the barrier that ends step c (kPipe: the
-    // state wave reads chunk c + 2 at the end of step c + 1), so each wait leaves
-    // only the newest chunk's copies in flight.
-    constexpr int kAhead = kOutRing - 1;
-    constexpr int kLead = kPipe ? 2 : 1;
-    static_assert(kPer * (kAhead - kLead) <= 23, "graded wait range");
-    for (int c = 0; c < kAhead && c < nch; ++c) issue(c);
-    wait_vm(mine * (min(nch, kAhead) - min(nch, kLead)));  // chunks before kLead landed
-    lds_barrier();
-    for (int lc = 0; lc < nch; ++lc) {
-      const int nxt = lc + kAhead;
-      if (nxt < nch) issue(nxt);
-      wait_vm(mine * (min(nch, nxt + 1) - min(nch, lc + kLead + 1)));  // chunk lc + kLead landed
-      lds_barrier();
-    }
-    lds_barrier();  // the closing barrier of the output and store waves
-    return;
-  }
-
-  const int start = w.seq_start[n], end = w.seq_end[n];
-  if (wave == kStoreWave) {
-    // ------------------------------------------------------------ stores
-    // Chunk c's outputs, staged by the output waves during step c + 1, go out as
-    // 16-byte row pieces during step c + 2 (the staging tile has a slot per chunk
-    // parity), so the output waves never wait on a store.
+    // Wave kStoreWave also stores the outputs: chunk c's, staged by the output
+    // waves during step c + 1, go out as 16-byte row pieces during step c + 2 (the
+    // staging tile has a slot per chunk parity), so the output waves never wait
+    // on a store.  Every lane stores (rows past the sequence end into the
+    // workspace sink), so that the waits below count the stores exactly.
     constexpr int kRowPieces = 2 * NCT;  // 16-byte pieces per output row
+    const bool stores = lw == 0;
     auto store_chunk = [&](int c) {
       const int t0 = start + c * C, rows = min(C, end - t0);
 #pragma unroll
       for (int xx = 0; xx < kRowPieces; ++xx) {
         const int pc = lane + 64 * xx, r = pc / kRowPieces, piece = pc % kRowPieces;
         const uint4 v4 = *reinterpret_cast<const uint4*>(&sl.ob[c & 1][r][8 * piece]);
-        if (r < rows)
-          *reinterpret_cast<uint4*>(o + ((size_t)(t0 + r) * H + h) * D + 16 * NCT * group + 8 * piece) = v4;
+        uint4* dst = r < rows
+            ? reinterpret_cast<uint4*>(o + ((size_t)(t0 + r) * H + h) * D + 16 * NCT * group + 8 * piece)
+            : reinterpret_cast<uint4*>(w.sink) + (lane & 15);
+        *dst = v4;
       }
     };
+    // Chunk c + kLead must have landed by the barrier that ends step c (kPipe: the
+    // state wave reads chunk c + 2 at the end of step c + 1), so each wait leaves
+    // only the newest chunk's copies (and the step's stores) in flight.
+    constexpr int kAhead = kOutRing - 1;
+    constexpr int kLead = kPipe ? 2 : 1;
+    static_assert(kPer * (kAhead - kLead) + kRowPieces <= 23, "graded wait range");
+    for (int c = 0; c < kAhead && c < nch; ++c) issue(c);
+    wait_vm(mine * (min(nch, kAhead) - min(nch, kLead)));  // chunks before kLead landed
     lds_barrier();
     for (int lc = 0; lc < nch; ++lc) {
-      if (lc >= 2) store_chunk(lc - 2);
+      const int nxt = lc + kAhead;
+      if (nxt < nch) issue(nxt);
+      const bool st = stores && lc >= 2;
+      if (st) store_chunk(lc - 2);
+      // chunk lc + kLead landed
+      wait_vm(mine * (min(nch, nxt + 1) - min(nch, lc + kLead + 1)) + (st ? kRowPieces : 0));
       lds_barrier();
     }
-    if (nch >= 2) store_chunk(nch - 2);
+    if (stores && nch >= 2) store_chunk(nch - 2);
     lds_barrier();  // the last chunk's outputs are staged
-    if (nch >= 1) store_chunk(nch - 1);
+    if (stores && nch >= 1) store_chunk(nch - 1);
     return;
   }
 
