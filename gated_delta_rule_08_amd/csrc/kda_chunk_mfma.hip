@@ -408,6 +408,19 @@ __device__ __forceinline__ void build_header(PrepSmem& sm, const int32_t* __rest
 // issue until the CU's memory pipeline takes them.  Part 0: k, q; part 1: v,
 // beta; parts 2 and 3: the first and last eight of the thread's 16 gate rows
 // (one channel each; a wave reads 64 consecutive channels of a row).
+// The inputs are read once: non-temporal loads, which do not displace what the
+// caches hold (on a cold call that also spares the write-back of the dirty lines
+// they would evict).
+typedef unsigned int ntu32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 nt_load4(const void* p) {
+  const ntu32x4 x = __builtin_nontemporal_load(reinterpret_cast<const ntu32x4*>(p));
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+template <typename T>
+__device__ __forceinline__ T nt_load(const T* p) {
+  return __builtin_nontemporal_load(p);
+}
+
 template <int kGate, bool kAdd, bool kRaw, int kPart>
 __device__ __forceinline__ void prep_load_part(PrepIn& in, const ItemPos& p, const uint16_t* q,
                                                const uint16_t* k, const uint16_t* v,
@@ -427,16 +440,16 @@ __device__ __forceinline__ void prep_load_part(PrepIn& in, const ItemPos& p, con
       const int u = tid + kPrepThreads * i, r = u >> 4, cc = (u & 15) * 8;
       const uint32_t gi = __umul24((uint32_t)min(r, p.c - 1), rowstride) + cc;
       if constexpr (kPart == 0) {
-        in.k[i] = *reinterpret_cast<const uint4*>(k + base + gi);
-        in.q[i] = *reinterpret_cast<const uint4*>(q + base + gi);
+        in.k[i] = nt_load4(k + base + gi);
+        in.q[i] = nt_load4(q + base + gi);
       } else {
-        in.v[i] = *reinterpret_cast<const uint4*>(v + base + gi);
+        in.v[i] = nt_load4(v + base + gi);
       }
     }
     if constexpr (kPart == 1 && !kAdd) {
       const uint32_t bi = __umul24((uint32_t)min(tid & 63, p.c - 1), (uint32_t)H);
-      if (kRaw) in.b16 = (b16 + bbase)[bi];
-      else in.beta = (beta + bbase)[bi];
+      if (kRaw) in.b16 = nt_load(b16 + bbase + bi);
+      else in.beta = nt_load(beta + bbase + bi);
     }
   } else {
     const int col = tid & (D - 1), qt = tid >> 7;
@@ -445,12 +458,12 @@ __device__ __forceinline__ void prep_load_part(PrepIn& in, const ItemPos& p, con
       const uint32_t row = (uint32_t)min(16 * qt + i, p.c - 1);
       if (kGate == kGateScalar) {
         const uint32_t gi = __umul24(row, (uint32_t)H);
-        if (kRaw) in.gl[i] = (g16 + bbase)[gi];
-        else in.g[i] = (g + bbase)[gi];
+        if (kRaw) in.gl[i] = nt_load(g16 + bbase + gi);
+        else in.g[i] = nt_load(g + bbase + gi);
       } else if (kGate == kGateChannel) {
         const uint32_t gi = __umul24(row, rowstride) + col;
-        if (kRaw) in.gl[i] = (g16 + base)[gi];
-        else in.g[i] = (g + base)[gi];
+        if (kRaw) in.gl[i] = nt_load(g16 + base + gi);
+        else in.g[i] = nt_load(g + base + gi);
       }
     }
   }

@@ -187,11 +187,14 @@ def test_prefill_c1_full():
     _log(f"c1 rel err o={e_o:.2e} state={e_s:.2e}")
 
 
-def test_prefill_mfma_ragged_varlen_slots():
+@pytest.mark.parametrize("H", [3, 8])
+def test_prefill_mfma_ragged_varlen_slots(H):
+    """Ragged sequences (empty, one token, a chunk and one row, ...) with state slots;
+    H = 3: 24 chains, 16 state columns per scan workgroup; H = 8: 64 chains, 32."""
     rng = np.random.default_rng(11)
     lens = [1, 63, 64, 65, 0, 130, 200, 7]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    H, d, N = 3, 128, len(lens)
+    d, N = 128, len(lens)
     p = workloads.random_problem(rng, int(cu[-1]), H, d, d, io_dtype="bf16")
     p["cu_seqlens"] = cu
     pool = (0.02 * rng.standard_normal((N + 3, H, d, d))).astype(np.float32)
