@@ -2271,16 +2271,16 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
     for (int x = 0; x < 2; ++x) {
       const int u = tid + kGradThreads * x, r = min(u >> 4, c - 1), cc = (u & 15) * 8;
       const size_t gi = (row0 + r * rs) * D + cc;
-      kx[x] = *reinterpret_cast<const uint4*>(k + gi);
-      qx[x] = *reinterpret_cast<const uint4*>(q + gi);
+      kx[x] = nt_load4(k + gi);
+      qx[x] = nt_load4(q + gi);
     }
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int u = tid + kGradThreads * x, r = min(u >> 5, c - 1), cc = (u & 31) * 4;
       if (kGate == kGateChannel) {
-        gx[x] = *reinterpret_cast<const uint4*>(g + (row0 + r * rs) * D + cc);
+        gx[x] = nt_load4(g + (row0 + r * rs) * D + cc);
       } else if (kGate == kGateScalar) {
-        const uint32_t b = __float_as_uint(g[row0 + r * rs]);
+        const uint32_t b = __float_as_uint(nt_load(g + row0 + r * rs));
         gx[x] = make_uint4(b, b, b, b);
       } else {
         gx[x] = make_uint4(0, 0, 0, 0);
@@ -2299,7 +2299,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
     }
   }
   if (tid < C) {
-    const float bt = kAdd ? 1.f : beta[row0 + min(tid, c - 1) * rs];
+    const float bt = kAdd ? 1.f : nt_load(beta + row0 + min(tid, c - 1) * rs);
     sm.bs[tid] = tid < c ? bt : 0.f;
     sm.db[tid] = 0.f;
   }
@@ -2347,7 +2347,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
-        vx[m][jj] = v[(row0 + min(16 * m + 4 * lg + jj, c - 1) * rs) * D + cg];
+        vx[m][jj] = nt_load(v + (row0 + min(16 * m + 4 * lg + jj, c - 1) * rs) * D + cg);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       f32x4 r2 = {0.f, 0.f, 0.f, 0.f};
@@ -2376,8 +2376,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
   for (int hf = 0; hf < 2; ++hf) {
     {
       const int r = tid >> 3, cc = (tid & 7) * 8;
-      const uint4 x = *reinterpret_cast<const uint4*>(d_o + (row0 + min(r, c - 1) * rs) * D +
-                                                      64 * hf + cc);
+      const uint4 x = nt_load4(d_o + (row0 + min(r, c - 1) * rs) * D + 64 * hf + cc);
       *reinterpret_cast<uint4*>(&sm.y.h.dO[r][cc]) = keep_if(x, r < c);
     }
     {
