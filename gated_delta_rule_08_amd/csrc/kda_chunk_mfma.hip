@@ -420,6 +420,11 @@ template <typename T>
 __device__ __forceinline__ T nt_load(const T* p) {
   return __builtin_nontemporal_load(p);
 }
+template <typename T>
+__device__ __forceinline__ T nt_load16(const T* p) {  // any 16-byte operand tile
+  static_assert(sizeof(T) == 16, "16-byte loads");
+  return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const ntu32x4*>(p)));
+}
 
 template <int kGate, bool kAdd, bool kRaw, int kPart>
 __device__ __forceinline__ void prep_load_part(PrepIn& in, const ItemPos& p, const uint16_t* q,
@@ -2313,7 +2318,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
-        if (m < 2 || s2 == 1) tT[m][s2] = tmt[(m * 2 + s2) * 64 + lane];
+        if (m < 2 || s2 == 1) tT[m][s2] = nt_load16(tmt + (m * 2 + s2) * 64 + lane);
   }
   block_sync();
   {
@@ -2340,7 +2345,8 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
   // pass), then dV = Diag(beta) dR and the dbeta term rowsum(dR * V)
   {
     const bf16x8* duc = reinterpret_cast<const bf16x8*>(w.duc + ci * kUcBytes);
-    const bf16x8 dub0 = duc[(wave * 2 + 0) * 64 + lane], dub1 = duc[(wave * 2 + 1) * 64 + lane];
+    const bf16x8 dub0 = nt_load16(duc + (wave * 2 + 0) * 64 + lane);
+    const bf16x8 dub1 = nt_load16(duc + (wave * 2 + 1) * 64 + lane);
     const int cg = 16 * wave + li;
     uint16_t vx[4][4];  // V at this lane's dR positions, loaded before any is used
 #pragma unroll
@@ -2382,7 +2388,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
     {
       // U from the B-operand layout: [column tile][row half][lane], rows in kpos order
       const int ctl = tid >> 7, s2 = (tid >> 6) & 1, ln = tid & 63;
-      const u16x8 u8 = uc[((4 * hf + ctl) * 2 + s2) * 64 + ln];
+      const u16x8 u8 = nt_load16(uc + ((4 * hf + ctl) * 2 + s2) * 64 + ln);
       const int cl = 16 * ctl + (ln & 15), g4 = ln >> 4;
 #pragma unroll
       for (int e = 0; e < 8; ++e) sm.y.h.U[32 * s2 + kpos(g4, e)][cl] = u8[e];
@@ -2392,7 +2398,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
       // S and X from [column tile][row block of 32][lane], rows in kpos order
       const int u = tid + kGradThreads * x, ctl = u >> 8, s = (u >> 6) & 3, ln = u & 63;
       const size_t idx = (size_t)((4 * hf + ctl) * 4 + s) * 64 + ln;
-      const u16x8 s8 = sc[idx], d8 = dsc[idx];
+      const u16x8 s8 = nt_load16(sc + idx), d8 = nt_load16(dsc + idx);
       const int cl = 16 * ctl + (ln & 15), g4 = ln >> 4;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -2472,7 +2478,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
         const bool low = J <= R;
         const float aq = low && j <= r ? aAq[x][jj] : 0.f;
         const float ak = !kAdd && low && j < r ? -aAk[x][jj] : 0.f;   // dA_kk = -(dR U^T)
-        const float mv = !kAdd && low && j < r ? mk[((R * 4 + J) * 16 + 4 * lg + jj) * 16 + li] : 0.f;
+        const float mv = !kAdd && low && j < r ? nt_load(mk + ((R * 4 + J) * 16 + 4 * lg + jj) * 16 + li) : 0.f;
         // dbeta_r += sum_j dA_kk[r,j] M_kk[r,j]; R is 0 or 1 (x = 0), 2 or 3 (x = 1)
         const float add = ak * mv;
         pb[8 * x + jj] += (R & 1) ? 0.f : add;
