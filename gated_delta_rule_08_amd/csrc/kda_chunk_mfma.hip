@@ -408,9 +408,11 @@ __device__ __forceinline__ void build_header(PrepSmem& sm, const int32_t* __rest
 // issue until the CU's memory pipeline takes them.  Part 0: k, q; part 1: v,
 // beta; parts 2 and 3: the first and last eight of the thread's 16 gate rows
 // (one channel each; a wave reads 64 consecutive channels of a row).
-// The inputs are read once: non-temporal loads, which do not displace what the
-// caches hold (on a cold call that also spares the write-back of the dirty lines
-// they would evict).
+// The per-head rows of q, k, v and the channel gates are read once: non-temporal
+// loads, which do not displace what the caches hold (on a cold call that also
+// spares the write-back of the dirty lines they would evict).  beta and a scalar
+// gate are one value per token and head, so one 128-byte line holds a token's
+// values for many heads and the items of those heads share it: plain loads.
 typedef unsigned int ntu32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 nt_load4(const void* p) {
   const ntu32x4 x = __builtin_nontemporal_load(reinterpret_cast<const ntu32x4*>(p));
@@ -453,8 +455,8 @@ __device__ __forceinline__ void prep_load_part(PrepIn& in, const ItemPos& p, con
     }
     if constexpr (kPart == 1 && !kAdd) {
       const uint32_t bi = __umul24((uint32_t)min(tid & 63, p.c - 1), (uint32_t)H);
-      if (kRaw) in.b16 = nt_load(b16 + bbase + bi);
-      else in.beta = nt_load(beta + bbase + bi);
+      if (kRaw) in.b16 = b16[bbase + bi];
+      else in.beta = beta[bbase + bi];
     }
   } else {
     const int col = tid & (D - 1), qt = tid >> 7;
@@ -463,8 +465,8 @@ __device__ __forceinline__ void prep_load_part(PrepIn& in, const ItemPos& p, con
       const uint32_t row = (uint32_t)min(16 * qt + i, p.c - 1);
       if (kGate == kGateScalar) {
         const uint32_t gi = __umul24(row, (uint32_t)H);
-        if (kRaw) in.gl[i] = nt_load(g16 + bbase + gi);
-        else in.g[i] = nt_load(g + bbase + gi);
+        if (kRaw) in.gl[i] = g16[bbase + gi];
+        else in.g[i] = g[bbase + gi];
       } else if (kGate == kGateChannel) {
         const uint32_t gi = __umul24(row, rowstride) + col;
         if (kRaw) in.gl[i] = nt_load(g16 + base + gi);
@@ -2285,7 +2287,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
       if (kGate == kGateChannel) {
         gx[x] = nt_load4(g + (row0 + r * rs) * D + cc);
       } else if (kGate == kGateScalar) {
-        const uint32_t b = __float_as_uint(nt_load(g + row0 + r * rs));
+        const uint32_t b = __float_as_uint(g[row0 + r * rs]);
         gx[x] = make_uint4(b, b, b, b);
       } else {
         gx[x] = make_uint4(0, 0, 0, 0);
@@ -2304,7 +2306,7 @@ __global__ __launch_bounds__(kGradThreads) void grad_kernel(
     }
   }
   if (tid < C) {
-    const float bt = kAdd ? 1.f : nt_load(beta + row0 + min(tid, c - 1) * rs);
+    const float bt = kAdd ? 1.f : beta[row0 + min(tid, c - 1) * rs];
     sm.bs[tid] = tid < c ? bt : 0.f;
     sm.db[tid] = 0.f;
   }
