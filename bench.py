@@ -13,6 +13,8 @@ resident in HBM before timing starts.
 Each timed step is one prefill pass (then, in its own loop, one decode step).
 Before every timed step a 1 GiB fill evicts the 256 MB Infinity Cache, so
 inputs come from HBM; the fill is outside the HIP events that time the step.
+Each leg runs its W warm-up steps, continued until the GPU has been busy with
+them for 0.1 s (its clocks climb over the first tens of milliseconds of work).
 `value` is prefill tokens/s = T / (mean event time of one kda_chunk_fwd call);
 decode steps/s is reported next to it with its own roofline.  The oracle
 (fp64, host threads) is timed on the same prefill input as a CPU baseline.
@@ -96,6 +98,28 @@ def _events_ms(pairs):
     return [s.elapsed_time(e) for s, e in pairs]
 
 
+# The GPU's clocks climb over the first tens of milliseconds of work after an idle spell
+# (such as the host-side input generation before each leg): measured on the c1 prefill,
+# the first 50 evicted calls after 0.2 s of idle ran 107 -> 91 us, while calls that
+# follow continuous work run at 91 us from the first.  Every leg therefore keeps the GPU
+# busy with its own call for at least this long before the timed steps.
+SETTLE_S = 0.1
+
+
+def _warm(torch, step, flush, warmup):
+    """`warmup` untimed steps (each after an eviction), continued until the GPU has been
+    busy with them for SETTLE_S; the host stays at most 8 calls ahead of the GPU."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < SETTLE_S:
+        flush()
+        step()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def _launch_times(kda, stream, step, steps, flush):
     """Per-launch durations (ms) of `steps` calls, each after an eviction, from HIP events
     that the library records on `stream` after each of its launches."""
@@ -143,10 +167,7 @@ def bench_prefill(kda, torch, steps, warmup, flush):
         kda.kda_chunk_fwd(q, k, v, g, beta, cu, chunk=cfg.chunk, states=states, write_final=True,
                           o=o, workspace=ws, stream=stream)
 
-    for _ in range(warmup):
-        flush()
-        step()
-    torch.cuda.synchronize()
+    _warm(torch, step, flush, warmup)
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for _ in range(steps)]
     t0 = time.perf_counter()
@@ -221,10 +242,7 @@ def bench_variants(kda, torch, steps, warmup, flush):
                 kda.kda_chunk_fwd(q, k, v, gg, bb, cu, chunk=cfg.chunk, states=states,
                                   write_final=True, o=o, workspace=ws, stream=stream, **kw)
 
-        for _ in range(warmup):
-            flush()
-            step()
-        torch.cuda.synchronize()
+        _warm(torch, step, flush, warmup)
         pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                  for _ in range(steps)]
         for s_, e_ in pairs:
@@ -248,10 +266,7 @@ BACKWARD_BYTES_PER_TOKEN_HEAD = (3 * 2 * 128 + 4 * 128 + 4 + 2 * 128) + (3 * 2 *
 def _time_calls(torch, step, steps, warmup, flush):
     """Mean HIP-event time (ms) of step() on the current stream, cache evicted before each."""
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        flush()
-        step()
-    torch.cuda.synchronize()
+    _warm(torch, step, flush, warmup)
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for _ in range(steps)]
     for s_, e_ in pairs:
@@ -287,10 +302,7 @@ def bench_backward(kda, torch, steps, warmup, flush, with_variants=True):
         kda.kda_chunk_bwd(q, k, v, g, beta, cu, do, chunk=cfg.chunk, workspace=ws, stream=stream,
                           out=out)
 
-    for _ in range(warmup):
-        flush()
-        step()
-    torch.cuda.synchronize()
+    _warm(torch, step, flush, warmup)
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for _ in range(steps)]
     for s_, e_ in pairs:
@@ -361,10 +373,7 @@ def bench_decode(kda, torch, steps, warmup, flush):
     def step():
         kda.kda_decode_step(q, k, v, g, beta, states, o=o, stream=stream)
 
-    for _ in range(warmup):
-        flush()
-        step()
-    torch.cuda.synchronize()
+    _warm(torch, step, flush, warmup)
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for _ in range(steps)]
     for s, e in pairs:
@@ -429,10 +438,7 @@ def bench_context(kda, torch, flush, calls=5, warmup=2):
         call = lambda: kda.kda_chunk_fwd(q, k, v, g, beta, cu, chunk=cfg.chunk, states=states,
                                          read_initial=cfg.with_s0, write_final=True, o=o,
                                          workspace=ws)
-        for _ in range(warmup):
-            flush()
-            call()
-        torch.cuda.synchronize()
+        _warm(torch, call, flush, warmup)
         stream = torch.cuda.current_stream()
         ms, per = [], {}
         for _ in range(calls):
