@@ -781,14 +781,53 @@ __device__ __forceinline__ void prep_role(
     }
     lds_barrier();
     if (prefetch) prep_load_part<kGate, kAdd, kRaw, 3>(in, pos, q, k, v, g, beta, H, tid);
+    // The operands of the last phase that do not involve T, for channel tile
+    // `tile` and K half s2 (unit u = 2 tile + s2): Kd^T (stored), (beta K Gam)^T
+    // and beta V in MFMA-operand order, parked in the LDS of the row-side Gram
+    // operands, which nothing reads after the Gram blocks.
+    const int wv = __builtin_amdgcn_readfirstlane(wave);  // scalar role choices
+    auto form_operands = [&](int u) {
+      const int tile = u >> 1, s2 = u & 1, ch = 16 * tile + li;
+      // every read first, then the arithmetic: one LDS round trip, not one per row
+      const float gl = sm.G[C - 1][ch];
+      const float4 b0 = *reinterpret_cast<const float4*>(&sm.bs[32 * s2 + 4 * lg]);
+      const float4 b1 = *reinterpret_cast<const float4*>(&sm.bs[32 * s2 + 16 + 4 * lg]);
+      float kv[8], gv[8], vv[8];
+#pragma unroll
+      for (int qq = 0; qq < 8; ++qq) {
+        const int j = 32 * s2 + kpos(lg, qq);
+        kv[qq] = ld_bf(sm.K[j], ch);
+        gv[qq] = sm.G[j][ch];
+        vv[qq] = ld_bf(sm.V[j], ch);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const float bj[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      float fb[8], fd[8], fv[8];
+#pragma unroll
+      for (int qq = 0; qq < 8; ++qq) {
+        fb[qq] = bj[qq] * kv[qq] * exp2_fast(gv[qq]);
+        fd[qq] = kv[qq] * exp2_fast(gl - gv[qq]);
+        fv[qq] = bj[qq] * vv[qq];  // B operand of Ut for value tile `tile`
+      }
+      uint16_t* kd_out = reinterpret_cast<uint16_t*>(w.kd + ci * kKdBytes);
+      *reinterpret_cast<bf16x8*>(kd_out + ((size_t)u * 64 + lane) * 8) = pack8(fd);
+      sm.rk[u][lane] = pack8(fb);
+      sm.rq[u][lane] = pack8(fv);
+    };
     // Off-diagonal blocks by distance L = R - J, the blocks of one distance in
     // parallel (one wave each): T_RJ = -T_RR X with X = sum_{J<=K<R} A_RK T_KJ,
     // both products on fp32 MFMA.  The second product takes X straight from the
     // accumulators: at step jj lane group g contributes contraction index 4g+jj.
+    // The waves a distance leaves idle form the 16 operand units meanwhile:
+    // units 0-4 at distance 1 (waves 3-7), 5-10 at 2 (waves 2-7), 11-15 at 3
+    // (waves 1-5).
 #pragma unroll
     for (int L = 1; L < 4; ++L) {
-      if (wave < 4 - L) {
-        const int J = wave, R = J + L;
+      if (wv >= 4 - L) {
+        const int u = (L == 1 ? 0 : L == 2 ? 5 : 11) + wv - (4 - L);
+        if (u < 16) form_operands(u);
+      } else {
+        const int J = wv, R = J + L;
         f32x4 x = {0.f, 0.f, 0.f, 0.f};
         for (int Kb = J; Kb < R; ++Kb)
 #pragma unroll
@@ -831,25 +870,14 @@ __device__ __forceinline__ void prep_role(
           const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
           tt[m][s2] = pack8(f);
         }
-      const int tile = wave, ch = 16 * tile + li;
-      // (beta K Gam)^T (A operand of W^T) and Kd^T (stored) for channel tile `tile`
-      uint16_t* kd_out = reinterpret_cast<uint16_t*>(w.kd + ci * kKdBytes);
-      const float gl = sm.G[C - 1][ch];
+      const int tile = wave;
+      // (beta K Gam)^T (A operand of W^T) and beta V (B operand of Ut) for channel
+      // tile `tile`, formed during the off-diagonal blocks
       bf16x8 abkg[2], bv[2];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        float fb[8], fd[8], fv[8];
-#pragma unroll
-        for (int qq = 0; qq < 8; ++qq) {
-          const int j = 32 * s2 + kpos(lg, qq);
-          const float kv = ld_bf(sm.K[j], ch), gv = sm.G[j][ch], bj = sm.bs[j];
-          fb[qq] = bj * kv * exp2_fast(gv);
-          fd[qq] = kv * exp2_fast(gl - gv);
-          fv[qq] = bj * ld_bf(sm.V[j], ch);  // B operand of Ut for value tile `tile`
-        }
-        *reinterpret_cast<bf16x8*>(kd_out + ((size_t)(tile * 2 + s2) * 64 + lane) * 8) = pack8(fd);
-        abkg[s2] = pack8(fb);
-        bv[s2] = pack8(fv);
+        abkg[s2] = sm.rk[tile * 2 + s2][lane];
+        bv[s2] = sm.rq[tile * 2 + s2][lane];
       }
       // -W: [m = nt][s = tile / 2][lane][slots (tile & 1) * 4 ..]
       uint16_t* wn_out = reinterpret_cast<uint16_t*>(w.wn + ci * kWnBytes);
@@ -911,12 +939,16 @@ __device__ __forceinline__ void prep_role(
         const int ch = 16 * wave + li;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          float fq[8];
+          float qv[8], gv[8], fq[8];
 #pragma unroll
           for (int qq = 0; qq < 8; ++qq) {
             const int j = 32 * s2 + kpos(lg, qq);
-            fq[qq] = ld_bf(sm.Q[j], ch) * exp2_fast(sm.G[j][ch]);
+            qv[qq] = ld_bf(sm.Q[j], ch);
+            gv[qq] = sm.G[j][ch];
           }
+          __builtin_amdgcn_sched_barrier(0);  // the reads together, then the arithmetic
+#pragma unroll
+          for (int qq = 0; qq < 8; ++qq) fq[qq] = qv[qq] * exp2_fast(gv[qq]);
           *reinterpret_cast<bf16x8*>(w.qgt + ci * kKdBytes +
                                      ((size_t)(wave * 2 + s2) * 64 + lane) * 16) = pack8(fq);
         }
@@ -925,12 +957,17 @@ __device__ __forceinline__ void prep_role(
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int opi = wave * 2 + x, m = opi >> 2, sk = opi & 3, r = 16 * m + li;
-        float fk[8];
+        float kv[8], gl[8], gv[8], fk[8];
 #pragma unroll
         for (int qq = 0; qq < 8; ++qq) {
           const int cc = 32 * sk + kpos(lg, qq);
-          fk[qq] = ld_bf(sm.K[r], cc) * exp2_fast(sm.G[C - 1][cc] - sm.G[r][cc]);
+          kv[qq] = ld_bf(sm.K[r], cc);
+          gl[qq] = sm.G[C - 1][cc];
+          gv[qq] = sm.G[r][cc];
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int qq = 0; qq < 8; ++qq) fk[qq] = kv[qq] * exp2_fast(gl[qq] - gv[qq]);
         *reinterpret_cast<bf16x8*>(w.kdr + ci * kKdBytes + ((size_t)opi * 64 + lane) * 16) = pack8(fk);
       }
     }
