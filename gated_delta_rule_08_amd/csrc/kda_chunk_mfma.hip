@@ -182,10 +182,13 @@ Workspace carve(void* base, int32_t T, int32_t N, int H, bool bwd = false) {
   w.chunk_off = hdr + 3 * N;
   p += header_bytes(N);
   const size_t ci = nchunks_max(T, N) * (size_t)H;
+  // Q*Gam and A_qk in the forward scans' layouts serve only the forward outputs;
+  // the backward reads neither
+  w.qg = w.aq = nullptr;
   w.wn = p; p += align256(ci * kWnBytes);
-  w.qg = p; p += align256(ci * kQgBytes);
+  if (!bwd) { w.qg = p; p += align256(ci * kQgBytes); }
   w.kd = p; p += align256(ci * kKdBytes);
-  w.aq = p; p += align256(ci * kAqBytes);
+  if (!bwd) { w.aq = p; p += align256(ci * kAqBytes); }
   w.ut = p; p += align256(ci * kUtBytes);
   w.gc = p; p += align256(ci * kGcBytes);
   w.sc = w.uc = nullptr;
@@ -619,6 +622,11 @@ __device__ __forceinline__ void prep_role(
   for (; item < total; item += nwg) {
     const size_t ci = (size_t)item;  // items are numbered chunk-major: ci = gc * H + h
     const int c = pos.c;
+    // the next item's position, looked up here so that its header reads are not
+    // on the path of the first prefetch
+    const int next = item + nwg;
+    const bool prefetch = next < total;
+    if (prefetch) pos = where(next);
     lds_barrier();  // the previous item is done with LDS
     prep_stage<kGate, kAdd, kRaw>(sm, in, c, tid, gate_min);
 
@@ -647,17 +655,12 @@ __device__ __forceinline__ void prep_role(
     // (here, before the Gram blocks, before the diagonal inverse, before the
     // off-diagonal blocks), not at the top of the item where the previous
     // item's output stores still occupy the memory pipeline.
-    const int next = item + nwg;
-    const bool prefetch = next < total;
-    if (prefetch) {
-      pos = where(next);
-      prep_load_part<kGate, kAdd, kRaw, 0>(in, pos, q, k, v, g, beta, H, tid);
-    }
+    if (prefetch) prep_load_part<kGate, kAdd, kRaw, 0>(in, pos, q, k, v, g, beta, H, tid);
     lds_barrier();
 
     // ---- row-side Gram operands and Q*Gam, two (block R, K-block s) units per lane
     {
-      uint16_t* qg_out = reinterpret_cast<uint16_t*>(w.qg + ci * kQgBytes);
+      uint16_t* qg_out = kBwd ? nullptr : reinterpret_cast<uint16_t*>(w.qg + ci * kQgBytes);
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int R = (tid >> 8) + 2 * x, s = wave & 3, r = 16 * R + li;
@@ -676,7 +679,8 @@ __device__ __forceinline__ void prep_role(
         }
         sm.rk[R * 4 + s][lane] = pack8(fk);
         sm.rq[R * 4 + s][lane] = pack8(fq);
-        *reinterpret_cast<bf16x8*>(qg_out + ((size_t)(R * 4 + s) * 64 + lane) * 8) = pack8(fg);
+        if constexpr (!kBwd)
+          *reinterpret_cast<bf16x8*>(qg_out + ((size_t)(R * 4 + s) * 64 + lane) * 8) = pack8(fg);
       }
     }
     lds_barrier();
@@ -689,7 +693,7 @@ __device__ __forceinline__ void prep_role(
     // so the dependency chain is 15 steps deep.
     {
       const int wv = __builtin_amdgcn_readfirstlane(wave);  // scalar role choices
-      uint16_t* aq_out = reinterpret_cast<uint16_t*>(w.aq + ci * kAqBytes);
+      uint16_t* aq_out = kBwd ? nullptr : reinterpret_cast<uint16_t*>(w.aq + ci * kAqBytes);
       auto gram = [&](int R, int J) {
         f32x4 acck, accq;
         const bool wide = fmaxf(sm.spr[2 * R], sm.spr[2 * R + 1]) > kMaxSpread * kLog2e;
@@ -721,11 +725,13 @@ __device__ __forceinline__ void prep_role(
             if (j <= r) sm.A[j][r] = qv[jj];
           }
         }
-        // A_qk as the scan's A operand: [m = R][s' = J / 2][lane][slots (J & 1) * 4 ..]
-        uint16_t* dst = aq_out + ((size_t)(R * 2 + (J >> 1)) * 64 + lane) * 8 + (J & 1) * 4;
-        *reinterpret_cast<uint2*>(dst) =
-            make_uint2((uint32_t)f32_to_bf16(qv[0]) | ((uint32_t)f32_to_bf16(qv[1]) << 16),
-                       (uint32_t)f32_to_bf16(qv[2]) | ((uint32_t)f32_to_bf16(qv[3]) << 16));
+        // A_qk as the forward scan's A operand: [m = R][s' = J / 2][lane][slots (J & 1) * 4 ..]
+        if constexpr (!kBwd) {
+          uint16_t* dst = aq_out + ((size_t)(R * 2 + (J >> 1)) * 64 + lane) * 8 + (J & 1) * 4;
+          *reinterpret_cast<uint2*>(dst) =
+              make_uint2((uint32_t)f32_to_bf16(qv[0]) | ((uint32_t)f32_to_bf16(qv[1]) << 16),
+                         (uint32_t)f32_to_bf16(qv[2]) | ((uint32_t)f32_to_bf16(qv[3]) << 16));
+        }
       };
       auto invert_diag = [&](int J) {
         if (lane < 16) {
@@ -743,6 +749,7 @@ __device__ __forceinline__ void prep_role(
       };
       auto zero_aq_upper = [&]() {
         // blocks above the diagonal stored by the scan: (R, J) = (0,1), (2,3)
+        if constexpr (kBwd) return;
         const uint2 z = make_uint2(0, 0);
         *reinterpret_cast<uint2*>(aq_out + ((size_t)(0 * 2 + 0) * 64 + lane) * 8 + 4) = z;
         *reinterpret_cast<uint2*>(aq_out + ((size_t)(2 * 2 + 1) * 64 + lane) * 8 + 4) = z;
@@ -2767,9 +2774,10 @@ kda_status_t launch_chunk_mfma(const kda_shape_t* sh, int32_t T, int32_t N, cons
 
 size_t chunk_mfma_bwd_workspace_bytes(int H, int32_t T, int32_t N) {
   const size_t ci = nchunks_max(T, N) * (size_t)H;
-  return header_bytes(N) + align256(ci * kWnBytes) + align256(ci * kQgBytes) +
-         align256(ci * kKdBytes) + align256(ci * kAqBytes) + align256(ci * kUtBytes) +
-         align256(ci * kGcBytes) + align256(ci * kScBytes) + align256(ci * kUcBytes) +
+  // carve(..., bwd = true): no Q*Gam or A_qk in the forward scans' layouts
+  return header_bytes(N) + align256(ci * kWnBytes) + align256(ci * kKdBytes) +
+         align256(ci * kUtBytes) + align256(ci * kGcBytes) + align256(ci * kScBytes) +
+         align256(ci * kUcBytes) +
          3 * align256(ci * kKdBytes) + align256(ci * kAqBytes) + align256(ci * kMkBytes) +
          align256(ci * kTmBytes) + align256(ci * kScBytes) + align256(ci * kUcBytes) + 256;
 }

@@ -283,7 +283,7 @@ size_t kda_chunk_bwd_workspace_bytes(const kda_shape_t* shape, int32_t chunk,
  *                KDA_ADDITIVE; KDA_WRITE_FINAL_STATE and unknown bits are
  *                KDA_ERR_INVALID_ARGUMENT.
  * workspace      device scratch of kda_chunk_bwd_workspace_bytes() bytes, 256-byte
- *                aligned (248.5 KiB per chunk and head of chunk capacity, the capacity
+ *                aligned (224.5 KiB per chunk and head of chunk capacity, the capacity
  *                being total_tokens / chunk + num_seqs chunks, plus a small header).
  * Supported: io_dtype KDA_BF16, dk = dv = 128, chunk 64 (else KDA_ERR_UNSUPPORTED).
  * num_seqs == 0 is a no-op returning KDA_OK.  total_tokens == 0 makes every

@@ -204,16 +204,16 @@ def test_header_alignment_contract_matches_validation():
     assert "o           device [total_tokens, H, dv], io dtype, fully overwritten;\n" \
            " *             16-byte aligned" in text
     assert "q, k, v, states  16-byte aligned" in text
-    assert "248.5 KiB per chunk and head" in text
+    assert "224.5 KiB per chunk and head" in text
 
 
 def test_backward_workspace_per_chunk_head(lib):
-    """248.5 KiB of operands per (chunk, head) of capacity, plus a header under 4 KiB."""
+    """224.5 KiB of operands per (chunk, head) of capacity, plus a header under 4 KiB."""
     sh = _shape(16, 128, 128, 1)
     a = lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(sh), 64, 4096, 1)
     b = lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(sh), 64, 8192, 1)
-    assert b - a == 64 * 16 * int(248.5 * 1024)
-    assert 0 <= a - 65 * 16 * int(248.5 * 1024) < 8192
+    assert b - a == 64 * 16 * int(224.5 * 1024)
+    assert 0 <= a - 65 * 16 * int(224.5 * 1024) < 8192
 
 
 def test_noalloc_prefill_validation(lib):
