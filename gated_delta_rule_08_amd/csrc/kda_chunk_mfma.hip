@@ -754,7 +754,7 @@ __device__ __forceinline__ void prep_role(
         *reinterpret_cast<uint2*>(aq_out + ((size_t)(0 * 2 + 0) * 64 + lane) * 8 + 4) = z;
         *reinterpret_cast<uint2*>(aq_out + ((size_t)(2 * 2 + 1) * 64 + lane) * 8 + 4) = z;
       };
-      if constexpr (!kAdd && !kBwd) {
+      if constexpr (!kAdd) {
         // Round 1: wave w < 4 forms the diagonal pair (w, w), waves 4..7 the
         // pairs (1,0) (2,1) (3,2) (2,0).  Round 2: waves 0..3 invert their own
         // diagonal block (no barrier: the wave wrote it itself, and a wave's LDS
@@ -771,7 +771,7 @@ __device__ __forceinline__ void prep_role(
         else if (wv < 6) gram(3, 5 - wv);  // wave 4: (3,1), wave 5: (3,0)
         if (prefetch) prep_load_part<kGate, kAdd, kRaw, 2>(in, pos, q, k, v, g, beta, H, tid);
       } else {
-        // The variants that hold more registers take the 10 pairs in the order
+        // The additive write (no inverse: T = I) takes the 10 pairs in the order
         // (3,3) (3,2) (3,1) (3,0) (2,2) (2,1) (2,0) (1,1) (1,0) (0,0), computed
         // rather than read from a table (a memory read would wait for the next
         // item's prefetched loads), and invert after a barrier.
