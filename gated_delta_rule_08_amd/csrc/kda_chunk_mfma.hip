@@ -771,7 +771,7 @@ __device__ __forceinline__ void prep_role(
         else if (wv < 6) gram(3, 5 - wv);  // wave 4: (3,1), wave 5: (3,0)
         if (prefetch) prep_load_part<kGate, kAdd, kRaw, 2>(in, pos, q, k, v, g, beta, H, tid);
       } else {
-        // The additive write (no inverse: T = I) takes the 10 pairs in the order
+        // The additive write (A_kk = 0, so T = I) takes the 10 pairs in the order
         // (3,3) (3,2) (3,1) (3,0) (2,2) (2,1) (2,0) (1,1) (1,0) (0,0), computed
         // rather than read from a table (a memory read would wait for the next
         // item's prefetched loads), and invert after a barrier.
