@@ -687,6 +687,43 @@ __device__ __forceinline__ void prep_role(
 
     if (prefetch) prep_load_part<kGate, kAdd, kRaw, 1>(in, pos, q, k, v, g, beta, H, tid);
 
+    // The backward's (Q*Gam)^T and Kd operand tiles need K, Q and G only.  Unit b < 16:
+    // (Q*Gam)^T as the reverse scan's A operand (M = channel, K = row), channel tile
+    // b >> 1, K half b & 1; unit b >= 16: Kd as an A operand (M = row, K = channel),
+    // tile b - 16.  Waves that the Gram round and the last off-diagonal distance leave
+    // idle take units 12-15 and 28-31; the item's tail takes the other 24.
+    auto bwd_unit = [&](int b) {
+      if (b < 16) {
+        const int ch = 16 * (b >> 1) + li, s2 = b & 1;
+        float qv[8], gv[8], fq[8];
+#pragma unroll
+        for (int qq = 0; qq < 8; ++qq) {
+          const int j = 32 * s2 + kpos(lg, qq);
+          qv[qq] = ld_bf(sm.Q[j], ch);
+          gv[qq] = sm.G[j][ch];
+        }
+        __builtin_amdgcn_sched_barrier(0);  // the reads together, then the arithmetic
+#pragma unroll
+        for (int qq = 0; qq < 8; ++qq) fq[qq] = qv[qq] * exp2_fast(gv[qq]);
+        *reinterpret_cast<bf16x8*>(w.qgt + ci * kKdBytes + ((size_t)b * 64 + lane) * 16) = pack8(fq);
+      } else {
+        const int opi = b - 16, m = opi >> 2, sk = opi & 3, r = 16 * m + li;
+        float kv[8], gl[8], gv[8], fk[8];
+#pragma unroll
+        for (int qq = 0; qq < 8; ++qq) {
+          const int cc = 32 * sk + kpos(lg, qq);
+          kv[qq] = ld_bf(sm.K[r], cc);
+          gl[qq] = sm.G[C - 1][cc];
+          gv[qq] = sm.G[r][cc];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int qq = 0; qq < 8; ++qq) fk[qq] = kv[qq] * exp2_fast(gl[qq] - gv[qq]);
+        *reinterpret_cast<bf16x8*>(w.kdr + ci * kKdBytes + ((size_t)opi * 64 + lane) * 16) = pack8(fk);
+      }
+    };
+    constexpr bool kEarlyUnits = kBwd && !kAdd;
+
     // ---- gated Gram blocks, then the diagonal blocks of T = (I + A_kk)^-1.
     // T_JJ = (I + A_JJ)^-1 by right-looking forward substitution (wave J, lane =
     // column): once x[m] is final it is eliminated from every later row at once,
@@ -767,8 +804,14 @@ __device__ __forceinline__ void prep_role(
           gram(x == 3 ? 2 : x + 1, x == 3 ? 0 : x);
         }
         if (wv == 7) zero_aq_upper();
-        if (wv < 4) invert_diag(wv);
-        else if (wv < 6) gram(3, 5 - wv);  // wave 4: (3,1), wave 5: (3,0)
+        if (wv < 4) {
+          invert_diag(wv);
+        } else if (wv < 6) {
+          gram(3, 5 - wv);  // wave 4: (3,1), wave 5: (3,0)
+        } else if constexpr (kEarlyUnits) {
+          bwd_unit(12 + 2 * (wv - 6));
+          bwd_unit(13 + 2 * (wv - 6));
+        }
         if (prefetch) prep_load_part<kGate, kAdd, kRaw, 2>(in, pos, q, k, v, g, beta, H, tid);
       } else {
         // The additive write (A_kk = 0, so T = I) takes the 10 pairs in the order
@@ -832,7 +875,12 @@ __device__ __forceinline__ void prep_role(
     for (int L = 1; L < 4; ++L) {
       if (wv >= 4 - L) {
         const int u = (L == 1 ? 0 : L == 2 ? 5 : 11) + wv - (4 - L);
-        if (u < 16) form_operands(u);
+        if (u < 16) {
+          form_operands(u);
+        } else if constexpr (kEarlyUnits) {  // waves 6 and 7 at distance 3
+          bwd_unit(28 + 2 * (wv - 6));
+          bwd_unit(29 + 2 * (wv - 6));
+        }
       } else {
         const int J = wv, R = J + L;
         f32x4 x = {0.f, 0.f, 0.f, 0.f};
@@ -941,41 +989,16 @@ __device__ __forceinline__ void prep_role(
           if (32 * s2 + kpos(lg, e) < j) f[e] = 0.f;
         *reinterpret_cast<bf16x8*>(w.aqt + ci * kAqBytes + ((size_t)wave * 64 + lane) * 16) = pack8(f);
       }
-      {
-        // (Q*Gam)^T as the reverse scan's A operand (M = channel, K = row)
-        const int ch = 16 * wave + li;
+      // the units not taken earlier: 24 (three per wave), or all 32 (four per wave)
+      if constexpr (kEarlyUnits) {
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          float qv[8], gv[8], fq[8];
-#pragma unroll
-          for (int qq = 0; qq < 8; ++qq) {
-            const int j = 32 * s2 + kpos(lg, qq);
-            qv[qq] = ld_bf(sm.Q[j], ch);
-            gv[qq] = sm.G[j][ch];
-          }
-          __builtin_amdgcn_sched_barrier(0);  // the reads together, then the arithmetic
-#pragma unroll
-          for (int qq = 0; qq < 8; ++qq) fq[qq] = qv[qq] * exp2_fast(gv[qq]);
-          *reinterpret_cast<bf16x8*>(w.qgt + ci * kKdBytes +
-                                     ((size_t)(wave * 2 + s2) * 64 + lane) * 16) = pack8(fq);
+        for (int x = 0; x < 3; ++x) {
+          const int idx = 3 * wv + x;
+          bwd_unit(idx < 12 ? idx : idx + 4);
         }
-      }
-      // Kd as an A operand (M = row, K = channel), two operand tiles per wave
+      } else {
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int opi = wave * 2 + x, m = opi >> 2, sk = opi & 3, r = 16 * m + li;
-        float kv[8], gl[8], gv[8], fk[8];
-#pragma unroll
-        for (int qq = 0; qq < 8; ++qq) {
-          const int cc = 32 * sk + kpos(lg, qq);
-          kv[qq] = ld_bf(sm.K[r], cc);
-          gl[qq] = sm.G[C - 1][cc];
-          gv[qq] = sm.G[r][cc];
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int qq = 0; qq < 8; ++qq) fk[qq] = kv[qq] * exp2_fast(gl[qq] - gv[qq]);
-        *reinterpret_cast<bf16x8*>(w.kdr + ci * kKdBytes + ((size_t)opi * 64 + lane) * 16) = pack8(fk);
+        for (int x = 0; x < 4; ++x) bwd_unit(x < 2 ? 2 * wv + x : 16 + 2 * wv + (x - 2));
       }
     }
   }
