@@ -724,12 +724,53 @@ __device__ __forceinline__ void prep_role(
     };
     constexpr bool kEarlyUnits = kBwd && !kAdd;
 
+    const int wv = __builtin_amdgcn_readfirstlane(wave);  // scalar role choices
+    // The operands of the last phase that do not involve T, for channel tile
+    // `tile` and K half s2 (unit u = 2 tile + s2): Kd^T (stored), (beta K Gam)^T
+    // and beta V in MFMA-operand order (ob, ov), parked in the LDS of the row-side
+    // Gram operands once nothing reads those any more (after the Gram blocks).
+    auto form_operands = [&](int u, bf16x8& ob, bf16x8& ov) {
+      const int tile = u >> 1, s2 = u & 1, ch = 16 * tile + li;
+      // every read first, then the arithmetic: one LDS round trip, not one per row
+      const float gl = sm.G[C - 1][ch];
+      const float4 b0 = *reinterpret_cast<const float4*>(&sm.bs[32 * s2 + 4 * lg]);
+      const float4 b1 = *reinterpret_cast<const float4*>(&sm.bs[32 * s2 + 16 + 4 * lg]);
+      float kv[8], gv[8], vv[8];
+#pragma unroll
+      for (int qq = 0; qq < 8; ++qq) {
+        const int j = 32 * s2 + kpos(lg, qq);
+        kv[qq] = ld_bf(sm.K[j], ch);
+        gv[qq] = sm.G[j][ch];
+        vv[qq] = ld_bf(sm.V[j], ch);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const float bj[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      float fb[8], fd[8], fv[8];
+#pragma unroll
+      for (int qq = 0; qq < 8; ++qq) {
+        fb[qq] = bj[qq] * kv[qq] * exp2_fast(gv[qq]);
+        fd[qq] = kv[qq] * exp2_fast(gl - gv[qq]);
+        fv[qq] = bj[qq] * vv[qq];  // B operand of Ut for value tile `tile`
+      }
+      uint16_t* kd_out = reinterpret_cast<uint16_t*>(w.kd + ci * kKdBytes);
+      *reinterpret_cast<bf16x8*>(kd_out + ((size_t)u * 64 + lane) * 8) = pack8(fd);
+      ob = pack8(fb);
+      ov = pack8(fv);
+    };
+    auto park = [&](int u, const bf16x8& ob, const bf16x8& ov) {
+      sm.rk[u][lane] = ob;
+      sm.rq[u][lane] = ov;
+    };
+    // the forward's units 0-3, formed by waves 6 and 7 beside the diagonal inverse
+    // (the Gram blocks may still read the LDS they go to) and parked at distance 1
+    constexpr bool kFwdEarly = !kAdd && !kBwd;
+    bf16x8 held[4];
+
     // ---- gated Gram blocks, then the diagonal blocks of T = (I + A_kk)^-1.
     // T_JJ = (I + A_JJ)^-1 by right-looking forward substitution (wave J, lane =
     // column): once x[m] is final it is eliminated from every later row at once,
     // so the dependency chain is 15 steps deep.
     {
-      const int wv = __builtin_amdgcn_readfirstlane(wave);  // scalar role choices
       uint16_t* aq_out = kBwd ? nullptr : reinterpret_cast<uint16_t*>(w.aq + ci * kAqBytes);
       auto gram = [&](int R, int J) {
         f32x4 acck, accq;
@@ -811,6 +852,9 @@ __device__ __forceinline__ void prep_role(
         } else if constexpr (kEarlyUnits) {
           bwd_unit(12 + 2 * (wv - 6));
           bwd_unit(13 + 2 * (wv - 6));
+        } else {
+          form_operands(2 * (wv - 6), held[0], held[1]);
+          form_operands(2 * (wv - 6) + 1, held[2], held[3]);
         }
         if (prefetch) prep_load_part<kGate, kAdd, kRaw, 2>(in, pos, q, k, v, g, beta, H, tid);
       } else {
@@ -831,55 +875,42 @@ __device__ __forceinline__ void prep_role(
     }
     lds_barrier();
     if (prefetch) prep_load_part<kGate, kAdd, kRaw, 3>(in, pos, q, k, v, g, beta, H, tid);
-    // The operands of the last phase that do not involve T, for channel tile
-    // `tile` and K half s2 (unit u = 2 tile + s2): Kd^T (stored), (beta K Gam)^T
-    // and beta V in MFMA-operand order, parked in the LDS of the row-side Gram
-    // operands, which nothing reads after the Gram blocks.
-    const int wv = __builtin_amdgcn_readfirstlane(wave);  // scalar role choices
-    auto form_operands = [&](int u) {
-      const int tile = u >> 1, s2 = u & 1, ch = 16 * tile + li;
-      // every read first, then the arithmetic: one LDS round trip, not one per row
-      const float gl = sm.G[C - 1][ch];
-      const float4 b0 = *reinterpret_cast<const float4*>(&sm.bs[32 * s2 + 4 * lg]);
-      const float4 b1 = *reinterpret_cast<const float4*>(&sm.bs[32 * s2 + 16 + 4 * lg]);
-      float kv[8], gv[8], vv[8];
-#pragma unroll
-      for (int qq = 0; qq < 8; ++qq) {
-        const int j = 32 * s2 + kpos(lg, qq);
-        kv[qq] = ld_bf(sm.K[j], ch);
-        gv[qq] = sm.G[j][ch];
-        vv[qq] = ld_bf(sm.V[j], ch);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      const float bj[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-      float fb[8], fd[8], fv[8];
-#pragma unroll
-      for (int qq = 0; qq < 8; ++qq) {
-        fb[qq] = bj[qq] * kv[qq] * exp2_fast(gv[qq]);
-        fd[qq] = kv[qq] * exp2_fast(gl - gv[qq]);
-        fv[qq] = bj[qq] * vv[qq];  // B operand of Ut for value tile `tile`
-      }
-      uint16_t* kd_out = reinterpret_cast<uint16_t*>(w.kd + ci * kKdBytes);
-      *reinterpret_cast<bf16x8*>(kd_out + ((size_t)u * 64 + lane) * 8) = pack8(fd);
-      sm.rk[u][lane] = pack8(fb);
-      sm.rq[u][lane] = pack8(fv);
-    };
     // Off-diagonal blocks by distance L = R - J, the blocks of one distance in
     // parallel (one wave each): T_RJ = -T_RR X with X = sum_{J<=K<R} A_RK T_KJ,
     // both products on fp32 MFMA.  The second product takes X straight from the
     // accumulators: at step jj lane group g contributes contraction index 4g+jj.
-    // The waves a distance leaves idle form the 16 operand units meanwhile:
-    // units 0-4 at distance 1 (waves 3-7), 5-10 at 2 (waves 2-7), 11-15 at 3
-    // (waves 1-5).
+    // The waves a distance leaves idle form the 16 operand units meanwhile.  The
+    // forward: units 0-3 formed earlier are parked at distance 1, which forms none
+    // (its blocks are the shortest), 4-9 at 2 (waves 2-7), 10-15 at 3 (waves 1-6).
+    // The other variants: units 0-4 at distance 1 (waves 3-7), 5-10 at 2 (waves
+    // 2-7), 11-15 at 3 (waves 1-5).
 #pragma unroll
     for (int L = 1; L < 4; ++L) {
       if (wv >= 4 - L) {
-        const int u = (L == 1 ? 0 : L == 2 ? 5 : 11) + wv - (4 - L);
-        if (u < 16) {
-          form_operands(u);
-        } else if constexpr (kEarlyUnits) {  // waves 6 and 7 at distance 3
-          bwd_unit(28 + 2 * (wv - 6));
-          bwd_unit(29 + 2 * (wv - 6));
+        if constexpr (kFwdEarly) {
+          if (L == 1) {
+            if (wv >= 6) {
+              park(2 * (wv - 6), held[0], held[1]);
+              park(2 * (wv - 6) + 1, held[2], held[3]);
+            }
+          } else {
+            const int u = (L == 2 ? 4 : 10) + wv - (4 - L);
+            if (u < 16) {
+              bf16x8 ob, ov;
+              form_operands(u, ob, ov);
+              park(u, ob, ov);
+            }
+          }
+        } else {
+          const int u = (L == 1 ? 0 : L == 2 ? 5 : 11) + wv - (4 - L);
+          if (u < 16) {
+            bf16x8 ob, ov;
+            form_operands(u, ob, ov);
+            park(u, ob, ov);
+          } else if constexpr (kEarlyUnits) {  // waves 6 and 7 at distance 3
+            bwd_unit(28 + 2 * (wv - 6));
+            bwd_unit(29 + 2 * (wv - 6));
+          }
         }
       } else {
         const int J = wv, R = J + L;
