@@ -512,6 +512,16 @@ __device__ __forceinline__ uint4 prepare_row8(uint4 raw) {
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// normalize(silu(x)) of an item's raw q and k rows, in their load registers (the 16
+// lanes of a row group hold one row, so every lane takes part)
+__device__ __forceinline__ void prep_raw_qk(PrepIn& in) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    in.k[i] = prepare_row8(in.k[i]);
+    in.q[i] = prepare_row8(in.q[i]);
+  }
+}
+
 template <int kGate, bool kAdd, bool kRaw>
 __device__ __forceinline__ void prep_stage(PrepSmem& sm, const PrepIn& in, int c, int tid,
                                            float gate_min) {
@@ -520,9 +530,9 @@ __device__ __forceinline__ void prep_stage(PrepSmem& sm, const PrepIn& in, int c
   for (int i = 0; i < 2; ++i) {
     const int u = tid + kPrepThreads * i, r = u >> 4, cc = (u & 15) * 8;
     const bool ok = r < c;
-    // kRaw: the 16 lanes of a row group hold one row (every lane takes part in the sum)
-    const uint4 kk = kRaw ? prepare_row8(in.k[i]) : in.k[i];
-    const uint4 qq = kRaw ? prepare_row8(in.q[i]) : in.q[i];
+    // kRaw: q and k arrive prepared (prep_raw_qk, during the previous item)
+    const uint4 kk = in.k[i];
+    const uint4 qq = in.q[i];
     const uint4 a = ok ? kk : z4, b = ok ? qq : z4, d = ok ? in.v[i] : z4;
     uint2* pk = reinterpret_cast<uint2*>(&sm.K[r][cc]);
     uint2* pq = reinterpret_cast<uint2*>(&sm.Q[r][cc]);
@@ -618,6 +628,7 @@ __device__ __forceinline__ void prep_role(
   // prefetched registers only has to cover the loads, not the stores issued
   // after them.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  if constexpr (kRaw) prep_raw_qk(in);
 
   for (; item < total; item += nwg) {
     const size_t ci = (size_t)item;  // items are numbered chunk-major: ci = gc * H + h
@@ -989,6 +1000,11 @@ __device__ __forceinline__ void prep_role(
         else ut_even = u;
       }
       if (tid < D) reinterpret_cast<float*>(w.gc + ci * kGcBytes)[tid] = exp2_fast(sm.G[C - 1][tid]);
+      // the next item's raw q and k (loaded during this item) are prepared here,
+      // where the vector ALU has room, rather than at its staging
+      if constexpr (kRaw) {
+        if (prefetch) prep_raw_qk(in);
+      }
       if constexpr (kBwd) {
         // -W^T (M = channel, K = row): W tiles with rows in the accumulator, packed in pairs
         f32x4 wr[4];
