@@ -50,7 +50,10 @@ namespace {
 
 constexpr int C = 64;     // chunk
 constexpr int D = 128;    // dk = dv
-constexpr int KP = D + 4;  // bf16 LDS row stride (elements); 264 bytes
+// bf16 LDS row stride (elements) of the prep's K, Q, V tiles: 272 bytes, so that a
+// row piece of 8 elements is one 16-byte write and the row reads of the Gram
+// operands (16 rows x 4 lane groups) fall on distinct banks in each half-wave
+constexpr int KP = D + 8;
 constexpr int GP = D + 4;  // fp32 LDS row stride for G
 constexpr int AP = C + 4;  // fp32 LDS row stride for A_kk and T
 constexpr float kMaxSpread = 80.f;
@@ -277,6 +280,7 @@ struct PrepSmem {
   int32_t he[384];       // sanitised ends
   int32_t ho[385];       // chunk offsets (prefix sums of chunk counts, capped)
 };
+static_assert(sizeof(PrepSmem) <= 160 * 1024, "the prep's LDS");
 // Up to this many sequences the prep builds the sequence header in LDS itself
 // (and workgroup 0 publishes it for the later launches), so no separate index
 // launch precedes it.
@@ -534,12 +538,9 @@ __device__ __forceinline__ void prep_stage(PrepSmem& sm, const PrepIn& in, int c
     const uint4 kk = in.k[i];
     const uint4 qq = in.q[i];
     const uint4 a = ok ? kk : z4, b = ok ? qq : z4, d = ok ? in.v[i] : z4;
-    uint2* pk = reinterpret_cast<uint2*>(&sm.K[r][cc]);
-    uint2* pq = reinterpret_cast<uint2*>(&sm.Q[r][cc]);
-    uint2* pv = reinterpret_cast<uint2*>(&sm.V[r][cc]);
-    pk[0] = make_uint2(a.x, a.y); pk[1] = make_uint2(a.z, a.w);
-    pq[0] = make_uint2(b.x, b.y); pq[1] = make_uint2(b.z, b.w);
-    pv[0] = make_uint2(d.x, d.y); pv[1] = make_uint2(d.z, d.w);
+    *reinterpret_cast<uint4*>(&sm.K[r][cc]) = a;
+    *reinterpret_cast<uint4*>(&sm.Q[r][cc]) = b;
+    *reinterpret_cast<uint4*>(&sm.V[r][cc]) = d;
   }
   const float bt = kAdd ? 1.f : kRaw ? sigmoid(bf16_to_f32(in.b16)) : in.beta;
   if (tid < C) sm.bs[tid] = tid < c ? bt : 0.f;
@@ -1051,7 +1052,7 @@ __device__ __forceinline__ void prep_role(
   }
 }
 
-// LDS use (~153 KiB) allows one workgroup (two waves per SIMD) per CU.
+// LDS use (≈ 159 KiB) allows one workgroup (two waves per SIMD) per CU.
 template <int kGate, bool kAdd, bool kRaw, bool kBwd>
 __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
