@@ -616,15 +616,29 @@ __device__ __forceinline__ void prep_role(
   PrepSmem& sm = *reinterpret_cast<PrepSmem*>(smem_raw);
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+  // The first item's loads are issued before the sequence header is known, for the
+  // position the item has when the batch is one sequence from token 0 (chunk wg / H
+  // of head wg % H, rows clamped inside [0, T)), so that they overlap the header's own
+  // loads; a workgroup whose item turns out to lie elsewhere loads it again.
+  PrepIn in;
+  ItemPos spec;
+  spec.gc = wg / H;
+  spec.h = wg - spec.gc * H;
+  spec.t0 = spec.gc * C;
+  spec.c = spec.t0 < T ? min(C, T - spec.t0) : 0;
+  if (spec.c > 0) prep_load<kGate, kAdd, kRaw>(in, spec, q, k, v, g, beta, H, tid);
   if (fused) build_header(sm, cu, N, T, cap, w, wg == 0, tid);
   auto where = [&](int it) { return fused ? locate_lds(sm, N, H, it) : locate(hd, N, H, it); };
   const int total = (fused ? sm.ho[N] : hd.chunk_off[N]) * H;
   int item = wg;
-  if (item >= total) return;  // uniform
+  if (item >= total) {  // uniform
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load left in flight
+    return;
+  }
 
-  PrepIn in;
   ItemPos pos = where(item);
-  prep_load<kGate, kAdd, kRaw>(in, pos, q, k, v, g, beta, H, tid);
+  if (spec.c == 0 || pos.t0 != spec.t0 || pos.c != spec.c || pos.h != spec.h)
+    prep_load<kGate, kAdd, kRaw>(in, pos, q, k, v, g, beta, H, tid);
   // Wait for the first item here, so that inside the loop the wait for the
   // prefetched registers only has to cover the loads, not the stores issued
   // after them.
