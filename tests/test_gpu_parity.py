@@ -361,10 +361,11 @@ def _many_sequences(seed, N, H, max_len):
     return p, s0, rng
 
 
-@pytest.mark.parametrize("N", [385, 520])
-def test_prefill_more_sequences_than_the_fused_header(N):
-    """More than 384 sequences: the sequence header comes from its own launch instead of
-    the prep's LDS copy; every chain is compared (ragged lengths, empty sequences, slots)."""
+@pytest.mark.parametrize("N", [384, 385, 520])
+def test_prefill_sequences_around_the_fused_header_limit(N):
+    """384 sequences (the most for which the prep builds the sequence header itself) and
+    more (the header then comes from its own launch); every chain is compared (ragged
+    lengths, empty sequences, slots)."""
     p, s0, rng = _many_sequences(60 + N, N, 2, 130)
     cu = p["cu_seqlens"]
     _log(f"prefill N={N} T={cu[-1]} H=2 empty={(np.diff(cu) == 0).sum()}")
