@@ -32,9 +32,10 @@
 //     only loop-carried dependency of the method (heqinghuang section 10: the
 //     only sequential loop is over chunks).  The waves of a workgroup share
 //     each chunk's operands through LDS.  With few chains, dedicated loader
-//     waves copy the operands so the compute waves never wait on the copies
-//     (and with very few, a wave of its own forms the outputs beside the state
-//     wave); with many chains, one workgroup per head fetches them once per chunk.
+//     waves copy the operands so the compute waves never wait on the copies,
+//     and output waves of their own form the outputs one step behind the state
+//     waves (a store wave writes them); with many chains, one workgroup per
+//     head fetches them once per chunk.
 //
 // Numerics of the gated Gram products: exp(G_r - G_j) is split at the first
 // row s of the 16-row block of r as exp(G_r - G_s) * exp(G_s - G_j).  For j in
