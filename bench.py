@@ -36,6 +36,7 @@ import gc
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -56,12 +57,20 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 TRAFFIC_BACKWARD_FILE = os.path.join(ROOT, "profiles", "traffic_backward.json")
 
 
+def _code_text(src: str) -> str:
+    """The source with its comments removed and its whitespace collapsed: what the
+    compiler sees, so that an edit of a comment keeps the digest."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def _source_digest() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_delta_rule_08_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 
