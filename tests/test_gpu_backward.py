@@ -103,12 +103,14 @@ def test_backward_long_sequence():
     _case(49, [16384], 2, s0=True, d_final=True)
 
 
-def test_backward_more_sequences_than_the_fused_header():
-    """450 packed sequences of 0-100 tokens (a tenth empty), 2 heads: the sequence header
-    comes from its own launch instead of the prep's LDS copy."""
+@pytest.mark.parametrize("N", [384, 450])
+def test_backward_sequences_around_the_fused_header_limit(N):
+    """384 packed sequences (the most for which the prep builds the sequence header
+    itself) and 450 (the header then comes from its own launch), 0-100 tokens each (a
+    tenth empty), 2 heads."""
     rng = np.random.default_rng(48)
-    lens = rng.integers(1, 101, size=450)
-    lens[rng.random(450) < 0.1] = 0
+    lens = rng.integers(1, 101, size=N)
+    lens[rng.random(N) < 0.1] = 0
     _case(48, [int(x) for x in lens], 2, s0=True, d_final=True)
 
 
